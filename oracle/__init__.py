@@ -1,0 +1,14 @@
+"""CPU oracle of the sparse-MoE FFN layer forward -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import this package.  It shares no code with the HIP library and
+never imports it.  Every function is float64 numpy (``moe_ref``) or pure
+Python (``brute``); see each module's header for the passages it follows.
+"""
+from .moe_ref import (TIE_EPS, MoERef, aux_loss, capacity_of, capacity_ranks, expert_counts,
+                      expert_ffn, gelu, is_valid_topk, moe_forward_ref, moe_forward_ref_from_inputs,
+                      renormalised_weights, router_logits, select_topk, softmax, widen)
+
+__all__ = ["TIE_EPS", "MoERef", "aux_loss", "capacity_of", "capacity_ranks", "expert_counts",
+           "expert_ffn", "gelu", "is_valid_topk", "moe_forward_ref", "moe_forward_ref_from_inputs",
+           "renormalised_weights", "router_logits", "select_topk", "softmax", "widen"]

@@ -1,0 +1,299 @@
+"""CPU oracle of the sparse Mixture-of-Experts FFN layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (``sparse_mixture_experts_28_amd``) and never imports it.
+
+The layer reaches exactly (up to rounding order) a result with a plain
+definition, MoE(x) = sum_i G(x)_i * E_i(x) with G the renormalised top-k
+softmax gate, plus the capacity cap and the shared experts.  So this oracle
+is that definition written out in float64, one step per function, with no
+blocking, fusion or reordering.  bfloat16 inputs (uint16 bit patterns) are
+widened exactly to float64 first; no intermediate is ever rounded.
+
+Pages cited (each by its title and its own section):
+  [guide]    "AI-Research-SKILLs MoE 训练实战：稀疏专家模型的架构、路由、负载均衡与推理优化全指南"
+             (news.rkmt.cn) -- §3.1 basic MoE layer, §4.1 data-flow diagram,
+             §4.2 routing mechanisms, §4.3 auxiliary loss, §7.1 DeepSeekMoE,
+             §7.2 Switch Transformers, §8.2 capacity factor.
+  [tutorial] "混合专家大模型MoE架构选型与部署实践教程" (developer.baidu.com) --
+             part 5, the generic gate / layer pseudo-code (SparseMoEGate, SimpleMoELayer).
+  [bee]      "[BEE-30064] 混合專家架構與服務" -- "專家路由工作原理" (how routing works).
+  [ch7]      "第7章 Mixture of Experts（MoE）架构" (glsqs.com) -- §7.1 formal
+             definition, §7.2 Top-K gating, §7.3 shared experts, §7.4 balance loss
+             and capacity, and the tensor-shape trace.
+
+Readings taken where the pages are silent or disagree (every one is listed
+with its reason in the design notes of this repository):
+  * selection is made on the logits, descending, ties to the lower expert
+    index; softmax-then-top-k and top-k-then-softmax agree exactly;
+  * a token is flagged when its k-th and (k+1)-th largest logits differ by
+    less than TIE_EPS (its routing is then decided by rounding, not by the
+    method); "order-ambiguous" when two adjacent logits inside its top k do;
+  * aux = E * sum_e f_e P_e with f_e = c_e / (T k) over all k choices before
+    any capacity drop, P_e the mean full softmax over all T tokens, no alpha;
+  * capacity cap = ceil(cf * T / E) in double, counting tokens (not T*k);
+    per expert, assignments are kept in ascending token order; a dropped
+    assignment contributes nothing and the surviving weights are not
+    renormalised;
+  * GELU is the exact erf form; the expert output b2 sits inside the
+    weighted term;
+  * shared experts are stored after the routed ones, weight 1, no capacity.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Callable, Optional, Sequence
+
+import numpy as np
+from scipy.special import erf
+
+TIE_EPS = 1e-6
+
+
+# ---------------------------------------------------------------- inputs --
+def widen(a, kind: str) -> np.ndarray:
+    """Exact conversion of an input array to float64.
+
+    kind "bf16": ``a`` holds bfloat16 bit patterns (uint16); a bfloat16 is
+    the top half of a float32, so shifting left by 16 gives that float32
+    exactly, and float32 -> float64 is exact.  kind "f32": a float32 array.
+    """
+    if kind == "bf16":
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if kind == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if kind == "f64":
+        return np.asarray(a, dtype=np.float64)
+    raise ValueError(f"unknown input kind {kind!r}")
+
+
+# ---------------------------------------------------------------- router --
+def router_logits(x: np.ndarray, W_g: np.ndarray, b_g: Optional[np.ndarray] = None) -> np.ndarray:
+    """l[t,e] = sum_c x[t,c] W_g[e,c] (+ b_g[e]).
+
+    The router is one linear layer d -> E ([bee] "how routing works": bias-free;
+    [guide] §6.1 and [tutorial] part 5 likewise); W_g has the nn.Linear layout
+    [E, d].  The optional b_g is a fixed logit offset used only to skew loads
+    in a synthetic workload ([guide] §4.3 mentions a bias on the logits).
+    """
+    l = x @ W_g.T
+    if b_g is not None:
+        l = l + np.asarray(b_g, dtype=np.float64)[None, :]
+    return l
+
+
+def softmax(l: np.ndarray) -> np.ndarray:
+    """p[t,e] = exp(l[t,e] - m_t) / sum_e' exp(l[t,e'] - m_t), m_t = max_e l[t,e]
+    ([guide] §3.1; [tutorial] part 5: softmax over the expert axis)."""
+    m = l.max(axis=1, keepdims=True)
+    z = np.exp(l - m)
+    return z / z.sum(axis=1, keepdims=True)
+
+
+@dataclass
+class Selection:
+    idx: np.ndarray          # [T,k] int64, slot 0 = largest logit
+    tie_flag: np.ndarray     # [T] bool: k-th vs (k+1)-th logit gap < TIE_EPS
+    order_flag: np.ndarray   # [T] bool: an adjacent gap inside the top k < TIE_EPS
+
+
+def select_topk(l: np.ndarray, k: int, eps: float = TIE_EPS) -> Selection:
+    """The k experts with the largest logits, descending, ties to the lower index.
+
+    ([guide] §3.1 and §4.2; [bee] "how routing works" step 2; [ch7] §7.2 Top-K
+    gating.)  A stable sort of the negated logits keeps equal logits in
+    ascending expert order, which is the tie rule.
+    """
+    T, E = l.shape
+    order = np.argsort(-l, axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int64)
+    s = np.take_along_axis(l, order, axis=1)
+    if k < E:
+        tie = (s[:, k - 1] - s[:, k]) < eps
+    else:
+        tie = np.zeros(T, dtype=bool)
+    if k > 1:
+        order_amb = np.any((s[:, : k - 1] - s[:, 1:k]) < eps, axis=1)
+    else:
+        order_amb = np.zeros(T, dtype=bool)
+    return Selection(idx=idx, tie_flag=tie, order_flag=order_amb)
+
+
+def is_valid_topk(l_row: np.ndarray, chosen: Sequence[int], eps: float = TIE_EPS) -> bool:
+    """True iff ``chosen`` is a set of k distinct experts that is a top-k set
+    of ``l_row`` up to near-ties: no expert left out has a logit more than
+    ``eps`` above the smallest chosen logit."""
+    chosen = [int(c) for c in chosen]
+    E = l_row.shape[0]
+    if len(set(chosen)) != len(chosen) or any(c < 0 or c >= E for c in chosen):
+        return False
+    rest = [e for e in range(E) if e not in set(chosen)]
+    if not rest:
+        return True
+    return float(max(l_row[rest])) <= float(min(l_row[chosen])) + eps
+
+
+def renormalised_weights(p: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """w[t,j] = p[t, idx[t,j]] / sum_j' p[t, idx[t,j']] ([guide] §3.1: the k
+    scores are divided by their sum; [tutorial] part 5 likewise).  Equals the
+    softmax over the k selected logits ([bee] step 3; [ch7] §7.2)."""
+    sel = np.take_along_axis(p, idx, axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def expert_counts(idx: np.ndarray, E: int) -> np.ndarray:
+    """c_e = number of (token, slot) assignments routed to expert e, before capacity."""
+    return np.bincount(idx.ravel(), minlength=E).astype(np.int64)
+
+
+def aux_loss(counts: np.ndarray, p: np.ndarray, k: int) -> tuple[float, np.ndarray, np.ndarray]:
+    """Switch balance loss E * sum_e f_e P_e, unscaled ([guide] §4.3; [ch7] §7.4).
+
+    f_e = c_e / (T k): the fraction of the T*k assignments sent to e;
+    P_e = (1/T) sum_t p[t,e]: the mean router probability of e.
+    Returns (aux, f, P)."""
+    T, E = p.shape
+    f = counts.astype(np.float64) / float(T * k)
+    P = p.mean(axis=0)
+    return float(E * np.sum(f * P)), f, P
+
+
+# -------------------------------------------------------------- capacity --
+def capacity_of(capacity_factor: float, T: int, E: int) -> Optional[int]:
+    """cap = ceil(cf * T / E) computed in double; None (no limit) when cf <= 0.
+
+    [guide] §8.2 and [ch7] §7.4 give C = CF * tokens / experts, counting
+    tokens; the ceiling follows the switch-style workload's own statement."""
+    if capacity_factor is None or capacity_factor <= 0:
+        return None
+    return int(math.ceil(float(capacity_factor) * float(T) / float(E)))
+
+
+def capacity_ranks(idx: np.ndarray, E: int) -> np.ndarray:
+    """rank[t,j] = number of earlier tokens t' < t that were routed to idx[t,j].
+
+    Each expert receives its assignments in ascending token order; a token's
+    k experts are distinct, so the slot index never breaks a tie."""
+    T, k = idx.shape
+    rank = np.empty((T, k), dtype=np.int64)
+    seen = np.zeros(E, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            rank[t, j] = seen[e]
+            seen[e] += 1
+    return rank
+
+
+# ---------------------------------------------------------------- experts --
+def gelu(u: np.ndarray) -> np.ndarray:
+    """GELU, exact erf form: 0.5 u (1 + erf(u / sqrt 2)) (nn.GELU's default,
+    used by the expert FFN of [guide] §3.1)."""
+    return 0.5 * u * (1.0 + erf(u / math.sqrt(2.0)))
+
+
+def expert_ffn(xr: np.ndarray, W1: np.ndarray, b1: np.ndarray, W2: np.ndarray, b2: np.ndarray) -> np.ndarray:
+    """y = W2 GELU(W1 x + b1) + b2 for each row of xr ([guide] §3.1: Linear(d, h),
+    GELU, Linear(h, d), both with bias; [tutorial] part 5 likewise).
+    W1 is [h, d] and W2 is [d, h] (nn.Linear layout)."""
+    u = xr @ W1.T + b1[None, :]
+    return gelu(u) @ W2.T + b2[None, :]
+
+
+# ------------------------------------------------------------------ layer --
+@dataclass
+class MoERef:
+    logits: np.ndarray       # [T,E]
+    probs: np.ndarray        # [T,E]
+    idx: np.ndarray          # [T,k]
+    w: np.ndarray            # [T,k]
+    tie_flag: np.ndarray     # [T]
+    order_flag: np.ndarray   # [T]
+    counts: np.ndarray       # [E] before capacity
+    kept: np.ndarray         # [E] after capacity
+    rank: np.ndarray         # [T,k] token-order rank within the expert
+    slot_kept: np.ndarray    # [T,k] bool
+    slot_pos: np.ndarray     # [T,k] row in the expert-sorted buffer, -1 if dropped
+    offsets: np.ndarray      # [E+1] exclusive scan of kept
+    cap: Optional[int]
+    aux: float
+    f: np.ndarray
+    P: np.ndarray
+    rows: np.ndarray         # token ids whose outputs are in ``out``
+    out: np.ndarray          # [len(rows), d] float64
+
+
+def moe_forward_ref(x, W_g, get_expert: Callable[[int], tuple], E: int, k: int,
+                    capacity_factor: float = 0.0, n_shared: int = 0, b_g=None,
+                    kind: str = "f32", rows: Optional[Sequence[int]] = None,
+                    override_idx: Optional[np.ndarray] = None) -> MoERef:
+    """The whole layer forward in float64.
+
+    x [T,d] and W_g [E,d] are raw inputs of ``kind`` ("f32", "bf16" bit
+    patterns, or "f64"); ``get_expert(e)`` returns the raw (W1 [h,d], b1 [h],
+    W2 [d,h], b2 [d]) of expert e, routed for e < E and shared for
+    E <= e < E + n_shared; b_g is an optional float32 logit offset [E].
+
+    ``rows`` restricts the expert computation to those tokens (routing,
+    counts, capacity and aux always use all T tokens).  ``override_idx``
+    replaces the selection with a given [T,k] choice (used to continue the
+    comparison after a near-tie was resolved the other way by rounding).
+
+    Steps ([guide] §3.1 and §7.1; [ch7] §7.1 MoE(x) = sum G_i E_i(x)):
+      1 logits  2 softmax  3 top-k  4 renormalise  5 counts and aux
+      6 capacity in token order  7 weighted routed experts  8 shared experts.
+    """
+    xf = widen(x, kind)
+    T, d = xf.shape
+    l = router_logits(xf, widen(W_g, kind), b_g)
+    p = softmax(l)
+    sel = select_topk(l, k)
+    idx = sel.idx if override_idx is None else np.asarray(override_idx, dtype=np.int64).reshape(T, k)
+    w = renormalised_weights(p, idx)
+    counts = expert_counts(idx, E)
+    aux, f, P = aux_loss(counts, p, k)
+
+    cap = capacity_of(capacity_factor, T, E)
+    rank = capacity_ranks(idx, E)
+    slot_kept = np.ones((T, k), dtype=bool) if cap is None else (rank < cap)
+    kept = counts.copy() if cap is None else np.minimum(counts, cap)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept)
+    slot_pos = np.where(slot_kept, offsets[idx] + rank, -1)
+
+    rows_arr = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    want = np.zeros(T, dtype=bool)
+    want[rows_arr] = True
+    row_of = np.full(T, -1, dtype=np.int64)
+    row_of[rows_arr] = np.arange(rows_arr.size)
+    out = np.zeros((rows_arr.size, d), dtype=np.float64)
+
+    for e in range(E):
+        tok, slot = np.nonzero((idx == e) & slot_kept & want[:, None])
+        if tok.size == 0:
+            continue
+        W1, b1, W2, b2 = (widen(a, kind) for a in get_expert(e))
+        y = expert_ffn(xf[tok], W1, b1, W2, b2)
+        # a token occurs at most once per expert, so this scatter has no collisions
+        out[row_of[tok]] += w[tok, slot][:, None] * y
+
+    for s in range(n_shared):
+        W1, b1, W2, b2 = (widen(a, kind) for a in get_expert(E + s))
+        out += expert_ffn(xf[rows_arr], W1, b1, W2, b2)
+
+    return MoERef(logits=l, probs=p, idx=idx, w=w, tie_flag=sel.tie_flag,
+                  order_flag=sel.order_flag, counts=counts, kept=kept, rank=rank,
+                  slot_kept=slot_kept, slot_pos=slot_pos, offsets=offsets, cap=cap,
+                  aux=aux, f=f, P=P, rows=rows_arr, out=out)
+
+
+def moe_forward_ref_from_inputs(inp, rows=None, override_idx=None) -> MoERef:
+    """Convenience wrapper over an object with ``cfg``, ``x``, ``W_g``, ``b_g``
+    and ``expert(e)`` (the seeded workload generator's interface)."""
+    c = inp.cfg
+    return moe_forward_ref(inp.x, inp.W_g, inp.expert, c.E, c.k, c.cf, c.S, inp.b_g,
+                           kind=c.dtype, rows=rows, override_idx=override_idx)

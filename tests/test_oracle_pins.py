@@ -1,0 +1,370 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of the pages prints a worked numeric example of the layer, so the
+oracle is pinned by: hand-derived closed-form fixtures (tests/golden, each
+citing the passage it follows), brute force on tiny inputs (oracle.brute,
+an independent scalar derivation), library routines (torch CPU float64
+topk / gelu / linear), closed forms of the balance loss, capacity
+invariants, and symmetry properties of the combine.  Each check is a plain
+function so ``test_oracle_mutants`` can plant mistakes in the oracle and
+show that some pin catches every one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle.moe_ref as ref
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------ helpers --
+def rand_case(rng, T, d, h, E, k, S=0, wscale=1.0, bias=True):
+    x = rng.standard_normal((T, d))
+    W_g = rng.standard_normal((E, d)) * wscale
+    experts = []
+    for _ in range(E + S):
+        W1 = rng.standard_normal((h, d)) * 0.5
+        b1 = rng.standard_normal(h) * 0.3 if bias else np.zeros(h)
+        W2 = rng.standard_normal((d, h)) * 0.5
+        b2 = rng.standard_normal(d) * 0.3 if bias else np.zeros(d)
+        experts.append((W1, b1, W2, b2))
+    return x, W_g, experts
+
+
+def run_ref(x, W_g, experts, E, k, cf=0.0, S=0, b_g=None, **kw):
+    return ref.moe_forward_ref(x, W_g, lambda e: experts[e], E, k, cf, S, b_g, kind="f64", **kw)
+
+
+def to_lists(a):
+    return [list(map(float, r)) for r in np.asarray(a)]
+
+
+def brute_case(x, W_g, experts, k, cap=None, S=0, b_g=None):
+    ex = [(to_lists(W1), list(map(float, b1)), to_lists(W2), list(map(float, b2)))
+          for (W1, b1, W2, b2) in experts]
+    return brute.brute_layer(to_lists(x), to_lists(W_g), ex, k, cap=cap, n_shared=S,
+                             b_g=None if b_g is None else list(map(float, b_g)))
+
+
+def ffn_torch(xr, W1, b1, W2, b2):
+    """Library-routine expert FFN: torch CPU float64 linear + exact GELU."""
+    import torch
+    import torch.nn.functional as F
+    t = lambda a: torch.as_tensor(np.asarray(a), dtype=torch.float64)
+    u = F.linear(t(xr), t(W1), t(b1))
+    return F.linear(F.gelu(u, approximate="none"), t(W2), t(b2)).numpy()
+
+
+# --------------------------------------------------------------- checks --
+def check_weights_sum_to_one():
+    """Renormalised top-k weights sum to 1 per token ([guide] §3.1 comment on the
+    renormalisation; §4.1 diagram 0.6 + 0.4); k = 1 gives weight 1 exactly."""
+    rng = np.random.default_rng(1)
+    for (T, d, E, k) in [(50, 8, 6, 2), (40, 5, 7, 3), (30, 4, 4, 1), (20, 6, 9, 9)]:
+        x, W_g, ex = rand_case(rng, T, d, 3, E, k)
+        r = run_ref(x, W_g, ex, E, k)
+        assert np.allclose(r.w.sum(1), 1.0, atol=1e-12, rtol=0)
+        assert np.all(r.w > 0)
+        if k == 1:
+            assert np.all(r.w == 1.0)
+        # weights follow the selection order (descending logits)
+        assert np.all(np.diff(r.w, axis=1) <= 1e-15)
+
+
+def check_against_brute():
+    """Oracle == brute force (subset enumeration, explicit queues, scalar loops)."""
+    rng = np.random.default_rng(2)
+    cases = [(6, 4, 3, 4, 2, 0, None), (8, 3, 2, 5, 3, 0, None), (7, 2, 4, 3, 1, 0, 0.5),
+             (8, 3, 3, 5, 2, 1, 1.0), (5, 4, 2, 2, 2, 2, None), (8, 2, 3, 4, 2, 0, 0.5),
+             (8, 3, 2, 5, 1, 0, 1.0), (4, 3, 3, 3, 3, 1, 0.5)]
+    for (T, d, h, E, k, S, cf) in cases:
+        for trial in range(3):
+            x, W_g, ex = rand_case(rng, T, d, h, E, k, S)
+            b_g = rng.standard_normal(E) if trial == 2 else None
+            r = run_ref(x, W_g, ex, E, k, cf or 0.0, S, b_g)
+            assert not r.tie_flag.any()
+            cap = None if not cf else int(math.ceil(cf * T / E))
+            b = brute_case(x, W_g, ex, k, cap=cap, S=S, b_g=b_g)
+            assert r.idx.tolist() == b["idx"]
+            assert np.allclose(r.w, np.array(b["w"]), rtol=0, atol=1e-13)
+            assert r.counts.tolist() == b["counts"]
+            assert r.kept.tolist() == b["kept"]
+            assert (r.counts - r.kept).tolist() == b["dropped"]
+            assert r.slot_kept.tolist() == b["slot_kept"]
+            assert abs(r.aux - b["aux"]) < 1e-13
+            assert np.allclose(r.out, np.array(b["out"]), rtol=0, atol=1e-11)
+
+
+def check_topk_vs_torch():
+    """The top-k set and order equal torch.topk (CPU float64) on unflagged tokens."""
+    import torch
+    rng = np.random.default_rng(3)
+    for (T, d, E, k) in [(300, 16, 8, 2), (200, 32, 64, 1), (100, 24, 256, 8), (64, 8, 5, 5)]:
+        x, W_g, _ = rand_case(rng, T, d, 2, E, k)
+        l = ref.router_logits(x, W_g)
+        sel = ref.select_topk(l, k)
+        v, i = torch.topk(torch.as_tensor(l), k, dim=1)
+        i = i.numpy()
+        for t in range(T):
+            if sel.tie_flag[t]:
+                continue
+            assert set(sel.idx[t]) == set(i[t])
+            if not sel.order_flag[t]:
+                assert list(sel.idx[t]) == list(i[t])
+
+
+def check_tie_rule():
+    """Exact ties go to the lower expert index and are flagged."""
+    l = np.array([[1.0, 2.0, 2.0, 0.5], [3.0, 3.0, 3.0, 3.0], [0.0, 5.0, 1.0, 1.0 + 2e-7]])
+    sel = ref.select_topk(l, 2)
+    assert sel.idx.tolist() == [[1, 2], [0, 1], [1, 3]]
+    assert sel.tie_flag.tolist() == [False, True, True]
+    assert sel.order_flag.tolist() == [True, True, False]
+    assert ref.is_valid_topk(l[1], [2, 3]) and ref.is_valid_topk(l[2], [1, 2])
+    assert not ref.is_valid_topk(l[0], [0, 1]) and not ref.is_valid_topk(l[0], [1, 1])
+
+
+def check_dense_limit():
+    """k = E without capacity: out = sum_e softmax(l)_e FFN_e(x) ([ch7] §7.1),
+    computed here with no top-k and no permutation, through torch library calls."""
+    rng = np.random.default_rng(4)
+    for (T, d, h, E) in [(20, 6, 10, 4), (9, 3, 5, 7)]:
+        x, W_g, ex = rand_case(rng, T, d, h, E, E)
+        r = run_ref(x, W_g, ex, E, E)
+        l = x @ W_g.T
+        p = np.exp(l - l.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        dense = sum(p[:, e:e + 1] * ffn_torch(x, *ex[e]) for e in range(E))
+        assert np.allclose(r.out, dense, rtol=0, atol=1e-12)
+
+
+def check_aux_closed_forms():
+    """Balance loss E sum f P ([guide] §4.3, [ch7] §7.4) on closed-form cases."""
+    rng = np.random.default_rng(5)
+    # (i) zero router: P uniform (1/E) so aux = E * sum f / E = 1, whatever the routing
+    for (E, k) in [(8, 2), (5, 1), (64, 1), (6, 3)]:
+        x = rng.standard_normal((40, 4))
+        r = run_ref(x, np.zeros((E, 4)), [(np.zeros((2, 4)), np.zeros(2), np.zeros((4, 2)), np.zeros(4))] * E, E, k)
+        assert abs(r.aux - 1.0) < 1e-14
+        assert r.idx[:, 0].tolist() == [0] * 40      # everyone ties -> lowest indices
+    # (ii) cyclic one-hot tokens and a circulant router W_g[e, c] = a[(e - c) mod E]
+    # with a strictly decreasing: token c picks experts c, c+1, .., c+k-1 (mod E),
+    # so f is uniform, and P_e averages every rotation of softmax(a), so P is uniform
+    for (E, k, m) in [(4, 1, 3), (6, 2, 2), (8, 3, 1)]:
+        x = np.tile(np.eye(E), (m, 1))
+        a = 3.0 - 0.5 * np.arange(E)
+        W_g = np.array([[a[(e - c) % E] for c in range(E)] for e in range(E)])
+        ex = [(np.zeros((2, E)), np.zeros(2), np.zeros((E, 2)), np.zeros(E))] * E
+        r = run_ref(x, W_g, ex, E, k)
+        assert np.allclose(r.f, 1.0 / E) and np.allclose(r.P, 1.0 / E)
+        assert abs(r.aux - 1.0) < 1e-14
+    # (iii) every token to expert 0 with p -> 1: aux -> E (k = 1)
+    E = 8
+    x = np.ones((10, 1))
+    W_g = np.array([[60.0]] + [[0.0]] * (E - 1))
+    ex = [(np.zeros((2, 1)), np.zeros(2), np.zeros((1, 2)), np.zeros(1))] * E
+    r = run_ref(x, W_g, ex, E, 1)
+    assert abs(r.aux - E) < 1e-9
+    # (iv) the definition: aux = E * sum_e (c_e / (T k)) * mean_t p[t, e], by explicit loops
+    x, W_g, ex = rand_case(rng, 30, 5, 2, 6, 2)
+    r = run_ref(x, W_g, ex, 6, 2)
+    c = [sum(1 for t in range(30) for j in range(2) if r.idx[t, j] == e) for e in range(6)]
+    Pm = [math.fsum(r.probs[t, e] for t in range(30)) / 30 for e in range(6)]
+    assert abs(r.aux - 6 * math.fsum(c[e] / 60 * Pm[e] for e in range(6))) < 1e-14
+    # (v) f uniform gives exactly 1 whatever P is; a skewed f can push it above 1
+    ex = [(np.zeros((2, 2)), np.zeros(2), np.zeros((2, 2)), np.zeros(2))] * 2
+    x = np.array([[1.0, 0.0], [0.0, 1.0]])
+    W_g = np.array([[2.0, 0.0], [0.0, 0.1]])
+    r = run_ref(x, W_g, ex[:2], 2, 1)
+    assert r.counts.tolist() == [1, 1] and abs(r.aux - 1.0) < 1e-14   # f uniform -> exactly 1
+    W_g = np.array([[2.0, -1.0], [0.0, 0.0]])
+    r = run_ref(np.array([[1.0, 0.0], [1.0, 0.0], [0.0, 1.0]]), W_g, ex[:2], 2, 1)
+    f = np.array([2 / 3, 1 / 3])
+    assert np.allclose(r.f, f) and abs(r.aux - 2 * np.dot(f, r.P)) < 1e-14 and r.aux > 1.0
+    # (vi) and it can fall below 1: each token nearly ties its choice with expert 2,
+    # which no token picks, so f = (1/2, 1/2, 0) while P ~ (1/4, 1/4, 1/2): aux ~ 3/4
+    x = np.array([[1.0, 0.0], [0.0, 1.0]])
+    W_g = np.array([[0.0, -30.0], [-30.0, 0.0], [-0.01, -0.01]])
+    ex3 = [(np.zeros((2, 2)), np.zeros(2), np.zeros((2, 2)), np.zeros(2))] * 3
+    r = run_ref(x, W_g, ex3, 3, 1)
+    assert r.idx[:, 0].tolist() == [0, 1]
+    assert abs(r.aux - 3 * (0.5 * r.P[0] + 0.5 * r.P[1])) < 1e-14 and 0.74 < r.aux < 0.76
+
+
+def check_capacity():
+    """Capacity = ceil(cf T / E) counted in tokens ([guide] §8.2; [ch7] §7.4);
+    drops in token order; invariants and brute-force queues."""
+    assert ref.capacity_of(1.25, 4096, 64) == 80     # switch-shaped workload
+    assert ref.capacity_of(1.5, 16384, 64) == 384    # glam-shaped workload
+    assert ref.capacity_of(1.0, 6, 4) == 2           # ceil(1.5)
+    assert ref.capacity_of(0.0, 10, 2) is None and ref.capacity_of(-1.0, 10, 2) is None
+    rng = np.random.default_rng(6)
+    for (T, E, k) in [(60, 5, 2), (80, 8, 1), (50, 4, 3)]:
+        x, W_g, ex = rand_case(rng, T, 4, 2, E, k)
+        W_g[0] += 1.5                          # skew toward expert 0 so caps bind
+        prev = None
+        for cf in [0.1, 0.25, 0.5, 1.0, 2.0, float(E)]:
+            r = run_ref(x, W_g, ex, E, k, cf)
+            cap = ref.capacity_of(cf, T, E)
+            assert r.kept.sum() + (r.counts - r.kept).sum() == T * k
+            assert np.all(r.kept <= cap) and np.all(r.kept == np.minimum(r.counts, cap))
+            assert r.slot_kept.sum() == r.kept.sum()
+            if prev is not None:
+                assert np.all(r.kept >= prev)                          # monotone in cf
+                assert np.all(r.slot_kept[prev_mask])                  # kept sets grow
+            prev, prev_mask = r.kept, r.slot_kept
+            if cf >= E:
+                assert r.slot_kept.all()                               # cap >= T
+            # the kept assignments of an expert are its first ``cap`` tokens
+            for e in range(E):
+                toks = [t for t in range(T) for j in range(k) if r.idx[t, j] == e]
+                kept_toks = [t for t in range(T) for j in range(k) if r.idx[t, j] == e and r.slot_kept[t, j]]
+                assert kept_toks == toks[:cap]
+            # slot_pos: contiguous per-expert segments in expert order
+            pos = np.sort(r.slot_pos[r.slot_kept])
+            assert pos.tolist() == list(range(int(r.kept.sum())))
+        # cap = 1: each expert keeps only its first token
+        r = run_ref(x, W_g, ex, E, k, 0.5 * E / T)
+        assert r.cap == 1 and np.all(r.kept == np.minimum(r.counts, 1))
+        for e in range(E):
+            first = [t for t in range(T) if e in r.idx[t]][:1]
+            assert [t for t in range(T) for j in range(k) if r.idx[t, j] == e and r.slot_kept[t, j]] == first
+
+
+def check_dropped_contribute_nothing():
+    """A dropped assignment adds nothing and the others are not renormalised."""
+    rng = np.random.default_rng(7)
+    x, W_g, ex = rand_case(rng, 40, 4, 3, 4, 2)
+    W_g[1] += 2.0
+    full = run_ref(x, W_g, ex, 4, 2)
+    r = run_ref(x, W_g, ex, 4, 2, 0.5)
+    assert (~r.slot_kept).any()
+    for t in range(40):
+        acc = np.zeros(4)
+        for j in range(2):
+            if r.slot_kept[t, j]:
+                acc += full.w[t, j] * ffn_torch(x[t:t + 1], *ex[full.idx[t, j]])[0]
+        assert np.allclose(r.out[t], acc, rtol=0, atol=1e-12)
+
+
+def check_ffn_library():
+    """Expert FFN == torch F.linear + F.gelu(approximate='none') in float64, and
+    GELU == u * Phi(u) from math.erf."""
+    rng = np.random.default_rng(8)
+    W1, b1, W2, b2 = (rng.standard_normal(s) for s in [(12, 5), 12, (5, 12), 5])
+    xr = rng.standard_normal((7, 5))
+    assert np.allclose(ref.expert_ffn(xr, W1, b1, W2, b2), ffn_torch(xr, W1, b1, W2, b2), rtol=0, atol=1e-13)
+    for u in [-3.0, -1.0, -0.1, 0.0, 0.3, 1.0, 2.5]:
+        assert abs(float(ref.gelu(np.array([u]))[0]) - u * 0.5 * (1 + math.erf(u / math.sqrt(2)))) < 1e-15
+
+
+def check_combine_symmetries():
+    """Identical experts; relabelling experts; permuting tokens."""
+    rng = np.random.default_rng(9)
+    T, d, h, E, k = 32, 5, 7, 6, 2
+    x, W_g, ex = rand_case(rng, T, d, h, E, k)
+    same = [ex[0]] * E
+    y = ffn_torch(x, *ex[0])
+    r = run_ref(x, W_g, same, E, k)
+    assert np.allclose(r.out, y, rtol=0, atol=1e-12)                     # sum of weights is 1
+    r = run_ref(x, W_g, same, E, k, 0.5)
+    kept_w = (r.w * r.slot_kept).sum(1, keepdims=True)
+    assert np.allclose(r.out, kept_w * y, rtol=0, atol=1e-12)            # drops: kept weight only
+    # relabel experts: permute router rows and expert params together
+    perm = rng.permutation(E)
+    r0 = run_ref(x, W_g, ex, E, k)
+    r1 = run_ref(x, W_g[perm], [ex[p] for p in perm], E, k)
+    ok = ~r0.tie_flag
+    assert np.allclose(r0.out[ok], r1.out[ok], rtol=0, atol=1e-12)
+    assert np.all(perm[r1.idx[ok]] == r0.idx[ok])
+    # token permutation equivariance (no capacity)
+    tp = rng.permutation(T)
+    r2 = run_ref(x[tp], W_g, ex, E, k)
+    assert np.allclose(r2.out, r0.out[tp], rtol=0, atol=1e-12)
+
+
+def check_shared():
+    """Shared experts: always on, weight 1 ([guide] §7.1; [ch7] §7.3)."""
+    rng = np.random.default_rng(10)
+    T, d, h, E, k = 20, 4, 6, 5, 2
+    x, W_g, ex = rand_case(rng, T, d, h, E, k, S=2)
+    zeroed = [(W1, b1, np.zeros_like(W2), np.zeros_like(b2)) for (W1, b1, W2, b2) in ex[:E]] + ex[E:]
+    r = run_ref(x, W_g, zeroed, E, k, 0.0, 2)
+    assert np.allclose(r.out, ffn_torch(x, *ex[E]) + ffn_torch(x, *ex[E + 1]), rtol=0, atol=1e-12)
+    r0 = run_ref(x, W_g, ex, E, k, 0.0, 0)
+    r1 = run_ref(x, W_g, ex, E, k, 0.5, 1)
+    r1n = run_ref(x, W_g, ex, E, k, 0.5, 0)
+    assert np.allclose(r1.out - r1n.out, ffn_torch(x, *ex[E]), rtol=0, atol=1e-12)   # never capacity-limited
+    assert r1.kept.tolist() == r1n.kept.tolist() and r0.counts.sum() == T * k
+
+
+def check_golden_fixtures():
+    """Hand-derived closed forms (tests/golden): the 0.6 / 0.4 diagram of the
+    [guide] §4.1 flow, and the first-come capacity queue of [guide] §8.2."""
+    Phi1 = 0.5 * (1.0 + math.erf(1.0 / math.sqrt(2.0)))
+    g = json.load(open(os.path.join(GOLDEN, "two_of_three_experts.json")))
+    x = np.array(g["x"])
+    W_g = np.array([[0.0 if v is None else math.log(v)] for v in g["W_g_logs"]])
+    ex = [tuple(np.array(e[n], dtype=np.float64) for n in ("W1", "b1", "W2", "b2")) for e in g["experts"]]
+    r = run_ref(x, W_g, ex, 3, g["k"])
+    assert r.idx.tolist() == g["expected"]["idx"]
+    assert np.allclose(r.w, [[0.6, 0.4]], rtol=0, atol=1e-15)
+    assert r.counts.tolist() == g["expected"]["counts"]
+    assert abs(r.aux - 1.25) < 1e-15
+    assert abs(r.out[0, 0] - (0.6 * (2 * Phi1 - 1) + 0.4 * 1.5)) < 1e-15
+
+    g = json.load(open(os.path.join(GOLDEN, "capacity_queue.json")))
+    x = np.array(g["x"])
+    W_g = np.array(g["W_g"])
+    ex = [tuple(np.array(e[n], dtype=np.float64) for n in ("W1", "b1", "W2", "b2")) for e in g["experts"]]
+    r = run_ref(x, W_g, ex, 2, g["k"], g["capacity_factor"])
+    e_ = g["expected"]
+    assert r.cap == e_["cap"] and r.idx.tolist() == e_["idx"]
+    assert r.counts.tolist() == e_["counts"] and r.kept.tolist() == e_["kept"]
+    assert r.slot_pos.tolist() == e_["slot_pos"]
+    want = [Phi1] * 3 + [0.0] * 2 + [-(1 - Phi1)]
+    assert np.allclose(r.out[:, 0], want, rtol=0, atol=1e-15)
+    s = math.e / (math.e + 1 / math.e)
+    P = [(5 * s + (1 - s)) / 6, (5 * (1 - s) + s) / 6]
+    assert abs(r.aux - 2 * (5 / 6 * P[0] + 1 / 6 * P[1])) < 1e-15
+
+
+def check_rows_and_override():
+    """Restricting outputs to some rows, and overriding the selection, are consistent."""
+    rng = np.random.default_rng(11)
+    x, W_g, ex = rand_case(rng, 30, 4, 5, 6, 2, S=1)
+    full = run_ref(x, W_g, ex, 6, 2, 0.7, 1)
+    rows = [0, 3, 17, 29]
+    part = run_ref(x, W_g, ex, 6, 2, 0.7, 1, rows=rows)
+    assert np.allclose(part.out, full.out[rows], rtol=0, atol=1e-14)
+    assert part.slot_pos.tolist() == full.slot_pos.tolist()
+    same = run_ref(x, W_g, ex, 6, 2, 0.7, 1, override_idx=full.idx)
+    assert np.array_equal(same.out, full.out)
+    alt = full.idx.copy()
+    alt[5] = alt[5][::-1]
+    swapped = run_ref(x, W_g, ex, 6, 2, 0.7, 1, override_idx=alt)
+    assert np.allclose(swapped.w[5], full.w[5][::-1])
+
+
+def check_widen_bf16():
+    """bf16 bit patterns widen exactly: 0x3F80 = 1, 0xC000 = -2, 0x3E80 = 0.25,
+    0x0001 = 2^-133 (smallest subnormal), 0x7F7F = largest finite."""
+    bits = np.array([0x3F80, 0xC000, 0x3E80, 0x0001, 0x7F7F], dtype=np.uint16)
+    v = ref.widen(bits, "bf16")
+    assert v.tolist() == [1.0, -2.0, 0.25, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127]
+
+
+ALL_CHECKS = [check_weights_sum_to_one, check_against_brute, check_topk_vs_torch, check_tie_rule,
+              check_dense_limit, check_aux_closed_forms, check_capacity, check_dropped_contribute_nothing,
+              check_ffn_library, check_combine_symmetries, check_shared, check_golden_fixtures,
+              check_rows_and_override, check_widen_bf16]
+
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=[c.__name__ for c in ALL_CHECKS])
+def test_pin(check):
+    check()

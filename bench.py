@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-MoE FFN layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload mixtral] [--no-cpu-baseline]
+
+A step is one full layer forward (router, scan, scatter, expert phase 1,
+expert phase 2, combine) over one batch of seeded synthetic tokens already
+resident in HBM.  Prints ONE JSON line with tokens/s, the roofline of the
+dominant kernel (live HIP-event timing of every stage) and the CPU oracle
+timed on a bounded sample of the same workload.
+
+Only one GPU is used; --gpus N with N > 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/s + % bf16 MFMA peak, Mixtral-shape E=8 top-2"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_28_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
+
+# oracle sample per workload: the first N tokens (about 10-30 s of host work)
+CPU_SAMPLE_TOKENS = {"tiny": 64, "switch": 4096, "mixtral": 1024, "glam": 2048, "deepseek": 256}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral", choices=["tiny", "switch", "mixtral", "glam", "deepseek"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = workload default)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemm_source_sha():
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from committed counter runs,
+    or None when absent or taken on another version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get(workload)
+    if not entry or entry.get("gemm_source_sha") != gemm_source_sha():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, stacked, ntok: int):
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    c = inp.cfg
+    ntok = min(ntok, c.T)
+    W1, b1, W2, b2 = stacked
+    x = inp.x[:ntok]
+    t0 = time.perf_counter()
+    oracle.moe_forward_ref(x, inp.W_g, lambda e: (W1[e], b1[e], W2[e], b2[e]), c.E, c.k,
+                           float(np.float32(c.cf)), c.S, inp.b_g, kind=c.dtype)
+    dt = time.perf_counter() - t0
+    threads = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    cores = max(threads) if threads else 1
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {ntok} of {c.T} tokens of the same workload (routing and capacity over the sample), "
+                      f"float64 numpy oracle, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py runs on exactly one GPU: the layer is measured on one MI355X and no multi-GPU "
+              "path is built (expert parallelism is a design note only).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_mixture_experts_28_amd as moe
+    from synthetic import make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(args.workload, seed=args.seed)
+    c = inp.cfg
+    t0 = time.perf_counter()
+    stacked = inp.stacked()
+    log(f"generated {args.workload} in {time.perf_counter() - t0:.1f} s")
+
+    def up(a):
+        if c.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    x, W_g = up(inp.x), up(inp.W_g)
+    W1, b1, W2, b2 = (up(a) for a in stacked)
+    b_g = None if inp.b_g is None else torch.from_numpy(inp.b_g).to(dev)
+    dt_code = moe.MOE_BF16 if c.dtype == "bf16" else moe.MOE_F32
+    T, d, h, E, k, S = c.T, c.d, c.h, c.E, c.k, c.S
+    nbytes = moe.moe_workspace_bytes(T, d, h, E, k, S, dt_code)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((T, d), dtype=x.dtype, device=dev)
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    aux = torch.empty((1,), dtype=torch.float32, device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    kept = torch.empty((E,), dtype=torch.int32, device=dev)
+    slot_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    launch = moe.MoeLaunch()
+    launch.T, launch.d, launch.h, launch.dtype = T, d, h, dt_code
+    launch.b_g = b_g.data_ptr() if b_g is not None else None
+    launch.expert_counts, launch.expert_kept, launch.slot_pos = counts.data_ptr(), kept.data_ptr(), slot_pos.data_ptr()
+    launch.workspace, launch.workspace_bytes = ws.data_ptr(), ws.numel()
+    launch.stream = stream.cuda_stream
+
+    nst = moe.MOE_NUM_STAGE_EVENTS
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nst)] for _ in range(args.steps)]
+    for row in events:
+        for e in row:
+            e.record(stream)          # creates the handle
+    ev_arrays = [(ctypes.c_void_p * nst)(*[int(e.cuda_event) for e in row]) for row in events]
+    ptrs = (x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), b1.data_ptr(), W2.data_ptr(), b2.data_ptr())
+
+    def step(ev=None):
+        launch.stage_events = None if ev is None else ctypes.cast(ev, ctypes.c_void_p)
+        st = moe.moe_forward(*ptrs, E, k, float(c.cf), S, out.data_ptr(), topk_idx.data_ptr(), topk_w.data_ptr(),
+                             aux.data_ptr(), launch)
+        if st != moe.MOE_OK:
+            raise RuntimeError(moe.moe_status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(ev_arrays[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    log(f"timed {args.steps} steps in {wall * 1e3:.2f} ms")
+
+    stage_ms = np.array([[events[i][s].elapsed_time(events[i][s + 1]) for s in range(nst - 1)]
+                         for i in range(args.steps)]).mean(axis=0)
+    stages = dict(zip(moe.STAGES, stage_ms.tolist()))
+
+    kept_np = kept.cpu().numpy().astype(np.int64)
+    a_kept = int(kept_np.sum())
+    rows = a_kept + S * T
+    s = 2 if c.dtype == "bf16" else 4
+    gemm_flops = 2.0 * d * h * rows                      # per launch (each phase)
+    active = int((kept_np > 0).sum()) + S
+    bytes_router = T * d * s + E * d * s + 8 * T * k
+    bytes_scatter = T * d * s + a_kept * d * s + 8 * T * k
+    bytes_combine = rows * d * s + T * d * s + 8 * T * k
+    bytes_gemm1 = active * h * d * s + rows * (d + h) * s
+    bytes_gemm2 = active * h * d * s + rows * (h + d) * s
+
+    def gbs(b, ms):
+        return b / (ms * 1e-3) / 1e9
+
+    def tfs(f, ms):
+        return f / (ms * 1e-3) / 1e12
+
+    per_stage = {
+        "router": {"ms": stages["router"], "GB/s": gbs(bytes_router, stages["router"]), "bytes": bytes_router},
+        "scan": {"ms": stages["scan"]},
+        "scatter": {"ms": stages["scatter"], "GB/s": gbs(bytes_scatter, stages["scatter"]), "bytes": bytes_scatter},
+        "expert_phase1": {"ms": stages["expert_phase1"], "TFLOP/s": tfs(gemm_flops, stages["expert_phase1"]),
+                          "GB/s": gbs(bytes_gemm1, stages["expert_phase1"]), "flops": gemm_flops},
+        "expert_phase2": {"ms": stages["expert_phase2"], "TFLOP/s": tfs(gemm_flops, stages["expert_phase2"]),
+                          "GB/s": gbs(bytes_gemm2, stages["expert_phase2"]), "flops": gemm_flops},
+        "combine": {"ms": stages["combine"], "GB/s": gbs(bytes_combine, stages["combine"]), "bytes": bytes_combine},
+    }
+    dom = "expert_phase1" if stages["expert_phase1"] >= stages["expert_phase2"] else "expert_phase2"
+    dom_ms = stages[dom]
+    dom_bytes = bytes_gemm1 if dom == "expert_phase1" else bytes_gemm2
+    traffic = measured_traffic(args.workload)
+    if c.dtype == "f32":
+        roof = {"bound": "alu", "achieved": tfs(gemm_flops, dom_ms), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
+    elif args.workload == "mixtral":
+        roof = {"bound": "mfma", "achieved": tfs(gemm_flops, dom_ms), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:   # fine-grained experts stream their weights: HBM-bound
+        roof = {"bound": "hbm", "achieved": gbs(dom_bytes, dom_ms), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
+    roof["kernel"] = f"gemm ({dom})"
+    gemm_ms = stages["expert_phase1"] + stages["expert_phase2"]
+    roof["gemm_both_phases_frac_of_bf16_peak"] = tfs(2 * gemm_flops, gemm_ms) / PEAK_BF16_TFLOPS
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies done")
+
+    result = {
+        "metric": METRIC,
+        "value": T * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic (seeded normal inputs and random-init weights of the named shapes)",
+        "config": {"workload": f"{args.workload}-shaped MoE layer: T={T} d={d} h={h} E={E} k={k} shared={S} "
+                               f"capacity_factor={c.cf} {c.dtype}",
+                   "T": T, "d": d, "h": h, "E": E, "k": k, "n_shared": S, "capacity_factor": c.cf,
+                   "kept_assignments": a_kept, "dropped_assignments": T * k - a_kept},
+        "roofline": roof,
+        "stages": per_stage,
+        "layer_ms_events": float(stage_ms.sum()),
+    }
+    if not args.no_cpu_baseline:
+        ntok = args.cpu_tokens or CPU_SAMPLE_TOKENS[args.workload]
+        log(f"cpu baseline: oracle on {ntok} tokens")
+        result["cpu_baseline"] = cpu_baseline(inp, stacked, ntok)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,126 @@
+/*
+ * moe.h -- C ABI of libmoe: the forward pass of one sparse Mixture-of-Experts
+ * FFN layer on an AMD Instinct MI355X (gfx950).
+ *
+ * The operation (pages: "AI-Research-SKILLs MoE 训练实战…全指南" §3.1 basic MoE
+ * layer, §4.3 auxiliary loss, §7.1 DeepSeekMoE shared experts, §8.2 capacity
+ * factor; "第7章 Mixture of Experts（MoE）架构" §7.1 MoE(x) = sum_i G(x)_i E_i(x),
+ * §7.4 balance loss and capacity; "[BEE-30064] 混合專家架構與服務", how routing
+ * works):
+ *
+ *   l[t,e]  = sum_c x[t,c] W_g[e,c] (+ b_g[e])              router, no bias
+ *   p[t,:]  = softmax(l[t,:])
+ *   idx[t,:] = the k largest logits, descending, ties to the lower expert index
+ *   w[t,j]  = p[t,idx[t,j]] / sum_j' p[t,idx[t,j']]          renormalised
+ *   cap     = ceil(cf * T / E) (cf <= 0: no limit); for each expert the
+ *             assignments are kept in ascending token order while fewer than
+ *             cap have been kept, the rest are dropped (contribute nothing)
+ *   out[t]  = sum_{kept j} w[t,j] (W2_e GELU(W1_e x[t] + b1_e) + b2_e),  e = idx[t,j]
+ *           + sum_{s<S} FFN_{E+s}(x[t])                      shared, weight 1
+ *   aux     = E * sum_e f_e P_e,  f_e = c_e/(T k) (c_e counted before capacity),
+ *             P_e = mean_t p[t,e]                            unscaled
+ *   GELU(u) = u * Phi(u) (erf form).
+ *
+ * Conventions
+ *   - Every pointer argument is a DEVICE pointer owned by the caller.  The
+ *     library allocates no device memory, keeps no state between calls and
+ *     never synchronises: moe_forward enqueues its kernels on launch->stream
+ *     and returns.  Calls on different streams need distinct workspaces.
+ *   - Matrices are row-major.  Weight matrices use the nn.Linear (out, in)
+ *     layout.  dtype applies to x, W_g, W1, b1, W2, b2 and out: MOE_F32 is
+ *     IEEE float32, MOE_BF16 is bfloat16 (uint16 bit patterns).
+ *   - Validation happens on the host before anything is launched; on error
+ *     nothing is launched and no output is touched.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,          /* null required pointer, T/d/h/E <= 0, k < 1, k > E, n_shared < 0 */
+  MOE_ERR_UNSUPPORTED = 2,  /* E > MOE_MAX_EXPERTS, k > MOE_MAX_TOPK, n_shared > MOE_MAX_SHARED,
+                               d or h not a multiple of 8, pointer not 16-byte aligned, unknown
+                               dtype, or a row count that overflows int32 */
+  MOE_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than moe_workspace_bytes(...) */
+  MOE_ERR_HIP = 4           /* a HIP launch reported an error (hipGetLastError) */
+} moe_status_t;
+
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 8
+#define MOE_MAX_SHARED 8
+
+/* Stage boundaries at which optional timing events are recorded (see
+ * moe_launch_t.stage_events): before the router, then after the router, the
+ * scan, the scatter, expert phase 1 (x W1^T + b1, GELU), expert phase 2
+ * (h W2^T + b2) and the combine. */
+#define MOE_NUM_STAGE_EVENTS 7
+
+typedef struct {
+  int32_t T;            /* tokens (rows of x), >= 1 */
+  int32_t d;            /* model dimension, multiple of 8 */
+  int32_t h;            /* expert hidden dimension, multiple of 8 */
+  moe_dtype_t dtype;    /* dtype of x, W_g, W1, b1, W2, b2, out */
+  const float* b_g;     /* [E] float32 added to the router logits before softmax and
+                           selection, or NULL (no router bias) */
+  int32_t* expert_counts; /* [E] out, or NULL: assignments per expert before capacity (c_e) */
+  int32_t* expert_kept;   /* [E] out, or NULL: assignments kept after capacity */
+  int32_t* slot_pos;      /* [T,k] out, or NULL: row of assignment (t,j) in the
+                             expert-sorted buffer (expert e's rows start at
+                             sum_{e'<e} kept_e'), or -1 if dropped */
+  void* workspace;        /* device scratch of at least moe_workspace_bytes(...) bytes,
+                             256-byte aligned; contents need not be initialised */
+  size_t workspace_bytes;
+  hipStream_t stream;     /* stream all kernels are enqueued on (0 = default stream) */
+  hipEvent_t* stage_events; /* NULL, or MOE_NUM_STAGE_EVENTS created events that are
+                               recorded on `stream` at the stage boundaries */
+} moe_launch_t;
+
+/* Bytes of device workspace moe_forward needs for this problem shape (0 if
+ * the shape is invalid).  Dominated by the expert-sorted token copy
+ * [T*k, d], the hidden buffer [(T*k + S*T), h] and the expert-output buffer
+ * [(T*k + S*T), d] in dtype. */
+size_t moe_workspace_bytes(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k,
+                           int32_t n_shared, moe_dtype_t dtype);
+
+/* The layer forward described above.
+ *   x        [T, d]          input tokens (a batch and sequence flattened, as on the pages)
+ *   W_g      [E, d]          router weight
+ *   W1       [E+S, h, d]     first expert linear; experts 0..E-1 routed, E..E+S-1 shared
+ *   b1       [E+S, h]
+ *   W2       [E+S, d, h]     second expert linear
+ *   b2       [E+S, d]
+ *   E        routed experts, 1..MOE_MAX_EXPERTS
+ *   k        experts per token, 1..min(E, MOE_MAX_TOPK)
+ *   capacity_factor  <= 0: no capacity limit; else cap = ceil(cf*T/E) (double precision)
+ *   n_shared shared experts S, 0..MOE_MAX_SHARED
+ *   out      [T, d]          layer output, dtype (bf16: accumulated in float32, rounded once)
+ *   topk_idx [T, k] int32    slot j = the (j+1)-th largest logit (before capacity)
+ *   topk_w   [T, k] float32  renormalised weights of those slots (before capacity)
+ *   aux_loss [1]    float32  E * sum_e f_e P_e
+ *   launch   shape, dtype, optional outputs, workspace and stream (required)
+ * Returns MOE_OK once everything is enqueued, or an error code (see moe_status_t). */
+moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const void* b1,
+                         const void* W2, const void* b2, int32_t E, int32_t k,
+                         float capacity_factor, int32_t n_shared, void* out,
+                         int32_t* topk_idx, float* topk_w, float* aux_loss,
+                         const moe_launch_t* launch);
+
+/* Static, human-readable name of a status code. */
+const char* moe_status_string(moe_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,117 @@
+// moe_combine: out[t] = sum over kept slots j of w[t,j] * Y[slot_pos[t,j]]
+//                     + sum over shared experts s of Y_shared[s][t].
+//
+// Pages: "AI-Research-SKILLs MoE 训练实战…全指南" §3.1 (the k expert outputs are
+// weighted by the renormalised router scores and summed) and §7.1 (shared
+// experts are added to the routed output with weight 1); "第7章 Mixture of
+// Experts" §7.1 (MoE(x) = sum_i G(x)_i E_i(x)) and §7.4 (an overflowed token's
+// slot contributes nothing; the residual outside the layer carries it).
+//
+// A gather, not a scatter: one workgroup per token reads its k expert rows and
+// its shared rows, accumulates in float32 in slot order then shared order, and
+// rounds once.  No atomics, so the result is bitwise reproducible.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void acc_bf16x8(float (&a)[8], u32x4 v, float w) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[2 * i] = fmaf(w, __uint_as_float(v[i] << 16), a[2 * i]);
+    a[2 * i + 1] = fmaf(w, __uint_as_float(v[i] & 0xffff0000u), a[2 * i + 1]);
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_bf16_kernel(Problem p, const u32x4* __restrict__ y,
+                                                           const int32_t* __restrict__ slot_pos,
+                                                           const float* __restrict__ topk_w,
+                                                           u32x4* __restrict__ out, int vec_per_row) {
+  __shared__ int32_t s_pos[MOE_MAX_TOPK];
+  __shared__ float s_w[MOE_MAX_TOPK];
+  const int t = blockIdx.x;
+  const int k = p.k;
+  if (threadIdx.x < k) {
+    s_pos[threadIdx.x] = slot_pos[static_cast<size_t>(t) * k + threadIdx.x];
+    s_w[threadIdx.x] = topk_w[static_cast<size_t>(t) * k + threadIdx.x];
+  }
+  __syncthreads();
+  const size_t routed_rows = static_cast<size_t>(p.T) * p.k;
+  for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int pos = s_pos[j];
+      if (pos >= 0) acc_bf16x8(a, y[static_cast<size_t>(pos) * vec_per_row + c], s_w[j]);
+    }
+    for (int s = 0; s < p.S; ++s) {
+      const size_t row = routed_rows + static_cast<size_t>(s) * p.T + t;
+      acc_bf16x8(a, y[row * vec_per_row + c], 1.0f);
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = static_cast<uint32_t>(f32_to_bf16(a[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(a[2 * i + 1])) << 16);
+    out[static_cast<size_t>(t) * vec_per_row + c] = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_f32_kernel(Problem p, const float4* __restrict__ y,
+                                                          const int32_t* __restrict__ slot_pos,
+                                                          const float* __restrict__ topk_w,
+                                                          float4* __restrict__ out, int vec_per_row) {
+  __shared__ int32_t s_pos[MOE_MAX_TOPK];
+  __shared__ float s_w[MOE_MAX_TOPK];
+  const int t = blockIdx.x;
+  const int k = p.k;
+  if (threadIdx.x < k) {
+    s_pos[threadIdx.x] = slot_pos[static_cast<size_t>(t) * k + threadIdx.x];
+    s_w[threadIdx.x] = topk_w[static_cast<size_t>(t) * k + threadIdx.x];
+  }
+  __syncthreads();
+  const size_t routed_rows = static_cast<size_t>(p.T) * p.k;
+  for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const int pos = s_pos[j];
+      if (pos >= 0) {
+        const float4 v = y[static_cast<size_t>(pos) * vec_per_row + c];
+        const float w = s_w[j];
+        a.x = fmaf(w, v.x, a.x);
+        a.y = fmaf(w, v.y, a.y);
+        a.z = fmaf(w, v.z, a.z);
+        a.w = fmaf(w, v.w, a.w);
+      }
+    }
+    for (int s = 0; s < p.S; ++s) {
+      const size_t row = routed_rows + static_cast<size_t>(s) * p.T + t;
+      const float4 v = y[row * vec_per_row + c];
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+    }
+    out[static_cast<size_t>(t) * vec_per_row + c] = a;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Problem& p, const float* topk_w, const Workspace& ws, void* out,
+                          hipStream_t st) {
+  const int elem = p.dtype == MOE_BF16 ? 2 : 4;
+  const int vec_per_row = p.d * elem / 16;
+  const int threads = vec_per_row >= 256 ? 256 : (vec_per_row >= 128 ? 128 : 64);
+  if (p.dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_bf16_kernel, dim3(p.T), dim3(threads), 0, st, p,
+                       static_cast<const u32x4*>(ws.ybuf), ws.slot_pos, topk_w, static_cast<u32x4*>(out),
+                       vec_per_row);
+  else
+    hipLaunchKernelGGL(combine_f32_kernel, dim3(p.T), dim3(threads), 0, st, p,
+                       static_cast<const float4*>(ws.ybuf), ws.slot_pos, topk_w, static_cast<float4*>(out),
+                       vec_per_row);
+  return hipGetLastError();
+}
+
+}  // namespace moe

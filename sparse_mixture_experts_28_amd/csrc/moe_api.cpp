@@ -1,0 +1,171 @@
+// Host side of the C ABI (include/moe.h): validation, workspace carving and the
+// launch sequence router -> scan -> scatter -> expert phase 1 -> phase 2 -> combine,
+// all enqueued on the caller's stream with no host synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_bytes(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+struct Layout {
+  size_t xperm, hbuf, ybuf, local_rank, tile_hist, p_part, counts, kept, slot_pos, seg, total;
+};
+
+Layout layout_of(const Problem& p) {
+  const size_t s = elem_bytes(p.dtype);
+  const size_t A = static_cast<size_t>(p.T) * p.k;
+  const size_t R = A + static_cast<size_t>(p.S) * p.T;
+  const size_t te = static_cast<size_t>(p.ntile) * p.E;
+  Layout L;
+  size_t off = 0;
+  L.xperm = off;      off += align_up(A * p.d * s);
+  L.hbuf = off;       off += align_up(R * p.h * s);
+  L.ybuf = off;       off += align_up(R * p.d * s);
+  L.local_rank = off; off += align_up(A * 4);
+  L.tile_hist = off;  off += align_up(te * 4);
+  L.p_part = off;     off += align_up(te * 4);
+  L.counts = off;     off += align_up(static_cast<size_t>(p.E) * 4);
+  L.kept = off;       off += align_up(static_cast<size_t>(p.E) * 4);
+  L.slot_pos = off;   off += align_up(A * 4);
+  L.seg = off;        off += align_up(seg_table_ints(p.E + p.S, p.E) * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+size_t workspace_bytes(const Problem& p) { return layout_of(p).total; }
+
+Workspace carve_workspace(const Problem& p, void* base, size_t bytes_available, bool* ok) {
+  const Layout L = layout_of(p);
+  Workspace w{};
+  *ok = base != nullptr && bytes_available >= L.total && aligned(base, kAlign);
+  if (!*ok) return w;
+  char* b = static_cast<char*>(base);
+  w.xperm = b + L.xperm;
+  w.hbuf = b + L.hbuf;
+  w.ybuf = b + L.ybuf;
+  w.local_rank = reinterpret_cast<int32_t*>(b + L.local_rank);
+  w.tile_hist = reinterpret_cast<int32_t*>(b + L.tile_hist);
+  w.p_part = reinterpret_cast<float*>(b + L.p_part);
+  w.counts = reinterpret_cast<int32_t*>(b + L.counts);
+  w.kept = reinterpret_cast<int32_t*>(b + L.kept);
+  w.slot_pos = reinterpret_cast<int32_t*>(b + L.slot_pos);
+  w.seg = reinterpret_cast<int32_t*>(b + L.seg);
+  w.bytes = L.total;
+  return w;
+}
+
+namespace {
+
+// Shape checks shared by moe_workspace_bytes and moe_forward.
+moe_status_t check_shape(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int32_t S, int dtype) {
+  if (T < 1 || d < 1 || h < 1 || E < 1 || k < 1 || k > E || S < 0) return MOE_ERR_ARG;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || S > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
+  if (d % 8 != 0 || h % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long rows = static_cast<long long>(T) * k + static_cast<long long>(S) * T;
+  if (rows > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+Problem make_problem(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int32_t S, moe_dtype_t dt,
+                     float cf) {
+  Problem p;
+  p.T = T;
+  p.d = d;
+  p.h = h;
+  p.E = E;
+  p.k = k;
+  p.S = S;
+  p.dtype = dt;
+  p.ntile = (T + kRouterTile - 1) / kRouterTile;
+  if (cf > 0.f) {
+    const double c = std::ceil(static_cast<double>(cf) * static_cast<double>(T) / static_cast<double>(E));
+    p.cap = c >= static_cast<double>(INT32_MAX) ? INT32_MAX : static_cast<int>(c);
+  } else {
+    p.cap = INT32_MAX;
+  }
+  p.gemm_bm = gemm_m_tile(p);
+  return p;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+size_t moe_workspace_bytes(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int32_t n_shared,
+                           moe_dtype_t dtype) {
+  if (moe::check_shape(T, d, h, E, k, n_shared, static_cast<int>(dtype)) != MOE_OK) return 0;
+  return moe::workspace_bytes(moe::make_problem(T, d, h, E, k, n_shared, dtype, 0.f));
+}
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_ARG: return "MOE_ERR_ARG: invalid argument (null pointer or size out of range)";
+    case MOE_ERR_UNSUPPORTED:
+      return "MOE_ERR_UNSUPPORTED: unsupported shape, dtype or pointer alignment";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
+  }
+  return "unknown moe_status_t";
+}
+
+moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const void* b1, const void* W2,
+                         const void* b2, int32_t E, int32_t k, float capacity_factor, int32_t n_shared,
+                         void* out, int32_t* topk_idx, float* topk_w, float* aux_loss,
+                         const moe_launch_t* launch) {
+  using namespace moe;
+  if (launch == nullptr) return MOE_ERR_ARG;
+  if (!x || !W_g || !W1 || !b1 || !W2 || !b2 || !out || !topk_idx || !topk_w || !aux_loss) return MOE_ERR_ARG;
+  if (std::isnan(capacity_factor)) return MOE_ERR_ARG;
+  const moe_status_t sc = check_shape(launch->T, launch->d, launch->h, E, k, n_shared,
+                                      static_cast<int>(launch->dtype));
+  if (sc != MOE_OK) return sc;
+  const void* a16[] = {x, W_g, W1, b1, W2, b2, out};
+  for (const void* q : a16)
+    if (!aligned(q, 16)) return MOE_ERR_UNSUPPORTED;
+  const void* a4[] = {topk_idx, topk_w, aux_loss, launch->b_g, launch->expert_counts, launch->expert_kept,
+                      launch->slot_pos};
+  for (const void* q : a4)
+    if (q && !aligned(q, 4)) return MOE_ERR_UNSUPPORTED;
+
+  const Problem p = make_problem(launch->T, launch->d, launch->h, E, k, n_shared, launch->dtype, capacity_factor);
+  bool ok = false;
+  Workspace ws = carve_workspace(p, launch->workspace, launch->workspace_bytes, &ok);
+  if (!ok) return MOE_ERR_WORKSPACE;
+  if (launch->slot_pos) ws.slot_pos = launch->slot_pos;
+
+  hipStream_t st = launch->stream;
+  hipEvent_t* ev = launch->stage_events;
+  int ei = 0;
+  auto mark = [&]() -> bool { return ev == nullptr || hipEventRecord(ev[ei++], st) == hipSuccess; };
+
+  if (!mark()) return MOE_ERR_HIP;
+  if (launch_router(p, x, W_g, launch->b_g, topk_idx, topk_w, ws, st) != hipSuccess || !mark()) return MOE_ERR_HIP;
+  if (launch_scan(p, ws, aux_loss, launch->expert_counts, launch->expert_kept, st) != hipSuccess || !mark())
+    return MOE_ERR_HIP;
+  if (launch_scatter(p, x, topk_idx, ws, st) != hipSuccess || !mark()) return MOE_ERR_HIP;
+  if (launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 1, st) != hipSuccess || !mark()) return MOE_ERR_HIP;
+  if (launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 2, st) != hipSuccess || !mark()) return MOE_ERR_HIP;
+  if (launch_combine(p, topk_w, ws, out, st) != hipSuccess || !mark()) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Internal declarations shared by the HIP translation units of libmoe.
+// Not part of the public ABI (that is include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ------------------------------------------------------------ constants --
+constexpr int kRouterTile = 64;     // tokens per router workgroup (= permute rank tile)
+constexpr int kRouterThreads = 256; // 4 waves x 16 tokens
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------- bf16 helpers --
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x0040u;
+  return static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded);
+}
+
+// ----------------------------------------------------- workspace layout --
+// All regions are carved from one caller-owned device buffer, each aligned to
+// 256 bytes.  Row counts: A = T*k routed rows (worst case, no drops),
+// R = A + S*T rows of the expert hidden / output buffers (shared experts at
+// the fixed row offset A + s*T).
+struct Workspace {
+  void* xperm;          // [A, d]     expert-sorted copies of the token rows
+  void* hbuf;           // [R, h]     GELU(x W1^T + b1)
+  void* ybuf;           // [R, d]     h W2^T + b2
+  int32_t* local_rank;  // [T, k]     rank of (t,j) among earlier tokens of its 64-token tile
+  int32_t* tile_hist;   // [ntile, E] assignments per (tile, expert); becomes the tile base
+  float* p_part;        // [ntile, E] per-tile sums of the softmax probabilities
+  int32_t* counts;      // [E]
+  int32_t* kept;        // [E]
+  int32_t* slot_pos;    // [T, k]
+  int32_t* seg;         // segment table, see SegTable
+  size_t bytes;
+};
+
+// Segment table written by the scan kernel and read by the grouped GEMM and
+// the scatter: nseg = E + S segments.  Stored as int32 arrays back to back:
+//   rows[nseg]        rows of the segment (kept_e, or T for a shared expert)
+//   a_off[nseg]       first row of the segment in its A source for phase 1
+//                     (xperm for routed experts, x for shared experts)
+//   o_off[nseg]       first row of the segment in hbuf / ybuf
+//   tile_start[nseg+1] prefix sum of ceil(rows / BM) (M tiles of the GEMM)
+//   route_off[E]      exclusive scan of kept (row offset of expert e in xperm)
+struct SegTable {
+  int32_t* rows;
+  int32_t* a_off;
+  int32_t* o_off;
+  int32_t* tile_start;
+  int32_t* route_off;
+};
+
+__host__ __device__ inline SegTable seg_table(int32_t* base, int nseg, int E) {
+  SegTable s;
+  s.rows = base;
+  s.a_off = base + nseg;
+  s.o_off = base + 2 * nseg;
+  s.tile_start = base + 3 * nseg;
+  s.route_off = base + 4 * nseg + 1;
+  (void)E;
+  return s;
+}
+inline size_t seg_table_ints(int nseg, int E) { return static_cast<size_t>(4 * nseg + 1 + E); }
+
+struct Problem {
+  int T, d, h, E, k, S;
+  moe_dtype_t dtype;
+  int cap;       // capacity per expert; INT32_MAX when unlimited
+  int ntile;     // ceil(T / kRouterTile)
+  int gemm_bm;   // M tile of the grouped GEMM (for the tile prefix)
+};
+
+Workspace carve_workspace(const Problem& p, void* base, size_t bytes_available, bool* ok);
+size_t workspace_bytes(const Problem& p);
+
+// ------------------------------------------------------ kernel launchers --
+// Each returns hipGetLastError() after its launch(es).
+hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const float* b_g,
+                         int32_t* topk_idx, float* topk_w, const Workspace& ws, hipStream_t st);
+hipError_t launch_scan(const Problem& p, const Workspace& ws, float* aux_loss,
+                       int32_t* counts_out, int32_t* kept_out, hipStream_t st);
+hipError_t launch_scatter(const Problem& p, const void* x, const int32_t* topk_idx,
+                          const Workspace& ws, hipStream_t st);
+hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, const void* b1,
+                             const void* W2, const void* b2, const Workspace& ws, int phase,
+                             hipStream_t st);
+hipError_t launch_combine(const Problem& p, const float* topk_w, const Workspace& ws, void* out,
+                          hipStream_t st);
+
+// Which GEMM kernel serves a problem; the M tile decides the tile prefix.
+bool gemm_fast_path(const Problem& p);
+int gemm_m_tile(const Problem& p);
+
+}  // namespace moe

@@ -49,6 +49,13 @@ class MoeLaunch(ctypes.Structure):
 
 
 def _load():
+    # torch ships its own HIP runtime.  Loading torch first puts that runtime in
+    # the process's global symbol scope, so libmoe's HIP calls bind to it and the
+    # process has one runtime: torch's device pointers and streams are then valid
+    # in libmoe's launches.  Loaded the other way round, libmoe would bind to a
+    # second runtime that cannot open the device while torch's holds it.
+    import torch  # noqa: F401
+
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run `python -m sparse_mixture_experts_28_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)

@@ -18,8 +18,8 @@
 // 2 x 2 grid, each wave (BM/2) x 128 as blocks of the 32x32x16 bf16 MFMA with
 // float32 accumulators.  Operands are read with buffer loads whose range check
 // returns zero past a segment's last row, so ragged tails need no clamping; A and B tiles double-buffered
-// in LDS (128 KB) with a 16-byte-chunk XOR swizzle (chunk ^ row % 8) so the
-// MFMA operand reads are bank-conflict free.  The grid is persistent, one
+// in LDS with a 16-byte-chunk XOR swizzle so the MFMA operand reads are
+// bank-conflict free.  The grid is persistent, one
 // workgroup per CU; workgroup b runs on XCD b % 8, and the logical tile order
 // gives each XCD a contiguous run of tiles grouped 8 M-tiles x N so
 // concurrently running tiles share A and B panels in that XCD's L2.
@@ -27,6 +27,11 @@
 //
 // Fallback (any shape, float32 or bf16): 64 x 64 SIMT tiles, float32 accumulation.
 #include "moe_internal.h"
+
+// Pin the MFMA / LDS-read / global-load interleave of the K steps.
+#ifndef MOE_GEMM_SCHED
+#define MOE_GEMM_SCHED 1
+#endif
 
 namespace moe {
 namespace {
@@ -45,6 +50,20 @@ struct GemmArgs {
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Workgroup barrier for the direct-load kernels.  __syncthreads() also waits
+// for every outstanding global load (its fence emits vmcnt(0)), which would
+// drain the global->LDS loads kept in flight across stages.  This barrier
+// waits only for this wave's own LDS operations (lgkmcnt(0)); callers wait for
+// the loads of a stage (vmcnt) themselves before the barrier that publishes it.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63 (no wait), expcnt 7 (no wait), lgkmcnt 0
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
@@ -65,6 +84,13 @@ constexpr int kBN = 256, kBK = 64;
 constexpr int kGroupM = 8;
 constexpr int kCh = kBK / 8;                   // 16-byte chunks per tile row
 constexpr int kRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data format (gfx9 family)
+
+// LDS layout of a tile row of 64 bf16 (8 chunks of 16 bytes): logical chunk c
+// of row r is stored at chunk c ^ (r & 7) ^ ((r >> 3) & 1).  A ds_read_b128
+// of 16 consecutive rows at one logical chunk then touches 16 distinct
+// 16-byte bank groups whether the LDS serves 8 or 16 lanes per cycle, and so
+// does a ds_write_b128 of 2 rows x 8 chunks.
+__device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7) ^ ((row >> 3) & 1); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
@@ -216,6 +242,179 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
+// ------------------------------------------------------ 8-wave MFMA path --
+// 256 x 256 x 64 tile, 8 waves (2 per SIMD) in a 2 (M) x 4 (N) grid, wave tile
+// 128 x 64 = 4 x 2 blocks of the 32x32x16 MFMA (128 float accumulators per
+// lane).  With two waves per SIMD, one wave's MFMAs cover the other's LDS and
+// memory waits.  Operand fragments are double-buffered in registers across
+// the four 16-deep k-steps of a tile step.  Tiles reach LDS directly
+// (buffer_load ... lds writes 64 lanes x 16 bytes contiguously at a
+// wave-uniform LDS address), without passing through registers.
+template <bool GELU>
+__global__ __launch_bounds__(512) void gemm_bf16_w8_kernel(GemmArgs g) {
+  constexpr int BM = 256;
+  constexpr int kStage = (BM + kBN) * kCh;     // u32x4 per LDS stage (64 KB)
+  __shared__ u32x4 lds[2 * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
+  const int total_mt = uniform(st.tile_start[g.nseg]);
+  const int ntn = g.N / kBN;
+  const int total = total_mt * ntn;
+  const int nk = g.K / kBK;
+  const uint32_t row_bytes = static_cast<uint32_t>(g.K) * 2u;
+
+  const int per_xcd = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+
+  const uint16_t* Wb = static_cast<const uint16_t*>(g.W);
+  const uint16_t* Bias = static_cast<const uint16_t*>(g.bias);
+  uint16_t* C = static_cast<uint16_t*>(g.C);
+
+  // direct loads: wave w, load i fills LDS rows 64 i + 8 w + lane / 8 at physical
+  // chunk lane % 8, so the lane fetches the logical chunk that lands there
+  const int dr_row = 8 * wave + (lane >> 3);
+  const int dr_ch = (lane & 7) ^ (dr_row & 7) ^ ((dr_row >> 3) & 1);
+  const int rd_row = lane & 31;
+
+  for (int it = 0;; ++it) {
+    const int L = it * gridDim.x + xcd * per_xcd + slot;
+    if (L >= total) break;
+    const int gsz = kGroupM * ntn;
+    const int grp = L / gsz;
+    const int first_m = grp * kGroupM;
+    const int gm = min(kGroupM, total_mt - first_m);
+    const int r = L - grp * gsz;
+    const int mt = first_m + r % gm;
+    const int nt = r / gm;
+
+    const int s = uniform(find_segment(st.tile_start, g.nseg, mt));
+    const int rows = uniform(st.rows[s]);
+    const int m0 = (mt - uniform(st.tile_start[s])) * BM;
+    const int a_off = uniform(g.a_by_o_off ? st.o_off[s] : st.a_off[s]);
+    const int o_off = uniform(st.o_off[s]);
+    const uint16_t* A = static_cast<const uint16_t*>(s < g.E ? g.a_routed : g.a_shared) +
+                        static_cast<size_t>(a_off) * g.K;
+    const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, static_cast<uint32_t>(rows) * row_bytes);
+    const __amdgpu_buffer_rsrc_t rb_rsrc =
+        make_rsrc(Wb + static_cast<size_t>(s) * g.N * g.K, static_cast<uint32_t>(g.N) * row_bytes);
+    const int n0 = nt * kBN;
+    const uint32_t step64 = 64u * row_bytes;
+    const uint32_t va = static_cast<uint32_t>(m0 + dr_row) * row_bytes + dr_ch * 16;
+    const uint32_t vb = static_cast<uint32_t>(n0 + dr_row) * row_bytes + dr_ch * 16;
+
+    floatx16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    auto issue = [&](int stage, int kb) {
+      u32x4* base = lds + stage * kStage + (8 * wave) * kCh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra_rsrc, (__attribute__((address_space(3))) void*)(base + 64 * i * kCh), 16, va, i * step64 + kb, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb_rsrc, (__attribute__((address_space(3))) void*)(base + (BM + 64 * i) * kCh), 16, vb,
+            i * step64 + kb, 0, 0);
+      }
+    };
+    // this wave's loads into the other stage have landed (published by the barrier)
+    auto commit = [&](int) { __builtin_amdgcn_s_waitcnt(0); };
+
+    issue(0, 0);
+    commit(0);
+    lds_barrier();
+
+    // One K step: fragments of k-substep ks+1 and (when `load`) the next
+    // stage's global loads are issued between the MFMAs of ks, one at a time,
+    // so LDS and memory latency overlap the matrix pipe.
+    auto kstep = [&](int kt, bool load) {
+      const int cur = kt & 1;
+      const u32x4* sa = lds + cur * kStage;
+      const u32x4* sb = sa + BM * kCh;
+      bf16x8 fa[2][4], fb[2][2];
+      auto frag = [&](int ks, int buf) {
+        const int ch = swz(rd_row, 2 * ks + (lane >> 5));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          fa[buf][i] = __builtin_bit_cast(bf16x8, sa[(wm * 128 + i * 32 + rd_row) * kCh + ch]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          fb[buf][j] = __builtin_bit_cast(bf16x8, sb[(wn * 64 + j * 32 + rd_row) * kCh + ch]);
+      };
+      frag(0, 0);
+      if (load) issue(cur ^ 1, (kt + 1) * kBK * 2);
+#pragma unroll
+      for (int ks = 0; ks < kBK / 16; ++ks) {
+        if (ks + 1 < kBK / 16) frag(ks + 1, (ks + 1) & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
+#if MOE_GEMM_SCHED
+        if (ks == 0 && load) {
+#pragma unroll
+          for (int q = 0; q < 6; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 global load
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        } else if (ks + 1 < kBK / 16) {
+#pragma unroll
+          for (int q = 0; q < 6; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
+#endif
+      }
+      if (load) commit(cur ^ 1);
+      lds_barrier();
+    };
+    for (int kt = 0; kt + 1 < nk; ++kt) kstep(kt, true);
+    kstep(nk - 1, false);
+
+    // epilogue: accumulator v of block (i, j) holds row 8 (v / 4) + 4 (lane / 32) + v % 4,
+    // column lane % 32 of that block
+    const int col0 = n0 + wn * 64 + (lane & 31);
+    float bj[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bj[j] = bf16_to_f32(Bias[static_cast<size_t>(s) * g.N + col0 + j * 32]);
+    const bool full = m0 + BM <= rows;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rl = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (full || rl < rows) {
+          uint16_t* crow = C + static_cast<size_t>(o_off + rl) * g.N + col0;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float val = acc[i][j][v] + bj[j];
+            if (GELU) val = gelu_erf(val);
+            crow[j * 32] = f32_to_bf16(val);
+          }
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ SIMT path --
 constexpr int kSB = 64, kSK = 16;
 
@@ -342,9 +541,9 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
     grid = (grid + 7) / 8 * 8;
     if (p.gemm_bm == 256) {
       if (phase == 1)
-        hipLaunchKernelGGL((gemm_bf16_kernel<256, true>), dim3(grid), dim3(256), 0, st, g);
+        hipLaunchKernelGGL((gemm_bf16_w8_kernel<true>), dim3(grid), dim3(512), 0, st, g);
       else
-        hipLaunchKernelGGL((gemm_bf16_kernel<256, false>), dim3(grid), dim3(256), 0, st, g);
+        hipLaunchKernelGGL((gemm_bf16_w8_kernel<false>), dim3(grid), dim3(512), 0, st, g);
     } else {
       if (phase == 1)
         hipLaunchKernelGGL((gemm_bf16_kernel<128, true>), dim3(grid), dim3(256), 0, st, g);

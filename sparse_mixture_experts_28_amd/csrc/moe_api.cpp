@@ -6,6 +6,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 
 #include "moe.h"
 #include "moe_internal.h"
@@ -155,16 +156,25 @@ moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const v
   hipStream_t st = launch->stream;
   hipEvent_t* ev = launch->stage_events;
   int ei = 0;
-  auto mark = [&]() -> bool { return ev == nullptr || hipEventRecord(ev[ei++], st) == hipSuccess; };
+  // a stale error from an earlier, unrelated HIP call must not be blamed on a launch here
+  (void)hipGetLastError();
+  auto check = [&](hipError_t e, const char* stage) -> bool {
+    if (e == hipSuccess && ev != nullptr) e = hipEventRecord(ev[ei++], st);
+    if (e != hipSuccess) {
+      std::fprintf(stderr, "libmoe: %s failed: %s (%s)\n", stage, hipGetErrorName(e), hipGetErrorString(e));
+      return false;
+    }
+    return true;
+  };
 
-  if (!mark()) return MOE_ERR_HIP;
-  if (launch_router(p, x, W_g, launch->b_g, topk_idx, topk_w, ws, st) != hipSuccess || !mark()) return MOE_ERR_HIP;
-  if (launch_scan(p, ws, aux_loss, launch->expert_counts, launch->expert_kept, st) != hipSuccess || !mark())
+  if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
+  if (!check(launch_router(p, x, W_g, launch->b_g, topk_idx, topk_w, ws, st), "router launch")) return MOE_ERR_HIP;
+  if (!check(launch_scan(p, ws, aux_loss, launch->expert_counts, launch->expert_kept, st), "scan launch"))
     return MOE_ERR_HIP;
-  if (launch_scatter(p, x, topk_idx, ws, st) != hipSuccess || !mark()) return MOE_ERR_HIP;
-  if (launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 1, st) != hipSuccess || !mark()) return MOE_ERR_HIP;
-  if (launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 2, st) != hipSuccess || !mark()) return MOE_ERR_HIP;
-  if (launch_combine(p, topk_w, ws, out, st) != hipSuccess || !mark()) return MOE_ERR_HIP;
+  if (!check(launch_scatter(p, x, topk_idx, ws, st), "scatter launch")) return MOE_ERR_HIP;
+  if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 1, st), "expert phase 1 launch")) return MOE_ERR_HIP;
+  if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 2, st), "expert phase 2 launch")) return MOE_ERR_HIP;
+  if (!check(launch_combine(p, topk_w, ws, out, st), "combine launch")) return MOE_ERR_HIP;
   return MOE_OK;
 }
 

@@ -11,19 +11,25 @@
 // routed experts).
 //
 // Both operands are K-contiguous (A rows and nn.Linear weight rows), so
-// C = A B^T is the "NT" product that MFMA prefers.
+// C = A B^T is the "NT" product that MFMA prefers.  All tiles are 256 columns
+// wide with K steps of 64; accumulation is float32 on the 32x32x16 bf16 MFMA;
+// the epilogue adds the bias and (phase 1) applies GELU(erf) in float32 and
+// rounds once to bf16.
 //
-// Fast path (bf16, N % 256 == 0, K % 64 == 0): BM x 256 x 64 macro tiles
-// (BM = 256, or 128 for fine-grained experts with few rows each), 4 waves in a
-// 2 x 2 grid, each wave (BM/2) x 128 as blocks of the 32x32x16 bf16 MFMA with
-// float32 accumulators.  Operands are read with buffer loads whose range check
-// returns zero past a segment's last row, so ragged tails need no clamping; A and B tiles double-buffered
-// in LDS with a 16-byte-chunk XOR swizzle so the MFMA operand reads are
-// bank-conflict free.  The grid is persistent, one
-// workgroup per CU; workgroup b runs on XCD b % 8, and the logical tile order
-// gives each XCD a contiguous run of tiles grouped 8 M-tiles x N so
-// concurrently running tiles share A and B panels in that XCD's L2.
-// Epilogue: bias, then (phase 1) GELU(erf), in float32, rounded once to bf16.
+// Two bf16 kernels, chosen by the average rows per expert:
+//  * 256-row tiles, 8 waves (compute-bound regime, e.g. 8 experts of ~2k rows):
+//    two waves per SIMD, 128 x 64 wave tiles, two 64 KB LDS stages filled by
+//    direct global->LDS loads one K step ahead.
+//  * 128-row tiles, 4 waves (weight-streaming regime: many experts of ~100-400
+//    rows): a 3-stage LDS ring filled two K steps ahead so ~96 KB per CU stay
+//    in flight.
+// Shared pieces: operands are read with buffer loads whose range check returns
+// zero past a segment's last row (ragged tails need no clamping); LDS rows use
+// a 16-byte-chunk XOR swizzle that makes the MFMA operand reads conflict-free;
+// the grid is persistent (one workgroup per CU); workgroup b runs on XCD b % 8
+// and the logical tile order gives each XCD a contiguous run of tiles grouped
+// 8 M-tiles x N, so concurrently running tiles share A and B panels in that
+// XCD's L2.
 //
 // Fallback (any shape, float32 or bf16): 64 x 64 SIMT tiles, float32 accumulation.
 #include "moe_internal.h"
@@ -95,151 +101,6 @@ __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7) ^ ((ro
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), kRsrcWord3);
-}
-
-// BM x 256 x 64 tile, 4 waves (2 x 2), wave tile (BM/2) x 128.
-template <int BM, bool GELU>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int FM = BM / 64;                  // 32-row MFMA blocks per wave
-  constexpr int LA = BM / 32;                  // A chunks loaded per thread
-  constexpr int LB = kBN / 32;                 // B chunks loaded per thread
-  constexpr int kStage = (BM + kBN) * kCh;     // u32x4 per LDS stage
-  __shared__ u32x4 lds[2 * kStage];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
-  const int total_mt = uniform(st.tile_start[g.nseg]);
-  const int ntn = g.N / kBN;
-  const int total = total_mt * ntn;
-  const int nk = g.K / kBK;
-  const uint32_t row_bytes = static_cast<uint32_t>(g.K) * 2u;
-
-  const int per_xcd = gridDim.x >> 3;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-
-  const uint16_t* Wb = static_cast<const uint16_t*>(g.W);
-  const uint16_t* Bias = static_cast<const uint16_t*>(g.bias);
-  uint16_t* C = static_cast<uint16_t*>(g.C);
-
-  const int ld_row = tid >> 3;   // + 32 i
-  const int ld_ch = tid & 7;
-  const int sw = ld_ch ^ (ld_row & 7);
-  // MFMA operand reads: row % 8 == lane % 8 for every block
-  const int rd_row = lane & 31;
-
-  for (int it = 0;; ++it) {
-    const int L = it * gridDim.x + xcd * per_xcd + slot;
-    if (L >= total) break;
-    // logical tile -> (M tile, N tile), grouped kGroupM M tiles at a time
-    const int gsz = kGroupM * ntn;
-    const int grp = L / gsz;
-    const int first_m = grp * kGroupM;
-    const int gm = min(kGroupM, total_mt - first_m);
-    const int r = L - grp * gsz;
-    const int mt = first_m + r % gm;
-    const int nt = r / gm;
-
-    // segment values are uniform across the workgroup; keep them in SGPRs
-    const int s = uniform(find_segment(st.tile_start, g.nseg, mt));
-    const int rows = uniform(st.rows[s]);
-    const int m0 = (mt - uniform(st.tile_start[s])) * BM;  // first row within the segment
-    const int a_off = uniform(g.a_by_o_off ? st.o_off[s] : st.a_off[s]);
-    const int o_off = uniform(st.o_off[s]);
-    const uint16_t* A = static_cast<const uint16_t*>(s < g.E ? g.a_routed : g.a_shared) +
-                        static_cast<size_t>(a_off) * g.K;
-    // rows past the segment read as zero (buffer bounds check) and are never stored
-    const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, static_cast<uint32_t>(rows) * row_bytes);
-    const __amdgpu_buffer_rsrc_t rb_rsrc =
-        make_rsrc(Wb + static_cast<size_t>(s) * g.N * g.K, static_cast<uint32_t>(g.N) * row_bytes);
-    const int n0 = nt * kBN;
-    const uint32_t va = static_cast<uint32_t>(m0 + ld_row) * row_bytes + ld_ch * 16;
-    const uint32_t vb = static_cast<uint32_t>(n0 + ld_row) * row_bytes + ld_ch * 16;
-    const uint32_t step32 = 32u * row_bytes;
-
-    floatx16 acc[FM][4];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    u32x4 ra[LA], rb[LB];
-#pragma unroll
-    for (int i = 0; i < LA; ++i) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, va, i * step32, 0);
-#pragma unroll
-    for (int i = 0; i < LB; ++i) rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, vb, i * step32, 0);
-#pragma unroll
-    for (int i = 0; i < LA; ++i) lds[(ld_row + 32 * i) * kCh + sw] = ra[i];
-#pragma unroll
-    for (int i = 0; i < LB; ++i) lds[(BM + ld_row + 32 * i) * kCh + sw] = rb[i];
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        const int kb = (kt + 1) * kBK * 2;
-#pragma unroll
-        for (int i = 0; i < LA; ++i) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, va, i * step32 + kb, 0);
-#pragma unroll
-        for (int i = 0; i < LB; ++i) rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, vb, i * step32 + kb, 0);
-      }
-      const u32x4* sa = lds + cur * kStage;
-      const u32x4* sb = sa + BM * kCh;
-#pragma unroll
-      for (int ks = 0; ks < kBK / 16; ++ks) {
-        const int ch = (2 * ks + (lane >> 5)) ^ (lane & 7);
-        bf16x8 af[FM], bfv[4];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[i] = __builtin_bit_cast(bf16x8, sa[(wm * (BM / 2) + i * 32 + rd_row) * kCh + ch]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bfv[j] = __builtin_bit_cast(bf16x8, sb[(wn * 128 + j * 32 + rd_row) * kCh + ch]);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
-      }
-      if (more) {
-        u32x4* dst = lds + (cur ^ 1) * kStage;
-#pragma unroll
-        for (int i = 0; i < LA; ++i) dst[(ld_row + 32 * i) * kCh + sw] = ra[i];
-#pragma unroll
-        for (int i = 0; i < LB; ++i) dst[(BM + ld_row + 32 * i) * kCh + sw] = rb[i];
-      }
-      __syncthreads();
-    }
-
-    // epilogue: 32x32 block (i, j), accumulator v of this lane holds
-    // row 8 (v / 4) + 4 (lane / 32) + v % 4, column lane % 32
-    const int col0 = n0 + wn * 128 + (lane & 31);
-    float bj[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bj[j] = bf16_to_f32(Bias[static_cast<size_t>(s) * g.N + col0 + j * 32]);
-    const bool full = m0 + BM <= rows;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rl = m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (full || rl < rows) {
-          uint16_t* crow = C + static_cast<size_t>(o_off + rl) * g.N + col0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float val = acc[i][j][v] + bj[j];
-            if (GELU) val = gelu_erf(val);
-            crow[j * 32] = f32_to_bf16(val);
-          }
-        }
-      }
-    }
-  }
 }
 
 // ------------------------------------------------------ 8-wave MFMA path --
@@ -415,6 +276,158 @@ __global__ __launch_bounds__(512) void gemm_bf16_w8_kernel(GemmArgs g) {
   }
 }
 
+// ------------------------------------------------- 128-row streaming path --
+// For experts with few rows each (fine-grained experts, capacity-limited
+// experts) the GEMM is bound by streaming the expert weights from HBM.
+// 128 x 256 x 64 tiles, 4 waves (2 x 2, wave tile 64 x 128), direct
+// global->LDS loads into a 3-stage LDS ring (48 KB per stage), issued two K
+// steps ahead so ~96 KB per CU stay in flight.  The barrier before K step
+// k+1 waits only for stage k+1 (vmcnt), never for stage k+2.
+template <bool GELU>
+__global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(GemmArgs g) {
+  constexpr int BM = 128;
+  constexpr int NS = 3;
+  constexpr int kStage = (BM + kBN) * kCh;     // u32x4 per stage (48 KB)
+  constexpr int LA = BM / 32, LB = kBN / 32;   // direct loads per wave per stage (4 + 8)
+  __shared__ u32x4 lds[NS * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
+  const int total_mt = uniform(st.tile_start[g.nseg]);
+  const int ntn = g.N / kBN;
+  const int total = total_mt * ntn;
+  const int nk = g.K / kBK;
+  const uint32_t row_bytes = static_cast<uint32_t>(g.K) * 2u;
+
+  const int per_xcd = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+
+  const uint16_t* Wb = static_cast<const uint16_t*>(g.W);
+  const uint16_t* Bias = static_cast<const uint16_t*>(g.bias);
+  uint16_t* C = static_cast<uint16_t*>(g.C);
+
+  // direct loads: wave w's load i fills LDS rows 8 (4 i + w) + lane / 8 at
+  // physical chunk lane % 8, fetching the logical chunk that lands there
+  const int dr_row = 8 * wave + (lane >> 3);
+  const int dr_ch = swz(dr_row, lane & 7);
+  const int rd_row = lane & 31;
+
+  for (int it = 0;; ++it) {
+    const int L = it * gridDim.x + xcd * per_xcd + slot;
+    if (L >= total) break;
+    const int gsz = kGroupM * ntn;
+    const int gq = L / gsz;
+    const int first_m = gq * kGroupM;
+    const int gm = min(kGroupM, total_mt - first_m);
+    const int r = L - gq * gsz;
+    const int mt = first_m + r % gm;
+    const int nt = r / gm;
+
+    const int s = uniform(find_segment(st.tile_start, g.nseg, mt));
+    const int rows = uniform(st.rows[s]);
+    const int m0 = (mt - uniform(st.tile_start[s])) * BM;
+    const int a_off = uniform(g.a_by_o_off ? st.o_off[s] : st.a_off[s]);
+    const int o_off = uniform(st.o_off[s]);
+    const uint16_t* A = static_cast<const uint16_t*>(s < g.E ? g.a_routed : g.a_shared) +
+                        static_cast<size_t>(a_off) * g.K;
+    const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, static_cast<uint32_t>(rows) * row_bytes);
+    const __amdgpu_buffer_rsrc_t rb_rsrc =
+        make_rsrc(Wb + static_cast<size_t>(s) * g.N * g.K, static_cast<uint32_t>(g.N) * row_bytes);
+    const int n0 = nt * kBN;
+    const uint32_t step32 = 32u * row_bytes;
+    const uint32_t va = static_cast<uint32_t>(m0 + dr_row) * row_bytes + dr_ch * 16;
+    const uint32_t vb = static_cast<uint32_t>(n0 + dr_row) * row_bytes + dr_ch * 16;
+
+    floatx16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    auto issue = [&](int k) {
+      u32x4* base = lds + (k % NS) * kStage + (8 * wave) * kCh;
+      const int kb = k * kBK * 2;
+#pragma unroll
+      for (int i = 0; i < LA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra_rsrc, (__attribute__((address_space(3))) void*)(base + 32 * i * kCh), 16, va, i * step32 + kb, 0, 0);
+#pragma unroll
+      for (int i = 0; i < LB; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb_rsrc, (__attribute__((address_space(3))) void*)(base + (BM + 32 * i) * kCh), 16, vb,
+            i * step32 + kb, 0, 0);
+    };
+
+    issue(0);
+    if (nk > 1) {
+      issue(1);
+      __builtin_amdgcn_s_waitcnt(0x0F7C);   // vmcnt <= 12: stage 0 landed, stage 1 may be in flight
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    lds_barrier();
+
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 2 < nk) issue(kt + 2);      // slot of stage kt-1, read before the last barrier
+      const u32x4* sa = lds + (kt % NS) * kStage;
+      const u32x4* sb = sa + BM * kCh;
+      bf16x8 fa[2][2], fb[2][4];
+      auto frag = [&](int ks, int buf) {
+        const int ch = swz(rd_row, 2 * ks + (lane >> 5));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          fa[buf][i] = __builtin_bit_cast(bf16x8, sa[(wm * 64 + i * 32 + rd_row) * kCh + ch]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          fb[buf][j] = __builtin_bit_cast(bf16x8, sb[(wn * 128 + j * 32 + rd_row) * kCh + ch]);
+      };
+      frag(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < kBK / 16; ++ks) {
+        if (ks + 1 < kBK / 16) frag(ks + 1, (ks + 1) & 1);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
+      }
+      // before K step kt+1: its stage has landed (stage kt+2's loads may stay in flight)
+      if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(0x0F7C);
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+      lds_barrier();
+    }
+
+    // epilogue: accumulator v of block (i, j) holds row 8 (v / 4) + 4 (lane / 32) + v % 4,
+    // column lane % 32 of that block
+    const int col0 = n0 + wn * 128 + (lane & 31);
+    float bj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bj[j] = bf16_to_f32(Bias[static_cast<size_t>(s) * g.N + col0 + j * 32]);
+    const bool full = m0 + BM <= rows;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rl = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (full || rl < rows) {
+          uint16_t* crow = C + static_cast<size_t>(o_off + rl) * g.N + col0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float val = acc[i][j][v] + bj[j];
+            if (GELU) val = gelu_erf(val);
+            crow[j * 32] = f32_to_bf16(val);
+          }
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ SIMT path --
 constexpr int kSB = 64, kSK = 16;
 
@@ -503,7 +516,8 @@ bool gemm_fast_path(const Problem& p) {
   return rows * widest * 2 < (1LL << 31) && static_cast<long long>(p.h) * p.d * 2 < (1LL << 31);
 }
 
-// 256-row tiles for segments that average >= 512 rows, else 128-row tiles.
+// 256-row tiles (compute-bound, 8-wave kernel) for segments that average
+// >= 512 rows; 128-row tiles (weight streaming kernel) otherwise.
 int gemm_m_tile(const Problem& p) {
   if (!gemm_fast_path(p)) return kSB;
   long long avg = static_cast<long long>(p.T) * p.k / p.E;
@@ -546,9 +560,9 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
         hipLaunchKernelGGL((gemm_bf16_w8_kernel<false>), dim3(grid), dim3(512), 0, st, g);
     } else {
       if (phase == 1)
-        hipLaunchKernelGGL((gemm_bf16_kernel<128, true>), dim3(grid), dim3(256), 0, st, g);
+        hipLaunchKernelGGL((gemm_bf16_stream_kernel<true>), dim3(grid), dim3(256), 0, st, g);
       else
-        hipLaunchKernelGGL((gemm_bf16_kernel<128, false>), dim3(grid), dim3(256), 0, st, g);
+        hipLaunchKernelGGL((gemm_bf16_stream_kernel<false>), dim3(grid), dim3(256), 0, st, g);
     }
   } else {
     // upper bound of M tiles: sum_e ceil(rows_e / 64) <= ceil(T k / 64) + E + S ceil(T / 64)

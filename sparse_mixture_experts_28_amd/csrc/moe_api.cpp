@@ -23,7 +23,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t elem_bytes(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t xperm, hbuf, ybuf, local_rank, tile_hist, p_part, counts, kept, slot_pos, seg, total;
+  size_t xperm, hbuf, ybuf, local_rank, tile_hist, p_part, counts, kept, slot_pos, seg, logits, total;
 };
 
 Layout layout_of(const Problem& p) {
@@ -43,6 +43,7 @@ Layout layout_of(const Problem& p) {
   L.kept = off;       off += align_up(static_cast<size_t>(p.E) * 4);
   L.slot_pos = off;   off += align_up(A * 4);
   L.seg = off;        off += align_up(seg_table_ints(p.E + p.S, p.E) * 4);
+  L.logits = off;     off += align_up(static_cast<size_t>(p.T) * ((p.E + 63) / 64 * 64) * 8);
   L.total = off;
   return L;
 }
@@ -67,6 +68,7 @@ Workspace carve_workspace(const Problem& p, void* base, size_t bytes_available, 
   w.kept = reinterpret_cast<int32_t*>(b + L.kept);
   w.slot_pos = reinterpret_cast<int32_t*>(b + L.slot_pos);
   w.seg = reinterpret_cast<int32_t*>(b + L.seg);
+  w.logits = reinterpret_cast<double*>(b + L.logits);
   w.bytes = L.total;
   return w;
 }

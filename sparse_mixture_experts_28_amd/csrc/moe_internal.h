@@ -42,12 +42,13 @@ struct Workspace {
   void* hbuf;           // [R, h]     GELU(x W1^T + b1)
   void* ybuf;           // [R, d]     h W2^T + b2
   int32_t* local_rank;  // [T, k]     rank of (t,j) among earlier tokens of its 64-token tile
-  int32_t* tile_hist;   // [ntile, E] assignments per (tile, expert); becomes the tile base
-  float* p_part;        // [ntile, E] per-tile sums of the softmax probabilities
+  int32_t* tile_hist;   // [E, ntile] assignments per (expert, tile); becomes the tile base
+  float* p_part;        // [E, ntile] per-tile sums of the softmax probabilities
   int32_t* counts;      // [E]
   int32_t* kept;        // [E]
   int32_t* slot_pos;    // [T, k]
   int32_t* seg;         // segment table, see SegTable
+  double* logits;       // [T, Epad] float64 router logits (bf16 path), Epad <= ceil64(E)
   size_t bytes;
 };
 

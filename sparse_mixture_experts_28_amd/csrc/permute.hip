@@ -8,8 +8,8 @@
 // E * sum f_i P_i); "第7章" tensor-shape trace (the token -> expert reordering
 // is the real cost of the layer).
 //
-// scan    (1 workgroup): for every expert, an exclusive scan of its per-tile
-//         counts over the tiles in token order gives each tile's base rank;
+// scan    (1 workgroup of 1024): for every expert, an exclusive scan of its
+//         per-tile counts over the tiles in token order gives each tile's base rank;
 //         the total is c_e, kept_e = min(c_e, cap); an exclusive scan of kept
 //         over experts gives the segment offsets; the balance loss is
 //         finalised from c and the per-tile probability sums (float64, fixed
@@ -24,70 +24,124 @@
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(256) void scan_kernel(Problem p, int32_t* tile_hist, const float* p_part,
-                                                   int32_t* counts, int32_t* kept, int32_t* seg_base,
-                                                   float* aux_loss, int32_t* counts_out,
-                                                   int32_t* kept_out) {
+constexpr int kScanThreads = 1024;
+
+// Thread t works on expert e = t % E over the tiles of chunk c = t / E (C
+// chunks of consecutive tiles); per-chunk totals are scanned over c in LDS in
+// fixed order, so bases, counts and the probability sums are deterministic.
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* tile_hist, const float* p_part,
+                                                            int32_t* counts, int32_t* kept, int32_t* seg_base,
+                                                            float* aux_loss, int32_t* counts_out,
+                                                            int32_t* kept_out) {
+  __shared__ int32_t s_sum[kScanThreads];
+  __shared__ double s_psum[kScanThreads];
   __shared__ int32_t s_kept[MOE_MAX_EXPERTS];
   __shared__ int32_t s_cnt[MOE_MAX_EXPERTS];
   __shared__ double s_P[MOE_MAX_EXPERTS];
   const int E = p.E;
   const int nseg = p.E + p.S;
   SegTable st = seg_table(seg_base, nseg, E);
+  const int C = max(1, kScanThreads / E);
+  const int tpc = (p.ntile + C - 1) / C;
+  const int t = threadIdx.x;
+  const int e = t % E, c = t / E;
+  const bool active = c < C;
+  const int tb = c * tpc, te = min(p.ntile, tb + tpc);
 
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = 0;
-    double psum = 0.0;
-    for (int tile = 0; tile < p.ntile; ++tile) {
-      const size_t i = static_cast<size_t>(tile) * E + e;
-      const int h = tile_hist[i];
-      tile_hist[i] = run;       // becomes the tile's base rank for expert e
-      run += h;
-      psum += static_cast<double>(p_part[i]);
+  // 1. chunk totals (per-expert layout [E][ntile]: each thread reads a contiguous run)
+  int sum = 0;
+  double psum = 0.0;
+  const int32_t* hrow = tile_hist + static_cast<size_t>(e) * p.ntile;
+  const float* prow = p_part + static_cast<size_t>(e) * p.ntile;
+  if (active) {
+#pragma unroll 8
+    for (int tile = tb; tile < te; ++tile) {
+      sum += hrow[tile];
+      psum += static_cast<double>(prow[tile]);
     }
-    const int kp = min(run, p.cap);
-    counts[e] = run;
-    kept[e] = kp;
-    if (counts_out) counts_out[e] = run;
-    if (kept_out) kept_out[e] = kp;
-    s_kept[e] = kp;
-    s_cnt[e] = run;
-    s_P[e] = psum / static_cast<double>(p.T);
+    s_sum[c * E + e] = sum;
+    s_psum[c * E + e] = psum;
   }
   __syncthreads();
-
-  if (threadIdx.x == 0) {
-    // aux = E * sum_e f_e P_e, f_e = c_e / (T k)
-    const double tk = static_cast<double>(p.T) * static_cast<double>(p.k);
-    double s = 0.0;
-    for (int e = 0; e < E; ++e) s += (static_cast<double>(s_cnt[e]) / tk) * s_P[e];
-    *aux_loss = static_cast<float>(static_cast<double>(E) * s);
-
-    // segment table: routed experts then shared experts
-    int off = 0;
-    int tiles = 0;
-    const int bm = p.gemm_bm;
-    const int routed_rows = p.T * p.k;
-    for (int e = 0; e < nseg; ++e) {
-      int rows, a_off, o_off;
-      if (e < E) {
-        rows = s_kept[e];
-        a_off = off;
-        o_off = off;
-        st.route_off[e] = off;
-        off += rows;
-      } else {
-        rows = p.T;
-        a_off = 0;
-        o_off = routed_rows + (e - E) * p.T;
-      }
-      st.rows[e] = rows;
-      st.a_off[e] = a_off;
-      st.o_off[e] = o_off;
-      st.tile_start[e] = tiles;
-      tiles += (rows + bm - 1) / bm;
+  // 2. per expert: exclusive scan of the chunk totals (in place), totals
+  if (t < E) {
+    int run = 0;
+    double pr = 0.0;
+    for (int q = 0; q < C; ++q) {
+      const int v = s_sum[q * E + t];
+      s_sum[q * E + t] = run;
+      run += v;
+      pr += s_psum[q * E + t];
     }
-    st.tile_start[nseg] = tiles;
+    const int kp = min(run, p.cap);
+    counts[t] = run;
+    kept[t] = kp;
+    if (counts_out) counts_out[t] = run;
+    if (kept_out) kept_out[t] = kp;
+    s_kept[t] = kp;
+    s_cnt[t] = run;
+    s_P[t] = pr / static_cast<double>(p.T);
+  }
+  __syncthreads();
+  // 3. tile bases within the chunk
+  if (active) {
+    int run = s_sum[c * E + e];
+    int32_t* wrow = tile_hist + static_cast<size_t>(e) * p.ntile;
+#pragma unroll 8
+    for (int tile = tb; tile < te; ++tile) {
+      const int h = wrow[tile];
+      wrow[tile] = run;         // becomes the tile's base rank for expert e
+      run += h;
+    }
+  }
+
+  // 4. aux = E * sum_e f_e P_e, f_e = c_e / (T k): a fixed-order tree over experts
+  __shared__ double s_aux[MOE_MAX_EXPERTS];
+  const double tk = static_cast<double>(p.T) * static_cast<double>(p.k);
+  if (t < MOE_MAX_EXPERTS) s_aux[t] = t < E ? (static_cast<double>(s_cnt[t]) / tk) * s_P[t] : 0.0;
+  // 5. segment table: one thread per segment (routed experts, then shared)
+  constexpr int kSegSlots = 512;   // >= MOE_MAX_EXPERTS + MOE_MAX_SHARED
+  __shared__ int32_t s_rows[kSegSlots];
+  __shared__ int32_t s_tiles[kSegSlots];
+  const int bm = p.gemm_bm;
+  int my_rows = 0, my_tiles = 0;
+  if (t < nseg) {
+    my_rows = t < E ? s_kept[t] : p.T;
+    my_tiles = (my_rows + bm - 1) / bm;
+  }
+  if (t < kSegSlots) {
+    s_rows[t] = t < E ? my_rows : 0;     // only routed rows are packed in the sorted buffer
+    s_tiles[t] = my_tiles;
+  }
+  __syncthreads();
+  for (int w = MOE_MAX_EXPERTS / 2; w > 0; w >>= 1) {
+    if (t < w) s_aux[t] += s_aux[t + w];
+    __syncthreads();
+  }
+  if (t == 0) *aux_loss = static_cast<float>(static_cast<double>(E) * s_aux[0]);
+  // inclusive scans of routed rows and of M tiles over the segments
+  for (int off = 1; off < kSegSlots; off <<= 1) {
+    int ar = 0, at = 0;
+    if (t < kSegSlots && t >= off) {
+      ar = s_rows[t - off];
+      at = s_tiles[t - off];
+    }
+    __syncthreads();
+    if (t < kSegSlots) {
+      s_rows[t] += ar;
+      s_tiles[t] += at;
+    }
+    __syncthreads();
+  }
+  if (t < nseg) {
+    const int routed_rows = p.T * p.k;
+    const int excl_rows = s_rows[t] - (t < E ? my_rows : 0);
+    st.rows[t] = my_rows;
+    st.a_off[t] = t < E ? excl_rows : 0;
+    st.o_off[t] = t < E ? excl_rows : routed_rows + (t - E) * p.T;
+    st.tile_start[t] = s_tiles[t] - my_tiles;
+    if (t < E) st.route_off[t] = excl_rows;
+    if (t == nseg - 1) st.tile_start[nseg] = s_tiles[t];
   }
 }
 
@@ -106,7 +160,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(Problem p, const Vec* __re
     const int j = threadIdx.x;
     const int e = topk_idx[static_cast<size_t>(t) * k + j];
     const int tile = t / kRouterTile;
-    const int rank = tile_base[static_cast<size_t>(tile) * p.E + e] + local_rank[static_cast<size_t>(t) * k + j];
+    const int rank = tile_base[static_cast<size_t>(e) * p.ntile + tile] + local_rank[static_cast<size_t>(t) * k + j];
     SegTable st = seg_table(const_cast<int32_t*>(seg_base), p.E + p.S, p.E);
     const int pos = rank < p.cap ? st.route_off[e] + rank : -1;
     slot_pos[static_cast<size_t>(t) * k + j] = pos;
@@ -127,7 +181,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(Problem p, const Vec* __re
 
 hipError_t launch_scan(const Problem& p, const Workspace& ws, float* aux_loss, int32_t* counts_out,
                        int32_t* kept_out, hipStream_t st) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, st, p, ws.tile_hist, ws.p_part, ws.counts,
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, st, p, ws.tile_hist, ws.p_part, ws.counts,
                      ws.kept, ws.seg, aux_loss, counts_out, kept_out);
   return hipGetLastError();
 }

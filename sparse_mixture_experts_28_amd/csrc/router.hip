@@ -25,6 +25,8 @@
 namespace moe {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kFlushSteps = 8;  // MFMA k-steps (of 32) per float32 chunk -> 256 elements
 
 struct RouterArgs {
@@ -36,10 +38,8 @@ struct RouterArgs {
   int32_t* local_rank;
   int32_t* tile_hist;
   float* p_part;
-  int T, d, E, k;
+  int T, d, E, k, ntile;
 };
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-lane argmax: larger value wins, equal values go to the lower index.
 __device__ __forceinline__ void argmax16(double& v, int& i) {
@@ -68,7 +68,7 @@ __device__ __forceinline__ float sum16(float v) {
 template <int NB>
 __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0) {
   __shared__ int32_t s_idx[kRouterTile * MOE_MAX_TOPK];
-  __shared__ int32_t s_rank[kRouterTile * MOE_MAX_TOPK];
+  __shared__ unsigned long long s_mask[16 * NB];
   __shared__ float s_p[4][16 * NB];
 
   const int lane = threadIdx.x & 63;
@@ -151,22 +151,26 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
 
   const int ntok = min(kRouterTile, a.T - tile0);
   const int tile = tile0 / kRouterTile;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    a.p_part[static_cast<size_t>(tile) * E + e] = ((s_p[0][e] + s_p[1][e]) + s_p[2][e]) + s_p[3][e];
-    // in-tile ranks in token order: a token's k experts are distinct, so each
-    // token adds at most one assignment to expert e
-    int cnt = 0;
-    for (int r = 0; r < ntok; ++r) {
-      for (int j = 0; j < k; ++j) {
-        if (s_idx[r * MOE_MAX_TOPK + j] == e) { s_rank[r * MOE_MAX_TOPK + j] = cnt++; break; }
-      }
-    }
-    a.tile_hist[static_cast<size_t>(tile) * E + e] = cnt;
+  // In-tile ranks in token order.  mask[e] has bit r set iff token r of the
+  // tile chose e (a token's k experts are distinct, and OR is order-free, so
+  // the masks are deterministic); the rank of (r, j) is the number of earlier
+  // tokens in its expert's mask, the tile histogram the mask's population.
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_mask[e] = 0ull;
+  __syncthreads();
+  if (threadIdx.x < ntok) {
+    const int r = threadIdx.x;
+    for (int j = 0; j < k; ++j) atomicOr(&s_mask[s_idx[r * MOE_MAX_TOPK + j]], 1ull << r);
   }
   __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    // per-expert layout [E][ntile]: the scan reads each expert's tiles contiguously
+    a.p_part[static_cast<size_t>(e) * a.ntile + tile] = ((s_p[0][e] + s_p[1][e]) + s_p[2][e]) + s_p[3][e];
+    a.tile_hist[static_cast<size_t>(e) * a.ntile + tile] = __popcll(s_mask[e]);
+  }
   for (int i = threadIdx.x; i < ntok * k; i += blockDim.x) {
     const int r = i / k, j = i - r * k;
-    a.local_rank[static_cast<size_t>(tile0 + r) * k + j] = s_rank[r * MOE_MAX_TOPK + j];
+    const unsigned long long below = (1ull << r) - 1ull;
+    a.local_rank[static_cast<size_t>(tile0 + r) * k + j] = __popcll(s_mask[s_idx[r * MOE_MAX_TOPK + j]] & below);
   }
 }
 
@@ -269,6 +273,174 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(RouterArgs a
   route_tile<NB>(a, acc, tile0);
 }
 
+// ---- bf16 inputs, d % 256 == 0: logits kernel + selection kernel ----
+//
+// Logits.  A workgroup (4 waves) owns TT = 64 / KS tokens and ES = 16 * NBW
+// experts; the KS waves that share 16 tokens split the blocks of P k-steps
+// (32 elements each) of d round-robin.  Operands go straight from memory into
+// registers (x rows once per expert slice; the router weight from L2), two
+// blocks in flight, 16x16x32 MFMA in float32 per block (<= 256 elements),
+// blocks added in float64, the KS partials summed in float64 in fixed order.
+// Output: float64 logits [T, Epad].
+constexpr uint32_t kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kRsrcWord3);
+}
+
+struct LogitArgs {
+  const uint16_t* x;
+  const uint16_t* W;
+  double* logits;   // [T, Epad]
+  int T, d, E, Epad;
+};
+
+template <int NBW, int KS>
+__global__ __launch_bounds__(256) void router_logits_kernel(LogitArgs a) {
+  constexpr int ES = 16 * NBW;
+  constexpr int TT = 64 / KS;
+  constexpr int P = NBW == 1 ? 8 : (NBW == 2 ? 4 : 2);   // k-steps per block
+  __shared__ double red[4][ES][16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tg = wave / KS, kw = wave % KS;
+  const int c = lane & 15, g = lane >> 4;
+  const int tile0 = blockIdx.x * TT;
+  const int e0 = blockIdx.y * ES;
+  const uint32_t rb = static_cast<uint32_t>(a.d) * 2u;   // bytes per row
+  const int nrows = min(TT, a.T - tile0);
+  const int nexp = min(ES, a.E - e0);
+  // out-of-range token rows and expert rows read as zero (buffer range check)
+  const __amdgpu_buffer_rsrc_t xs = rsrc(a.x + static_cast<size_t>(tile0) * a.d, static_cast<uint32_t>(nrows) * rb);
+  const __amdgpu_buffer_rsrc_t ws = rsrc(a.W + static_cast<size_t>(e0) * a.d, static_cast<uint32_t>(max(nexp, 0)) * rb);
+  const uint32_t xo = static_cast<uint32_t>(tg * 16 + c) * rb + g * 16;
+  uint32_t wo[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) wo[nb] = static_cast<uint32_t>(nb * 16 + c) * rb + g * 16;
+
+  const int nblk = a.d / (32 * P);
+  double acc[NBW][4];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[nb][v] = 0.0;
+
+  u32x4 xa[2][P], wa[2][P][NBW];
+  auto load = [&](int blk, int buf) {
+    const uint32_t kb = static_cast<uint32_t>(blk) * (P * 64);
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      xa[buf][q] = __builtin_amdgcn_raw_buffer_load_b128(xs, xo, kb + q * 64, 0);
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) wa[buf][q][nb] = __builtin_amdgcn_raw_buffer_load_b128(ws, wo[nb], kb + q * 64, 0);
+    }
+  };
+  auto compute = [&](int buf) {
+    floatx4 part[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) part[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < P; ++q)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+        part[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[buf][q]),
+                                                            __builtin_bit_cast(bf16x8, wa[buf][q][nb]), part[nb], 0, 0, 0);
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[nb][v] += static_cast<double>(part[nb][v]);
+  };
+  // blocks kw, kw + KS, ...: two in flight, buffers alternate (unrolled by two
+  // so that every register index is a compile-time constant)
+  int blk = kw;
+  if (blk < nblk) load(blk, 0);
+  while (blk < nblk) {
+    if (blk + KS < nblk) load(blk + KS, 1);
+    compute(0);
+    blk += KS;
+    if (blk >= nblk) break;
+    if (blk + KS < nblk) load(blk + KS, 0);
+    compute(1);
+    blk += KS;
+  }
+
+  // lane (c, g) holds tokens tg*16 + 4g + v and experts nb*16 + c
+  if constexpr (KS == 1) {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = tile0 + tg * 16 + 4 * g + v;
+        if (t < a.T) a.logits[static_cast<size_t>(t) * a.Epad + e0 + nb * 16 + c] = acc[nb][v];
+      }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave][nb * 16 + c][4 * g + v] = acc[nb][v];
+    __syncthreads();
+    // 16 tokens per token group: sum the KS partials in wave order
+    for (int i = threadIdx.x; i < TT * ES; i += blockDim.x) {
+      const int tl = i / ES, e = i - tl * ES;
+      const int grp = tl / 16, r = tl - grp * 16;
+      double sum = 0.0;
+#pragma unroll
+      for (int q = 0; q < KS; ++q) sum += red[grp * KS + q][e][r];
+      const int t = tile0 + tl;
+      if (t < a.T) a.logits[static_cast<size_t>(t) * a.Epad + e0 + e] = sum;
+    }
+  }
+}
+
+// Selection from float64 logits [T, Epad] for one 64-token tile: the logits are
+// placed in the MFMA-result register layout route_tile expects.
+template <int NB>
+__global__ __launch_bounds__(kRouterThreads) void router_select_kernel(RouterArgs a, const double* logits, int Epad) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = lane & 15;
+  const int g = lane >> 4;
+  const int tile0 = blockIdx.x * kRouterTile;
+  double acc[NB][4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int t = tile0 + wave * 16 + g * 4 + v;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int e = nb * 16 + c;
+      acc[nb][v] = (t < a.T && e < Epad) ? logits[static_cast<size_t>(t) * Epad + e] : 0.0;
+    }
+  }
+  route_tile<NB>(a, acc, tile0);
+}
+
+template <int NBW, int KS>
+hipError_t launch_logits(const Problem& p, const LogitArgs& la, hipStream_t st) {
+  constexpr int ES = 16 * NBW;
+  constexpr int TT = 64 / KS;
+  dim3 grid((p.T + TT - 1) / TT, (p.E + ES - 1) / ES);
+  hipLaunchKernelGGL((router_logits_kernel<NBW, KS>), grid, dim3(256), 0, st, la);
+  return hipGetLastError();
+}
+
+template <int NBW>
+hipError_t launch_logits_ks(const Problem& p, const LogitArgs& la, hipStream_t st) {
+  constexpr int ES = 16 * NBW;
+  const long long slices = (p.E + ES - 1) / ES;
+  // smallest token tile (most split of d) that still gives >= 512 workgroups
+  if (static_cast<long long>((p.T + 63) / 64) * slices >= 512) return launch_logits<NBW, 1>(p, la, st);
+  if (static_cast<long long>((p.T + 31) / 32) * slices >= 512) return launch_logits<NBW, 2>(p, la, st);
+  return launch_logits<NBW, 4>(p, la, st);
+}
+
+template <int NB>
+hipError_t launch_select(const Problem& p, const RouterArgs& a, const double* logits, int Epad, hipStream_t st) {
+  hipLaunchKernelGGL((router_select_kernel<NB>), dim3(p.ntile), dim3(kRouterThreads), 0, st, a, logits, Epad);
+  return hipGetLastError();
+}
+
 template <int NB>
 hipError_t launch_nb(const Problem& p, const RouterArgs& a, hipStream_t st) {
   dim3 grid(p.ntile), block(kRouterThreads);
@@ -296,7 +468,28 @@ hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const
   a.d = p.d;
   a.E = p.E;
   a.k = p.k;
+  a.ntile = p.ntile;
   const int nb = (p.E + 15) / 16;
+  if (p.dtype == MOE_BF16 && p.d % 256 == 0 && ws.logits != nullptr) {
+    LogitArgs la;
+    la.x = static_cast<const uint16_t*>(x);
+    la.W = static_cast<const uint16_t*>(W_g);
+    la.logits = ws.logits;
+    la.T = p.T;
+    la.d = p.d;
+    la.E = p.E;
+    const int nbw = nb <= 1 ? 1 : (nb <= 2 ? 2 : 4);
+    la.Epad = ((p.E + 16 * nbw - 1) / (16 * nbw)) * 16 * nbw;
+    hipError_t e = nbw == 1 ? launch_logits_ks<1>(p, la, st)
+                 : nbw == 2 ? launch_logits_ks<2>(p, la, st)
+                            : launch_logits_ks<4>(p, la, st);
+    if (e != hipSuccess) return e;
+    if (nb <= 1) return launch_select<1>(p, a, la.logits, la.Epad, st);
+    if (nb <= 2) return launch_select<2>(p, a, la.logits, la.Epad, st);
+    if (nb <= 4) return launch_select<4>(p, a, la.logits, la.Epad, st);
+    if (nb <= 8) return launch_select<8>(p, a, la.logits, la.Epad, st);
+    return launch_select<16>(p, a, la.logits, la.Epad, st);
+  }
   if (nb <= 1) return launch_nb<1>(p, a, st);
   if (nb <= 2) return launch_nb<2>(p, a, st);
   if (nb <= 4) return launch_nb<4>(p, a, st);

@@ -34,10 +34,6 @@
 // Fallback (any shape, float32 or bf16): 64 x 64 SIMT tiles, float32 accumulation.
 #include "moe_internal.h"
 
-// Pin the MFMA / LDS-read / global-load interleave of the K steps.
-#ifndef MOE_GEMM_SCHED
-#define MOE_GEMM_SCHED 1
-#endif
 
 namespace moe {
 namespace {
@@ -75,6 +71,32 @@ __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
 }
 
+// GELU(v) = v/2 (1 + erf(v / sqrt 2)) with erf from Abramowitz & Stegun 7.1.26
+// (Hastings' rational approximation, |error| <= 1.5e-7 in erf): for z >= 0,
+// erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z);
+// odd in z.  Branch-free: one reciprocal, one exp2 and ~12 VALU operations.
+__device__ __forceinline__ float gelu_as(float v) {
+  const float z = fabsf(v) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float q = fmaf(t, 1.061405429f, -1.453152027f);
+  q = fmaf(t, q, 1.421413741f);
+  q = fmaf(t, q, -0.284496736f);
+  q = fmaf(t, q, 0.254829592f);
+  q *= t;
+  const float e = __builtin_amdgcn_exp2f((z * -1.44269504088896341f) * z);   // exp(-z^2)
+  const float erf_v = copysignf(fmaf(-q, e, 1.0f), v);
+  const float hv = 0.5f * v;
+  return fmaf(hv, erf_v, hv);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+// two floats -> two bfloat16 (round to nearest even) packed low/high
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const floatx2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 // segment s containing global M-tile mt: tile_start[s] <= mt < tile_start[s+1]
 __device__ __forceinline__ int find_segment(const int32_t* tile_start, int nseg, int mt) {
   int lo = 0, hi = nseg - 1;
@@ -103,29 +125,61 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            static_cast<int>(bytes), kRsrcWord3);
 }
 
-// ------------------------------------------------------ 8-wave MFMA path --
-// 256 x 256 x 64 tile, 8 waves (2 per SIMD) in a 2 (M) x 4 (N) grid, wave tile
-// 128 x 64 = 4 x 2 blocks of the 32x32x16 MFMA (128 float accumulators per
-// lane).  With two waves per SIMD, one wave's MFMAs cover the other's LDS and
-// memory waits.  Operand fragments are double-buffered in registers across
-// the four 16-deep k-steps of a tile step.  Tiles reach LDS directly
-// (buffer_load ... lds writes 64 lanes x 16 bytes contiguously at a
-// wave-uniform LDS address), without passing through registers.
-template <bool GELU>
-__global__ __launch_bounds__(512) void gemm_bf16_w8_kernel(GemmArgs g) {
-  constexpr int BM = 256;
-  constexpr int kStage = (BM + kBN) * kCh;     // u32x4 per LDS stage (64 KB)
-  __shared__ u32x4 lds[2 * kStage];
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding (n < 64) and does not wait on LDS or export counters
+constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// ------------------------------------------------------------ MFMA path --
+// BM x 256 x 64 tiles, BM in {128, 160, 256}; 4 waves (one per SIMD) in
+// a 2 x 2 grid, wave tile (BM / 2) x 128 built from the 16x16x32 bf16 MFMA:
+// (BM / 32) x 8 blocks of 4 float accumulators per lane (up to 256, held in
+// the accumulation registers).  The 16x16x32 form moves half the accumulator
+// register traffic per FLOP of the 32x32x16 form; on this part, whose clock
+// drops under full MFMA load, energy per FLOP sets the speed.
+//
+// Operands reach LDS by direct loads (buffer_load ... lds: 64 lanes x 16
+// bytes at a wave-uniform LDS address) into an NS-slot ring of 64-deep
+// stages ((BM + 256) rows x 128 bytes).  A K step works on two 32-deep
+// slices of its stage, in a fixed issue order (every MFMA followed by at most
+// one LDS fragment read and one direct load):
+//   slice 0: MFMAs; read slice 1 of stage t
+//   slice 1: wait for stage t+1 and the barrier that publishes it; stage t is
+//            then in registers in every wave, so its slot is refilled with
+//            stage t+NS; MFMAs; read slice 0 of stage t+1 (early in the
+//            slice); direct loads of stage t+NS (spread over the slice)
+// so fragment reads have a slice of MFMAs to land and (NS - 1) stages of
+// loads stay in flight.  NS = 3 for BM <= 160 (weight streaming: ~100 KB per
+// CU in flight), 2 for BM = 256 (two 64 KB stages).
+//
+// The tile height is chosen per problem so that an expert's rows usually
+// fill whole tiles: every M tile of an expert re-streams that expert's
+// weight panel, so rows spread over fewer, fuller tiles mean fewer weight bytes.
+//
+// Epilogue: the MFMA takes the B fragment first, so each block is
+// accumulated transposed: lane l holds output row 16 i + l % 16 of the wave
+// tile and the four consecutive columns 16 j + 4 (l / 16) + 0..3; bias, then
+// (phase 1) GELU, in float32, rounded once to bf16, one 8-byte store.
+template <bool GELU, int BM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_mfma_kernel(GemmArgs g) {
+  constexpr int NS = BM <= 160 ? 3 : 2;
+  constexpr int MB = BM / 32;                  // 16-row blocks per wave
+  constexpr int NR = MB + 8;                   // fragment reads per slice = direct loads per stage, per wave
+  constexpr int MF = MB * 8;                   // MFMAs per slice
+  constexpr int LS = MF / NR;                  // direct loads go one every LS MFMAs
+  constexpr int kStage = (BM + kBN) * kCh;     // u32x4 per LDS stage
+  static_assert(MF >= 2 * NR, "slice too short for its reads and loads");
+  __shared__ u32x4 lds[NS * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
   const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
   const int total_mt = uniform(st.tile_start[g.nseg]);
   const int ntn = g.N / kBN;
   const int total = total_mt * ntn;
-  const int nk = g.K / kBK;
+  const int nk = g.K / kBK;                    // >= 4: K is a multiple of 256 on this path
   const uint32_t row_bytes = static_cast<uint32_t>(g.K) * 2u;
 
   const int per_xcd = gridDim.x >> 3;
@@ -135,11 +189,11 @@ __global__ __launch_bounds__(512) void gemm_bf16_w8_kernel(GemmArgs g) {
   const uint16_t* Bias = static_cast<const uint16_t*>(g.bias);
   uint16_t* C = static_cast<uint16_t*>(g.C);
 
-  // direct loads: wave w, load i fills LDS rows 64 i + 8 w + lane / 8 at physical
-  // chunk lane % 8, so the lane fetches the logical chunk that lands there
+  // direct loads: wave w's load i fills LDS rows 32 i + 8 w + lane / 8 of its
+  // operand at physical chunk lane % 8, fetching the logical chunk that lands there
   const int dr_row = 8 * wave + (lane >> 3);
-  const int dr_ch = (lane & 7) ^ (dr_row & 7) ^ ((dr_row >> 3) & 1);
-  const int rd_row = lane & 31;
+  const int dr_ch = swz(dr_row, lane & 7);
+  const int rd_row = lane & 15;
 
   for (int it = 0;; ++it) {
     const int L = it * gridDim.x + xcd * per_xcd + slot;
@@ -163,265 +217,132 @@ __global__ __launch_bounds__(512) void gemm_bf16_w8_kernel(GemmArgs g) {
     const __amdgpu_buffer_rsrc_t rb_rsrc =
         make_rsrc(Wb + static_cast<size_t>(s) * g.N * g.K, static_cast<uint32_t>(g.N) * row_bytes);
     const int n0 = nt * kBN;
-    const uint32_t step64 = 64u * row_bytes;
-    const uint32_t va = static_cast<uint32_t>(m0 + dr_row) * row_bytes + dr_ch * 16;
-    const uint32_t vb = static_cast<uint32_t>(n0 + dr_row) * row_bytes + dr_ch * 16;
-
-    floatx16 acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    auto issue = [&](int stage, int kb) {
-      u32x4* base = lds + stage * kStage + (8 * wave) * kCh;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra_rsrc, (__attribute__((address_space(3))) void*)(base + 64 * i * kCh), 16, va, i * step64 + kb, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb_rsrc, (__attribute__((address_space(3))) void*)(base + (BM + 64 * i) * kCh), 16, vb,
-            i * step64 + kb, 0, 0);
-      }
-    };
-    // this wave's loads into the other stage have landed (published by the barrier)
-    auto commit = [&](int) { __builtin_amdgcn_s_waitcnt(0); };
-
-    issue(0, 0);
-    commit(0);
-    lds_barrier();
-
-    // One K step: fragments of k-substep ks+1 and (when `load`) the next
-    // stage's global loads are issued between the MFMAs of ks, one at a time,
-    // so LDS and memory latency overlap the matrix pipe.
-    auto kstep = [&](int kt, bool load) {
-      const int cur = kt & 1;
-      const u32x4* sa = lds + cur * kStage;
-      const u32x4* sb = sa + BM * kCh;
-      bf16x8 fa[2][4], fb[2][2];
-      auto frag = [&](int ks, int buf) {
-        const int ch = swz(rd_row, 2 * ks + (lane >> 5));
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fa[buf][i] = __builtin_bit_cast(bf16x8, sa[(wm * 128 + i * 32 + rd_row) * kCh + ch]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          fb[buf][j] = __builtin_bit_cast(bf16x8, sb[(wn * 64 + j * 32 + rd_row) * kCh + ch]);
-      };
-      frag(0, 0);
-      if (load) issue(cur ^ 1, (kt + 1) * kBK * 2);
-#pragma unroll
-      for (int ks = 0; ks < kBK / 16; ++ks) {
-        if (ks + 1 < kBK / 16) frag(ks + 1, (ks + 1) & 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
-#if MOE_GEMM_SCHED
-        if (ks == 0 && load) {
-#pragma unroll
-          for (int q = 0; q < 6; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 global load
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        } else if (ks + 1 < kBK / 16) {
-#pragma unroll
-          for (int q = 0; q < 6; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        }
-#endif
-      }
-      if (load) commit(cur ^ 1);
-      lds_barrier();
-    };
-    for (int kt = 0; kt + 1 < nk; ++kt) kstep(kt, true);
-    kstep(nk - 1, false);
-
-    // epilogue: accumulator v of block (i, j) holds row 8 (v / 4) + 4 (lane / 32) + v % 4,
-    // column lane % 32 of that block
-    const int col0 = n0 + wn * 64 + (lane & 31);
-    float bj[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) bj[j] = bf16_to_f32(Bias[static_cast<size_t>(s) * g.N + col0 + j * 32]);
-    const bool full = m0 + BM <= rows;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rl = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (full || rl < rows) {
-          uint16_t* crow = C + static_cast<size_t>(o_off + rl) * g.N + col0;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            float val = acc[i][j][v] + bj[j];
-            if (GELU) val = gelu_erf(val);
-            crow[j * 32] = f32_to_bf16(val);
-          }
-        }
-      }
-    }
-  }
-}
-
-// ------------------------------------------------- 128-row streaming path --
-// For experts with few rows each (fine-grained experts, capacity-limited
-// experts) the GEMM is bound by streaming the expert weights from HBM.
-// 128 x 256 x 64 tiles, 4 waves (2 x 2, wave tile 64 x 128), direct
-// global->LDS loads into a 3-stage LDS ring (48 KB per stage), issued two K
-// steps ahead so ~96 KB per CU stay in flight.  The barrier before K step
-// k+1 waits only for stage k+1 (vmcnt), never for stage k+2.
-template <bool GELU>
-__global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(GemmArgs g) {
-  constexpr int BM = 128;
-  constexpr int NS = 3;
-  constexpr int kStage = (BM + kBN) * kCh;     // u32x4 per stage (48 KB)
-  constexpr int LA = BM / 32, LB = kBN / 32;   // direct loads per wave per stage (4 + 8)
-  __shared__ u32x4 lds[NS * kStage];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
-  const int total_mt = uniform(st.tile_start[g.nseg]);
-  const int ntn = g.N / kBN;
-  const int total = total_mt * ntn;
-  const int nk = g.K / kBK;
-  const uint32_t row_bytes = static_cast<uint32_t>(g.K) * 2u;
-
-  const int per_xcd = gridDim.x >> 3;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-
-  const uint16_t* Wb = static_cast<const uint16_t*>(g.W);
-  const uint16_t* Bias = static_cast<const uint16_t*>(g.bias);
-  uint16_t* C = static_cast<uint16_t*>(g.C);
-
-  // direct loads: wave w's load i fills LDS rows 8 (4 i + w) + lane / 8 at
-  // physical chunk lane % 8, fetching the logical chunk that lands there
-  const int dr_row = 8 * wave + (lane >> 3);
-  const int dr_ch = swz(dr_row, lane & 7);
-  const int rd_row = lane & 31;
-
-  for (int it = 0;; ++it) {
-    const int L = it * gridDim.x + xcd * per_xcd + slot;
-    if (L >= total) break;
-    const int gsz = kGroupM * ntn;
-    const int gq = L / gsz;
-    const int first_m = gq * kGroupM;
-    const int gm = min(kGroupM, total_mt - first_m);
-    const int r = L - gq * gsz;
-    const int mt = first_m + r % gm;
-    const int nt = r / gm;
-
-    const int s = uniform(find_segment(st.tile_start, g.nseg, mt));
-    const int rows = uniform(st.rows[s]);
-    const int m0 = (mt - uniform(st.tile_start[s])) * BM;
-    const int a_off = uniform(g.a_by_o_off ? st.o_off[s] : st.a_off[s]);
-    const int o_off = uniform(st.o_off[s]);
-    const uint16_t* A = static_cast<const uint16_t*>(s < g.E ? g.a_routed : g.a_shared) +
-                        static_cast<size_t>(a_off) * g.K;
-    const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, static_cast<uint32_t>(rows) * row_bytes);
-    const __amdgpu_buffer_rsrc_t rb_rsrc =
-        make_rsrc(Wb + static_cast<size_t>(s) * g.N * g.K, static_cast<uint32_t>(g.N) * row_bytes);
-    const int n0 = nt * kBN;
     const uint32_t step32 = 32u * row_bytes;
     const uint32_t va = static_cast<uint32_t>(m0 + dr_row) * row_bytes + dr_ch * 16;
     const uint32_t vb = static_cast<uint32_t>(n0 + dr_row) * row_bytes + dr_ch * 16;
 
-    floatx16 acc[2][4];
+    floatx4 acc[MB][8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
 
-    auto issue = [&](int k) {
-      u32x4* base = lds + (k % NS) * kStage + (8 * wave) * kCh;
-      const int kb = k * kBK * 2;
-#pragma unroll
-      for (int i = 0; i < LA; ++i)
+    // fragment q of 32-deep slice sl of the stage in ring slot rs: q < MB -> A block q,
+    // else B block q - MB; slice sl of every stage lives in fragment buffer sl
+    bf16x8 fa[2][MB], fb[2][8];
+    auto frag1 = [&](int rs, int sl, int q) {
+      const u32x4* sa = lds + rs * kStage;
+      const int ch = swz(rd_row, 4 * sl + (lane >> 4));
+      if (q < MB)
+        fa[sl][q] = __builtin_bit_cast(bf16x8, sa[(wm * (BM / 2) + q * 16 + rd_row) * kCh + ch]);
+      else
+        fb[sl][q - MB] = __builtin_bit_cast(bf16x8, sa[(BM + wn * 128 + (q - MB) * 16 + rd_row) * kCh + ch]);
+    };
+    // direct load q of stage k into ring slot rs: q < MB -> A rows 32 q + .., else B rows 32 (q - MB) + ..
+    auto issue1 = [&](int rs, int k, int q) {
+      u32x4* base = lds + rs * kStage + (8 * wave) * kCh;
+      const int qq = q < MB ? q : q - MB;
+      const uint32_t soff = static_cast<uint32_t>(qq) * step32 + static_cast<uint32_t>(k * kBK * 2);
+      if (q < MB)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra_rsrc, (__attribute__((address_space(3))) void*)(base + 32 * i * kCh), 16, va, i * step32 + kb, 0, 0);
-#pragma unroll
-      for (int i = 0; i < LB; ++i)
+            ra_rsrc, (__attribute__((address_space(3))) void*)(base + 32 * q * kCh), 16, va, soff, 0, 0);
+      else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb_rsrc, (__attribute__((address_space(3))) void*)(base + (BM + 32 * i) * kCh), 16, vb,
-            i * step32 + kb, 0, 0);
+            rb_rsrc, (__attribute__((address_space(3))) void*)(base + (BM + 32 * (q - MB)) * kCh), 16, vb, soff, 0, 0);
     };
 
-    issue(0);
-    if (nk > 1) {
-      issue(1);
-      __builtin_amdgcn_s_waitcnt(0x0F7C);   // vmcnt <= 12: stage 0 landed, stage 1 may be in flight
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+    // prologue: stages 0 .. NS-1 in flight, stage 0 published, its slice 0 read
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+#pragma unroll
+      for (int q = 0; q < NR; ++q) issue1(k, k, q);
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm((NS - 1) * NR));
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < NR; ++q) frag1(0, 0, q);
+
+    // cur: ring slot of stage t (t % NS); stage t+1 sits in the next slot and
+    // stage t+NS refills slot cur.  The last NS steps are peeled so every
+    // flag is a compile-time constant in the unrolled body.
+    // pend: stage t+2's loads may be in flight at the wait for stage t+1
+    auto kstep = [&](int t, int cur, bool refill, bool next, bool pend) {
+      const int nxt = cur + 1 == NS ? 0 : cur + 1;
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+#pragma unroll
+        for (int q = 0; q < MF; ++q) {
+          if (sl == 1 && q == 0 && next) {
+            // stage t+1 landed (stage t+2's loads, if any, may stay in flight)
+            if (pend) __builtin_amdgcn_s_waitcnt(vm_wait_imm(NR));
+            else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+            lds_barrier();
+          }
+          const int i = q >> 3, j = q & 7;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[sl][j], fa[sl][i], acc[i][j], 0, 0, 0);
+          if (sl == 0 && (q & 1) == 0 && (q >> 1) < NR) frag1(cur, 1, q >> 1);
+          if (sl == 1 && (q & 1) == 0 && (q >> 1) < NR && next) frag1(nxt, 0, q >> 1);
+          if (sl == 1 && (q % LS) == LS - 1 && (q / LS) < NR && refill) issue1(cur, t + NS, q / LS);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    // Shorter tiles leave accumulation registers free, and the register
+    // allocator then shuttles accumulators between register files inside the
+    // loop.  Occupying the rest of that file with values pinned there across
+    // the loop keeps the accumulators in place.
+    constexpr int kPad = (256 - MB * 32) / 4;
+    floatx4 pin[kPad > 0 ? kPad : 1];
+    if constexpr (kPad > 0) {
+#pragma unroll
+      for (int k = 0; k < kPad; ++k) {
+        pin[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+        __asm__ volatile("" : "+a"(pin[k]));
+      }
     }
+    int t = 0, cur = 0;
+    for (; t + NS < nk; ++t) {
+      kstep(t, cur, true, true, NS == 3);
+      cur = cur + 1 == NS ? 0 : cur + 1;
+    }
+    if constexpr (NS == 3) {
+      // stage t+2 = nk-1 was issued a step ago and may still be in flight
+      kstep(t++, cur, false, true, true);
+      cur = cur + 1 == NS ? 0 : cur + 1;
+    }
+    kstep(t, cur, false, true, false);
+    kstep(t + 1, cur + 1 == NS ? 0 : cur + 1, false, false, false);
+    if constexpr (kPad > 0) {
+#pragma unroll
+      for (int k = 0; k < kPad; ++k) __asm__ volatile("" ::"a"(pin[k]));
+    }
+    // the next tile's first loads reuse the ring: every wave is done reading
     lds_barrier();
 
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 2 < nk) issue(kt + 2);      // slot of stage kt-1, read before the last barrier
-      const u32x4* sa = lds + (kt % NS) * kStage;
-      const u32x4* sb = sa + BM * kCh;
-      bf16x8 fa[2][2], fb[2][4];
-      auto frag = [&](int ks, int buf) {
-        const int ch = swz(rd_row, 2 * ks + (lane >> 5));
+    const int cbase = n0 + wn * 128 + 4 * (lane >> 4);
+    const uint16_t* brow = Bias + static_cast<size_t>(s) * g.N + cbase;
+    uint2 bq[8];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          fa[buf][i] = __builtin_bit_cast(bf16x8, sa[(wm * 64 + i * 32 + rd_row) * kCh + ch]);
+    for (int j = 0; j < 8; ++j) bq[j] = *reinterpret_cast<const uint2*>(brow + 16 * j);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          fb[buf][j] = __builtin_bit_cast(bf16x8, sb[(wn * 128 + j * 32 + rd_row) * kCh + ch]);
-      };
-      frag(0, 0);
+    for (int i = 0; i < MB; ++i) {
+      const int rl = m0 + wm * (BM / 2) + i * 16 + (lane & 15);
+      if (rl < rows) {
+        uint16_t* crow = C + static_cast<size_t>(o_off + rl) * g.N + cbase;
 #pragma unroll
-      for (int ks = 0; ks < kBK / 16; ++ks) {
-        if (ks + 1 < kBK / 16) frag(ks + 1, (ks + 1) & 1);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
-      }
-      // before K step kt+1: its stage has landed (stage kt+2's loads may stay in flight)
-      if (kt + 2 < nk) __builtin_amdgcn_s_waitcnt(0x0F7C);
-      else __builtin_amdgcn_s_waitcnt(0x0F70);
-      lds_barrier();
-    }
-
-    // epilogue: accumulator v of block (i, j) holds row 8 (v / 4) + 4 (lane / 32) + v % 4,
-    // column lane % 32 of that block
-    const int col0 = n0 + wn * 128 + (lane & 31);
-    float bj[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bj[j] = bf16_to_f32(Bias[static_cast<size_t>(s) * g.N + col0 + j * 32]);
-    const bool full = m0 + BM <= rows;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rl = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (full || rl < rows) {
-          uint16_t* crow = C + static_cast<size_t>(o_off + rl) * g.N + col0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float val = acc[i][j][v] + bj[j];
-            if (GELU) val = gelu_erf(val);
-            crow[j * 32] = f32_to_bf16(val);
+        for (int j = 0; j < 8; ++j) {
+          float v0 = acc[i][j][0] + __uint_as_float(bq[j].x << 16);
+          float v1 = acc[i][j][1] + __uint_as_float(bq[j].x & 0xffff0000u);
+          float v2 = acc[i][j][2] + __uint_as_float(bq[j].y << 16);
+          float v3 = acc[i][j][3] + __uint_as_float(bq[j].y & 0xffff0000u);
+          if (GELU) {
+            v0 = gelu_as(v0);
+            v1 = gelu_as(v1);
+            v2 = gelu_as(v2);
+            v3 = gelu_as(v3);
           }
+          *reinterpret_cast<uint2*>(crow + 16 * j) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
         }
       }
     }
@@ -516,13 +437,27 @@ bool gemm_fast_path(const Problem& p) {
   return rows * widest * 2 < (1LL << 31) && static_cast<long long>(p.h) * p.d * 2 < (1LL << 31);
 }
 
-// 256-row tiles (compute-bound, 8-wave kernel) for segments that average
-// >= 512 rows; 128-row tiles (weight streaming kernel) otherwise.
+// Tile height of the MFMA path.  Experts averaging >= 512 rows: 256 (the
+// compute-bound case).  Otherwise the height in {128, 160, 256} that
+// covers the expected rows of an expert with the fewest padded rows: the
+// capacity when it binds (an expert then holds exactly that many rows when
+// full), else 1.25 x the mean T k / E as headroom for uneven routing; ties
+// go to the taller tile, which streams each weight panel for more rows.
 int gemm_m_tile(const Problem& p) {
   if (!gemm_fast_path(p)) return kSB;
-  long long avg = static_cast<long long>(p.T) * p.k / p.E;
-  if (p.cap < avg) avg = p.cap;
-  return avg >= 512 ? 256 : 128;
+  const long long mean = (static_cast<long long>(p.T) * p.k + p.E - 1) / p.E;
+  if (mean >= 512 && p.cap >= 512) return 256;
+  const long long want = p.cap < mean ? p.cap : (mean * 5 + 3) / 4;
+  int best = 256;
+  long long best_pad = (want + 255) / 256 * 256;
+  for (int bm : {160, 128}) {
+    const long long pad = (want + bm - 1) / bm * bm;
+    if (pad < best_pad) {
+      best = bm;
+      best_pad = pad;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, const void* b1, const void* W2,
@@ -553,16 +488,20 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
   if (gemm_fast_path(p)) {
     int grid = num_cus();
     grid = (grid + 7) / 8 * 8;
-    if (p.gemm_bm == 256) {
-      if (phase == 1)
-        hipLaunchKernelGGL((gemm_bf16_w8_kernel<true>), dim3(grid), dim3(512), 0, st, g);
-      else
-        hipLaunchKernelGGL((gemm_bf16_w8_kernel<false>), dim3(grid), dim3(512), 0, st, g);
-    } else {
-      if (phase == 1)
-        hipLaunchKernelGGL((gemm_bf16_stream_kernel<true>), dim3(grid), dim3(256), 0, st, g);
-      else
-        hipLaunchKernelGGL((gemm_bf16_stream_kernel<false>), dim3(grid), dim3(256), 0, st, g);
+    const dim3 gd(grid), bd(256);
+    switch (p.gemm_bm) {
+      case 128:
+        if (phase == 1) hipLaunchKernelGGL((gemm_bf16_mfma_kernel<true, 128>), gd, bd, 0, st, g);
+        else hipLaunchKernelGGL((gemm_bf16_mfma_kernel<false, 128>), gd, bd, 0, st, g);
+        break;
+      case 160:
+        if (phase == 1) hipLaunchKernelGGL((gemm_bf16_mfma_kernel<true, 160>), gd, bd, 0, st, g);
+        else hipLaunchKernelGGL((gemm_bf16_mfma_kernel<false, 160>), gd, bd, 0, st, g);
+        break;
+      default:
+        if (phase == 1) hipLaunchKernelGGL((gemm_bf16_mfma_kernel<true, 256>), gd, bd, 0, st, g);
+        else hipLaunchKernelGGL((gemm_bf16_mfma_kernel<false, 256>), gd, bd, 0, st, g);
+        break;
     }
   } else {
     // upper bound of M tiles: sum_e ceil(rows_e / 64) <= ceil(T k / 64) + E + S ceil(T / 64)

@@ -45,7 +45,11 @@ REDUCED = {
     "tiny": ("tiny", {}),
     "switch": ("switch", {}),
     "mixtral_bm256": ("mixtral", dict(T=2100, d=256, h=512, E=4)),
-    "mixtral_bm128": ("mixtral", dict(T=600, d=512, h=1024)),
+    "mixtral_T600": ("mixtral", dict(T=600, d=512, h=1024)),
+    # expected rows per expert 128 (no capacity): 160-row tiles, 3-slot LDS ring
+    "tiles160_shared": ("deepseek", dict(T=512, d=256, h=512, E=32, k=8, S=1)),
+    # capacity 256 binds with 1024 rows per expert on average: 256-row tiles
+    "tiles256_capacity": ("glam", dict(T=2048, d=256, h=512, E=4, k=2, cf=0.5)),
     "glam_reduced": ("glam", dict(T=1000, d=256, h=512, E=16)),
     "deepseek_reduced": ("deepseek", dict(T=300, d=512, h=256, E=64)),
     "dense_k_eq_E": ("mixtral", dict(T=130, d=256, h=256, E=4, k=4)),

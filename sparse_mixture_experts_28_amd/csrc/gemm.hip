@@ -49,6 +49,8 @@ struct GemmArgs {
   void* C;               // [rows][N]
   const int32_t* seg;    // segment table
   int nseg, E, N, K;
+  float* part;           // fp32 partial tiles of the split tail (part_cap tiles of BM x 256)
+  int part_cap;
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -129,6 +131,44 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // are outstanding (n < 64) and does not wait on LDS or export counters
 constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
+// Logical tile L -> (M tile, N tile): groups of kGroupM consecutive M tiles
+// (adjacent rows of the same or neighbouring experts) sweep all N tiles,
+// M fastest, so tiles that run together share A and B panels in L2.
+__device__ __forceinline__ void tile_of(int L, int total_mt, int ntn, int& mt, int& nt) {
+  const int gsz = kGroupM * ntn;
+  const int grp = L / gsz;
+  const int first_m = grp * kGroupM;
+  const int gm = min(kGroupM, total_mt - first_m);
+  const int r = L - grp * gsz;
+  mt = first_m + r % gm;
+  nt = r / gm;
+}
+
+// Split of the last partial round of a persistent launch of P workgroups
+// over `total` tiles: the `tail` = total mod P tiles of that round are cut
+// along K into S pieces each (S = P / tail, at most nk / 4 steps per piece
+// and at most part_cap pieces), so the round keeps the whole grid busy.  The
+// pieces leave float32 partial tiles; a fix-up kernel sums each tile's S
+// pieces in order, so results do not depend on timing.
+struct TailPlan {
+  int full;   // tiles computed whole
+  int tail;   // tiles computed in pieces (0 if no split)
+  int S;      // pieces per tail tile
+};
+
+__device__ __forceinline__ TailPlan tail_plan(int total, int P, int nk, int part_cap) {
+  TailPlan tp{total, 0, 1};
+  const int tail = total % P;
+  if (tail == 0) return tp;
+  int S = min(P / tail, nk / 4);
+  S = min(S, part_cap / tail);
+  if (S < 2) return tp;
+  tp.full = total - tail;
+  tp.tail = tail;
+  tp.S = S;
+  return tp;
+}
+
 // ------------------------------------------------------------ MFMA path --
 // BM x 256 x 64 tiles, BM in {128, 160, 256}; 4 waves (one per SIMD) in
 // a 2 x 2 grid, wave tile (BM / 2) x 128 built from the 16x16x32 bf16 MFMA:
@@ -195,16 +235,23 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
   const int dr_ch = swz(dr_row, lane & 7);
   const int rd_row = lane & 15;
 
+  const TailPlan tp = tail_plan(total, gridDim.x, nk, g.part_cap);
+  const int items = tp.full + tp.tail * tp.S;
+
   for (int it = 0;; ++it) {
-    const int L = it * gridDim.x + xcd * per_xcd + slot;
-    if (L >= total) break;
-    const int gsz = kGroupM * ntn;
-    const int grp = L / gsz;
-    const int first_m = grp * kGroupM;
-    const int gm = min(kGroupM, total_mt - first_m);
-    const int r = L - grp * gsz;
-    const int mt = first_m + r % gm;
-    const int nt = r / gm;
+    const int w = it * gridDim.x + xcd * per_xcd + slot;
+    if (w >= items) break;
+    // work item w: a whole tile (w < full), or piece p of tail tile full + idx / S
+    int L = w, k0 = 0, kn = nk, piece = -1;
+    if (w >= tp.full) {
+      piece = w - tp.full;
+      const int p = piece % tp.S;
+      L = tp.full + piece / tp.S;
+      k0 = p * nk / tp.S;
+      kn = (p + 1) * nk / tp.S - k0;           // >= 4
+    }
+    int mt, nt;
+    tile_of(L, total_mt, ntn, mt, nt);
 
     const int s = uniform(find_segment(st.tile_start, g.nseg, mt));
     const int rows = uniform(st.rows[s]);
@@ -240,11 +287,12 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
       else
         fb[sl][q - MB] = __builtin_bit_cast(bf16x8, sa[(BM + wn * 128 + (q - MB) * 16 + rd_row) * kCh + ch]);
     };
-    // direct load q of stage k into ring slot rs: q < MB -> A rows 32 q + .., else B rows 32 (q - MB) + ..
+    // direct load q of stage k (K step k0 + k) into ring slot rs: q < MB -> A rows
+    // 32 q + .., else B rows 32 (q - MB) + ..
     auto issue1 = [&](int rs, int k, int q) {
       u32x4* base = lds + rs * kStage + (8 * wave) * kCh;
       const int qq = q < MB ? q : q - MB;
-      const uint32_t soff = static_cast<uint32_t>(qq) * step32 + static_cast<uint32_t>(k * kBK * 2);
+      const uint32_t soff = static_cast<uint32_t>(qq) * step32 + static_cast<uint32_t>((k0 + k) * kBK * 2);
       if (q < MB)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ra_rsrc, (__attribute__((address_space(3))) void*)(base + 32 * q * kCh), 16, va, soff, 0, 0);
@@ -302,12 +350,12 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
       }
     }
     int t = 0, cur = 0;
-    for (; t + NS < nk; ++t) {
+    for (; t + NS < kn; ++t) {
       kstep(t, cur, true, true, NS == 3);
       cur = cur + 1 == NS ? 0 : cur + 1;
     }
     if constexpr (NS == 3) {
-      // stage t+2 = nk-1 was issued a step ago and may still be in flight
+      // stage t+2 = kn-1 was issued a step ago and may still be in flight
       kstep(t++, cur, false, true, true);
       cur = cur + 1 == NS ? 0 : cur + 1;
     }
@@ -320,15 +368,27 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
     // the next tile's first loads reuse the ring: every wave is done reading
     lds_barrier();
 
+    // Epilogue.  A piece of a tail tile stores its float32 partial tile
+    // (row-major BM x 256, buffer stores: one lane offset plus scalar and
+    // immediate offsets); a whole tile adds the bias, applies GELU (phase 1)
+    // and stores bf16.  The choice is made per 16-row block so only that
+    // block's accumulators are live in vector registers at a time.
     const int cbase = n0 + wn * 128 + 4 * (lane >> 4);
     const uint16_t* brow = Bias + static_cast<size_t>(s) * g.N + cbase;
     uint2 bq[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) bq[j] = *reinterpret_cast<const uint2*>(brow + 16 * j);
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(g.part, static_cast<uint32_t>(g.part_cap) * BM * kBN * 4u);
+    const uint32_t pv = (static_cast<uint32_t>(wm * (BM / 2) + (lane & 15)) * kBN + wn * 128 + 4 * (lane >> 4)) * 4u;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int rl = m0 + wm * (BM / 2) + i * 16 + (lane & 15);
-      if (rl < rows) {
+      if (piece >= 0) {
+        const uint32_t ps = (static_cast<uint32_t>(piece) * BM + i * 16) * kBN * 4u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), pr, pv + 64 * j, ps, 0);
+      } else if (rl < rows) {
         uint16_t* crow = C + static_cast<size_t>(o_off + rl) * g.N + cbase;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -346,6 +406,45 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
         }
       }
     }
+  }
+}
+
+// Fix-up of the split tail: workgroup b finishes tail tile b.  Each thread
+// owns four consecutive columns; the S partial tiles are summed in piece
+// order, then bias, GELU (phase 1) and one bf16 rounding, as in the epilogue.
+template <bool GELU, int BM>
+__global__ __launch_bounds__(256) void gemm_tail_fixup_kernel(GemmArgs g, int P) {
+  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
+  const int total_mt = st.tile_start[g.nseg];
+  const int ntn = g.N / kBN;
+  const TailPlan tp = tail_plan(total_mt * ntn, P, g.K / kBK, g.part_cap);
+  const int tt = blockIdx.x;
+  if (tp.tail == 0 || tt >= tp.tail) return;
+  int mt, nt;
+  tile_of(tp.full + tt, total_mt, ntn, mt, nt);
+  const int s = find_segment(st.tile_start, g.nseg, mt);
+  const int rows = st.rows[s];
+  const int m0 = (mt - st.tile_start[s]) * BM;
+  const int o_off = st.o_off[s];
+  const int c = 4 * (threadIdx.x & 63);
+  const int n = nt * kBN + c;
+  const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g.bias) + static_cast<size_t>(s) * g.N + n);
+  const float b0 = __uint_as_float(b.x << 16), b1 = __uint_as_float(b.x & 0xffff0000u);
+  const float b2 = __uint_as_float(b.y << 16), b3 = __uint_as_float(b.y & 0xffff0000u);
+  const float* part = g.part + static_cast<size_t>(tt) * tp.S * BM * kBN;
+  uint16_t* C = static_cast<uint16_t*>(g.C);
+  for (int rr = threadIdx.x >> 6; rr < BM && m0 + rr < rows; rr += 4) {
+    floatx4 a = *reinterpret_cast<const floatx4*>(part + static_cast<size_t>(rr) * kBN + c);
+    for (int p = 1; p < tp.S; ++p) a += *reinterpret_cast<const floatx4*>(part + (static_cast<size_t>(p) * BM + rr) * kBN + c);
+    float v0 = a[0] + b0, v1 = a[1] + b1, v2 = a[2] + b2, v3 = a[3] + b3;
+    if (GELU) {
+      v0 = gelu_as(v0);
+      v1 = gelu_as(v1);
+      v2 = gelu_as(v2);
+      v3 = gelu_as(v3);
+    }
+    *reinterpret_cast<uint2*>(C + static_cast<size_t>(o_off + m0 + rr) * g.N + n) =
+        make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
   }
 }
 
@@ -485,24 +584,34 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
     g.N = p.d;
     g.K = p.h;
   }
+  g.part = ws.part;
+  g.part_cap = ws.part_cap;
   if (gemm_fast_path(p)) {
     int grid = num_cus();
     grid = (grid + 7) / 8 * 8;
     const dim3 gd(grid), bd(256);
+    // the fix-up runs right after the GEMM on the same stream; it returns at
+    // once when the tail was not split
+#define MOE_GEMM_LAUNCH(GELU_, BM_)                                                         \
+  do {                                                                                      \
+    hipLaunchKernelGGL((gemm_bf16_mfma_kernel<GELU_, BM_>), gd, bd, 0, st, g);              \
+    hipLaunchKernelGGL((gemm_tail_fixup_kernel<GELU_, BM_>), gd, bd, 0, st, g, grid);       \
+  } while (0)
     switch (p.gemm_bm) {
       case 128:
-        if (phase == 1) hipLaunchKernelGGL((gemm_bf16_mfma_kernel<true, 128>), gd, bd, 0, st, g);
-        else hipLaunchKernelGGL((gemm_bf16_mfma_kernel<false, 128>), gd, bd, 0, st, g);
+        if (phase == 1) MOE_GEMM_LAUNCH(true, 128);
+        else MOE_GEMM_LAUNCH(false, 128);
         break;
       case 160:
-        if (phase == 1) hipLaunchKernelGGL((gemm_bf16_mfma_kernel<true, 160>), gd, bd, 0, st, g);
-        else hipLaunchKernelGGL((gemm_bf16_mfma_kernel<false, 160>), gd, bd, 0, st, g);
+        if (phase == 1) MOE_GEMM_LAUNCH(true, 160);
+        else MOE_GEMM_LAUNCH(false, 160);
         break;
       default:
-        if (phase == 1) hipLaunchKernelGGL((gemm_bf16_mfma_kernel<true, 256>), gd, bd, 0, st, g);
-        else hipLaunchKernelGGL((gemm_bf16_mfma_kernel<false, 256>), gd, bd, 0, st, g);
+        if (phase == 1) MOE_GEMM_LAUNCH(true, 256);
+        else MOE_GEMM_LAUNCH(false, 256);
         break;
     }
+#undef MOE_GEMM_LAUNCH
   } else {
     // upper bound of M tiles: sum_e ceil(rows_e / 64) <= ceil(T k / 64) + E + S ceil(T / 64)
     const long long max_mt = (static_cast<long long>(p.T) * p.k + kSB - 1) / kSB + p.E +

@@ -23,7 +23,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t elem_bytes(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t xperm, hbuf, ybuf, local_rank, tile_hist, p_part, counts, kept, slot_pos, seg, logits, total;
+  size_t xperm, hbuf, ybuf, local_rank, tile_hist, p_part, counts, kept, slot_pos, seg, logits, part, total;
+  int part_cap;
 };
 
 Layout layout_of(const Problem& p) {
@@ -44,6 +45,10 @@ Layout layout_of(const Problem& p) {
   L.slot_pos = off;   off += align_up(A * 4);
   L.seg = off;        off += align_up(seg_table_ints(p.E + p.S, p.E) * 4);
   L.logits = off;     off += align_up(static_cast<size_t>(p.T) * ((p.E + 63) / 64 * 64) * 8);
+  // sized for the tallest tile: moe_workspace_bytes has no capacity factor,
+  // and the tile height moe_forward picks can depend on it
+  L.part_cap = gemm_fast_path(p) ? kGemmPartCap : 0;
+  L.part = off;       off += align_up(static_cast<size_t>(L.part_cap) * 256 * 256 * 4);
   L.total = off;
   return L;
 }
@@ -69,6 +74,8 @@ Workspace carve_workspace(const Problem& p, void* base, size_t bytes_available, 
   w.slot_pos = reinterpret_cast<int32_t*>(b + L.slot_pos);
   w.seg = reinterpret_cast<int32_t*>(b + L.seg);
   w.logits = reinterpret_cast<double*>(b + L.logits);
+  w.part = reinterpret_cast<float*>(b + L.part);
+  w.part_cap = L.part_cap;
   w.bytes = L.total;
   return w;
 }

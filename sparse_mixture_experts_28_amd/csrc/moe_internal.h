@@ -49,6 +49,8 @@ struct Workspace {
   int32_t* slot_pos;    // [T, k]
   int32_t* seg;         // segment table, see SegTable
   double* logits;       // [T, Epad] float64 router logits (bf16 path), Epad <= ceil64(E)
+  float* part;          // [part_cap, BM, 256] float32 partial tiles of the grouped GEMM's split tail
+  int part_cap;         // partial tiles the buffer holds (0: no split)
   size_t bytes;
 };
 
@@ -108,5 +110,7 @@ hipError_t launch_combine(const Problem& p, const float* topk_w, const Workspace
 // Which GEMM kernel serves a problem; the M tile decides the tile prefix.
 bool gemm_fast_path(const Problem& p);
 int gemm_m_tile(const Problem& p);
+// partial tiles reserved for the grouped GEMM's split tail (one per workgroup of a 256-CU part)
+constexpr int kGemmPartCap = 256;
 
 }  // namespace moe

@@ -52,7 +52,8 @@ def test_workspace_bytes():
     n = f(T, d, h, E, k, S, moe.MOE_BF16)
     A = T * k
     big = A * d * 2 + A * h * 2 + A * d * 2
-    assert big <= n <= big + 64 * 1024 * 1024
+    # plus routing tables, float64 logits and 256 float32 partial tiles of 256 x 256 for the GEMM's split tail
+    assert big + 256 * 256 * 256 * 4 <= n <= big + 128 * 1024 * 1024
     assert f(T, d, h, E, k, 1, moe.MOE_BF16) > n                 # shared rows
     assert f(T, d, h, E, k, S, moe.MOE_F32) > n                  # wider elements
     for bad in [(0, d, h, E, k, S), (T, d, h, E, E + 1, S), (T, 12, h, E, k, S), (T, d, h, 257, k, S),

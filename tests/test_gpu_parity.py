@@ -48,6 +48,9 @@ REDUCED = {
     "mixtral_T600": ("mixtral", dict(T=600, d=512, h=1024)),
     # expected rows per expert 128 (no capacity): 160-row tiles, 3-slot LDS ring
     "tiles160_shared": ("deepseek", dict(T=512, d=256, h=512, E=32, k=8, S=1)),
+    # 16 phase-1 tiles with K = 2048 on a 256-workgroup grid: the tail is cut
+    # 8 ways along K and finished by the fix-up kernel (GELU path)
+    "tail_split_deep_K": ("mixtral", dict(T=512, d=2048, h=512, E=4, k=2)),
     # capacity 256 binds with 1024 rows per expert on average: 256-row tiles
     "tiles256_capacity": ("glam", dict(T=2048, d=256, h=512, E=4, k=2, cf=0.5)),
     "glam_reduced": ("glam", dict(T=1000, d=256, h=512, E=16)),

@@ -409,42 +409,50 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
   }
 }
 
-// Fix-up of the split tail: workgroup b finishes tail tile b.  Each thread
-// owns four consecutive columns; the S partial tiles are summed in piece
-// order, then bias, GELU (phase 1) and one bf16 rounding, as in the epilogue.
+// Fix-up of the split tail, in 16-row chunks of the tail tiles strided over
+// the P workgroups.  Each thread owns four consecutive columns of four rows;
+// the S partial tiles are summed in piece order, then bias, GELU (phase 1)
+// and one bf16 rounding, as in the GEMM epilogue.
 template <bool GELU, int BM>
 __global__ __launch_bounds__(256) void gemm_tail_fixup_kernel(GemmArgs g, int P) {
   const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
   const int total_mt = st.tile_start[g.nseg];
   const int ntn = g.N / kBN;
   const TailPlan tp = tail_plan(total_mt * ntn, P, g.K / kBK, g.part_cap);
-  const int tt = blockIdx.x;
-  if (tp.tail == 0 || tt >= tp.tail) return;
-  int mt, nt;
-  tile_of(tp.full + tt, total_mt, ntn, mt, nt);
-  const int s = find_segment(st.tile_start, g.nseg, mt);
-  const int rows = st.rows[s];
-  const int m0 = (mt - st.tile_start[s]) * BM;
-  const int o_off = st.o_off[s];
+  if (tp.tail == 0) return;
+  constexpr int kChunks = BM / 16;
   const int c = 4 * (threadIdx.x & 63);
-  const int n = nt * kBN + c;
-  const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g.bias) + static_cast<size_t>(s) * g.N + n);
-  const float b0 = __uint_as_float(b.x << 16), b1 = __uint_as_float(b.x & 0xffff0000u);
-  const float b2 = __uint_as_float(b.y << 16), b3 = __uint_as_float(b.y & 0xffff0000u);
-  const float* part = g.part + static_cast<size_t>(tt) * tp.S * BM * kBN;
   uint16_t* C = static_cast<uint16_t*>(g.C);
-  for (int rr = threadIdx.x >> 6; rr < BM && m0 + rr < rows; rr += 4) {
-    floatx4 a = *reinterpret_cast<const floatx4*>(part + static_cast<size_t>(rr) * kBN + c);
-    for (int p = 1; p < tp.S; ++p) a += *reinterpret_cast<const floatx4*>(part + (static_cast<size_t>(p) * BM + rr) * kBN + c);
-    float v0 = a[0] + b0, v1 = a[1] + b1, v2 = a[2] + b2, v3 = a[3] + b3;
-    if (GELU) {
-      v0 = gelu_as(v0);
-      v1 = gelu_as(v1);
-      v2 = gelu_as(v2);
-      v3 = gelu_as(v3);
+  for (int w = blockIdx.x; w < tp.tail * kChunks; w += gridDim.x) {
+    const int tt = w / kChunks, r0 = (w % kChunks) * 16;
+    int mt, nt;
+    tile_of(tp.full + tt, total_mt, ntn, mt, nt);
+    const int s = find_segment(st.tile_start, g.nseg, mt);
+    const int rows = st.rows[s];
+    const int m0 = (mt - st.tile_start[s]) * BM;
+    const int o_off = st.o_off[s];
+    const int n = nt * kBN + c;
+    const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g.bias) + static_cast<size_t>(s) * g.N + n);
+    const float b0 = __uint_as_float(b.x << 16), b1 = __uint_as_float(b.x & 0xffff0000u);
+    const float b2 = __uint_as_float(b.y << 16), b3 = __uint_as_float(b.y & 0xffff0000u);
+    const float* part = g.part + static_cast<size_t>(tt) * tp.S * BM * kBN;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int rr = r0 + (threadIdx.x >> 6) + 4 * k;
+      if (m0 + rr >= rows) break;
+      floatx4 a = *reinterpret_cast<const floatx4*>(part + static_cast<size_t>(rr) * kBN + c);
+      for (int p = 1; p < tp.S; ++p)
+        a += *reinterpret_cast<const floatx4*>(part + (static_cast<size_t>(p) * BM + rr) * kBN + c);
+      float v0 = a[0] + b0, v1 = a[1] + b1, v2 = a[2] + b2, v3 = a[3] + b3;
+      if (GELU) {
+        v0 = gelu_as(v0);
+        v1 = gelu_as(v1);
+        v2 = gelu_as(v2);
+        v3 = gelu_as(v3);
+      }
+      *reinterpret_cast<uint2*>(C + static_cast<size_t>(o_off + m0 + rr) * g.N + n) =
+          make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
     }
-    *reinterpret_cast<uint2*>(C + static_cast<size_t>(o_off + m0 + rr) * g.N + n) =
-        make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
   }
 }
 

@@ -184,9 +184,13 @@ def main():
     gemm_flops = 2.0 * d * h * rows                      # per launch (each phase)
     active = int((kept_np > 0).sum()) + S
     bytes_router = T * d * s + E * d * s + 8 * T * k
-    bytes_scatter = T * d * s + a_kept * d * s + 8 * T * k
+    # the scatter reads each assignment's expert and in-tile rank and writes its
+    # slot and, for kept ones, the row's token (no token row is copied)
+    bytes_scatter = 12 * T * k + 4 * a_kept
     bytes_combine = rows * d * s + T * d * s + 8 * T * k
-    bytes_gemm1 = active * h * d * s + rows * (d + h) * s
+    # minimal traffic: active expert weights once, x once (phase 1 gathers its
+    # rows), H written once / read once, Y written once
+    bytes_gemm1 = active * h * d * s + T * d * s + rows * h * s
     bytes_gemm2 = active * h * d * s + rows * (h + d) * s
 
     def gbs(b, ms):

@@ -54,6 +54,14 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # a library can link and still not load: refuse one that leaves any of
+    # this project's symbols undefined (hipcc's host pass has been seen to
+    # drop a kernel's launch stub while still referencing it)
+    r = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "_ZN3moe" in l]
+    if r.returncode != 0 or missing:
+        os.remove(tmp)
+        raise RuntimeError("libmoe.so would not load; undefined: " + (", ".join(missing) or r.stderr))
     os.replace(tmp, LIB)
     if verbose:
         print(f"[build] wrote {LIB}")

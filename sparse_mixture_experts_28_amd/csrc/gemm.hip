@@ -39,10 +39,16 @@ namespace moe {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
+// Row r of segment s reads A row
+//   row_token[a_off_s + r]   phase 1, routed expert (gathered token rows of x)
+//   a_off_s + r              phase 1, shared expert (x rows in token order)
+//   o_off_s + r              phase 2 (hbuf rows of the segment)
 struct GemmArgs {
-  const void* a_routed;  // phase 1: xperm; phase 2: hbuf
-  const void* a_shared;  // phase 1: x;     phase 2: hbuf
+  const void* A;         // phase 1: x [T, d]; phase 2: hbuf [R, h]
+  int a_rows;            // rows of A (the range of its buffer descriptor)
+  const int32_t* row_token;  // phase 1: token of each expert-sorted row; phase 2: nullptr
   int a_by_o_off;        // phase 2: the A row offset of a segment is its output row offset
   const void* W;         // [nseg][N][K]
   const void* bias;      // [nseg][N]
@@ -258,14 +264,24 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
     const int m0 = (mt - uniform(st.tile_start[s])) * BM;
     const int a_off = uniform(g.a_by_o_off ? st.o_off[s] : st.a_off[s]);
     const int o_off = uniform(st.o_off[s]);
-    const uint16_t* A = static_cast<const uint16_t*>(s < g.E ? g.a_routed : g.a_shared) +
-                        static_cast<size_t>(a_off) * g.K;
-    const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, static_cast<uint32_t>(rows) * row_bytes);
+    const bool gather = g.row_token != nullptr && s < g.E;
+    const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(g.A, static_cast<uint32_t>(g.a_rows) * row_bytes);
     const __amdgpu_buffer_rsrc_t rb_rsrc =
         make_rsrc(Wb + static_cast<size_t>(s) * g.N * g.K, static_cast<uint32_t>(g.N) * row_bytes);
     const int n0 = nt * kBN;
     const uint32_t step32 = 32u * row_bytes;
-    const uint32_t va = static_cast<uint32_t>(m0 + dr_row) * row_bytes + dr_ch * 16;
+    // A: the lane's row of direct load q, looked up once per tile; rows past
+    // the segment get an offset past the end of A (the range check covers
+    // voffset + soffset: they read zero and touch no memory)
+    // (a vector type: hipcc's host pass omits this kernel's launch stub when a
+    // plain scalar array is captured by the load lambda below)
+    u32x8 va = {};
+#pragma unroll
+    for (int q = 0; q < MB; ++q) {
+      const int r = m0 + 32 * q + dr_row;
+      const int arow = r < rows ? (gather ? g.row_token[a_off + r] : a_off + r) : -1;
+      va[q] = arow >= 0 ? static_cast<uint32_t>(arow) * row_bytes + dr_ch * 16 : 0x80000000u;
+    }
     const uint32_t vb = static_cast<uint32_t>(n0 + dr_row) * row_bytes + dr_ch * 16;
 
     floatx4 acc[MB][8];
@@ -292,13 +308,13 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
     auto issue1 = [&](int rs, int k, int q) {
       u32x4* base = lds + rs * kStage + (8 * wave) * kCh;
       const int qq = q < MB ? q : q - MB;
-      const uint32_t soff = static_cast<uint32_t>(qq) * step32 + static_cast<uint32_t>((k0 + k) * kBK * 2);
+      const uint32_t kbytes = static_cast<uint32_t>((k0 + k) * kBK * 2);
       if (q < MB)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra_rsrc, (__attribute__((address_space(3))) void*)(base + 32 * q * kCh), 16, va, soff, 0, 0);
+            ra_rsrc, (__attribute__((address_space(3))) void*)(base + 32 * q * kCh), 16, va[q], kbytes, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb_rsrc, (__attribute__((address_space(3))) void*)(base + (BM + 32 * (q - MB)) * kCh), 16, vb, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rsrc, (__attribute__((address_space(3))) void*)(base + (BM + 32 * (q - MB)) * kCh),
+                                                 16, vb, static_cast<uint32_t>(qq) * step32 + kbytes, 0, 0);
     };
 
     // prologue: stages 0 .. NS-1 in flight, stage 0 published, its slice 0 read
@@ -478,7 +494,8 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmArgs g, int max_mt) 
   const int m0 = (mt - st.tile_start[s]) * kSB;
   const int n0 = blockIdx.y * kSB;
   const int a_off = g.a_by_o_off ? st.o_off[s] : st.a_off[s];
-  const TIn* A = static_cast<const TIn*>(s < g.E ? g.a_routed : g.a_shared) + static_cast<size_t>(a_off) * g.K;
+  const bool gather = g.row_token != nullptr && s < g.E;
+  const TIn* A = static_cast<const TIn*>(g.A);
   const TIn* B = static_cast<const TIn*>(g.W) + static_cast<size_t>(s) * g.N * g.K;
   const TIn* Bias = static_cast<const TIn*>(g.bias) + static_cast<size_t>(s) * g.N;
   TIn* C = static_cast<TIn*>(g.C);
@@ -489,7 +506,8 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmArgs g, int max_mt) 
     for (int i = threadIdx.x; i < kSB * kSK; i += 256) {
       const int rr = i / kSK, kk = i % kSK;
       const int gm_ = m0 + rr, gk = k0 + kk, gn = n0 + rr;
-      sA[kk][rr] = (gm_ < rows && gk < g.K) ? ld_f32(A, static_cast<size_t>(gm_) * g.K + gk) : 0.f;
+      const int arow = gm_ < rows ? (gather ? g.row_token[a_off + gm_] : a_off + gm_) : 0;
+      sA[kk][rr] = (gm_ < rows && gk < g.K) ? ld_f32(A, static_cast<size_t>(arow) * g.K + gk) : 0.f;
       sB[kk][rr] = (gn < g.N && gk < g.K) ? ld_f32(B, static_cast<size_t>(gn) * g.K + gk) : 0.f;
     }
     __syncthreads();
@@ -574,8 +592,9 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
   g.nseg = p.E + p.S;
   g.E = p.E;
   if (phase == 1) {
-    g.a_routed = ws.xperm;
-    g.a_shared = x;
+    g.A = x;
+    g.a_rows = p.T;
+    g.row_token = ws.row_token;
     g.a_by_o_off = 0;
     g.W = W1;
     g.bias = b1;
@@ -583,8 +602,9 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
     g.N = p.h;
     g.K = p.d;
   } else {
-    g.a_routed = ws.hbuf;
-    g.a_shared = ws.hbuf;
+    g.A = ws.hbuf;
+    g.a_rows = p.T * p.k + p.S * p.T;
+    g.row_token = nullptr;
     g.a_by_o_off = 1;
     g.W = W2;
     g.bias = b2;

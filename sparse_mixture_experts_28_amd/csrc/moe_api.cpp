@@ -23,7 +23,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t elem_bytes(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t xperm, hbuf, ybuf, local_rank, tile_hist, p_part, counts, kept, slot_pos, seg, logits, part, total;
+  size_t row_token, hbuf, ybuf, local_rank, tile_hist, p_part, counts, kept, slot_pos, seg, logits, part, total;
   int part_cap;
 };
 
@@ -34,7 +34,7 @@ Layout layout_of(const Problem& p) {
   const size_t te = static_cast<size_t>(p.ntile) * p.E;
   Layout L;
   size_t off = 0;
-  L.xperm = off;      off += align_up(A * p.d * s);
+  L.row_token = off;  off += align_up(A * 4);
   L.hbuf = off;       off += align_up(R * p.h * s);
   L.ybuf = off;       off += align_up(R * p.d * s);
   L.local_rank = off; off += align_up(A * 4);
@@ -63,7 +63,7 @@ Workspace carve_workspace(const Problem& p, void* base, size_t bytes_available, 
   *ok = base != nullptr && bytes_available >= L.total && aligned(base, kAlign);
   if (!*ok) return w;
   char* b = static_cast<char*>(base);
-  w.xperm = b + L.xperm;
+  w.row_token = reinterpret_cast<int32_t*>(b + L.row_token);
   w.hbuf = b + L.hbuf;
   w.ybuf = b + L.ybuf;
   w.local_rank = reinterpret_cast<int32_t*>(b + L.local_rank);
@@ -180,7 +180,7 @@ moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const v
   if (!check(launch_router(p, x, W_g, launch->b_g, topk_idx, topk_w, ws, st), "router launch")) return MOE_ERR_HIP;
   if (!check(launch_scan(p, ws, aux_loss, launch->expert_counts, launch->expert_kept, st), "scan launch"))
     return MOE_ERR_HIP;
-  if (!check(launch_scatter(p, x, topk_idx, ws, st), "scatter launch")) return MOE_ERR_HIP;
+  if (!check(launch_scatter(p, topk_idx, ws, st), "scatter launch")) return MOE_ERR_HIP;
   if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 1, st), "expert phase 1 launch")) return MOE_ERR_HIP;
   if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 2, st), "expert phase 2 launch")) return MOE_ERR_HIP;
   if (!check(launch_combine(p, topk_w, ws, out, st), "combine launch")) return MOE_ERR_HIP;

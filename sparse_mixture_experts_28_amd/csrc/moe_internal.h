@@ -38,7 +38,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // R = A + S*T rows of the expert hidden / output buffers (shared experts at
 // the fixed row offset A + s*T).
 struct Workspace {
-  void* xperm;          // [A, d]     expert-sorted copies of the token rows
+  int32_t* row_token;   // [A]        token of each row of the expert-sorted order (kept assignments)
   void* hbuf;           // [R, h]     GELU(x W1^T + b1)
   void* ybuf;           // [R, d]     h W2^T + b2
   int32_t* local_rank;  // [T, k]     rank of (t,j) among earlier tokens of its 64-token tile
@@ -57,11 +57,12 @@ struct Workspace {
 // Segment table written by the scan kernel and read by the grouped GEMM and
 // the scatter: nseg = E + S segments.  Stored as int32 arrays back to back:
 //   rows[nseg]        rows of the segment (kept_e, or T for a shared expert)
-//   a_off[nseg]       first row of the segment in its A source for phase 1
-//                     (xperm for routed experts, x for shared experts)
+//   a_off[nseg]       first row of the segment in its phase-1 row list: the
+//                     expert-sorted order (row_token) for routed experts, x for
+//                     shared experts
 //   o_off[nseg]       first row of the segment in hbuf / ybuf
 //   tile_start[nseg+1] prefix sum of ceil(rows / BM) (M tiles of the GEMM)
-//   route_off[E]      exclusive scan of kept (row offset of expert e in xperm)
+//   route_off[E]      exclusive scan of kept (first row of expert e in the expert-sorted order)
 struct SegTable {
   int32_t* rows;
   int32_t* a_off;
@@ -99,8 +100,7 @@ hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const
                          int32_t* topk_idx, float* topk_w, const Workspace& ws, hipStream_t st);
 hipError_t launch_scan(const Problem& p, const Workspace& ws, float* aux_loss,
                        int32_t* counts_out, int32_t* kept_out, hipStream_t st);
-hipError_t launch_scatter(const Problem& p, const void* x, const int32_t* topk_idx,
-                          const Workspace& ws, hipStream_t st);
+hipError_t launch_scatter(const Problem& p, const int32_t* topk_idx, const Workspace& ws, hipStream_t st);
 hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, const void* b1,
                              const void* W2, const void* b2, const Workspace& ws, int phase,
                              hipStream_t st);

@@ -1,5 +1,5 @@
 // moe_permute: turn the router's per-tile histograms and in-tile ranks into a
-// deterministic, capacity-limited, expert-sorted copy of the token rows.
+// deterministic, capacity-limited, expert-sorted order of the token rows.
 //
 // Pages: "AI-Research-SKILLs MoE 训练实战…全指南" §3.1 (the mask of tokens routed
 // to each expert, gathered per expert), §8.2 and "第7章 Mixture of Experts"
@@ -14,9 +14,10 @@
 //         over experts gives the segment offsets; the balance loss is
 //         finalised from c and the per-tile probability sums (float64, fixed
 //         order); the grouped-GEMM segment table is written.
-// scatter (1 workgroup per token): rank = tile base + in-tile rank; the
-//         assignment is kept iff rank < cap; the token row is read once and
-//         written to every kept slot (16-byte vectors).
+// scatter (1 thread per assignment): rank = tile base + in-tile rank; the
+//         assignment is kept iff rank < cap; its row in the expert-sorted
+//         order and that row's token are recorded.  No token row is copied:
+//         the expert GEMM gathers x rows through row_token.
 //
 // No atomics anywhere: every result is a fixed function of the inputs.
 #include "moe_internal.h"
@@ -145,36 +146,26 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
   }
 }
 
-template <typename Vec>
-__global__ __launch_bounds__(256) void scatter_kernel(Problem p, const Vec* __restrict__ x,
-                                                      const int32_t* __restrict__ topk_idx,
+// One thread per assignment (t, j): its rank among expert e's assignments in
+// token order is the tile base plus the in-tile rank; kept iff rank < cap.
+// Writes the assignment's row in the expert-sorted order (slot_pos, -1 if
+// dropped) and that row's token (row_token), which the expert GEMM gathers
+// its phase-1 rows through.  Every kept row gets exactly one writer.
+__global__ __launch_bounds__(256) void scatter_kernel(Problem p, const int32_t* __restrict__ topk_idx,
                                                       const int32_t* __restrict__ local_rank,
                                                       const int32_t* __restrict__ tile_base,
                                                       const int32_t* __restrict__ seg_base,
                                                       int32_t* __restrict__ slot_pos,
-                                                      Vec* __restrict__ xperm, int vec_per_row) {
-  __shared__ int32_t s_pos[MOE_MAX_TOPK];
-  const int t = blockIdx.x;
-  const int k = p.k;
-  if (threadIdx.x < k) {
-    const int j = threadIdx.x;
-    const int e = topk_idx[static_cast<size_t>(t) * k + j];
-    const int tile = t / kRouterTile;
-    const int rank = tile_base[static_cast<size_t>(e) * p.ntile + tile] + local_rank[static_cast<size_t>(t) * k + j];
-    SegTable st = seg_table(const_cast<int32_t*>(seg_base), p.E + p.S, p.E);
-    const int pos = rank < p.cap ? st.route_off[e] + rank : -1;
-    slot_pos[static_cast<size_t>(t) * k + j] = pos;
-    s_pos[j] = pos;
-  }
-  __syncthreads();
-  const Vec* src = x + static_cast<size_t>(t) * vec_per_row;
-  for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
-    const Vec v = src[c];
-    for (int j = 0; j < k; ++j) {
-      const int pos = s_pos[j];
-      if (pos >= 0) xperm[static_cast<size_t>(pos) * vec_per_row + c] = v;
-    }
-  }
+                                                      int32_t* __restrict__ row_token) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= p.T * p.k) return;
+  const int t = i / p.k;
+  const int e = topk_idx[i];
+  const int rank = tile_base[static_cast<size_t>(e) * p.ntile + t / kRouterTile] + local_rank[i];
+  SegTable st = seg_table(const_cast<int32_t*>(seg_base), p.E + p.S, p.E);
+  const int pos = rank < p.cap ? st.route_off[e] + rank : -1;
+  slot_pos[i] = pos;
+  if (pos >= 0) row_token[pos] = t;
 }
 
 }  // namespace
@@ -186,15 +177,10 @@ hipError_t launch_scan(const Problem& p, const Workspace& ws, float* aux_loss, i
   return hipGetLastError();
 }
 
-hipError_t launch_scatter(const Problem& p, const void* x, const int32_t* topk_idx, const Workspace& ws,
-                          hipStream_t st) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const int elem = p.dtype == MOE_BF16 ? 2 : 4;
-  const int vec_per_row = p.d * elem / 16;
-  const int threads = vec_per_row >= 256 ? 256 : (vec_per_row >= 128 ? 128 : 64);
-  hipLaunchKernelGGL(scatter_kernel<u32x4>, dim3(p.T), dim3(threads), 0, st, p,
-                     static_cast<const u32x4*>(x), topk_idx, ws.local_rank, ws.tile_hist, ws.seg,
-                     ws.slot_pos, static_cast<u32x4*>(ws.xperm), vec_per_row);
+hipError_t launch_scatter(const Problem& p, const int32_t* topk_idx, const Workspace& ws, hipStream_t st) {
+  const int n = p.T * p.k;
+  hipLaunchKernelGGL(scatter_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, topk_idx, ws.local_rank,
+                     ws.tile_hist, ws.seg, ws.slot_pos, ws.row_token);
   return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@ def test_workspace_bytes():
     T, d, h, E, k, S = 8192, 4096, 14336, 8, 2, 0
     n = f(T, d, h, E, k, S, moe.MOE_BF16)
     A = T * k
-    big = A * d * 2 + A * h * 2 + A * d * 2
+    big = A * h * 2 + A * d * 2                      # hidden and expert-output rows
     # plus routing tables, float64 logits and 256 float32 partial tiles of 256 x 256 for the GEMM's split tail
     assert big + 256 * 256 * 256 * 4 <= n <= big + 128 * 1024 * 1024
     assert f(T, d, h, E, k, 1, moe.MOE_BF16) > n                 # shared rows

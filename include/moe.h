@@ -62,7 +62,8 @@ typedef enum {
 
 /* Stage boundaries at which optional timing events are recorded (see
  * moe_launch_t.stage_events): before the router, then after the router, the
- * scan, the scatter, expert phase 1 (x W1^T + b1, GELU), expert phase 2
+ * scan, the scatter (each kept assignment's row in the expert-sorted order;
+ * token rows are not copied), expert phase 1 (x W1^T + b1, GELU), expert phase 2
  * (h W2^T + b2) and the combine. */
 #define MOE_NUM_STAGE_EVENTS 7
 
@@ -87,9 +88,9 @@ typedef struct {
 } moe_launch_t;
 
 /* Bytes of device workspace moe_forward needs for this problem shape (0 if
- * the shape is invalid).  Dominated by the expert-sorted token copy
- * [T*k, d], the hidden buffer [(T*k + S*T), h] and the expert-output buffer
- * [(T*k + S*T), d] in dtype. */
+ * the shape is invalid).  Dominated by the hidden buffer [(T*k + S*T), h]
+ * and the expert-output buffer [(T*k + S*T), d] in dtype, plus 64 MB of
+ * float32 partial tiles for the bf16 grouped GEMM. */
 size_t moe_workspace_bytes(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k,
                            int32_t n_shared, moe_dtype_t dtype);
 

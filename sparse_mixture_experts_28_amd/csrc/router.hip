@@ -394,26 +394,98 @@ __global__ __launch_bounds__(256) void router_logits_kernel(LogitArgs a) {
   }
 }
 
-// Selection from float64 logits [T, Epad] for one 64-token tile: the logits are
-// placed in the MFMA-result register layout route_tile expects.
+// Selection from float64 logits [T, Epad] for one 64-token tile, one token
+// per 16-lane group (1024 threads): lane c of token r's group holds experts
+// nb * 16 + c.  Same results as route_tile, with 16 waves per tile instead of
+// 4 so that few, wide tiles (small T, many experts) still fill the CUs.
+constexpr int kSelectThreads = kRouterTile * 16;
+
 template <int NB>
-__global__ __launch_bounds__(kRouterThreads) void router_select_kernel(RouterArgs a, const double* logits, int Epad) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int c = lane & 15;
-  const int g = lane >> 4;
+__global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArgs a, const double* logits, int Epad) {
+  __shared__ int32_t s_idx[kRouterTile * MOE_MAX_TOPK];
+  __shared__ unsigned long long s_mask[MOE_MAX_EXPERTS];
+  __shared__ float s_p[kRouterTile][16 * NB + 1];
+
+  const int c = threadIdx.x & 15;
+  const int r = threadIdx.x >> 4;          // token within the tile
   const int tile0 = blockIdx.x * kRouterTile;
-  double acc[NB][4];
+  const int t = tile0 + r;
+  const bool tok_ok = t < a.T;             // uniform across the 16-lane group
+  const int E = a.E, k = a.k;
+
+  double val[NB];
+  double m = -INFINITY;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int t = tile0 + wave * 16 + g * 4 + v;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int e = nb * 16 + c;
+    double l = -INFINITY;
+    if (e < E && tok_ok) l = logits[static_cast<size_t>(t) * Epad + e] + (a.b_g ? static_cast<double>(a.b_g[e]) : 0.0);
+    val[nb] = l;
+    m = fmax(m, l);
+  }
+  m = max16(m);
+  float ev[NB];
+  float zl = 0.f;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    ev[nb] = (nb * 16 + c < E && tok_ok) ? __expf(static_cast<float>(val[nb] - m)) : 0.f;
+    zl += ev[nb];
+  }
+  const float z = sum16(zl);
+  const float inv = tok_ok ? 1.f / z : 0.f;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) s_p[r][nb * 16 + c] = ev[nb] * inv;
+
+  // k rounds of a 16-lane argmax over the not-yet-chosen experts
+  uint32_t taken = 0;
+  int my_idx = 0;
+  float my_e = 0.f;
+  float esum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    double bv = -INFINITY;
+    int bi = 0x7fffffff;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int e = nb * 16 + c;
-      acc[nb][v] = (t < a.T && e < Epad) ? logits[static_cast<size_t>(t) * Epad + e] : 0.0;
+      if (e < E && !((taken >> nb) & 1u) && val[nb] > bv) { bv = val[nb]; bi = e; }
+    }
+    argmax16(bv, bi);
+    if ((bi & 15) == c) taken |= 1u << (bi >> 4);
+    const float ej = __expf(static_cast<float>(bv - m));
+    esum += ej;
+    if (c == j) { my_idx = bi; my_e = ej; }
+  }
+  if (c < k) {
+    s_idx[r * MOE_MAX_TOPK + c] = tok_ok ? my_idx : -1;
+    if (tok_ok) {
+      a.topk_idx[static_cast<size_t>(t) * k + c] = my_idx;
+      a.topk_w[static_cast<size_t>(t) * k + c] = my_e / esum;
     }
   }
-  route_tile<NB>(a, acc, tile0);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_mask[e] = 0ull;
+  __syncthreads();
+
+  const int ntok = min(kRouterTile, a.T - tile0);
+  const int tile = tile0 / kRouterTile;
+  // In-tile ranks in token order, as in route_tile: OR-ed 64-bit token masks
+  // per expert (order-free, so deterministic); rank = earlier tokens in the mask.
+  if (threadIdx.x < ntok) {
+    const int rr = threadIdx.x;
+    for (int j = 0; j < k; ++j) atomicOr(&s_mask[s_idx[rr * MOE_MAX_TOPK + j]], 1ull << rr);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    // probability sum over the tile's tokens in token order
+    float ps = 0.f;
+    for (int rr = 0; rr < ntok; ++rr) ps += s_p[rr][e];
+    a.p_part[static_cast<size_t>(e) * a.ntile + tile] = ps;
+    a.tile_hist[static_cast<size_t>(e) * a.ntile + tile] = __popcll(s_mask[e]);
+  }
+  for (int i = threadIdx.x; i < ntok * k; i += blockDim.x) {
+    const int rr = i / k, j = i - rr * k;
+    const unsigned long long below = (1ull << rr) - 1ull;
+    a.local_rank[static_cast<size_t>(tile0 + rr) * k + j] = __popcll(s_mask[s_idx[rr * MOE_MAX_TOPK + j]] & below);
+  }
 }
 
 template <int NBW, int KS>
@@ -437,7 +509,7 @@ hipError_t launch_logits_ks(const Problem& p, const LogitArgs& la, hipStream_t s
 
 template <int NB>
 hipError_t launch_select(const Problem& p, const RouterArgs& a, const double* logits, int Epad, hipStream_t st) {
-  hipLaunchKernelGGL((router_select_kernel<NB>), dim3(p.ntile), dim3(kRouterThreads), 0, st, a, logits, Epad);
+  hipLaunchKernelGGL((router_select_kernel<NB>), dim3(p.ntile), dim3(kSelectThreads), 0, st, a, logits, Epad);
   return hipGetLastError();
 }
 

@@ -44,7 +44,7 @@ Layout layout_of(const Problem& p) {
   L.kept = off;       off += align_up(static_cast<size_t>(p.E) * 4);
   L.slot_pos = off;   off += align_up(A * 4);
   L.seg = off;        off += align_up(seg_table_ints(p.E + p.S, p.E) * 4);
-  L.logits = off;     off += align_up(static_cast<size_t>(p.T) * ((p.E + 63) / 64 * 64) * 8);
+  L.logits = off;     off += align_up(static_cast<size_t>(logit_splits(p)) * p.T * logit_pad(p.E) * 8);
   // sized for the tallest tile: moe_workspace_bytes has no capacity factor,
   // and the tile height moe_forward picks can depend on it
   L.part_cap = gemm_fast_path(p) ? kGemmPartCap : 0;

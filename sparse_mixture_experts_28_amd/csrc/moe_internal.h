@@ -48,7 +48,7 @@ struct Workspace {
   int32_t* kept;        // [E]
   int32_t* slot_pos;    // [T, k]
   int32_t* seg;         // segment table, see SegTable
-  double* logits;       // [T, Epad] float64 router logits (bf16 path), Epad <= ceil64(E)
+  double* logits;       // [KS, T, Epad] float64 partial router logits (bf16 path)
   float* part;          // [part_cap, BM, 256] float32 partial tiles of the grouped GEMM's split tail
   int part_cap;         // partial tiles the buffer holds (0: no split)
   size_t bytes;
@@ -110,6 +110,10 @@ hipError_t launch_combine(const Problem& p, const float* topk_w, const Workspace
 // Which GEMM kernel serves a problem; the M tile decides the tile prefix.
 bool gemm_fast_path(const Problem& p);
 int gemm_m_tile(const Problem& p);
+// router logits (bf16, d % 256 == 0): expert padding and split-K factor, which
+// size the float64 partial-logit workspace [KS][T][Epad]
+int logit_pad(int E);
+int logit_splits(const Problem& p);
 // partial tiles reserved for the grouped GEMM's split tail (one per workgroup of a 256-CU part)
 constexpr int kGemmPartCap = 256;
 

@@ -275,13 +275,16 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(RouterArgs a
 
 // ---- bf16 inputs, d % 256 == 0: logits kernel + selection kernel ----
 //
-// Logits.  A workgroup (4 waves) owns TT = 64 / KS tokens and ES = 16 * NBW
-// experts; the KS waves that share 16 tokens split the blocks of P k-steps
-// (32 elements each) of d round-robin.  Operands go straight from memory into
-// registers (x rows once per expert slice; the router weight from L2), two
-// blocks in flight, 16x16x32 MFMA in float32 per block (<= 256 elements),
-// blocks added in float64, the KS partials summed in float64 in fixed order.
-// Output: float64 logits [T, Epad].
+// Logits.  A workgroup computes 128 tokens x 64 experts over one of KS
+// contiguous ranges of d (split-K, so that small T or few experts still give
+// ~256 workgroups).  Both operands reach LDS by direct loads (buffer_load ...
+// lds) in 128-deep stages held in a 3-slot ring, so each workgroup reads its
+// x rows and router-weight rows once from L2 (per-wave register loads read
+// the weight once per wave and were bound by L2 requests).  Wave w owns
+// tokens 32 w .. 32 w + 31 x all 64 experts: 2 x 4 blocks of the 16x16x32
+// MFMA, float32 per 256-element chunk of d, chunks added in float64.  Output:
+// float64 partial logits [KS][T][Epad]; the selection kernel adds the KS
+// partials in order.
 constexpr uint32_t kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -292,106 +295,128 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 struct LogitArgs {
   const uint16_t* x;
   const uint16_t* W;
-  double* logits;   // [T, Epad]
-  int T, d, E, Epad;
+  double* logits;   // [KS][T][Epad]
+  int T, d, E, Epad, KS;
 };
 
-template <int NBW, int KS>
-__global__ __launch_bounds__(256) void router_logits_kernel(LogitArgs a) {
-  constexpr int ES = 16 * NBW;
-  constexpr int TT = 64 / KS;
-  constexpr int P = NBW == 1 ? 8 : (NBW == 2 ? 4 : 2);   // k-steps per block
-  __shared__ double red[4][ES][16];
+constexpr int kLgTok = 128, kLgExp = 64, kLgK = 128;   // tile and stage depth
+constexpr int kLgCh = kLgK / 8;                        // 16-byte chunks per stage row
+constexpr int kLgNS = 3;                               // ring slots
+constexpr int kLgLoads = (kLgTok + kLgExp) / 16;       // 1 KB direct loads per wave per stage (12)
+
+// LDS row of 16 chunks: logical chunk c of row r at c ^ (r & 15).  A
+// ds_read_b128 of 16 consecutive rows at one logical chunk then covers 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int lgswz(int row, int c) { return c ^ (row & 15); }
+
+__device__ __forceinline__ void lg_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt 0 only; direct loads are waited for by vmcnt
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void router_logits_kernel(LogitArgs a) {
+  constexpr int kStage = (kLgTok + kLgExp) * kLgCh;   // u32x4 per stage (48 KB)
+  __shared__ u32x4 lds[kLgNS * kStage];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int tg = wave / KS, kw = wave % KS;
-  const int c = lane & 15, g = lane >> 4;
-  const int tile0 = blockIdx.x * TT;
-  const int e0 = blockIdx.y * ES;
+  const int tok0 = blockIdx.x * kLgTok;
+  const int e0 = blockIdx.y * kLgExp;
+  const int ks = blockIdx.z;
   const uint32_t rb = static_cast<uint32_t>(a.d) * 2u;   // bytes per row
-  const int nrows = min(TT, a.T - tile0);
-  const int nexp = min(ES, a.E - e0);
-  // out-of-range token rows and expert rows read as zero (buffer range check)
-  const __amdgpu_buffer_rsrc_t xs = rsrc(a.x + static_cast<size_t>(tile0) * a.d, static_cast<uint32_t>(nrows) * rb);
+  const int nrows = min(kLgTok, a.T - tok0);
+  const int nexp = min(kLgExp, a.E - e0);
+  // out-of-range token and expert rows read as zero (buffer range check)
+  const __amdgpu_buffer_rsrc_t xs = rsrc(a.x + static_cast<size_t>(tok0) * a.d, static_cast<uint32_t>(nrows) * rb);
   const __amdgpu_buffer_rsrc_t ws = rsrc(a.W + static_cast<size_t>(e0) * a.d, static_cast<uint32_t>(max(nexp, 0)) * rb);
-  const uint32_t xo = static_cast<uint32_t>(tg * 16 + c) * rb + g * 16;
-  uint32_t wo[NBW];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) wo[nb] = static_cast<uint32_t>(nb * 16 + c) * rb + g * 16;
+  const int nchunk = a.d / 256;                      // 256-element chunks of d
+  const int c0 = ks * nchunk / a.KS, c1 = (ks + 1) * nchunk / a.KS;
+  const int nst = (c1 - c0) * (256 / kLgK);          // stages of this split (>= 2)
+  const uint32_t kbase = static_cast<uint32_t>(c0) * 512u;
 
-  const int nblk = a.d / (32 * P);
-  double acc[NBW][4];
+  // direct loads: load i of wave w fills stage rows 16 i + 4 w + lane / 16 at
+  // physical chunk lane % 16 (rows 0..127: x, 128..191: router weight)
+  const int dr = 4 * wave + (lane >> 4);
+  const uint32_t vo = static_cast<uint32_t>(dr) * rb + lgswz(dr, lane & 15) * 16;
+  auto issue = [&](int st) {
+    u32x4* base = lds + (st % kLgNS) * kStage + (4 * wave) * kLgCh;
+    const uint32_t kb = kbase + static_cast<uint32_t>(st) * (kLgK * 2);
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) acc[nb][v] = 0.0;
-
-  u32x4 xa[2][P], wa[2][P][NBW];
-  auto load = [&](int blk, int buf) {
-    const uint32_t kb = static_cast<uint32_t>(blk) * (P * 64);
-#pragma unroll
-    for (int q = 0; q < P; ++q) {
-      xa[buf][q] = __builtin_amdgcn_raw_buffer_load_b128(xs, xo, kb + q * 64, 0);
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) wa[buf][q][nb] = __builtin_amdgcn_raw_buffer_load_b128(ws, wo[nb], kb + q * 64, 0);
+    for (int i = 0; i < kLgLoads; ++i) {
+      if (i < kLgTok / 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (__attribute__((address_space(3))) void*)(base + 16 * i * kLgCh),
+                                                 16, vo, static_cast<uint32_t>(16 * i) * rb + kb, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ws, (__attribute__((address_space(3))) void*)(base + 16 * i * kLgCh), 16, vo,
+            static_cast<uint32_t>(16 * (i - kLgTok / 16)) * rb + kb, 0, 0);
     }
   };
-  auto compute = [&](int buf) {
-    floatx4 part[NBW];
+
+  const int rr = lane & 15, cg = lane >> 4;
+  double acc[2][4][4];
+  floatx4 part[2][4];
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) part[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int q = 0; q < P; ++q)
+    for (int eb = 0; eb < 4; ++eb) {
+      part[tb][eb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-        part[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[buf][q]),
-                                                            __builtin_bit_cast(bf16x8, wa[buf][q][nb]), part[nb], 0, 0, 0);
+      for (int v = 0; v < 4; ++v) acc[tb][eb][v] = 0.0;
+    }
+
+  issue(0);
+  issue(1);
+  for (int st = 0; st < nst; ++st) {
+    // stage st landed (stage st+1 may be in flight); every wave is past stage st-1
+    if (st + 1 < nst) __builtin_amdgcn_s_waitcnt(0x0F70 | kLgLoads);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    lg_barrier();
+    if (st + 2 < nst) issue(st + 2);
+    const u32x4* sa = lds + (st % kLgNS) * kStage;
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
+    for (int s = 0; s < kLgK / 32; ++s) {
+      const int ch = lgswz(rr, 4 * s + cg);
+      bf16x8 xf[2], wf[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[nb][v] += static_cast<double>(part[nb][v]);
-  };
-  // blocks kw, kw + KS, ...: two in flight, buffers alternate (unrolled by two
-  // so that every register index is a compile-time constant)
-  int blk = kw;
-  if (blk < nblk) load(blk, 0);
-  while (blk < nblk) {
-    if (blk + KS < nblk) load(blk + KS, 1);
-    compute(0);
-    blk += KS;
-    if (blk >= nblk) break;
-    if (blk + KS < nblk) load(blk + KS, 0);
-    compute(1);
-    blk += KS;
+      for (int tb = 0; tb < 2; ++tb)
+        xf[tb] = __builtin_bit_cast(bf16x8, sa[(32 * wave + 16 * tb + rr) * kLgCh + ch]);
+#pragma unroll
+      for (int eb = 0; eb < 4; ++eb)
+        wf[eb] = __builtin_bit_cast(bf16x8, sa[(kLgTok + 16 * eb + rr) * kLgCh + ch]);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb)
+          part[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[tb], wf[eb], part[tb][eb], 0, 0, 0);
+    }
+    if (st & 1) {   // a 256-element chunk is complete: add it in float64
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[tb][eb][v] += static_cast<double>(part[tb][eb][v]);
+          part[tb][eb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
   }
 
-  // lane (c, g) holds tokens tg*16 + 4g + v and experts nb*16 + c
-  if constexpr (KS == 1) {
+  // lane (rr, cg) of block (tb, eb) holds tokens 32 w + 16 tb + 4 cg + v, expert 16 eb + rr
+  double* out = a.logits + static_cast<size_t>(ks) * a.T * a.Epad;
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
+  for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = tile0 + tg * 16 + 4 * g + v;
-        if (t < a.T) a.logits[static_cast<size_t>(t) * a.Epad + e0 + nb * 16 + c] = acc[nb][v];
+    for (int v = 0; v < 4; ++v) {
+      const int t = tok0 + 32 * wave + 16 * tb + 4 * cg + v;
+      if (t < a.T) {
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb) out[static_cast<size_t>(t) * a.Epad + e0 + 16 * eb + rr] = acc[tb][eb][v];
       }
-  } else {
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave][nb * 16 + c][4 * g + v] = acc[nb][v];
-    __syncthreads();
-    // 16 tokens per token group: sum the KS partials in wave order
-    for (int i = threadIdx.x; i < TT * ES; i += blockDim.x) {
-      const int tl = i / ES, e = i - tl * ES;
-      const int grp = tl / 16, r = tl - grp * 16;
-      double sum = 0.0;
-#pragma unroll
-      for (int q = 0; q < KS; ++q) sum += red[grp * KS + q][e][r];
-      const int t = tile0 + tl;
-      if (t < a.T) a.logits[static_cast<size_t>(t) * a.Epad + e0 + e] = sum;
     }
-  }
 }
 
 // Selection from float64 logits [T, Epad] for one 64-token tile, one token
@@ -401,7 +426,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(LogitArgs a) {
 constexpr int kSelectThreads = kRouterTile * 16;
 
 template <int NB>
-__global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArgs a, const double* logits, int Epad) {
+__global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArgs a, const double* logits, int Epad,
+                                                                       int KS) {
   __shared__ int32_t s_idx[kRouterTile * MOE_MAX_TOPK];
   __shared__ unsigned long long s_mask[MOE_MAX_EXPERTS];
   __shared__ float s_p[kRouterTile][16 * NB + 1];
@@ -419,7 +445,12 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
   for (int nb = 0; nb < NB; ++nb) {
     const int e = nb * 16 + c;
     double l = -INFINITY;
-    if (e < E && tok_ok) l = logits[static_cast<size_t>(t) * Epad + e] + (a.b_g ? static_cast<double>(a.b_g[e]) : 0.0);
+    if (e < E && tok_ok) {
+      // the split-K partials, added in split order
+      l = logits[static_cast<size_t>(t) * Epad + e];
+      for (int q = 1; q < KS; ++q) l += logits[(static_cast<size_t>(q) * a.T + t) * Epad + e];
+      l += a.b_g ? static_cast<double>(a.b_g[e]) : 0.0;
+    }
     val[nb] = l;
     m = fmax(m, l);
   }
@@ -488,28 +519,10 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
   }
 }
 
-template <int NBW, int KS>
-hipError_t launch_logits(const Problem& p, const LogitArgs& la, hipStream_t st) {
-  constexpr int ES = 16 * NBW;
-  constexpr int TT = 64 / KS;
-  dim3 grid((p.T + TT - 1) / TT, (p.E + ES - 1) / ES);
-  hipLaunchKernelGGL((router_logits_kernel<NBW, KS>), grid, dim3(256), 0, st, la);
-  return hipGetLastError();
-}
-
-template <int NBW>
-hipError_t launch_logits_ks(const Problem& p, const LogitArgs& la, hipStream_t st) {
-  constexpr int ES = 16 * NBW;
-  const long long slices = (p.E + ES - 1) / ES;
-  // smallest token tile (most split of d) that still gives >= 512 workgroups
-  if (static_cast<long long>((p.T + 63) / 64) * slices >= 512) return launch_logits<NBW, 1>(p, la, st);
-  if (static_cast<long long>((p.T + 31) / 32) * slices >= 512) return launch_logits<NBW, 2>(p, la, st);
-  return launch_logits<NBW, 4>(p, la, st);
-}
-
 template <int NB>
-hipError_t launch_select(const Problem& p, const RouterArgs& a, const double* logits, int Epad, hipStream_t st) {
-  hipLaunchKernelGGL((router_select_kernel<NB>), dim3(p.ntile), dim3(kSelectThreads), 0, st, a, logits, Epad);
+hipError_t launch_select(const Problem& p, const RouterArgs& a, const double* logits, int Epad, int KS,
+                         hipStream_t st) {
+  hipLaunchKernelGGL((router_select_kernel<NB>), dim3(p.ntile), dim3(kSelectThreads), 0, st, a, logits, Epad, KS);
   return hipGetLastError();
 }
 
@@ -524,6 +537,18 @@ hipError_t launch_nb(const Problem& p, const RouterArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+int logit_pad(int E) { return (E + kLgExp - 1) / kLgExp * kLgExp; }
+
+// d is split into KS ranges of whole 256-element chunks so the logits launch
+// has ~256 workgroups (at most 8 splits, at least one chunk each)
+int logit_splits(const Problem& p) {
+  const long long tiles = static_cast<long long>((p.T + kLgTok - 1) / kLgTok) * (logit_pad(p.E) / kLgExp);
+  long long ks = (256 + tiles - 1) / tiles;
+  if (ks > 8) ks = 8;
+  if (ks > p.d / 256) ks = p.d / 256;
+  return ks < 1 ? 1 : static_cast<int>(ks);
+}
 
 hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const float* b_g,
                          int32_t* topk_idx, float* topk_w, const Workspace& ws, hipStream_t st) {
@@ -550,17 +575,17 @@ hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const
     la.T = p.T;
     la.d = p.d;
     la.E = p.E;
-    const int nbw = nb <= 1 ? 1 : (nb <= 2 ? 2 : 4);
-    la.Epad = ((p.E + 16 * nbw - 1) / (16 * nbw)) * 16 * nbw;
-    hipError_t e = nbw == 1 ? launch_logits_ks<1>(p, la, st)
-                 : nbw == 2 ? launch_logits_ks<2>(p, la, st)
-                            : launch_logits_ks<4>(p, la, st);
+    la.Epad = logit_pad(p.E);
+    la.KS = logit_splits(p);
+    const dim3 grid((p.T + kLgTok - 1) / kLgTok, la.Epad / kLgExp, la.KS);
+    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, st, la);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (nb <= 1) return launch_select<1>(p, a, la.logits, la.Epad, st);
-    if (nb <= 2) return launch_select<2>(p, a, la.logits, la.Epad, st);
-    if (nb <= 4) return launch_select<4>(p, a, la.logits, la.Epad, st);
-    if (nb <= 8) return launch_select<8>(p, a, la.logits, la.Epad, st);
-    return launch_select<16>(p, a, la.logits, la.Epad, st);
+    if (nb <= 1) return launch_select<1>(p, a, la.logits, la.Epad, la.KS, st);
+    if (nb <= 2) return launch_select<2>(p, a, la.logits, la.Epad, la.KS, st);
+    if (nb <= 4) return launch_select<4>(p, a, la.logits, la.Epad, la.KS, st);
+    if (nb <= 8) return launch_select<8>(p, a, la.logits, la.Epad, la.KS, st);
+    return launch_select<16>(p, a, la.logits, la.Epad, la.KS, st);
   }
   if (nb <= 1) return launch_nb<1>(p, a, st);
   if (nb <= 2) return launch_nb<2>(p, a, st);

@@ -122,10 +122,15 @@ constexpr int kCh = kBK / 8;                   // 16-byte chunks per tile row
 constexpr int kRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data format (gfx9 family)
 
 // LDS layout of a tile row of 64 bf16 (8 chunks of 16 bytes): logical chunk c
-// of row r is stored at chunk c ^ (r & 7) ^ ((r >> 3) & 1).  A ds_read_b128
-// of 16 consecutive rows at one logical chunk then touches 16 distinct
-// 16-byte bank groups whether the LDS serves 8 or 16 lanes per cycle, and so
-// does a ds_write_b128 of 2 rows x 8 chunks.
+// of row r is stored at chunk c ^ (r & 7) ^ ((r >> 3) & 1).  Fragment reads
+// (16x16x32: lane l holds row l % 16 of a block, 8 consecutive k) assign the
+// K chunks to lane quarters as chunk 2 (l / 16) + slice: slice 0 takes chunks
+// {0, 2, 4, 6}, slice 1 {1, 3, 5, 7}.  Measured with an LDS probe on gfx950,
+// that ds_read_b128 pattern has no bank conflicts under this swizzle, while
+// the natural order (quarter q reading chunk 4 slice + q) costs 4 conflict
+// cycles per read under any XOR swizzle tried and 12 without one.  A and B
+// use the same assignment, so each MFMA still contracts matching k of A and
+// B; only which 32 k share an MFMA changes.
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7) ^ ((row >> 3) & 1); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -297,7 +302,7 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
     bf16x8 fa[2][MB], fb[2][8];
     auto frag1 = [&](int rs, int sl, int q) {
       const u32x4* sa = lds + rs * kStage;
-      const int ch = swz(rd_row, 4 * sl + (lane >> 4));
+      const int ch = swz(rd_row, 2 * (lane >> 4) + sl);
       if (q < MB)
         fa[sl][q] = __builtin_bit_cast(bf16x8, sa[(wm * (BM / 2) + q * 16 + rd_row) * kCh + ch]);
       else

@@ -304,9 +304,10 @@ constexpr int kLgCh = kLgK / 8;                        // 16-byte chunks per sta
 constexpr int kLgNS = 3;                               // ring slots
 constexpr int kLgLoads = (kLgTok + kLgExp) / 16;       // 1 KB direct loads per wave per stage (12)
 
-// LDS row of 16 chunks: logical chunk c of row r at c ^ (r & 15).  A
-// ds_read_b128 of 16 consecutive rows at one logical chunk then covers 16
-// distinct 16-byte bank groups.
+// LDS row of 16 chunks (256 bytes): logical chunk c of row r at c ^ (r & 15).
+// Measured with an LDS probe on gfx950, the fragment reads (rows 0..15 of a
+// block at chunks 4 s .. 4 s + 3 in the four 16-lane quarters) then have no
+// bank conflicts.
 __device__ __forceinline__ int lgswz(int row, int c) { return c ^ (row & 15); }
 
 __device__ __forceinline__ void lg_barrier() {

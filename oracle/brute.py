@@ -9,8 +9,9 @@ queue per expert.  It shares no helper with ``oracle.moe_ref``.
 
 Definitions followed: the pages' layer of "AI-Research-SKILLs MoE 训练实战…全指南"
 §3.1 (router, softmax, top-k, renormalise, weighted expert sum), its §4.3
-balance loss, its §8.2 / "第7章 Mixture of Experts" §7.4 capacity, and the
-shared experts of its §7.1.
+balance loss and router z-loss, its §8.2 / "第7章 Mixture of Experts" §7.4
+capacity, the shared experts of its §7.1 and the SiLU, bias-free Mixtral
+expert of its §6.1.
 """
 from __future__ import annotations
 
@@ -42,11 +43,13 @@ def brute_topk(logits: Sequence[float], k: int):
 
 def brute_layer(x: List[List[float]], W_g: List[List[float]], experts, k: int,
                 cap: Optional[int] = None, n_shared: int = 0,
-                b_g: Optional[Sequence[float]] = None):
+                b_g: Optional[Sequence[float]] = None, activation: str = "gelu"):
     """x: T lists of d floats; W_g: E lists of d floats; experts: list of
-    (W1 [h][d], b1 [h], W2 [d][h], b2 [d]) for E routed then n_shared shared.
+    (W1 [h][d], b1 [h] or None, W2 [d][h], b2 [d] or None) for E routed then
+    n_shared shared; activation "gelu" (erf form) or "silu" (u / (1 + e^-u),
+    the Mixtral expert of the guide's §6.1).
 
-    Returns dict(out, idx, w, counts, kept, dropped, slot_kept, aux)."""
+    Returns dict(out, idx, w, counts, kept, dropped, slot_kept, aux, z)."""
     T = len(x)
     E = len(W_g)
     d = len(x[0])
@@ -86,12 +89,15 @@ def brute_layer(x: List[List[float]], W_g: List[List[float]], experts, k: int,
 
     def ffn(e, xt):
         W1, b1, W2, b2 = experts[e]
-        h = len(b1)
+        h = len(W1)
         g = []
         for i in range(h):
-            u = _dot(W1[i], xt) + b1[i]
-            g.append(0.5 * u * (1.0 + math.erf(u / math.sqrt(2.0))))
-        return [_dot(W2[c], g) + b2[c] for c in range(d)]
+            u = _dot(W1[i], xt) + (b1[i] if b1 is not None else 0.0)
+            if activation == "silu":
+                g.append(u / (1.0 + math.exp(-u)))
+            else:
+                g.append(0.5 * u * (1.0 + math.erf(u / math.sqrt(2.0))))
+        return [_dot(W2[c], g) + (b2[c] if b2 is not None else 0.0) for c in range(d)]
 
     out = [[0.0] * d for _ in range(T)]
     for t in range(T):
@@ -113,5 +119,9 @@ def brute_layer(x: List[List[float]], W_g: List[List[float]], experts, k: int,
         aux += f_e * P_e
     aux *= E
 
+    # router z-loss ([guide] §4.3): mean over tokens of log(sum_e exp l)^2,
+    # summed directly (tiny inputs only: no overflow guard)
+    z = math.fsum(math.log(math.fsum(math.exp(v) for v in logits[t])) ** 2 for t in range(T)) / T
+
     return dict(out=out, idx=idx, w=w, counts=counts, kept=kept, dropped=dropped,
-                slot_kept=slot_kept, aux=aux, logits=logits, probs=probs)
+                slot_kept=slot_kept, aux=aux, z=z, logits=logits, probs=probs)

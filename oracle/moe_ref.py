@@ -39,7 +39,12 @@ with its reason in the design notes of this repository):
     renormalised;
   * GELU is the exact erf form; the expert output b2 sits inside the
     weighted term;
-  * shared experts are stored after the routed ones, weight 1, no capacity.
+  * shared experts are stored after the routed ones, weight 1, no capacity;
+  * the router z-loss is the mean over tokens of the squared log-sum-exp of
+    that token's logits (router bias included), unscaled;
+  * SiLU is u * sigmoid(u); a missing expert bias (None) is a bias-free
+    Linear; min_capacity raises the capacity to at least that many tokens and
+    only applies when there is a capacity limit (cf > 0).
 """
 from __future__ import annotations
 
@@ -92,6 +97,18 @@ def softmax(l: np.ndarray) -> np.ndarray:
     m = l.max(axis=1, keepdims=True)
     z = np.exp(l - m)
     return z / z.sum(axis=1, keepdims=True)
+
+
+def router_z_loss(l: np.ndarray) -> float:
+    """Router z-loss: (1/T) sum_t (log sum_e exp l[t,e])^2, unscaled.
+
+    [guide] §4.3 adds it to the balance loss to keep the router's logits small
+    (the training loss weights it by 0.001, as its §8.5 repeats); it acts on
+    the logits themselves, so a router bias is included.  The log-sum-exp is
+    taken with the row maximum factored out, which cannot overflow."""
+    m = l.max(axis=1)
+    lse = m + np.log(np.exp(l - m[:, None]).sum(axis=1))
+    return float(np.mean(lse * lse))
 
 
 @dataclass
@@ -163,14 +180,17 @@ def aux_loss(counts: np.ndarray, p: np.ndarray, k: int) -> tuple[float, np.ndarr
 
 
 # -------------------------------------------------------------- capacity --
-def capacity_of(capacity_factor: float, T: int, E: int) -> Optional[int]:
-    """cap = ceil(cf * T / E) computed in double; None (no limit) when cf <= 0.
+def capacity_of(capacity_factor: float, T: int, E: int, min_capacity: int = 0) -> Optional[int]:
+    """cap = max(ceil(cf * T / E), min_capacity), the ceiling computed in
+    double; None (no limit) when cf <= 0, whatever min_capacity is.
 
     [guide] §8.2 and [ch7] §7.4 give C = CF * tokens / experts, counting
-    tokens; the ceiling follows the switch-style workload's own statement."""
+    tokens; the ceiling follows the switch-style workload's own statement.
+    [guide] §5.1's DeepSpeed block names a ``min_capacity`` knob without
+    defining it; it is read as a floor under the computed capacity."""
     if capacity_factor is None or capacity_factor <= 0:
         return None
-    return int(math.ceil(float(capacity_factor) * float(T) / float(E)))
+    return max(int(math.ceil(float(capacity_factor) * float(T) / float(E))), int(min_capacity))
 
 
 def capacity_ranks(idx: np.ndarray, E: int) -> np.ndarray:
@@ -196,12 +216,31 @@ def gelu(u: np.ndarray) -> np.ndarray:
     return 0.5 * u * (1.0 + erf(u / math.sqrt(2.0)))
 
 
-def expert_ffn(xr: np.ndarray, W1: np.ndarray, b1: np.ndarray, W2: np.ndarray, b2: np.ndarray) -> np.ndarray:
-    """y = W2 GELU(W1 x + b1) + b2 for each row of xr ([guide] §3.1: Linear(d, h),
-    GELU, Linear(h, d), both with bias; [tutorial] part 5 likewise).
+def silu(u: np.ndarray) -> np.ndarray:
+    """SiLU: u * sigmoid(u) = u / (1 + exp(-u)) ([guide] §6.1, the activation
+    of the Mixtral expert).  Written with exp(-|u|) so neither sign overflows."""
+    e = np.exp(-np.abs(u))
+    return np.where(u >= 0, u / (1.0 + e), u * e / (1.0 + e))
+
+
+ACTIVATIONS = {"gelu": gelu, "silu": silu}
+
+
+def expert_ffn(xr: np.ndarray, W1: np.ndarray, b1: Optional[np.ndarray], W2: np.ndarray,
+               b2: Optional[np.ndarray], activation: str = "gelu") -> np.ndarray:
+    """y = W2 act(W1 x + b1) + b2 for each row of xr.
+
+    [guide] §3.1: Linear(d, h), GELU, Linear(h, d), both with bias ([tutorial]
+    part 5 likewise); [guide] §6.1's Mixtral expert: Linear(d, h) without bias,
+    SiLU, Linear(h, d) without bias.  A bias given as None is absent.
     W1 is [h, d] and W2 is [d, h] (nn.Linear layout)."""
-    u = xr @ W1.T + b1[None, :]
-    return gelu(u) @ W2.T + b2[None, :]
+    u = xr @ W1.T
+    if b1 is not None:
+        u = u + b1[None, :]
+    y = ACTIVATIONS[activation](u) @ W2.T
+    if b2 is not None:
+        y = y + b2[None, :]
+    return y
 
 
 # ------------------------------------------------------------------ layer --
@@ -221,6 +260,7 @@ class MoERef:
     offsets: np.ndarray      # [E+1] exclusive scan of kept
     cap: Optional[int]
     aux: float
+    z: float                 # router z-loss
     f: np.ndarray
     P: np.ndarray
     rows: np.ndarray         # token ids whose outputs are in ``out``
@@ -230,13 +270,16 @@ class MoERef:
 def moe_forward_ref(x, W_g, get_expert: Callable[[int], tuple], E: int, k: int,
                     capacity_factor: float = 0.0, n_shared: int = 0, b_g=None,
                     kind: str = "f32", rows: Optional[Sequence[int]] = None,
-                    override_idx: Optional[np.ndarray] = None) -> MoERef:
+                    override_idx: Optional[np.ndarray] = None, activation: str = "gelu",
+                    min_capacity: int = 0) -> MoERef:
     """The whole layer forward in float64.
 
     x [T,d] and W_g [E,d] are raw inputs of ``kind`` ("f32", "bf16" bit
     patterns, or "f64"); ``get_expert(e)`` returns the raw (W1 [h,d], b1 [h],
     W2 [d,h], b2 [d]) of expert e, routed for e < E and shared for
-    E <= e < E + n_shared; b_g is an optional float32 logit offset [E].
+    E <= e < E + n_shared, either bias possibly None (bias-free Linear);
+    b_g is an optional float32 logit offset [E].  ``activation`` is "gelu"
+    or "silu"; ``min_capacity`` floors the capacity (see capacity_of).
 
     ``rows`` restricts the expert computation to those tokens (routing,
     counts, capacity and aux always use all T tokens).  ``override_idx``
@@ -244,7 +287,7 @@ def moe_forward_ref(x, W_g, get_expert: Callable[[int], tuple], E: int, k: int,
     comparison after a near-tie was resolved the other way by rounding).
 
     Steps ([guide] §3.1 and §7.1; [ch7] §7.1 MoE(x) = sum G_i E_i(x)):
-      1 logits  2 softmax  3 top-k  4 renormalise  5 counts and aux
+      1 logits  2 softmax  3 top-k  4 renormalise  5 counts, aux and z-loss
       6 capacity in token order  7 weighted routed experts  8 shared experts.
     """
     xf = widen(x, kind)
@@ -256,8 +299,9 @@ def moe_forward_ref(x, W_g, get_expert: Callable[[int], tuple], E: int, k: int,
     w = renormalised_weights(p, idx)
     counts = expert_counts(idx, E)
     aux, f, P = aux_loss(counts, p, k)
+    z = router_z_loss(l)
 
-    cap = capacity_of(capacity_factor, T, E)
+    cap = capacity_of(capacity_factor, T, E, min_capacity)
     rank = capacity_ranks(idx, E)
     slot_kept = np.ones((T, k), dtype=bool) if cap is None else (rank < cap)
     kept = counts.copy() if cap is None else np.minimum(counts, cap)
@@ -276,19 +320,19 @@ def moe_forward_ref(x, W_g, get_expert: Callable[[int], tuple], E: int, k: int,
         tok, slot = np.nonzero((idx == e) & slot_kept & want[:, None])
         if tok.size == 0:
             continue
-        W1, b1, W2, b2 = (widen(a, kind) for a in get_expert(e))
-        y = expert_ffn(xf[tok], W1, b1, W2, b2)
+        W1, b1, W2, b2 = (None if a is None else widen(a, kind) for a in get_expert(e))
+        y = expert_ffn(xf[tok], W1, b1, W2, b2, activation)
         # a token occurs at most once per expert, so this scatter has no collisions
         out[row_of[tok]] += w[tok, slot][:, None] * y
 
     for s in range(n_shared):
-        W1, b1, W2, b2 = (widen(a, kind) for a in get_expert(E + s))
-        out += expert_ffn(xf[rows_arr], W1, b1, W2, b2)
+        W1, b1, W2, b2 = (None if a is None else widen(a, kind) for a in get_expert(E + s))
+        out += expert_ffn(xf[rows_arr], W1, b1, W2, b2, activation)
 
     return MoERef(logits=l, probs=p, idx=idx, w=w, tie_flag=sel.tie_flag,
                   order_flag=sel.order_flag, counts=counts, kept=kept, rank=rank,
                   slot_kept=slot_kept, slot_pos=slot_pos, offsets=offsets, cap=cap,
-                  aux=aux, f=f, P=P, rows=rows_arr, out=out)
+                  aux=aux, z=z, f=f, P=P, rows=rows_arr, out=out)
 
 
 def moe_forward_ref_from_inputs(inp, rows=None, override_idx=None) -> MoERef:
@@ -296,4 +340,5 @@ def moe_forward_ref_from_inputs(inp, rows=None, override_idx=None) -> MoERef:
     and ``expert(e)`` (the seeded workload generator's interface)."""
     c = inp.cfg
     return moe_forward_ref(inp.x, inp.W_g, inp.expert, c.E, c.k, c.cf, c.S, inp.b_g,
-                           kind=c.dtype, rows=rows, override_idx=override_idx)
+                           kind=c.dtype, rows=rows, override_idx=override_idx,
+                           activation=c.activation, min_capacity=c.min_capacity)

@@ -15,7 +15,9 @@ Workloads (shapes from the models the pages name; distributions as stated):
 
 x ~ N(0,1); router and expert weights ~ N(0, 0.02); expert biases ~ N(0, 0.02)
 (zero for ``tiny``); the ``glam`` router bias ~ N(0,1) in fp32 skews the
-expert loads so that the capacity limit drops assignments.
+expert loads so that the capacity limit drops assignments.  Any workload can
+be overridden to the Mixtral expert form (``activation="silu"``,
+``expert_bias=False``) or given a ``min_capacity``.
 
 Every tensor is drawn per (tensor id, expert id) from its own PCG64 stream
 ``SeedSequence(seed, spawn_key=(tensor_id, expert_id))`` so one expert can be
@@ -48,6 +50,9 @@ class MoEConfig:
     bias_std: float = 0.02   # std of b1, b2 (0 => zero biases)
     w_std: float = 0.02
     router_bias_std: float = 0.0  # std of the fp32 router logit bias (0 => none)
+    activation: str = "gelu"      # expert activation, "gelu" or "silu"
+    expert_bias: bool = True      # False: bias-free expert Linears (b1, b2 are None)
+    min_capacity: int = 0         # floor under the capacity when cf > 0
 
     def replace(self, **kw) -> "MoEConfig":
         return dataclasses.replace(self, **kw)
@@ -129,11 +134,14 @@ class MoEInputs:
         return self._bg
 
     def expert(self, e: int):
-        """(W1 [h,d], b1 [h], W2 [d,h], b2 [d]) of expert e (routed or shared)."""
+        """(W1 [h,d], b1 [h], W2 [d,h], b2 [d]) of expert e (routed or shared);
+        b1 and b2 are None for bias-free experts."""
         c = self.cfg
         W1 = _pack(c, _normal(self.seed, TID_W1, e, (c.h, c.d), c.w_std))
         W2 = _pack(c, _normal(self.seed, TID_W2, e, (c.d, c.h), c.w_std))
-        if c.bias_std > 0:
+        if not c.expert_bias:
+            b1 = b2 = None
+        elif c.bias_std > 0:
             b1 = _pack(c, _normal(self.seed, TID_B1, e, (c.h,), c.bias_std))
             b2 = _pack(c, _normal(self.seed, TID_B2, e, (c.d,), c.bias_std))
         else:
@@ -143,17 +151,20 @@ class MoEInputs:
         return W1, b1, W2, b2
 
     def stacked(self):
-        """All expert parameters stacked: W1 [E+S,h,d], b1 [E+S,h], W2 [E+S,d,h], b2 [E+S,d]."""
+        """All expert parameters stacked: W1 [E+S,h,d], b1 [E+S,h], W2 [E+S,d,h],
+        b2 [E+S,d] (b1 and b2 None for bias-free experts)."""
         c = self.cfg
         n = c.E + c.S
         dt = np.uint16 if c.dtype == "bf16" else np.float32
         W1 = np.empty((n, c.h, c.d), dtype=dt)
-        b1 = np.empty((n, c.h), dtype=dt)
         W2 = np.empty((n, c.d, c.h), dtype=dt)
-        b2 = np.empty((n, c.d), dtype=dt)
+        b1 = np.empty((n, c.h), dtype=dt) if c.expert_bias else None
+        b2 = np.empty((n, c.d), dtype=dt) if c.expert_bias else None
 
         def fill(e):
-            W1[e], b1[e], W2[e], b2[e] = self.expert(e)
+            W1[e], eb1, W2[e], eb2 = self.expert(e)
+            if c.expert_bias:
+                b1[e], b2[e] = eb1, eb2
 
         # numpy's generators release the GIL, so experts are drawn in parallel
         with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:

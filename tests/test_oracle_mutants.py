@@ -37,13 +37,13 @@ MUTANTS = [
     ("gelu_tanh_approx", "return 0.5 * u * (1.0 + erf(u / math.sqrt(2.0)))",
      "return 0.5 * u * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * u ** 3)))"),
     ("gelu_wrong_sign", "return 0.5 * u * (1.0 + erf(u / math.sqrt(2.0)))", "return 0.5 * u * (1.0 - erf(u / math.sqrt(2.0)))"),
-    ("ffn_drops_b1", "u = xr @ W1.T + b1[None, :]", "u = xr @ W1.T"),
-    ("ffn_drops_b2", "return gelu(u) @ W2.T + b2[None, :]", "return gelu(u) @ W2.T"),
+    ("ffn_drops_b1", "u = u + b1[None, :]", "u = u"),
+    ("ffn_drops_b2", "y = y + b2[None, :]", "y = y"),
     # a transposed operand that only shows where the matrix is square (h == d)
-    ("ffn_W1_transposed_when_square", "u = xr @ W1.T + b1[None, :]",
-     "u = xr @ (W1 if W1.shape[0] == W1.shape[1] else W1.T) + b1[None, :]"),
-    ("ffn_W2_transposed_when_square", "return gelu(u) @ W2.T + b2[None, :]",
-     "return gelu(u) @ (W2 if W2.shape[0] == W2.shape[1] else W2.T) + b2[None, :]"),
+    ("ffn_W1_transposed_when_square", "u = xr @ W1.T",
+     "u = xr @ (W1 if W1.shape[0] == W1.shape[1] else W1.T)"),
+    ("ffn_W2_transposed_when_square", "y = ACTIVATIONS[activation](u) @ W2.T",
+     "y = ACTIVATIONS[activation](u) @ (W2 if W2.shape[0] == W2.shape[1] else W2.T)"),
     ("router_W_g_transposed_when_square", "l = x @ W_g.T", "l = x @ (W_g if W_g.shape[0] == W_g.shape[1] else W_g.T)"),
     ("router_drops_bias", "l = l + np.asarray(b_g, dtype=np.float64)[None, :]", "l = l"),
     ("b2_outside_weight", "out[row_of[tok]] += w[tok, slot][:, None] * y",
@@ -52,9 +52,27 @@ MUTANTS = [
      "out[row_of[tok]] += (w[tok, slot] / (w * slot_kept).sum(1)[tok])[:, None] * y"),
     ("dropped_slots_still_added", "tok, slot = np.nonzero((idx == e) & slot_kept & want[:, None])",
      "tok, slot = np.nonzero((idx == e) & want[:, None])"),
-    ("shared_weighted_half", "out += expert_ffn(xf[rows_arr], W1, b1, W2, b2)",
-     "out += 0.5 * expert_ffn(xf[rows_arr], W1, b1, W2, b2)"),
+    ("shared_weighted_half", "out += expert_ffn(xf[rows_arr], W1, b1, W2, b2, activation)",
+     "out += 0.5 * expert_ffn(xf[rows_arr], W1, b1, W2, b2, activation)"),
     ("bf16_widen_wrong_shift", "<< np.uint32(16)", "<< np.uint32(15)"),
+    ("z_loss_not_squared", "return float(np.mean(lse * lse))", "return float(np.mean(lse))"),
+    ("z_loss_square_of_mean", "return float(np.mean(lse * lse))", "return float(np.mean(lse) ** 2)"),
+    ("z_loss_sum_not_mean", "return float(np.mean(lse * lse))", "return float(np.sum(lse * lse))"),
+    ("z_loss_drops_max", "lse = m + np.log(", "lse = np.log("),
+    ("z_loss_no_max_shift", "lse = m + np.log(np.exp(l - m[:, None]).sum(axis=1))",
+     "lse = np.log(np.exp(l).sum(axis=1))"),
+    ("z_loss_on_probs", "z = router_z_loss(l)", "z = router_z_loss(p)"),
+    ("z_loss_without_router_bias", "z = router_z_loss(l)", "z = router_z_loss(xf @ widen(W_g, kind).T)"),
+    ("silu_negative_branch", "u * e / (1.0 + e))", "u / (1.0 + e))"),
+    ("silu_is_sigmoid", "return np.where(u >= 0, u / (1.0 + e), u * e / (1.0 + e))",
+     "return np.where(u >= 0, 1.0 / (1.0 + e), e / (1.0 + e))"),
+    ("activation_ignored", "y = ACTIVATIONS[activation](u) @ W2.T", "y = gelu(u) @ W2.T"),
+    ("min_capacity_ignored", "return max(int(math.ceil(float(capacity_factor) * float(T) / float(E))), int(min_capacity))",
+     "return int(math.ceil(float(capacity_factor) * float(T) / float(E)))"),
+    ("min_capacity_is_a_ceiling", "return max(int(math.ceil(float(capacity_factor) * float(T) / float(E))), int(min_capacity))",
+     "return min(int(math.ceil(float(capacity_factor) * float(T) / float(E))), int(min_capacity) or 2 ** 31)"),
+    ("min_capacity_applies_without_limit", "    if capacity_factor is None or capacity_factor <= 0:\n        return None\n    return max(",
+     "    if capacity_factor is None or capacity_factor <= 0:\n        return int(min_capacity) or None\n    return max("),
 ]
 
 

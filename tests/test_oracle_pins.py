@@ -44,11 +44,11 @@ def to_lists(a):
     return [list(map(float, r)) for r in np.asarray(a)]
 
 
-def brute_case(x, W_g, experts, k, cap=None, S=0, b_g=None):
-    ex = [(to_lists(W1), list(map(float, b1)), to_lists(W2), list(map(float, b2)))
-          for (W1, b1, W2, b2) in experts]
+def brute_case(x, W_g, experts, k, cap=None, S=0, b_g=None, activation="gelu"):
+    vec = lambda b: None if b is None else list(map(float, b))
+    ex = [(to_lists(W1), vec(b1), to_lists(W2), vec(b2)) for (W1, b1, W2, b2) in experts]
     return brute.brute_layer(to_lists(x), to_lists(W_g), ex, k, cap=cap, n_shared=S,
-                             b_g=None if b_g is None else list(map(float, b_g)))
+                             b_g=vec(b_g), activation=activation)
 
 
 def ffn_torch(xr, W1, b1, W2, b2):
@@ -97,6 +97,7 @@ def check_against_brute():
             assert (r.counts - r.kept).tolist() == b["dropped"]
             assert r.slot_kept.tolist() == b["slot_kept"]
             assert abs(r.aux - b["aux"]) < 1e-13
+            assert abs(r.z - b["z"]) < 1e-12
             assert np.allclose(r.out, np.array(b["out"]), rtol=0, atol=1e-11)
 
 
@@ -359,10 +360,130 @@ def check_widen_bf16():
     assert v.tolist() == [1.0, -2.0, 0.25, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127]
 
 
+def _no_ffn(E, d):
+    """E experts that output 0 (bias-free), for checks of the router alone."""
+    return [(np.zeros((2, d)), None, np.zeros((d, 2)), None)] * E
+
+
+def check_z_loss_closed_forms():
+    """Router z-loss (1/T) sum_t logsumexp(l_t)^2 ([guide] §4.3) on closed forms."""
+    rng = np.random.default_rng(12)
+    # (i) zero router: every logit is 0, so logsumexp = log E for every token
+    for E in [1, 2, 8, 64, 256]:
+        r = run_ref(rng.standard_normal((17, 3)), np.zeros((E, 3)), _no_ffn(E, 3), E, 1)
+        assert abs(r.z - math.log(E) ** 2) <= 1e-14 * max(1.0, math.log(E) ** 2)
+    # (ii) router bias only, l_t = log [1, 2, 3, 4] for every token: (log 10)^2
+    b = np.log(np.array([1.0, 2.0, 3.0, 4.0]))
+    r = run_ref(rng.standard_normal((9, 2)), np.zeros((4, 2)), _no_ffn(4, 2), 4, 2, b_g=b)
+    assert abs(r.z - math.log(10.0) ** 2) < 1e-14
+    # (iii) two experts with logits (a_t, 0): logsumexp = log(1 + e^a_t), the softplus
+    a = np.array([-3.0, -0.5, 0.0, 0.7, 2.0, 5.0])
+    r = run_ref(a[:, None], np.array([[1.0], [0.0]]), _no_ffn(2, 1), 2, 1)
+    assert abs(r.z - sum(math.log1p(math.exp(v)) ** 2 for v in a) / len(a)) < 1e-14
+    # (iv) large equal logits L: logsumexp = L + log E, without overflow
+    for (L, E) in [(1000.0, 8), (-1000.0, 3)]:
+        r = run_ref(np.ones((4, 1)), np.full((E, 1), L), _no_ffn(E, 1), E, 1)
+        assert abs(r.z - (L + math.log(E)) ** 2) <= 1e-13 * (L + math.log(E)) ** 2
+    # (v) a common logit shift c moves every logsumexp by c, so z(c) is a quadratic
+    # in c with leading coefficient 1: unit-step second differences are exactly 2
+    x, W_g, ex = rand_case(rng, 11, 4, 2, 5, 2)
+    z = [run_ref(x, W_g, ex, 5, 2, b_g=np.full(5, c)).z for c in (-1.0, 0.0, 1.0, 2.0)]
+    assert abs((z[2] - 2 * z[1] + z[0]) - 2.0) < 1e-12 and abs((z[3] - 2 * z[2] + z[1]) - 2.0) < 1e-12
+    # (vi) it depends on the router alone: not on k, the capacity or the experts
+    r1 = run_ref(x, W_g, ex, 5, 1, 0.5)
+    r2 = run_ref(x, W_g, _no_ffn(5, 4), 5, 3)
+    assert r1.z == r2.z == run_ref(x, W_g, ex, 5, 2).z
+
+
+def check_silu_and_bias_free():
+    """SiLU = u sigmoid(u) ([guide] §6.1): closed values, the identity
+    silu(u) - silu(-u) = u, torch's F.silu; the bias-free SiLU expert equals
+    torch F.linear without bias around F.silu; a None bias equals a zero bias."""
+    import torch
+    import torch.nn.functional as F
+    s = lambda u: float(ref.silu(np.array([u]))[0])
+    assert s(0.0) == 0.0
+    assert abs(s(1.0) - math.e / (math.e + 1.0)) < 1e-16
+    assert abs(s(-1.0) + 1.0 / (math.e + 1.0)) < 1e-16
+    assert s(800.0) == 800.0 and abs(s(-800.0)) < 1e-300 and math.isfinite(s(-800.0))
+    u = np.linspace(-30.0, 30.0, 241)
+    assert np.allclose(ref.silu(u) - ref.silu(-u), u, rtol=0, atol=1e-13)
+    assert np.allclose(ref.silu(u), F.silu(torch.as_tensor(u)).numpy(), rtol=1e-14, atol=1e-300)
+    rng = np.random.default_rng(13)
+    W1, W2 = rng.standard_normal((12, 5)), rng.standard_normal((5, 12))
+    xr = rng.standard_normal((7, 5))
+    t = lambda a: torch.as_tensor(a, dtype=torch.float64)
+    want = F.linear(F.silu(F.linear(t(xr), t(W1))), t(W2)).numpy()
+    assert np.allclose(ref.expert_ffn(xr, W1, None, W2, None, "silu"), want, rtol=0, atol=1e-13)
+    for act in ("gelu", "silu"):
+        assert np.array_equal(ref.expert_ffn(xr, W1, None, W2, None, act),
+                              ref.expert_ffn(xr, W1, np.zeros(12), W2, np.zeros(5), act))
+
+
+def check_min_capacity():
+    """Capacity floor min_capacity ([guide] §5.1 DeepSpeed block, with the §8.2
+    formula): cap = max(ceil(cf T / E), min_capacity); no limit stays no limit."""
+    assert ref.capacity_of(1.0, 8, 4, 4) == 4          # ceil(2) = 2: the floor binds
+    assert ref.capacity_of(1.25, 4096, 64, 4) == 80    # ceil(80) = 80: it does not
+    assert ref.capacity_of(2.0, 4096, 64, 4) == 128    # the eval capacity factor 2.0 of §5.1
+    assert ref.capacity_of(0.01, 100, 4, 3) == 3       # ceil(0.25) = 1 -> 3
+    assert ref.capacity_of(0.0, 10, 2, 4) is None and ref.capacity_of(-1.0, 10, 2, 7) is None
+    assert ref.capacity_of(1.0, 6, 4, 0) == 2          # no floor: ceil(1.5)
+    rng = np.random.default_rng(15)
+    x, W_g, ex = rand_case(rng, 40, 3, 2, 4, 2)
+    W_g[0] += 1.5
+    r0 = run_ref(x, W_g, ex, 4, 2, 0.2)                # ceil(2) = 2
+    r1 = run_ref(x, W_g, ex, 4, 2, 0.2, min_capacity=7)
+    assert r0.cap == 2 and r1.cap == 7
+    assert np.all(r1.kept == np.minimum(r1.counts, 7)) and np.all(r1.slot_kept[r0.slot_kept])
+    big = run_ref(x, W_g, ex, 4, 2, 0.2, min_capacity=40)   # floor >= T: nothing dropped
+    assert big.slot_kept.all() and np.allclose(big.out, run_ref(x, W_g, ex, 4, 2).out, rtol=0, atol=0)
+
+
+def check_mixtral_expert_against_brute():
+    """Bias-free SiLU experts with a capacity floor == brute force (scalar loops,
+    subset enumeration, explicit first-come queues)."""
+    rng = np.random.default_rng(14)
+    # (T, d, h, E, k, S, cf, min_capacity, cap worked out by hand)
+    cases = [(8, 3, 4, 4, 2, 0, 0.0, 0, None), (8, 3, 3, 5, 2, 1, 0.5, 3, 3),
+             (7, 2, 4, 3, 1, 0, 0.3, 2, 2), (6, 4, 2, 4, 2, 1, 1.0, 0, 2), (9, 2, 3, 3, 2, 0, 0.4, 5, 5)]
+    for (T, d, h, E, k, S, cf, mc, cap) in cases:
+        for trial in range(2):
+            x, W_g, ex = rand_case(rng, T, d, h, E, k, S)
+            ex = [(W1, None, W2, None) for (W1, _, W2, _) in ex]
+            b_g = rng.standard_normal(E) if trial == 1 else None
+            r = run_ref(x, W_g, ex, E, k, cf, S, b_g, activation="silu", min_capacity=mc)
+            assert not r.tie_flag.any() and r.cap == cap
+            b = brute_case(x, W_g, ex, k, cap=cap, S=S, b_g=b_g, activation="silu")
+            assert r.idx.tolist() == b["idx"] and r.kept.tolist() == b["kept"]
+            assert r.slot_kept.tolist() == b["slot_kept"]
+            assert abs(r.aux - b["aux"]) < 1e-13 and abs(r.z - b["z"]) < 1e-12
+            assert np.allclose(r.out, np.array(b["out"]), rtol=0, atol=1e-11)
+
+
+def check_golden_silu_min_capacity():
+    """Hand-derived fixture (tests/golden/silu_min_capacity.json): Mixtral expert
+    form of [guide] §6.1, a capacity floor, and the z-loss of [guide] §4.3."""
+    g = json.load(open(os.path.join(GOLDEN, "silu_min_capacity.json")))
+    vec = lambda v: None if v is None else np.array(v, dtype=np.float64)
+    ex = [tuple(vec(e[n]) for n in ("W1", "b1", "W2", "b2")) for e in g["experts"]]
+    r = run_ref(np.array(g["x"]), np.array(g["W_g"]), ex, 2, g["k"], g["capacity_factor"],
+                activation=g["activation"], min_capacity=g["min_capacity"])
+    e_ = g["expected"]
+    assert r.cap == e_["cap"] and r.idx.tolist() == e_["idx"]
+    assert r.counts.tolist() == e_["counts"] and r.kept.tolist() == e_["kept"]
+    assert r.slot_pos.tolist() == e_["slot_pos"]
+    want = [math.e / (math.e + 1)] * 4 + [0.0] + [-1 / (math.e + 1)]
+    assert np.allclose(r.out[:, 0], want, rtol=0, atol=1e-15)
+    assert abs(r.z - math.log(math.e + 1 / math.e) ** 2) < 1e-15
+
+
 ALL_CHECKS = [check_weights_sum_to_one, check_against_brute, check_topk_vs_torch, check_tie_rule,
               check_dense_limit, check_aux_closed_forms, check_capacity, check_dropped_contribute_nothing,
               check_ffn_library, check_combine_symmetries, check_shared, check_golden_fixtures,
-              check_rows_and_override, check_widen_bf16]
+              check_rows_and_override, check_widen_bf16, check_z_loss_closed_forms,
+              check_silu_and_bias_free, check_min_capacity, check_mixtral_expert_against_brute,
+              check_golden_silu_min_capacity]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=[c.__name__ for c in ALL_CHECKS])

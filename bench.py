@@ -2,6 +2,7 @@
 """Benchmark of the sparse-MoE FFN layer forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload mixtral] [--no-cpu-baseline]
+                    [--activation gelu|silu] [--no-expert-bias] [--min-capacity N]
 
 A step is one full layer forward (router, scan, scatter, expert phase 1,
 expert phase 2, combine) over one batch of seeded synthetic tokens already
@@ -47,6 +48,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = workload default)")
+    ap.add_argument("--activation", default="gelu", choices=["gelu", "silu"],
+                    help="expert activation (silu with --no-expert-bias: the Mixtral expert form)")
+    ap.add_argument("--no-expert-bias", action="store_true", help="bias-free expert Linears (NULL b1, b2)")
+    ap.add_argument("--min-capacity", type=int, default=0, help="capacity floor (with a capacity factor)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -85,9 +90,10 @@ def cpu_baseline(inp, stacked, ntok: int):
     ntok = min(ntok, c.T)
     W1, b1, W2, b2 = stacked
     x = inp.x[:ntok]
+    get = lambda e: (W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e])
     t0 = time.perf_counter()
-    oracle.moe_forward_ref(x, inp.W_g, lambda e: (W1[e], b1[e], W2[e], b2[e]), c.E, c.k,
-                           float(np.float32(c.cf)), c.S, inp.b_g, kind=c.dtype)
+    oracle.moe_forward_ref(x, inp.W_g, get, c.E, c.k, float(np.float32(c.cf)), c.S, inp.b_g, kind=c.dtype,
+                           activation=c.activation, min_capacity=c.min_capacity)
     dt = time.perf_counter() - t0
     threads = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
     cores = max(threads) if threads else 1
@@ -111,7 +117,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = make_inputs(args.workload, seed=args.seed)
+    inp = make_inputs(args.workload, seed=args.seed, activation=args.activation,
+                      expert_bias=not args.no_expert_bias, min_capacity=args.min_capacity)
     c = inp.cfg
     t0 = time.perf_counter()
     stacked = inp.stacked()
@@ -123,7 +130,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     x, W_g = up(inp.x), up(inp.W_g)
-    W1, b1, W2, b2 = (up(a) for a in stacked)
+    W1, b1, W2, b2 = (None if a is None else up(a) for a in stacked)
     b_g = None if inp.b_g is None else torch.from_numpy(inp.b_g).to(dev)
     dt_code = moe.MOE_BF16 if c.dtype == "bf16" else moe.MOE_F32
     T, d, h, E, k, S = c.T, c.d, c.h, c.E, c.k, c.S
@@ -133,6 +140,7 @@ def main():
     topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
     aux = torch.empty((1,), dtype=torch.float32, device=dev)
+    z_loss = torch.empty((1,), dtype=torch.float32, device=dev)
     counts = torch.empty((E,), dtype=torch.int32, device=dev)
     kept = torch.empty((E,), dtype=torch.int32, device=dev)
     slot_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -144,6 +152,9 @@ def main():
     launch.expert_counts, launch.expert_kept, launch.slot_pos = counts.data_ptr(), kept.data_ptr(), slot_pos.data_ptr()
     launch.workspace, launch.workspace_bytes = ws.data_ptr(), ws.numel()
     launch.stream = stream.cuda_stream
+    launch.z_loss = z_loss.data_ptr()
+    launch.activation = moe.ACTIVATIONS[c.activation]
+    launch.min_capacity = c.min_capacity
 
     nst = moe.MOE_NUM_STAGE_EVENTS
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nst)] for _ in range(args.steps)]
@@ -151,7 +162,8 @@ def main():
         for e in row:
             e.record(stream)          # creates the handle
     ev_arrays = [(ctypes.c_void_p * nst)(*[int(e.cuda_event) for e in row]) for row in events]
-    ptrs = (x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), b1.data_ptr(), W2.data_ptr(), b2.data_ptr())
+    ptr = lambda t: None if t is None else t.data_ptr()
+    ptrs = (x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), ptr(b1), W2.data_ptr(), ptr(b2))
 
     def step(ev=None):
         launch.stage_events = None if ev is None else ctypes.cast(ev, ctypes.c_void_p)
@@ -233,6 +245,10 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device copies done")
 
+    variant = ""
+    if c.activation != "gelu" or not c.expert_bias or c.min_capacity:
+        variant = (f", {c.activation} experts" + ("" if c.expert_bias else " without bias") +
+                   (f", min_capacity={c.min_capacity}" if c.min_capacity else ""))
     result = {
         "metric": METRIC,
         "value": T * args.steps / wall,
@@ -247,8 +263,9 @@ def main():
         "dtype": c.dtype,
         "data": "synthetic (seeded normal inputs and random-init weights of the named shapes)",
         "config": {"workload": f"{args.workload}-shaped MoE layer: T={T} d={d} h={h} E={E} k={k} shared={S} "
-                               f"capacity_factor={c.cf} {c.dtype}",
+                               f"capacity_factor={c.cf} {c.dtype}" + variant,
                    "T": T, "d": d, "h": h, "E": E, "k": k, "n_shared": S, "capacity_factor": c.cf,
+                   "activation": c.activation, "expert_bias": c.expert_bias, "min_capacity": c.min_capacity,
                    "kept_assignments": a_kept, "dropped_assignments": T * k - a_kept},
         "roofline": roof,
         "stages": per_stage,

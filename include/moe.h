@@ -3,23 +3,26 @@
  * FFN layer on an AMD Instinct MI355X (gfx950).
  *
  * The operation (pages: "AI-Research-SKILLs MoE 训练实战…全指南" §3.1 basic MoE
- * layer, §4.3 auxiliary loss, §7.1 DeepSeekMoE shared experts, §8.2 capacity
- * factor; "第7章 Mixture of Experts（MoE）架构" §7.1 MoE(x) = sum_i G(x)_i E_i(x),
- * §7.4 balance loss and capacity; "[BEE-30064] 混合專家架構與服務", how routing
- * works):
+ * layer, §4.3 auxiliary loss and router z-loss, §5.1 DeepSpeed MoE settings
+ * (min_capacity), §6.1 Mixtral expert (bias-free, SiLU), §7.1 DeepSeekMoE shared
+ * experts, §8.2 capacity factor; "第7章 Mixture of Experts（MoE）架构" §7.1
+ * MoE(x) = sum_i G(x)_i E_i(x), §7.4 balance loss and capacity; "[BEE-30064]
+ * 混合專家架構與服務", how routing works):
  *
  *   l[t,e]  = sum_c x[t,c] W_g[e,c] (+ b_g[e])              router, no bias
  *   p[t,:]  = softmax(l[t,:])
  *   idx[t,:] = the k largest logits, descending, ties to the lower expert index
  *   w[t,j]  = p[t,idx[t,j]] / sum_j' p[t,idx[t,j']]          renormalised
- *   cap     = ceil(cf * T / E) (cf <= 0: no limit); for each expert the
- *             assignments are kept in ascending token order while fewer than
- *             cap have been kept, the rest are dropped (contribute nothing)
- *   out[t]  = sum_{kept j} w[t,j] (W2_e GELU(W1_e x[t] + b1_e) + b2_e),  e = idx[t,j]
+ *   cap     = max(ceil(cf * T / E), min_capacity) (cf <= 0: no limit); for each
+ *             expert the assignments are kept in ascending token order while
+ *             fewer than cap have been kept, the rest are dropped (contribute nothing)
+ *   out[t]  = sum_{kept j} w[t,j] (W2_e act(W1_e x[t] + b1_e) + b2_e),  e = idx[t,j]
  *           + sum_{s<S} FFN_{E+s}(x[t])                      shared, weight 1
  *   aux     = E * sum_e f_e P_e,  f_e = c_e/(T k) (c_e counted before capacity),
  *             P_e = mean_t p[t,e]                            unscaled
- *   GELU(u) = u * Phi(u) (erf form).
+ *   z       = (1/T) sum_t (log sum_e exp l[t,e])^2           router z-loss, unscaled
+ *   act     = GELU(u) = u * Phi(u) (erf form), or SiLU(u) = u / (1 + e^-u);
+ *             a NULL b1 or b2 is a bias-free Linear.
  *
  * Conventions
  *   - Every pointer argument is a DEVICE pointer owned by the caller.  The
@@ -46,12 +49,16 @@ extern "C" {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
+/* Expert activation between the two Linears. */
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SILU = 1 } moe_activation_t;
+
 typedef enum {
   MOE_OK = 0,
-  MOE_ERR_ARG = 1,          /* null required pointer, T/d/h/E <= 0, k < 1, k > E, n_shared < 0 */
+  MOE_ERR_ARG = 1,          /* null required pointer, T/d/h/E <= 0, k < 1, k > E, n_shared < 0,
+                               min_capacity < 0, NaN capacity_factor */
   MOE_ERR_UNSUPPORTED = 2,  /* E > MOE_MAX_EXPERTS, k > MOE_MAX_TOPK, n_shared > MOE_MAX_SHARED,
                                d or h not a multiple of 8, pointer not 16-byte aligned, unknown
-                               dtype, or a row count that overflows int32 */
+                               dtype or activation, or a row count that overflows int32 */
   MOE_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than moe_workspace_bytes(...) */
   MOE_ERR_HIP = 4           /* a HIP launch reported an error (hipGetLastError) */
 } moe_status_t;
@@ -63,7 +70,7 @@ typedef enum {
 /* Stage boundaries at which optional timing events are recorded (see
  * moe_launch_t.stage_events): before the router, then after the router, the
  * scan, the scatter (each kept assignment's row in the expert-sorted order;
- * token rows are not copied), expert phase 1 (x W1^T + b1, GELU), expert phase 2
+ * token rows are not copied), expert phase 1 (x W1^T + b1, activation), expert phase 2
  * (h W2^T + b2) and the combine. */
 #define MOE_NUM_STAGE_EVENTS 7
 
@@ -85,6 +92,12 @@ typedef struct {
   hipStream_t stream;     /* stream all kernels are enqueued on (0 = default stream) */
   hipEvent_t* stage_events; /* NULL, or MOE_NUM_STAGE_EVENTS created events that are
                                recorded on `stream` at the stage boundaries */
+  float* z_loss;          /* [1] out, or NULL: router z-loss (1/T) sum_t (log sum_e exp l[t,e])^2,
+                             logits including b_g, unscaled (float64 partials, one rounding) */
+  int32_t activation;     /* moe_activation_t of every expert, routed and shared;
+                             0 = MOE_ACT_GELU (a zero-initialised struct keeps GELU) */
+  int32_t min_capacity;   /* >= 0: floor under the capacity when capacity_factor > 0
+                             (cap = max(ceil(cf*T/E), min_capacity)); ignored otherwise */
 } moe_launch_t;
 
 /* Bytes of device workspace moe_forward needs for this problem shape (0 if
@@ -98,12 +111,13 @@ size_t moe_workspace_bytes(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k
  *   x        [T, d]          input tokens (a batch and sequence flattened, as on the pages)
  *   W_g      [E, d]          router weight
  *   W1       [E+S, h, d]     first expert linear; experts 0..E-1 routed, E..E+S-1 shared
- *   b1       [E+S, h]
+ *   b1       [E+S, h]         or NULL: the first Linear has no bias
  *   W2       [E+S, d, h]     second expert linear
- *   b2       [E+S, d]
+ *   b2       [E+S, d]         or NULL: the second Linear has no bias
  *   E        routed experts, 1..MOE_MAX_EXPERTS
  *   k        experts per token, 1..min(E, MOE_MAX_TOPK)
- *   capacity_factor  <= 0: no capacity limit; else cap = ceil(cf*T/E) (double precision)
+ *   capacity_factor  <= 0: no capacity limit; else cap = max(ceil(cf*T/E), launch->min_capacity)
+ *            (the ceiling in double precision)
  *   n_shared shared experts S, 0..MOE_MAX_SHARED
  *   out      [T, d]          layer output, dtype (bf16: accumulated in float32, rounded once)
  *   topk_idx [T, k] int32    slot j = the (j+1)-th largest logit (before capacity)

@@ -12,10 +12,12 @@ import ctypes
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
-from ._lib import (EXPORTS, LIB_PATH, MOE_BF16, MOE_ERR_ARG, MOE_ERR_HIP, MOE_ERR_UNSUPPORTED,
-                   MOE_ERR_WORKSPACE, MOE_F32, MOE_MAX_EXPERTS, MOE_MAX_SHARED, MOE_MAX_TOPK,
-                   MOE_NUM_STAGE_EVENTS, MOE_OK, MoeLaunch, moe_forward, moe_status_string,
+from ._lib import (EXPORTS, LIB_PATH, MOE_ACT_GELU, MOE_ACT_SILU, MOE_BF16, MOE_ERR_ARG, MOE_ERR_HIP,
+                   MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_F32, MOE_MAX_EXPERTS, MOE_MAX_SHARED,
+                   MOE_MAX_TOPK, MOE_NUM_STAGE_EVENTS, MOE_OK, MoeLaunch, moe_forward, moe_status_string,
                    moe_workspace_bytes)
+
+ACTIVATIONS = {"gelu": MOE_ACT_GELU, "silu": MOE_ACT_SILU}
 
 STAGES = ("router", "scan", "scatter", "expert_phase1", "expert_phase2", "combine")
 
@@ -26,6 +28,7 @@ class MoEOutput:
     topk_idx: "object"       # [T, k] int32
     topk_w: "object"         # [T, k] float32
     aux_loss: "object"       # [1] float32
+    z_loss: "object"         # [1] float32, router z-loss
     expert_counts: "object"  # [E] int32
     expert_kept: "object"    # [E] int32
     slot_pos: "object"       # [T, k] int32
@@ -41,27 +44,32 @@ def _dtype_code(t) -> int:
 
 
 def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shared: int = 0, b_g=None,
-            *, stage_events: Optional[Sequence] = None, workspace=None) -> MoEOutput:
+            *, activation: str = "gelu", min_capacity: int = 0, stage_events: Optional[Sequence] = None,
+            workspace=None) -> MoEOutput:
     """Run the layer on torch tensors that live on one GPU.
 
-    x [T,d]; W_g [E,d]; W1 [E+S,h,d]; b1 [E+S,h]; W2 [E+S,d,h]; b2 [E+S,d]
-    (float32 or bfloat16, contiguous); b_g optional float32 [E].
+    x [T,d]; W_g [E,d]; W1 [E+S,h,d]; b1 [E+S,h] or None; W2 [E+S,d,h];
+    b2 [E+S,d] or None (float32 or bfloat16, contiguous; None = bias-free
+    Linear); b_g optional float32 [E].  ``activation`` is "gelu" or "silu";
+    ``min_capacity`` floors the capacity when capacity_factor > 0.
     ``stage_events``: optional list of MOE_NUM_STAGE_EVENTS torch.cuda.Event
     objects (already recorded once, so their handles exist) that the library
     records at its stage boundaries.  Raises RuntimeError on a non-zero status.
     """
     import torch
-    tensors = [x, W_g, W1, b1, W2, b2]
+    tensors = [t for t in (x, W_g, W1, b1, W2, b2) if t is not None]
     dev = x.device
     for t in tensors:
         if not t.is_cuda or t.device != dev or not t.is_contiguous() or t.dtype != x.dtype:
             raise ValueError("x, W_g, W1, b1, W2, b2 must be contiguous tensors of one dtype on one GPU")
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}")
     T, d = x.shape
     E = W_g.shape[0]
     h = W1.shape[1]
     S = n_shared
-    if W_g.shape != (E, d) or W1.shape != (E + S, h, d) or b1.shape != (E + S, h) or \
-            W2.shape != (E + S, d, h) or b2.shape != (E + S, d):
+    if W_g.shape != (E, d) or W1.shape != (E + S, h, d) or W2.shape != (E + S, d, h) or \
+            (b1 is not None and b1.shape != (E + S, h)) or (b2 is not None and b2.shape != (E + S, d)):
         raise ValueError("inconsistent shapes")
     if b_g is not None and (b_g.dtype != torch.float32 or b_g.shape != (E,) or b_g.device != dev):
         raise ValueError("b_g must be float32 [E] on the same GPU")
@@ -75,6 +83,7 @@ def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shar
     topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
     aux = torch.empty((1,), dtype=torch.float32, device=dev)
+    zl = torch.empty((1,), dtype=torch.float32, device=dev)
     counts = torch.empty((E,), dtype=torch.int32, device=dev)
     kept = torch.empty((E,), dtype=torch.int32, device=dev)
     slot_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -88,6 +97,9 @@ def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shar
     launch.workspace = workspace.data_ptr()
     launch.workspace_bytes = workspace.numel()
     launch.stream = torch.cuda.current_stream(dev).cuda_stream
+    launch.z_loss = zl.data_ptr()
+    launch.activation = ACTIVATIONS[activation]
+    launch.min_capacity = int(min_capacity)
     ev_arr = None
     if stage_events is not None:
         if len(stage_events) != MOE_NUM_STAGE_EVENTS:
@@ -97,15 +109,16 @@ def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shar
             raise ValueError("record each stage event once before passing it (creates its handle)")
         ev_arr = (ctypes.c_void_p * MOE_NUM_STAGE_EVENTS)(*handles)
         launch.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
-    status = moe_forward(x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), b1.data_ptr(), W2.data_ptr(),
-                         b2.data_ptr(), E, k, float(capacity_factor), S, out.data_ptr(), topk_idx.data_ptr(),
-                         topk_w.data_ptr(), aux.data_ptr(), launch)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    status = moe_forward(x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), ptr(b1), W2.data_ptr(), ptr(b2), E, k,
+                         float(capacity_factor), S, out.data_ptr(), topk_idx.data_ptr(), topk_w.data_ptr(),
+                         aux.data_ptr(), launch)
     if status != MOE_OK:
         raise RuntimeError(moe_status_string(status))
-    return MoEOutput(out, topk_idx, topk_w, aux, counts, kept, slot_pos)
+    return MoEOutput(out, topk_idx, topk_w, aux, zl, counts, kept, slot_pos)
 
 
 __all__ = ["forward", "MoEOutput", "moe_forward", "moe_workspace_bytes", "moe_status_string", "MoeLaunch",
-           "MOE_F32", "MOE_BF16", "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
+           "ACTIVATIONS", "MOE_ACT_GELU", "MOE_ACT_SILU", "MOE_F32", "MOE_BF16", "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
            "MOE_ERR_HIP", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SHARED", "MOE_NUM_STAGE_EVENTS",
            "STAGES", "EXPORTS", "LIB_PATH"]

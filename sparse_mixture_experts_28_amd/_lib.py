@@ -15,6 +15,9 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_F32 = 0
 MOE_BF16 = 1
 
+MOE_ACT_GELU = 0
+MOE_ACT_SILU = 1
+
 MOE_OK = 0
 MOE_ERR_ARG = 1
 MOE_ERR_UNSUPPORTED = 2
@@ -45,6 +48,9 @@ class MoeLaunch(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("stage_events", ctypes.c_void_p),
+        ("z_loss", ctypes.c_void_p),
+        ("activation", ctypes.c_int32),
+        ("min_capacity", ctypes.c_int32),
     ]
 
 

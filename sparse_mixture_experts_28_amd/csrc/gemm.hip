@@ -1,28 +1,25 @@
 // moe_grouped_gemm: the expert FFNs over the ragged expert segments.
-//   phase 1: H[seg rows] = GELU(A[seg rows] W1_e^T + b1_e)   (A = expert-sorted tokens,
+//   phase 1: H[seg rows] = act(A[seg rows] W1_e^T + b1_e)    (A = expert-sorted tokens,
 //                                                              or x for a shared expert)
 //   phase 2: Y[seg rows] = H[seg rows] W2_e^T + b2_e
+// act is GELU (erf form) or SiLU; a missing bias (NULL) is left out.
 //
 // Pages: "AI-Research-SKILLs MoE 训练实战…全指南" §3.1 (each expert is
 // Linear(d, 4d) -> GELU -> Linear(4d, d), with bias, applied to the tokens
-// routed to it) and §7.1 (shared experts see every token); "[BEE-30064]
+// routed to it), §6.1 (the Mixtral expert: bias-free Linear -> SiLU ->
+// bias-free Linear) and §7.1 (shared experts see every token); "[BEE-30064]
 // 混合專家架構與服務" (compute grows with the active parameters, memory with the
 // total); "第7章 Mixture of Experts" §7.3 (one shared plus many fine-grained
 // routed experts).
 //
 // Both operands are K-contiguous (A rows and nn.Linear weight rows), so
-// C = A B^T is the "NT" product that MFMA prefers.  All tiles are 256 columns
-// wide with K steps of 64; accumulation is float32 on the 32x32x16 bf16 MFMA;
-// the epilogue adds the bias and (phase 1) applies GELU(erf) in float32 and
-// rounds once to bf16.
+// C = A B^T is the "NT" product that MFMA prefers.  Tiles are BM x 256 with
+// K steps of 64, BM in {128, 160, 256} chosen per problem; accumulation is
+// float32 on the 16x16x32 bf16 MFMA; the epilogue adds the bias and (phase 1)
+// applies the activation in float32 and rounds once to bf16.  The tail of a
+// persistent launch is split along K (stream-K style) with a deterministic
+// fix-up.
 //
-// Two bf16 kernels, chosen by the average rows per expert:
-//  * 256-row tiles, 8 waves (compute-bound regime, e.g. 8 experts of ~2k rows):
-//    two waves per SIMD, 128 x 64 wave tiles, two 64 KB LDS stages filled by
-//    direct global->LDS loads one K step ahead.
-//  * 128-row tiles, 4 waves (weight-streaming regime: many experts of ~100-400
-//    rows): a 3-stage LDS ring filled two K steps ahead so ~96 KB per CU stay
-//    in flight.
 // Shared pieces: operands are read with buffer loads whose range check returns
 // zero past a segment's last row (ragged tails need no clamping); LDS rows use
 // a 16-byte-chunk XOR swizzle that makes the MFMA operand reads conflict-free;
@@ -51,7 +48,7 @@ struct GemmArgs {
   const int32_t* row_token;  // phase 1: token of each expert-sorted row; phase 2: nullptr
   int a_by_o_off;        // phase 2: the A row offset of a segment is its output row offset
   const void* W;         // [nseg][N][K]
-  const void* bias;      // [nseg][N]
+  const void* bias;      // [nseg][N], or nullptr (no bias)
   void* C;               // [rows][N]
   const int32_t* seg;    // segment table
   int nseg, E, N, K;
@@ -75,8 +72,21 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
+// activation of the first Linear: none (phase 2), GELU or SiLU
+constexpr int kActNone = 0, kActGelu = 1, kActSilu = 2;
+
 __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
+}
+
+// SiLU(v) = v / (1 + e^-v), IEEE division (SIMT path).  e^-v overflows to
+// +inf for v < -88 and the quotient is then -0, the limit.
+__device__ __forceinline__ float silu_exact(float v) { return v / (1.0f + expf(-v)); }
+
+// SiLU with the hardware exp2 and reciprocal (~1 ulp each), for the MFMA
+// epilogue whose results are rounded to bf16; the same limits as above.
+__device__ __forceinline__ float silu_fast(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.44269504088896341f));
 }
 
 // GELU(v) = v/2 (1 + erf(v / sqrt 2)) with erf from Abramowitz & Stegun 7.1.26
@@ -95,6 +105,20 @@ __device__ __forceinline__ float gelu_as(float v) {
   const float erf_v = copysignf(fmaf(-q, e, 1.0f), v);
   const float hv = 0.5f * v;
   return fmaf(hv, erf_v, hv);
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_fast(float v) {
+  if constexpr (ACT == kActGelu) return gelu_as(v);
+  else if constexpr (ACT == kActSilu) return silu_fast(v);
+  else return v;
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_exact(float v) {
+  if constexpr (ACT == kActGelu) return gelu_erf(v);
+  else if constexpr (ACT == kActSilu) return silu_exact(v);
+  else return v;
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -209,8 +233,8 @@ __device__ __forceinline__ TailPlan tail_plan(int total, int P, int nk, int part
 // Epilogue: the MFMA takes the B fragment first, so each block is
 // accumulated transposed: lane l holds output row 16 i + l % 16 of the wave
 // tile and the four consecutive columns 16 j + 4 (l / 16) + 0..3; bias, then
-// (phase 1) GELU, in float32, rounded once to bf16, one 8-byte store.
-template <bool GELU, int BM>
+// (phase 1) the activation, in float32, rounded once to bf16, one 8-byte store.
+template <int ACT, int BM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_mfma_kernel(GemmArgs g) {
   constexpr int NS = BM <= 160 ? 3 : 2;
@@ -391,14 +415,14 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
 
     // Epilogue.  A piece of a tail tile stores its float32 partial tile
     // (row-major BM x 256, buffer stores: one lane offset plus scalar and
-    // immediate offsets); a whole tile adds the bias, applies GELU (phase 1)
-    // and stores bf16.  The choice is made per 16-row block so only that
+    // immediate offsets); a whole tile adds the bias, applies the activation
+    // (phase 1) and stores bf16.  The choice is made per 16-row block so only that
     // block's accumulators are live in vector registers at a time.
     const int cbase = n0 + wn * 128 + 4 * (lane >> 4);
     const uint16_t* brow = Bias + static_cast<size_t>(s) * g.N + cbase;
     uint2 bq[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bq[j] = *reinterpret_cast<const uint2*>(brow + 16 * j);
+    for (int j = 0; j < 8; ++j) bq[j] = Bias ? *reinterpret_cast<const uint2*>(brow + 16 * j) : make_uint2(0u, 0u);
     const __amdgpu_buffer_rsrc_t pr = make_rsrc(g.part, static_cast<uint32_t>(g.part_cap) * BM * kBN * 4u);
     const uint32_t pv = (static_cast<uint32_t>(wm * (BM / 2) + (lane & 15)) * kBN + wn * 128 + 4 * (lane >> 4)) * 4u;
 #pragma unroll
@@ -417,12 +441,10 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
           float v1 = acc[i][j][1] + __uint_as_float(bq[j].x & 0xffff0000u);
           float v2 = acc[i][j][2] + __uint_as_float(bq[j].y << 16);
           float v3 = acc[i][j][3] + __uint_as_float(bq[j].y & 0xffff0000u);
-          if (GELU) {
-            v0 = gelu_as(v0);
-            v1 = gelu_as(v1);
-            v2 = gelu_as(v2);
-            v3 = gelu_as(v3);
-          }
+          v0 = act_fast<ACT>(v0);
+          v1 = act_fast<ACT>(v1);
+          v2 = act_fast<ACT>(v2);
+          v3 = act_fast<ACT>(v3);
           *reinterpret_cast<uint2*>(crow + 16 * j) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
         }
       }
@@ -432,9 +454,9 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
 
 // Fix-up of the split tail, in 16-row chunks of the tail tiles strided over
 // the P workgroups.  Each thread owns four consecutive columns of four rows;
-// the S partial tiles are summed in piece order, then bias, GELU (phase 1)
-// and one bf16 rounding, as in the GEMM epilogue.
-template <bool GELU, int BM>
+// the S partial tiles are summed in piece order, then bias, the activation
+// (phase 1) and one bf16 rounding, as in the GEMM epilogue.
+template <int ACT, int BM>
 __global__ __launch_bounds__(256) void gemm_tail_fixup_kernel(GemmArgs g, int P) {
   const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
   const int total_mt = st.tile_start[g.nseg];
@@ -453,7 +475,9 @@ __global__ __launch_bounds__(256) void gemm_tail_fixup_kernel(GemmArgs g, int P)
     const int m0 = (mt - st.tile_start[s]) * BM;
     const int o_off = st.o_off[s];
     const int n = nt * kBN + c;
-    const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g.bias) + static_cast<size_t>(s) * g.N + n);
+    const uint2 b = g.bias ? *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g.bias) +
+                                                             static_cast<size_t>(s) * g.N + n)
+                           : make_uint2(0u, 0u);
     const float b0 = __uint_as_float(b.x << 16), b1 = __uint_as_float(b.x & 0xffff0000u);
     const float b2 = __uint_as_float(b.y << 16), b3 = __uint_as_float(b.y & 0xffff0000u);
     const float* part = g.part + static_cast<size_t>(tt) * tp.S * BM * kBN;
@@ -465,12 +489,10 @@ __global__ __launch_bounds__(256) void gemm_tail_fixup_kernel(GemmArgs g, int P)
       for (int p = 1; p < tp.S; ++p)
         a += *reinterpret_cast<const floatx4*>(part + (static_cast<size_t>(p) * BM + rr) * kBN + c);
       float v0 = a[0] + b0, v1 = a[1] + b1, v2 = a[2] + b2, v3 = a[3] + b3;
-      if (GELU) {
-        v0 = gelu_as(v0);
-        v1 = gelu_as(v1);
-        v2 = gelu_as(v2);
-        v3 = gelu_as(v3);
-      }
+      v0 = act_fast<ACT>(v0);
+      v1 = act_fast<ACT>(v1);
+      v2 = act_fast<ACT>(v2);
+      v3 = act_fast<ACT>(v3);
       *reinterpret_cast<uint2*>(C + static_cast<size_t>(o_off + m0 + rr) * g.N + n) =
           make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
     }
@@ -485,7 +507,7 @@ __device__ __forceinline__ float ld_f32(const uint16_t* p, size_t i) { return bf
 __device__ __forceinline__ void st_out(float* p, size_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void st_out(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 
-template <typename TIn, bool GELU>
+template <typename TIn, int ACT>
 __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmArgs g, int max_mt) {
   __shared__ float sA[kSK][kSB + 1];
   __shared__ float sB[kSK][kSB + 1];
@@ -502,7 +524,7 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmArgs g, int max_mt) 
   const bool gather = g.row_token != nullptr && s < g.E;
   const TIn* A = static_cast<const TIn*>(g.A);
   const TIn* B = static_cast<const TIn*>(g.W) + static_cast<size_t>(s) * g.N * g.K;
-  const TIn* Bias = static_cast<const TIn*>(g.bias) + static_cast<size_t>(s) * g.N;
+  const TIn* Bias = g.bias ? static_cast<const TIn*>(g.bias) + static_cast<size_t>(s) * g.N : nullptr;
   TIn* C = static_cast<TIn*>(g.C);
 
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
@@ -539,8 +561,8 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmArgs g, int max_mt) 
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + tx * 4 + j;
       if (col >= g.N) continue;
-      float v = acc[i][j] + ld_f32(Bias, col);
-      if (GELU) v = gelu_erf(v);
+      float v = acc[i][j] + (Bias ? ld_f32(Bias, col) : 0.f);
+      v = act_exact<ACT>(v);
       st_out(C, static_cast<size_t>(o_off + rl) * g.N + col, v);
     }
   }
@@ -619,48 +641,49 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
   }
   g.part = ws.part;
   g.part_cap = ws.part_cap;
+  // the activation follows the first Linear only
+  const int act = phase == 2 ? kActNone : (p.act == MOE_ACT_SILU ? kActSilu : kActGelu);
   if (gemm_fast_path(p)) {
     int grid = num_cus();
     grid = (grid + 7) / 8 * 8;
     const dim3 gd(grid), bd(256);
     // the fix-up runs right after the GEMM on the same stream; it returns at
     // once when the tail was not split
-#define MOE_GEMM_LAUNCH(GELU_, BM_)                                                         \
+#define MOE_GEMM_LAUNCH(ACT_, BM_)                                                          \
   do {                                                                                      \
-    hipLaunchKernelGGL((gemm_bf16_mfma_kernel<GELU_, BM_>), gd, bd, 0, st, g);              \
-    hipLaunchKernelGGL((gemm_tail_fixup_kernel<GELU_, BM_>), gd, bd, 0, st, g, grid);       \
+    hipLaunchKernelGGL((gemm_bf16_mfma_kernel<ACT_, BM_>), gd, bd, 0, st, g);               \
+    hipLaunchKernelGGL((gemm_tail_fixup_kernel<ACT_, BM_>), gd, bd, 0, st, g, grid);        \
+  } while (0)
+#define MOE_GEMM_LAUNCH_BM(BM_)                                                             \
+  do {                                                                                      \
+    if (act == kActGelu) MOE_GEMM_LAUNCH(kActGelu, BM_);                                    \
+    else if (act == kActSilu) MOE_GEMM_LAUNCH(kActSilu, BM_);                               \
+    else MOE_GEMM_LAUNCH(kActNone, BM_);                                                    \
   } while (0)
     switch (p.gemm_bm) {
-      case 128:
-        if (phase == 1) MOE_GEMM_LAUNCH(true, 128);
-        else MOE_GEMM_LAUNCH(false, 128);
-        break;
-      case 160:
-        if (phase == 1) MOE_GEMM_LAUNCH(true, 160);
-        else MOE_GEMM_LAUNCH(false, 160);
-        break;
-      default:
-        if (phase == 1) MOE_GEMM_LAUNCH(true, 256);
-        else MOE_GEMM_LAUNCH(false, 256);
-        break;
+      case 128: MOE_GEMM_LAUNCH_BM(128); break;
+      case 160: MOE_GEMM_LAUNCH_BM(160); break;
+      default: MOE_GEMM_LAUNCH_BM(256); break;
     }
+#undef MOE_GEMM_LAUNCH_BM
 #undef MOE_GEMM_LAUNCH
   } else {
     // upper bound of M tiles: sum_e ceil(rows_e / 64) <= ceil(T k / 64) + E + S ceil(T / 64)
     const long long max_mt = (static_cast<long long>(p.T) * p.k + kSB - 1) / kSB + p.E +
                              static_cast<long long>(p.S) * ((p.T + kSB - 1) / kSB);
     dim3 grid(static_cast<unsigned>(max_mt), (g.N + kSB - 1) / kSB);
-    if (p.dtype == MOE_BF16) {
-      if (phase == 1)
-        hipLaunchKernelGGL((gemm_simt_kernel<uint16_t, true>), grid, dim3(256), 0, st, g, (int)max_mt);
-      else
-        hipLaunchKernelGGL((gemm_simt_kernel<uint16_t, false>), grid, dim3(256), 0, st, g, (int)max_mt);
-    } else {
-      if (phase == 1)
-        hipLaunchKernelGGL((gemm_simt_kernel<float, true>), grid, dim3(256), 0, st, g, (int)max_mt);
-      else
-        hipLaunchKernelGGL((gemm_simt_kernel<float, false>), grid, dim3(256), 0, st, g, (int)max_mt);
-    }
+#define MOE_SIMT_LAUNCH(TIN_)                                                                               \
+  do {                                                                                                      \
+    if (act == kActGelu)                                                                                    \
+      hipLaunchKernelGGL((gemm_simt_kernel<TIN_, kActGelu>), grid, dim3(256), 0, st, g, (int)max_mt);      \
+    else if (act == kActSilu)                                                                               \
+      hipLaunchKernelGGL((gemm_simt_kernel<TIN_, kActSilu>), grid, dim3(256), 0, st, g, (int)max_mt);      \
+    else                                                                                                    \
+      hipLaunchKernelGGL((gemm_simt_kernel<TIN_, kActNone>), grid, dim3(256), 0, st, g, (int)max_mt);      \
+  } while (0)
+    if (p.dtype == MOE_BF16) MOE_SIMT_LAUNCH(uint16_t);
+    else MOE_SIMT_LAUNCH(float);
+#undef MOE_SIMT_LAUNCH
   }
   return hipGetLastError();
 }

@@ -23,7 +23,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t elem_bytes(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t row_token, hbuf, ybuf, local_rank, tile_hist, p_part, counts, kept, slot_pos, seg, logits, part, total;
+  size_t row_token, hbuf, ybuf, local_rank, tile_hist, p_part, z_part, counts, kept, slot_pos, seg, logits, part,
+      total;
   int part_cap;
 };
 
@@ -40,6 +41,7 @@ Layout layout_of(const Problem& p) {
   L.local_rank = off; off += align_up(A * 4);
   L.tile_hist = off;  off += align_up(te * 4);
   L.p_part = off;     off += align_up(te * 4);
+  L.z_part = off;     off += align_up(static_cast<size_t>(p.ntile) * 8);
   L.counts = off;     off += align_up(static_cast<size_t>(p.E) * 4);
   L.kept = off;       off += align_up(static_cast<size_t>(p.E) * 4);
   L.slot_pos = off;   off += align_up(A * 4);
@@ -69,6 +71,7 @@ Workspace carve_workspace(const Problem& p, void* base, size_t bytes_available, 
   w.local_rank = reinterpret_cast<int32_t*>(b + L.local_rank);
   w.tile_hist = reinterpret_cast<int32_t*>(b + L.tile_hist);
   w.p_part = reinterpret_cast<float*>(b + L.p_part);
+  w.z_part = reinterpret_cast<double*>(b + L.z_part);
   w.counts = reinterpret_cast<int32_t*>(b + L.counts);
   w.kept = reinterpret_cast<int32_t*>(b + L.kept);
   w.slot_pos = reinterpret_cast<int32_t*>(b + L.slot_pos);
@@ -93,8 +96,9 @@ moe_status_t check_shape(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, 
   return MOE_OK;
 }
 
+// cap = max(ceil(cf T / E), min_cap) in double when cf > 0, else unlimited
 Problem make_problem(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int32_t S, moe_dtype_t dt,
-                     float cf) {
+                     float cf, int act = MOE_ACT_GELU, int32_t min_cap = 0) {
   Problem p;
   p.T = T;
   p.d = d;
@@ -103,9 +107,11 @@ Problem make_problem(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int3
   p.k = k;
   p.S = S;
   p.dtype = dt;
+  p.act = act;
   p.ntile = (T + kRouterTile - 1) / kRouterTile;
   if (cf > 0.f) {
-    const double c = std::ceil(static_cast<double>(cf) * static_cast<double>(T) / static_cast<double>(E));
+    double c = std::ceil(static_cast<double>(cf) * static_cast<double>(T) / static_cast<double>(E));
+    if (c < static_cast<double>(min_cap)) c = static_cast<double>(min_cap);
     p.cap = c >= static_cast<double>(INT32_MAX) ? INT32_MAX : static_cast<int>(c);
   } else {
     p.cap = INT32_MAX;
@@ -130,7 +136,7 @@ const char* moe_status_string(moe_status_t s) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_ARG: return "MOE_ERR_ARG: invalid argument (null pointer or size out of range)";
     case MOE_ERR_UNSUPPORTED:
-      return "MOE_ERR_UNSUPPORTED: unsupported shape, dtype or pointer alignment";
+      return "MOE_ERR_UNSUPPORTED: unsupported shape, dtype, activation or pointer alignment";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
   }
@@ -143,20 +149,22 @@ moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const v
                          const moe_launch_t* launch) {
   using namespace moe;
   if (launch == nullptr) return MOE_ERR_ARG;
-  if (!x || !W_g || !W1 || !b1 || !W2 || !b2 || !out || !topk_idx || !topk_w || !aux_loss) return MOE_ERR_ARG;
-  if (std::isnan(capacity_factor)) return MOE_ERR_ARG;
+  if (!x || !W_g || !W1 || !W2 || !out || !topk_idx || !topk_w || !aux_loss) return MOE_ERR_ARG;
+  if (std::isnan(capacity_factor) || launch->min_capacity < 0) return MOE_ERR_ARG;
+  if (launch->activation != MOE_ACT_GELU && launch->activation != MOE_ACT_SILU) return MOE_ERR_UNSUPPORTED;
   const moe_status_t sc = check_shape(launch->T, launch->d, launch->h, E, k, n_shared,
                                       static_cast<int>(launch->dtype));
   if (sc != MOE_OK) return sc;
   const void* a16[] = {x, W_g, W1, b1, W2, b2, out};
   for (const void* q : a16)
-    if (!aligned(q, 16)) return MOE_ERR_UNSUPPORTED;
-  const void* a4[] = {topk_idx, topk_w, aux_loss, launch->b_g, launch->expert_counts, launch->expert_kept,
-                      launch->slot_pos};
+    if (q && !aligned(q, 16)) return MOE_ERR_UNSUPPORTED;
+  const void* a4[] = {topk_idx, topk_w, aux_loss, launch->z_loss, launch->b_g, launch->expert_counts,
+                      launch->expert_kept, launch->slot_pos};
   for (const void* q : a4)
     if (q && !aligned(q, 4)) return MOE_ERR_UNSUPPORTED;
 
-  const Problem p = make_problem(launch->T, launch->d, launch->h, E, k, n_shared, launch->dtype, capacity_factor);
+  const Problem p = make_problem(launch->T, launch->d, launch->h, E, k, n_shared, launch->dtype, capacity_factor,
+                                 launch->activation, launch->min_capacity);
   bool ok = false;
   Workspace ws = carve_workspace(p, launch->workspace, launch->workspace_bytes, &ok);
   if (!ok) return MOE_ERR_WORKSPACE;
@@ -178,7 +186,8 @@ moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const v
 
   if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
   if (!check(launch_router(p, x, W_g, launch->b_g, topk_idx, topk_w, ws, st), "router launch")) return MOE_ERR_HIP;
-  if (!check(launch_scan(p, ws, aux_loss, launch->expert_counts, launch->expert_kept, st), "scan launch"))
+  if (!check(launch_scan(p, ws, aux_loss, launch->z_loss, launch->expert_counts, launch->expert_kept, st),
+             "scan launch"))
     return MOE_ERR_HIP;
   if (!check(launch_scatter(p, topk_idx, ws, st), "scatter launch")) return MOE_ERR_HIP;
   if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 1, st), "expert phase 1 launch")) return MOE_ERR_HIP;

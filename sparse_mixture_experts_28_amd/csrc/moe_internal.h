@@ -44,6 +44,7 @@ struct Workspace {
   int32_t* local_rank;  // [T, k]     rank of (t,j) among earlier tokens of its 64-token tile
   int32_t* tile_hist;   // [E, ntile] assignments per (expert, tile); becomes the tile base
   float* p_part;        // [E, ntile] per-tile sums of the softmax probabilities
+  double* z_part;       // [ntile]    per-tile sums of the squared log-sum-exp of the logits
   int32_t* counts;      // [E]
   int32_t* kept;        // [E]
   int32_t* slot_pos;    // [T, k]
@@ -86,7 +87,8 @@ inline size_t seg_table_ints(int nseg, int E) { return static_cast<size_t>(4 * n
 struct Problem {
   int T, d, h, E, k, S;
   moe_dtype_t dtype;
-  int cap;       // capacity per expert; INT32_MAX when unlimited
+  int act;       // moe_activation_t of the experts
+  int cap;       // capacity per expert (min_capacity applied); INT32_MAX when unlimited
   int ntile;     // ceil(T / kRouterTile)
   int gemm_bm;   // M tile of the grouped GEMM (for the tile prefix)
 };
@@ -98,7 +100,7 @@ size_t workspace_bytes(const Problem& p);
 // Each returns hipGetLastError() after its launch(es).
 hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const float* b_g,
                          int32_t* topk_idx, float* topk_w, const Workspace& ws, hipStream_t st);
-hipError_t launch_scan(const Problem& p, const Workspace& ws, float* aux_loss,
+hipError_t launch_scan(const Problem& p, const Workspace& ws, float* aux_loss, float* z_loss,
                        int32_t* counts_out, int32_t* kept_out, hipStream_t st);
 hipError_t launch_scatter(const Problem& p, const int32_t* topk_idx, const Workspace& ws, hipStream_t st);
 hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, const void* b1,

@@ -12,8 +12,9 @@
 //         per-tile counts over the tiles in token order gives each tile's base rank;
 //         the total is c_e, kept_e = min(c_e, cap); an exclusive scan of kept
 //         over experts gives the segment offsets; the balance loss is
-//         finalised from c and the per-tile probability sums (float64, fixed
-//         order); the grouped-GEMM segment table is written.
+//         finalised from c and the per-tile probability sums, the router
+//         z-loss from the per-tile sums of squared log-sum-exp (both float64,
+//         fixed order); the grouped-GEMM segment table is written.
 // scatter (1 thread per assignment): rank = tile base + in-tile rank; the
 //         assignment is kept iff rank < cap; its row in the expert-sorted
 //         order and that row's token are recorded.  No token row is copied:
@@ -31,9 +32,9 @@ constexpr int kScanThreads = 1024;
 // chunks of consecutive tiles); per-chunk totals are scanned over c in LDS in
 // fixed order, so bases, counts and the probability sums are deterministic.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* tile_hist, const float* p_part,
-                                                            int32_t* counts, int32_t* kept, int32_t* seg_base,
-                                                            float* aux_loss, int32_t* counts_out,
-                                                            int32_t* kept_out) {
+                                                            const double* z_part, int32_t* counts, int32_t* kept,
+                                                            int32_t* seg_base, float* aux_loss, float* z_loss,
+                                                            int32_t* counts_out, int32_t* kept_out) {
   __shared__ int32_t s_sum[kScanThreads];
   __shared__ double s_psum[kScanThreads];
   __shared__ int32_t s_kept[MOE_MAX_EXPERTS];
@@ -96,8 +97,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
     }
   }
 
-  // 4. aux = E * sum_e f_e P_e, f_e = c_e / (T k): a fixed-order tree over experts
+  // 4. aux = E * sum_e f_e P_e, f_e = c_e / (T k): a fixed-order tree over experts;
+  // z = (1/T) sum_t lse_t^2: contiguous runs of tiles per thread, then a fixed-order tree
   __shared__ double s_aux[MOE_MAX_EXPERTS];
+  __shared__ double s_z[kScanThreads];
+  {
+    const int zc = (p.ntile + kScanThreads - 1) / kScanThreads;
+    const int zb = t * zc, ze = min(p.ntile, zb + zc);
+    double zs = 0.0;
+    for (int tile = zb; tile < ze; ++tile) zs += z_part[tile];
+    s_z[t] = zs;
+  }
   const double tk = static_cast<double>(p.T) * static_cast<double>(p.k);
   if (t < MOE_MAX_EXPERTS) s_aux[t] = t < E ? (static_cast<double>(s_cnt[t]) / tk) * s_P[t] : 0.0;
   // 5. segment table: one thread per segment (routed experts, then shared)
@@ -120,6 +130,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
     __syncthreads();
   }
   if (t == 0) *aux_loss = static_cast<float>(static_cast<double>(E) * s_aux[0]);
+  for (int w = kScanThreads / 2; w > 0; w >>= 1) {
+    if (t < w) s_z[t] += s_z[t + w];
+    __syncthreads();
+  }
+  if (t == 0 && z_loss) *z_loss = static_cast<float>(s_z[0] / static_cast<double>(p.T));
   // inclusive scans of routed rows and of M tiles over the segments
   for (int off = 1; off < kSegSlots; off <<= 1) {
     int ar = 0, at = 0;
@@ -170,10 +185,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(Problem p, const int32_t* 
 
 }  // namespace
 
-hipError_t launch_scan(const Problem& p, const Workspace& ws, float* aux_loss, int32_t* counts_out,
+hipError_t launch_scan(const Problem& p, const Workspace& ws, float* aux_loss, float* z_loss, int32_t* counts_out,
                        int32_t* kept_out, hipStream_t st) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, st, p, ws.tile_hist, ws.p_part, ws.counts,
-                     ws.kept, ws.seg, aux_loss, counts_out, kept_out);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, st, p, ws.tile_hist, ws.p_part, ws.z_part,
+                     ws.counts, ws.kept, ws.seg, aux_loss, z_loss, counts_out, kept_out);
   return hipGetLastError();
 }
 

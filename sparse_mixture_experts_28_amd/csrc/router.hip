@@ -1,10 +1,11 @@
 // moe_router: router logits, softmax, top-k, renormalisation, per-tile sums of
-// the softmax probabilities (the P_e of the balance loss) and, for the permute,
-// per-tile expert histograms and in-tile token-order ranks.
+// the softmax probabilities (the P_e of the balance loss) and of the squared
+// log-sum-exp of the logits (the router z-loss) and, for the permute, per-tile
+// expert histograms and in-tile token-order ranks.
 //
 // Pages: "AI-Research-SKILLs MoE 训练实战…全指南" §3.1 (router linear, softmax,
 // top-k, divide the k scores by their sum) and §4.3 (balance loss from the mean
-// router probability); "[BEE-30064] 混合專家架構與服務", how routing works
+// router probability; router z-loss, the mean squared log-sum-exp of the logits); "[BEE-30064] 混合專家架構與服務", how routing works
 // (bias-free router, top-k, softmax over the k chosen); "第7章 Mixture of
 // Experts" tensor-shape trace (the router is a small (B n) x d x N matmul).
 //
@@ -38,8 +39,16 @@ struct RouterArgs {
   int32_t* local_rank;
   int32_t* tile_hist;
   float* p_part;
+  double* z_part;
   int T, d, E, k, ntile;
 };
+
+// squared log-sum-exp of a token's logits from its maximum m and
+// z = sum_e exp(l_e - m): (m + log z)^2 in float64
+__device__ __forceinline__ double lse_sq(double m, float z) {
+  const double lse = m + log(static_cast<double>(z));
+  return lse * lse;
+}
 
 // 16-lane argmax: larger value wins, equal values go to the lower index.
 __device__ __forceinline__ void argmax16(double& v, int& i) {
@@ -70,6 +79,7 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
   __shared__ int32_t s_idx[kRouterTile * MOE_MAX_TOPK];
   __shared__ unsigned long long s_mask[16 * NB];
   __shared__ float s_p[4][16 * NB];
+  __shared__ double s_z[kRouterTile];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -110,6 +120,7 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) pp[nb] += ev[nb] * inv;
     }
+    if (c == 0) s_z[r] = tok_ok ? lse_sq(m, z) : 0.0;
 
     // k rounds of a 16-lane argmax over the not-yet-chosen experts
     uint32_t taken = 0;
@@ -166,6 +177,12 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
     // per-expert layout [E][ntile]: the scan reads each expert's tiles contiguously
     a.p_part[static_cast<size_t>(e) * a.ntile + tile] = ((s_p[0][e] + s_p[1][e]) + s_p[2][e]) + s_p[3][e];
     a.tile_hist[static_cast<size_t>(e) * a.ntile + tile] = __popcll(s_mask[e]);
+  }
+  if (threadIdx.x == blockDim.x - 1) {
+    // z-loss partial of the tile, tokens in order
+    double zs = 0.0;
+    for (int r = 0; r < ntok; ++r) zs += s_z[r];
+    a.z_part[tile] = zs;
   }
   for (int i = threadIdx.x; i < ntok * k; i += blockDim.x) {
     const int r = i / k, j = i - r * k;
@@ -432,6 +449,7 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
   __shared__ int32_t s_idx[kRouterTile * MOE_MAX_TOPK];
   __shared__ unsigned long long s_mask[MOE_MAX_EXPERTS];
   __shared__ float s_p[kRouterTile][16 * NB + 1];
+  __shared__ double s_z[kRouterTile];
 
   const int c = threadIdx.x & 15;
   const int r = threadIdx.x >> 4;          // token within the tile
@@ -467,6 +485,7 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
   const float inv = tok_ok ? 1.f / z : 0.f;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) s_p[r][nb * 16 + c] = ev[nb] * inv;
+  if (c == 0) s_z[r] = tok_ok ? lse_sq(m, z) : 0.0;
 
   // k rounds of a 16-lane argmax over the not-yet-chosen experts
   uint32_t taken = 0;
@@ -512,6 +531,12 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
     for (int rr = 0; rr < ntok; ++rr) ps += s_p[rr][e];
     a.p_part[static_cast<size_t>(e) * a.ntile + tile] = ps;
     a.tile_hist[static_cast<size_t>(e) * a.ntile + tile] = __popcll(s_mask[e]);
+  }
+  if (threadIdx.x == blockDim.x - 1) {
+    // z-loss partial of the tile, tokens in order
+    double zs = 0.0;
+    for (int rr = 0; rr < ntok; ++rr) zs += s_z[rr];
+    a.z_part[tile] = zs;
   }
   for (int i = threadIdx.x; i < ntok * k; i += blockDim.x) {
     const int rr = i / k, j = i - rr * k;
@@ -562,6 +587,7 @@ hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const
   a.local_rank = ws.local_rank;
   a.tile_hist = ws.tile_hist;
   a.p_part = ws.p_part;
+  a.z_part = ws.z_part;
   a.T = p.T;
   a.d = p.d;
   a.E = p.E;

@@ -33,11 +33,27 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_launch_struct_layout():
-    # int32 T, d, h; enum dtype; then 8-byte pointers / size_t
+    # int32 T, d, h; enum dtype; then 8-byte pointers / size_t; z_loss; int32 activation, min_capacity
     L = moe.MoeLaunch
     assert L.T.offset == 0 and L.d.offset == 4 and L.h.offset == 8 and L.dtype.offset == 12
     assert L.b_g.offset == 16 and L.workspace_bytes.offset == 56 and L.stream.offset == 64
-    assert L.stage_events.offset == 72 and ctypes.sizeof(L) == 80
+    assert L.stage_events.offset == 72 and L.z_loss.offset == 80
+    assert L.activation.offset == 88 and L.min_capacity.offset == 92 and ctypes.sizeof(L) == 96
+
+
+def test_launch_struct_matches_header(tmp_path):
+    """The ctypes mirror has the offsets the C compiler gives moe_launch_t."""
+    fields = [f for f, _ in moe.MoeLaunch._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\nint main(void) {\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(moe_launch_t, {f}));\n' for f in fields) +
+                   '  printf("%zu\\n", sizeof(moe_launch_t));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", f"-I{os.path.join(ROOT, 'include')}", "-I/opt/rocm/include",
+                    str(src), "-o", str(exe)], check=True, capture_output=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [getattr(moe.MoeLaunch, f).offset for f in fields] + [ctypes.sizeof(moe.MoeLaunch)]
+    assert got == want
 
 
 def test_status_strings():
@@ -68,7 +84,8 @@ FAKE = 0x10000  # 16-byte aligned non-null address; never dereferenced (validati
 def call(**kw):
     args = dict(x=FAKE, W_g=FAKE, W1=FAKE, b1=FAKE, W2=FAKE, b2=FAKE, E=8, k=2, cf=0.0, S=0, out=FAKE,
                 idx=FAKE, w=FAKE, aux=FAKE)
-    lk = dict(T=64, d=32, h=64, dtype=moe.MOE_BF16, workspace=FAKE, workspace_bytes=0)
+    lk = dict(T=64, d=32, h=64, dtype=moe.MOE_BF16, workspace=FAKE, workspace_bytes=0, z_loss=None,
+              activation=moe.MOE_ACT_GELU, min_capacity=0)
     for key in list(kw):
         if key in lk:
             lk[key] = kw.pop(key)
@@ -76,15 +93,24 @@ def call(**kw):
     L = moe.MoeLaunch()
     L.T, L.d, L.h, L.dtype = lk["T"], lk["d"], lk["h"], lk["dtype"]
     L.workspace = lk["workspace"]
+    L.z_loss, L.activation, L.min_capacity = lk["z_loss"], lk["activation"], lk["min_capacity"]
     need = moe.moe_workspace_bytes(L.T, L.d, L.h, args["E"], args["k"], args["S"], L.dtype)
     L.workspace_bytes = lk["workspace_bytes"] if lk["workspace_bytes"] else need
     return moe.moe_forward(args["x"], args["W_g"], args["W1"], args["b1"], args["W2"], args["b2"], args["E"],
                            args["k"], args["cf"], args["S"], args["out"], args["idx"], args["w"], args["aux"], L)
 
 
-@pytest.mark.parametrize("field", ["x", "W_g", "W1", "b1", "W2", "b2", "out", "idx", "w", "aux"])
+@pytest.mark.parametrize("field", ["x", "W_g", "W1", "W2", "out", "idx", "w", "aux"])
 def test_null_required_pointer(field):
     assert call(**{field: None}) == moe.MOE_ERR_ARG
+
+
+@pytest.mark.parametrize("field", ["b1", "b2"])
+def test_null_bias_is_accepted(field):
+    # a bias-free Linear: the NULL passes the pointer checks and the call
+    # fails only at the (deliberately too small) workspace, before any launch
+    assert call(**{field: None}, workspace_bytes=1024) == moe.MOE_ERR_WORKSPACE
+    assert call(b1=None, b2=None, workspace_bytes=1024) == moe.MOE_ERR_WORKSPACE
 
 
 def test_null_launch():
@@ -103,6 +129,11 @@ def test_null_launch():
     (dict(out=FAKE + 4), moe.MOE_ERR_UNSUPPORTED), (dict(idx=FAKE + 2), moe.MOE_ERR_UNSUPPORTED),
     (dict(workspace=None), moe.MOE_ERR_WORKSPACE), (dict(workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
     (dict(workspace=FAKE + 16), moe.MOE_ERR_WORKSPACE), (dict(T=1 << 30, k=2, d=8, h=8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(activation=2), moe.MOE_ERR_UNSUPPORTED), (dict(activation=-1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(min_capacity=-1), moe.MOE_ERR_ARG), (dict(z_loss=FAKE + 2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(b1=FAKE + 8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(min_capacity=4, cf=1.0, workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
+    (dict(activation=moe.MOE_ACT_SILU, workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
 ])
 def test_rejected_on_host(kw, code):
     assert call(**kw) == code

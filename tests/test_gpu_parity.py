@@ -4,7 +4,9 @@ Reduced shapes (the oracle computes every output) span several tiles of
 every kernel and end in ragged tails; the five workloads run at full size
 with the oracle computing a sample of output rows; edge cases cover k = E,
 k = 1, E not a multiple of 16, a single token, empty experts, every token to
-one expert, capacity 1, several shared experts, d = 32, float32 and bf16.
+one expert, capacity 1, several shared experts, d = 32, float32 and bf16;
+the Mixtral expert form (SiLU, bias-free) on every GEMM kernel and a capacity
+floor (min_capacity) that binds.  Every case also compares the router z-loss.
 """
 import sys
 
@@ -66,6 +68,22 @@ REDUCED = {
     "f32_shared_capacity": ("switch", dict(T=500, d=64, h=128, E=8, k=2, S=1, cf=0.5)),
     "E256_top8": ("deepseek", dict(T=128, d=256, h=256, E=256, k=8, S=0)),
     "T_not_tile_multiple": ("glam", dict(T=67, d=256, h=256, E=8, k=2, cf=1.0)),
+    # Mixtral expert form: bias-free Linear -> SiLU -> bias-free Linear
+    "silu_nobias_bm256": ("mixtral", dict(T=2100, d=256, h=512, E=4, activation="silu", expert_bias=False)),
+    "silu_nobias_T600": ("mixtral", dict(T=600, d=512, h=1024, activation="silu", expert_bias=False)),
+    "silu_nobias_tail_split": ("mixtral", dict(T=512, d=2048, h=512, E=4, k=2, activation="silu",
+                                               expert_bias=False)),
+    "silu_bias_shared_tiles160": ("deepseek", dict(T=512, d=256, h=512, E=32, k=8, S=1, activation="silu")),
+    "silu_nobias_f32_simt": ("switch", dict(T=300, d=64, h=128, E=8, k=2, cf=0.5, activation="silu",
+                                            expert_bias=False)),
+    "gelu_nobias_bf16": ("glam", dict(T=700, d=256, h=512, E=16, expert_bias=False)),
+    "gelu_nobias_f32": ("tiny", dict(T=130, d=32, h=64, E=4, k=2, expert_bias=False)),
+    # capacity floor: ceil(0.1 * 1000 / 16) = 7 is raised to 40, which still drops
+    "min_capacity_binds_bf16": ("glam", dict(T=1000, d=256, h=512, E=16, cf=0.1, min_capacity=40)),
+    # ceil(0.25 * 500 / 8) = 16 raised to 30; f32 SIMT path, k = 1
+    "min_capacity_binds_f32": ("switch", dict(T=500, d=64, h=128, E=8, k=1, cf=0.25, min_capacity=30)),
+    # a floor above T: nothing is dropped
+    "min_capacity_above_T": ("glam", dict(T=300, d=256, h=256, E=8, k=2, cf=0.2, min_capacity=400)),
 }
 
 
@@ -74,7 +92,8 @@ def test_reduced_full_oracle(case):
     base, kw = REDUCED[case]
     inp = _case(base, **kw)
     c = inp.cfg
-    _say(f"[parity] {case}: T={c.T} d={c.d} h={c.h} E={c.E} k={c.k} S={c.S} cf={c.cf} {c.dtype}")
+    _say(f"[parity] {case}: T={c.T} d={c.d} h={c.h} E={c.E} k={c.k} S={c.S} cf={c.cf} "
+         f"min_cap={c.min_capacity} {c.activation} bias={c.expert_bias} {c.dtype}")
     stacked = inp.stacked()
     gpu = run_gpu(inp, stacked=stacked)
     rep = compare(inp, gpu, stacked=stacked)
@@ -111,20 +130,27 @@ def test_deterministic_bitwise():
     b = run_gpu(inp, stacked=stacked)
     for key in ("out", "idx", "w", "counts", "kept", "slot_pos"):
         assert np.array_equal(a[key], b[key]), key
-    assert a["aux"] == b["aux"]
+    assert a["aux"] == b["aux"] and a["z"] == b["z"]
 
 
 FULL_ROWS = {"tiny": None, "switch": None, "mixtral": 32, "glam": 32, "deepseek": 16}
 
 
-@pytest.mark.parametrize("name", ["tiny", "switch", "mixtral", "glam", "deepseek"])
+# the five workloads, plus the Mixtral-shaped layer with the Mixtral expert form
+FULL = {"tiny": {}, "switch": {}, "mixtral": {}, "glam": {}, "deepseek": {},
+        "mixtral_silu_nobias": dict(activation="silu", expert_bias=False)}
+
+
+@pytest.mark.parametrize("name", list(FULL))
 def test_full_size_workloads(name):
-    inp = make_inputs(name, seed=0)
+    base = name.split("_")[0]
+    inp = make_inputs(base, seed=0, **FULL[name])
     c = inp.cfg
-    _say(f"[parity-full] {name}: T={c.T} d={c.d} h={c.h} E={c.E} k={c.k} S={c.S} cf={c.cf} {c.dtype}")
+    _say(f"[parity-full] {name}: T={c.T} d={c.d} h={c.h} E={c.E} k={c.k} S={c.S} cf={c.cf} "
+         f"{c.activation} bias={c.expert_bias} {c.dtype}")
     stacked = inp.stacked()
     gpu = run_gpu(inp, stacked=stacked)
-    nrows = FULL_ROWS[name]
+    nrows = FULL_ROWS[base]
     rows = None
     if nrows is not None:
         rng = np.random.default_rng(1234)

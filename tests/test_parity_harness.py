@@ -1,7 +1,7 @@
 """The parity comparison itself, on the CPU: results built from the oracle pass,
 and planted discrepancies (a wrong count, a shifted slot, a wrong expert, an
-output off by more than the tolerance, a near-tie resolved the other way)
-are judged as the rules say."""
+output, aux or z-loss off by more than the tolerance, a near-tie resolved the
+other way) are judged as the rules say."""
 import numpy as np
 import pytest
 
@@ -12,7 +12,7 @@ from tests.parity import compare, oracle_for
 def fake_gpu(r, dtype):
     out = r.out.astype(np.float32).astype(np.float64)
     return dict(out=out, idx=r.idx.copy(), w=r.w.astype(np.float32).astype(np.float64), aux=float(np.float32(r.aux)),
-                counts=r.counts.copy(), kept=r.kept.copy(), slot_pos=r.slot_pos.copy())
+                z=float(np.float32(r.z)), counts=r.counts.copy(), kept=r.kept.copy(), slot_pos=r.slot_pos.copy())
 
 
 @pytest.fixture(scope="module")
@@ -28,7 +28,7 @@ def test_oracle_results_pass(case):
     assert rep["dropped"] > 0 and not rep["rerun"]
 
 
-@pytest.mark.parametrize("what", ["counts", "kept", "slot", "expert", "out", "aux", "weight", "order"])
+@pytest.mark.parametrize("what", ["counts", "kept", "slot", "expert", "out", "aux", "z", "weight", "order"])
 def test_discrepancy_fails(case, what):
     inp, stacked, r = case
     g = fake_gpu(r, "f32")
@@ -46,6 +46,8 @@ def test_discrepancy_fails(case, what):
         g["out"][7, 3] += 2e-5 * np.abs(r.out).max()
     elif what == "aux":
         g["aux"] += 2e-5
+    elif what == "z":
+        g["z"] += 2e-5 * max(1.0, r.z)
     elif what == "weight":
         g["w"][4, 0] += 2e-5
     elif what == "order":

@@ -125,3 +125,54 @@ def brute_layer(x: List[List[float]], W_g: List[List[float]], experts, k: int,
 
     return dict(out=out, idx=idx, w=w, counts=counts, kept=kept, dropped=dropped,
                 slot_kept=slot_kept, aux=aux, z=z, logits=logits, probs=probs)
+
+
+def brute_expert_choice_layer(x: List[List[float]], W_g: List[List[float]], experts, C: int,
+                              n_shared: int = 0, b_g: Optional[Sequence[float]] = None,
+                              activation: str = "gelu"):
+    """Expert-choice routing ([guide] §4.2; "第7章 Mixture of Experts" §7.2),
+    scalar loops: every expert's column of logits goes through the subset
+    enumeration of brute_topk (the C-subset of tokens with the largest logit
+    sum, the lexicographically smallest among equals); a chosen token is
+    weighted by its softmax probability of that expert.
+
+    Returns dict(out, tok [E][C] ascending, w [E][C], per_token, aux, z)."""
+    T = len(x)
+    E = len(W_g)
+    d = len(x[0])
+    logits = [[_dot(x[t], W_g[e]) + (b_g[e] if b_g is not None else 0.0) for e in range(E)] for t in range(T)]
+    probs = []
+    for t in range(T):
+        m = max(logits[t])
+        ex = [math.exp(v - m) for v in logits[t]]
+        z = math.fsum(ex)
+        probs.append([v / z for v in ex])
+
+    tok = [sorted(brute_topk([logits[t][e] for t in range(T)], C)) for e in range(E)]
+    w = [[probs[t][e] for t in tok[e]] for e in range(E)]
+    per_token = [sum(1 for e in range(E) if t in tok[e]) for t in range(T)]
+
+    def ffn(e, xt):
+        W1, b1, W2, b2 = experts[e]
+        g = []
+        for i in range(len(W1)):
+            u = _dot(W1[i], xt) + (b1[i] if b1 is not None else 0.0)
+            g.append(u / (1.0 + math.exp(-u)) if activation == "silu" else 0.5 * u * (1.0 + math.erf(u / math.sqrt(2.0))))
+        return [_dot(W2[c], g) + (b2[c] if b2 is not None else 0.0) for c in range(d)]
+
+    out = [[0.0] * d for _ in range(T)]
+    for e in range(E):
+        for c, t in enumerate(tok[e]):
+            y = ffn(e, x[t])
+            for i in range(d):
+                out[t][i] += w[e][c] * y[i]
+    for s in range(n_shared):
+        for t in range(T):
+            y = ffn(E + s, x[t])
+            for i in range(d):
+                out[t][i] += y[i]
+
+    # every expert receives C of the E*C assignments: f_e = 1/E
+    aux = E * math.fsum((1.0 / E) * (math.fsum(probs[t][e] for t in range(T)) / T) for e in range(E))
+    z = math.fsum(math.log(math.fsum(math.exp(v) for v in logits[t])) ** 2 for t in range(T)) / T
+    return dict(out=out, tok=tok, w=w, per_token=per_token, aux=aux, z=z)

@@ -44,7 +44,12 @@ with its reason in the design notes of this repository):
     that token's logits (router bias included), unscaled;
   * SiLU is u * sigmoid(u); a missing expert bias (None) is a bias-free
     Linear; min_capacity raises the capacity to at least that many tokens and
-    only applies when there is a capacity limit (cf > 0).
+    only applies when there is a capacity limit (cf > 0);
+  * expert-choice routing: each expert takes the C tokens with the largest
+    router logits (ties to the lower token index), listed in ascending token
+    order; a chosen token is weighted by its softmax probability of that
+    expert (the gate G(x) of the layer), not renormalised; a token may be
+    taken by several experts or by none.
 """
 from __future__ import annotations
 
@@ -333,6 +338,116 @@ def moe_forward_ref(x, W_g, get_expert: Callable[[int], tuple], E: int, k: int,
                   order_flag=sel.order_flag, counts=counts, kept=kept, rank=rank,
                   slot_kept=slot_kept, slot_pos=slot_pos, offsets=offsets, cap=cap,
                   aux=aux, z=z, f=f, P=P, rows=rows_arr, out=out)
+
+
+# --------------------------------------------------------- expert choice --
+@dataclass
+class ExpertChoice:
+    tok: np.ndarray          # [E, C] int64: expert e's tokens, ascending token order
+    flag: np.ndarray         # [E] bool: C-th vs (C+1)-th largest logit of the column < TIE_EPS apart
+
+
+def select_expert_choice(l: np.ndarray, C: int, eps: float = TIE_EPS) -> ExpertChoice:
+    """Expert choice: expert e takes the C tokens t with the largest l[t, e],
+    ties to the lower token index ([guide] §4.2, the router scores transposed
+    to (experts, tokens) and a top-k over tokens with k = the per-expert
+    capacity; [ch7] §7.2, each expert picks its top-C tokens).  The chosen
+    set is listed in ascending token order."""
+    T, E = l.shape
+    order = np.argsort(-l, axis=0, kind="stable")        # per expert: descending, ties -> lower token
+    tok = np.sort(order[:C, :], axis=0).T
+    s = np.take_along_axis(l, order, axis=0)
+    flag = np.zeros(E, dtype=bool) if C >= T else (s[C - 1, :] - s[C, :]) < eps
+    return ExpertChoice(tok=tok.astype(np.int64), flag=flag)
+
+
+def is_valid_expert_choice(l_col: np.ndarray, chosen: Sequence[int], eps: float = TIE_EPS) -> bool:
+    """True when ``chosen`` are distinct tokens and none of them has a logit
+    more than eps below an unchosen token's (a top-C set up to near-ties)."""
+    chosen = list(map(int, chosen))
+    if len(set(chosen)) != len(chosen):
+        return False
+    rest = np.delete(l_col, chosen)
+    return rest.size == 0 or float(l_col[chosen].min()) >= float(rest.max()) - eps
+
+
+def expert_choice_capacity(capacity_factor: float, T: int, E: int, min_capacity: int = 0) -> int:
+    """C = min(T, max(ceil(cf T / E), min_capacity)) for cf > 0: the capacity
+    formula of [guide] §8.2 (with the floor of its §5.1), an expert cannot
+    take more than the T tokens there are."""
+    cap = capacity_of(capacity_factor, T, E, min_capacity)
+    if cap is None:
+        raise ValueError("expert choice needs a capacity factor > 0")
+    return min(T, cap)
+
+
+@dataclass
+class ExpertChoiceRef:
+    logits: np.ndarray       # [T,E]
+    probs: np.ndarray        # [T,E]
+    tok: np.ndarray          # [E,C]
+    w: np.ndarray            # [E,C] probs[tok[e,c], e]
+    flag: np.ndarray         # [E]
+    per_token: np.ndarray    # [T] how many experts took each token
+    aux: float
+    z: float
+    P: np.ndarray
+    rows: np.ndarray
+    out: np.ndarray          # [len(rows), d]
+
+
+def moe_forward_expert_choice_ref(x, W_g, get_expert: Callable[[int], tuple], E: int, C: int,
+                                  n_shared: int = 0, b_g=None, kind: str = "f32",
+                                  rows: Optional[Sequence[int]] = None,
+                                  override_tok: Optional[np.ndarray] = None,
+                                  activation: str = "gelu") -> ExpertChoiceRef:
+    """The layer with expert-choice routing, in float64.
+
+    Inputs as moe_forward_ref; C (1..T) tokens per expert.  Steps: 1 logits
+    2 softmax over experts 3 each expert's top-C tokens 4 weights
+    w[e,c] = p[tok[e,c], e] 5 balance loss and z-loss 6 out[t] = sum over the
+    experts that took t of w FFN_e(x_t) 7 shared experts, weight 1.
+    ``override_tok`` replaces the selection ([E, C], used after a near-tie was
+    resolved the other way by rounding).
+
+    The balance loss keeps the layer's definition E sum_e f_e P_e with f_e the
+    fraction of all assignments that expert e receives: every expert receives
+    C of the E C, so f is uniform and the loss is sum_e P_e = 1."""
+    xf = widen(x, kind)
+    T, d = xf.shape
+    if not 1 <= C <= T:
+        raise ValueError("C must be in 1..T")
+    l = router_logits(xf, widen(W_g, kind), b_g)
+    p = softmax(l)
+    sel = select_expert_choice(l, C)
+    tok = sel.tok if override_tok is None else np.asarray(override_tok, dtype=np.int64).reshape(E, C)
+    w = p[tok, np.arange(E)[:, None]]
+    counts = np.full(E, C, dtype=np.int64)
+    f = counts / float(counts.sum())
+    P = np.mean(p, axis=0)
+    aux = float(E * np.sum(f * P))
+    z_ec = router_z_loss(l)
+    per_token = np.bincount(tok.ravel(), minlength=T).astype(np.int64)
+
+    rows_arr = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    want = np.zeros(T, dtype=bool)
+    want[rows_arr] = True
+    row_of = np.full(T, -1, dtype=np.int64)
+    row_of[rows_arr] = np.arange(rows_arr.size)
+    out = np.zeros((rows_arr.size, d), dtype=np.float64)
+    for e in range(E):
+        sel_c = np.nonzero(want[tok[e]])[0]
+        if sel_c.size == 0:
+            continue
+        toks = tok[e, sel_c]
+        W1, b1, W2, b2 = (None if a is None else widen(a, kind) for a in get_expert(e))
+        # the tokens of one expert are distinct, so this scatter has no collisions
+        out[row_of[toks]] += w[e, sel_c][:, None] * expert_ffn(xf[toks], W1, b1, W2, b2, activation)
+    for s_ in range(n_shared):
+        W1, b1, W2, b2 = (None if a is None else widen(a, kind) for a in get_expert(E + s_))
+        out = out + expert_ffn(xf[rows_arr], W1, b1, W2, b2, activation)
+    return ExpertChoiceRef(logits=l, probs=p, tok=tok, w=w, flag=sel.flag, per_token=per_token, aux=aux,
+                           z=z_ec, P=P, rows=rows_arr, out=out)
 
 
 def moe_forward_ref_from_inputs(inp, rows=None, override_idx=None) -> MoERef:

@@ -73,6 +73,19 @@ MUTANTS = [
      "return min(int(math.ceil(float(capacity_factor) * float(T) / float(E))), int(min_capacity) or 2 ** 31)"),
     ("min_capacity_applies_without_limit", "    if capacity_factor is None or capacity_factor <= 0:\n        return None\n    return max(",
      "    if capacity_factor is None or capacity_factor <= 0:\n        return int(min_capacity) or None\n    return max("),
+    ("ec_takes_smallest", 'order = np.argsort(-l, axis=0, kind="stable")', 'order = np.argsort(l, axis=0, kind="stable")'),
+    ("ec_ties_to_higher_token", 'order = np.argsort(-l, axis=0, kind="stable")',
+     'order = np.argsort(-l[::-1], axis=0, kind="stable"); order = l.shape[0] - 1 - order'),
+    ("ec_one_token_short", "tok = np.sort(order[:C, :], axis=0).T", "tok = np.sort(order[:max(C - 1, 1), :], axis=0).T"),
+    ("ec_flag_off_by_one", "(s[C - 1, :] - s[C, :]) < eps", "(s[C - 2, :] - s[C - 1, :]) < eps"),
+    ("ec_weight_softmax_over_tokens", "w = p[tok, np.arange(E)[:, None]]",
+     "w = (np.exp(l - l.max(0)) / np.exp(l - l.max(0)).sum(0))[tok, np.arange(E)[:, None]]"),
+    ("ec_weight_wrong_expert", "w = p[tok, np.arange(E)[:, None]]", "w = p[tok, (np.arange(E)[:, None] + 1) % E]"),
+    ("ec_weights_renormalised", "        out[row_of[toks]] += w[e, sel_c][:, None] * expert_ffn(",
+     "        out[row_of[toks]] += (w[e, sel_c] / np.maximum(np.bincount(tok.ravel(), weights=w.ravel(), minlength=T)[toks], 1e-300))[:, None] * expert_ffn("),
+    ("ec_capacity_not_clipped", "    return min(T, cap)", "    return cap"),
+    ("ec_shared_weighted_half", "        out = out + expert_ffn(xf[rows_arr], W1, b1, W2, b2, activation)",
+     "        out = out + 0.5 * expert_ffn(xf[rows_arr], W1, b1, W2, b2, activation)"),
 ]
 
 

@@ -478,12 +478,93 @@ def check_golden_silu_min_capacity():
     assert abs(r.z - math.log(math.e + 1 / math.e) ** 2) < 1e-15
 
 
+def run_ec(x, W_g, experts, E, C, S=0, b_g=None, **kw):
+    return ref.moe_forward_expert_choice_ref(x, W_g, lambda e: experts[e], E, C, S, b_g, kind="f64", **kw)
+
+
+def check_ec_against_brute():
+    """Expert choice == brute force (per-expert subset enumeration, scalar loops)."""
+    rng = np.random.default_rng(16)
+    # (T, d, h, E, C, S, activation)
+    cases = [(6, 3, 3, 3, 2, 0, "gelu"), (7, 2, 4, 4, 1, 0, "gelu"), (8, 3, 2, 2, 4, 1, "silu"),
+             (5, 4, 3, 3, 5, 0, "gelu"), (9, 2, 3, 4, 3, 1, "gelu"), (6, 3, 2, 5, 3, 0, "silu")]
+    for (T, d, h, E, C, S, act) in cases:
+        for trial in range(2):
+            x, W_g, ex = rand_case(rng, T, d, h, E, 1, S)
+            b_g = rng.standard_normal(E) if trial == 1 else None
+            r = run_ec(x, W_g, ex, E, C, S, b_g, activation=act)
+            assert not r.flag.any()
+            vec = lambda b: None if b is None else list(map(float, b))
+            exl = [(to_lists(W1), vec(b1), to_lists(W2), vec(b2)) for (W1, b1, W2, b2) in ex]
+            b = brute.brute_expert_choice_layer(to_lists(x), to_lists(W_g), exl, C, S, vec(b_g), act)
+            assert r.tok.tolist() == b["tok"] and r.per_token.tolist() == b["per_token"]
+            assert np.allclose(r.w, np.array(b["w"]), rtol=0, atol=1e-14)
+            assert abs(r.aux - b["aux"]) < 1e-13 and abs(r.z - b["z"]) < 1e-12
+            assert np.allclose(r.out, np.array(b["out"]), rtol=0, atol=1e-11)
+
+
+def check_ec_dense_limit_and_balance():
+    """C = T: every expert takes every token, so the layer is the dense softmax
+    mixture sum_e p_e FFN_e(x) ([ch7] §7.1), computed here through torch; any
+    C: each expert takes exactly C distinct tokens (perfect balance, [ch7]
+    §7.2), the taken logits dominate the untaken ones, and the balance loss is 1."""
+    rng = np.random.default_rng(17)
+    for (T, d, h, E) in [(20, 6, 10, 4), (9, 3, 5, 7)]:
+        x, W_g, ex = rand_case(rng, T, d, h, E, 1)
+        r = run_ec(x, W_g, ex, E, T)
+        l = x @ W_g.T
+        p = np.exp(l - l.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        dense = sum(p[:, e:e + 1] * ffn_torch(x, *ex[e]) for e in range(E))
+        assert np.allclose(r.out, dense, rtol=0, atol=1e-12)
+        assert np.all(r.per_token == E)
+    for (T, E, C) in [(50, 4, 7), (33, 8, 1), (40, 3, 20)]:
+        x, W_g, ex = rand_case(rng, T, 5, 2, E, 1)
+        r = run_ec(x, W_g, ex, E, C)
+        assert r.tok.shape == (E, C) and r.per_token.sum() == E * C
+        for e in range(E):
+            assert len(set(r.tok[e].tolist())) == C and np.all(np.diff(r.tok[e]) > 0)
+            un = np.setdiff1d(np.arange(T), r.tok[e])
+            assert un.size == 0 or r.logits[r.tok[e], e].min() >= r.logits[un, e].max()
+            assert np.allclose(r.w[e], r.probs[r.tok[e], e], rtol=0, atol=0)
+        assert abs(r.aux - 1.0) < 1e-12
+    # ties go to the lower token index; near-ties are flagged
+    l = np.array([[1.0, 0.0], [2.0, 0.0], [2.0, 5.0], [0.5, 5.0 - 5e-7]])
+    sel = ref.select_expert_choice(l, 2)
+    assert sel.tok.tolist() == [[1, 2], [2, 3]] and sel.flag.tolist() == [False, False]
+    sel = ref.select_expert_choice(l, 1)
+    assert sel.tok.tolist() == [[1], [2]] and sel.flag.tolist() == [True, True]
+    assert ref.is_valid_expert_choice(l[:, 0], [2]) and not ref.is_valid_expert_choice(l[:, 0], [0])
+    # capacity: ceil(cf T / E), floored by min_capacity, at most T
+    assert ref.expert_choice_capacity(2.0, 16384, 64) == 512
+    assert ref.expert_choice_capacity(1.0, 10, 4, 4) == 4 and ref.expert_choice_capacity(8.0, 10, 2) == 10
+
+
+def check_golden_expert_choice():
+    """Hand-derived fixture (tests/golden/expert_choice_four_tokens.json): [guide]
+    §4.2 / [ch7] §7.2 expert choice with a token that no expert takes."""
+    g = json.load(open(os.path.join(GOLDEN, "expert_choice_four_tokens.json")))
+    ex = [tuple(np.array(e[n], dtype=np.float64) for n in ("W1", "b1", "W2", "b2")) for e in g["experts"]]
+    Phi = lambda u: 0.5 * (1.0 + math.erf(u / math.sqrt(2.0)))
+    gelu = lambda u: u * Phi(u)
+    sig = lambda u: 1.0 / (1.0 + math.exp(-u))
+    x, W_g = np.array(g["x"]), np.array(g["W_g"])
+    r = run_ec(x, W_g, ex, 2, 1)
+    assert r.tok.tolist() == g["expected"]["C1"]["tok"] and r.per_token.tolist() == g["expected"]["C1"]["per_token"]
+    assert np.allclose(r.out[:, 0], [0.0, sig(4) * gelu(2), sig(2) * gelu(-1), 0.0], rtol=0, atol=1e-15)
+    r = run_ec(x, W_g, ex, 2, 2)
+    assert r.tok.tolist() == g["expected"]["C2"]["tok"] and r.per_token.tolist() == g["expected"]["C2"]["per_token"]
+    want = [sig(2) * gelu(1), sig(4) * gelu(2), sig(2) * gelu(-1), sig(-1) * gelu(0.5)]
+    assert np.allclose(r.out[:, 0], want, rtol=0, atol=1e-15)
+
+
 ALL_CHECKS = [check_weights_sum_to_one, check_against_brute, check_topk_vs_torch, check_tie_rule,
               check_dense_limit, check_aux_closed_forms, check_capacity, check_dropped_contribute_nothing,
               check_ffn_library, check_combine_symmetries, check_shared, check_golden_fixtures,
               check_rows_and_override, check_widen_bf16, check_z_loss_closed_forms,
               check_silu_and_bias_free, check_min_capacity, check_mixtral_expert_against_brute,
-              check_golden_silu_min_capacity]
+              check_golden_silu_min_capacity, check_ec_against_brute, check_ec_dense_limit_and_balance,
+              check_golden_expert_choice]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=[c.__name__ for c in ALL_CHECKS])

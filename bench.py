@@ -3,6 +3,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload mixtral] [--no-cpu-baseline]
                     [--activation gelu|silu] [--no-expert-bias] [--min-capacity N]
+                    [--routing top-k|expert-choice]
 
 A step is one full layer forward (router, scan, scatter, expert phase 1,
 expert phase 2, combine) over one batch of seeded synthetic tokens already
@@ -52,6 +53,8 @@ def parse():
                     help="expert activation (silu with --no-expert-bias: the Mixtral expert form)")
     ap.add_argument("--no-expert-bias", action="store_true", help="bias-free expert Linears (NULL b1, b2)")
     ap.add_argument("--min-capacity", type=int, default=0, help="capacity floor (with a capacity factor)")
+    ap.add_argument("--routing", default="top-k", choices=["top-k", "expert-choice"],
+                    help="expert-choice: each expert takes C = ceil(k T / E) tokens (the rows top-k routing makes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -82,7 +85,7 @@ def measured_traffic(workload: str, phase: str):
     return entry[phase]["fetch_bytes"] + entry[phase]["write_bytes"]
 
 
-def cpu_baseline(inp, stacked, ntok: int):
+def cpu_baseline(inp, stacked, ntok: int, ec: bool = False):
     from threadpoolctl import threadpool_info
 
     import oracle
@@ -92,8 +95,12 @@ def cpu_baseline(inp, stacked, ntok: int):
     x = inp.x[:ntok]
     get = lambda e: (W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e])
     t0 = time.perf_counter()
-    oracle.moe_forward_ref(x, inp.W_g, get, c.E, c.k, float(np.float32(c.cf)), c.S, inp.b_g, kind=c.dtype,
-                           activation=c.activation, min_capacity=c.min_capacity)
+    if ec:
+        oracle.moe_forward_expert_choice_ref(x, inp.W_g, get, c.E, min(ntok, -(-c.k * ntok // c.E)), c.S, inp.b_g,
+                                             kind=c.dtype, activation=c.activation)
+    else:
+        oracle.moe_forward_ref(x, inp.W_g, get, c.E, c.k, float(np.float32(c.cf)), c.S, inp.b_g, kind=c.dtype,
+                               activation=c.activation, min_capacity=c.min_capacity)
     dt = time.perf_counter() - t0
     threads = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
     cores = max(threads) if threads else 1
@@ -134,7 +141,14 @@ def main():
     b_g = None if inp.b_g is None else torch.from_numpy(inp.b_g).to(dev)
     dt_code = moe.MOE_BF16 if c.dtype == "bf16" else moe.MOE_F32
     T, d, h, E, k, S = c.T, c.d, c.h, c.E, c.k, c.S
-    nbytes = moe.moe_workspace_bytes(T, d, h, E, k, S, dt_code)
+    ec = args.routing == "expert-choice"
+    C = min(T, -(-k * T // E))
+    if ec:
+        nbytes = moe.moe_workspace_bytes_expert_choice(T, d, h, E, C, S, dt_code)
+        ec_token = torch.empty((E, C), dtype=torch.int32, device=dev)
+        ec_w = torch.empty((E, C), dtype=torch.float32, device=dev)
+    else:
+        nbytes = moe.moe_workspace_bytes(T, d, h, E, k, S, dt_code)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     out = torch.empty((T, d), dtype=x.dtype, device=dev)
     topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -167,8 +181,12 @@ def main():
 
     def step(ev=None):
         launch.stage_events = None if ev is None else ctypes.cast(ev, ctypes.c_void_p)
-        st = moe.moe_forward(*ptrs, E, k, float(c.cf), S, out.data_ptr(), topk_idx.data_ptr(), topk_w.data_ptr(),
-                             aux.data_ptr(), launch)
+        if ec:
+            st = moe.moe_forward_expert_choice(*ptrs, E, C, S, out.data_ptr(), ec_token.data_ptr(),
+                                               ec_w.data_ptr(), aux.data_ptr(), launch)
+        else:
+            st = moe.moe_forward(*ptrs, E, k, float(c.cf), S, out.data_ptr(), topk_idx.data_ptr(),
+                                 topk_w.data_ptr(), aux.data_ptr(), launch)
         if st != moe.MOE_OK:
             raise RuntimeError(moe.moe_status_string(st))
 
@@ -187,7 +205,7 @@ def main():
 
     stage_ms = np.array([[events[i][s].elapsed_time(events[i][s + 1]) for s in range(nst - 1)]
                          for i in range(args.steps)]).mean(axis=0)
-    stages = dict(zip(moe.STAGES, stage_ms.tolist()))
+    stages = dict(zip(moe.STAGES, stage_ms.tolist()))   # under expert choice "scatter" is the selection
 
     kept_np = kept.cpu().numpy().astype(np.int64)
     a_kept = int(kept_np.sum())
@@ -200,6 +218,14 @@ def main():
     # slot and, for kept ones, the row's token (no token row is copied)
     bytes_scatter = 12 * T * k + 4 * a_kept
     bytes_combine = rows * d * s + T * d * s + 8 * T * k
+    if ec:
+        # router also writes the expert-major float64 logits and each token's max and sum;
+        # the selection reads the logits once and writes the [E, T] rank table and, per
+        # taken pair, token, row token and weight (reading that token's max and sum);
+        # the combine reads the rank table and the weights instead of slot positions
+        bytes_router = T * d * s + E * d * s + 8 * E * T + 12 * T
+        bytes_scatter = 8 * E * T + 4 * E * T + 24 * E * C
+        bytes_combine = rows * d * s + T * d * s + 4 * E * T + 4 * E * C
     # minimal traffic: active expert weights once, x once (phase 1 gathers its
     # rows), H written once / read once, Y written once
     bytes_gemm1 = active * h * d * s + T * d * s + rows * h * s
@@ -214,7 +240,8 @@ def main():
     per_stage = {
         "router": {"ms": stages["router"], "GB/s": gbs(bytes_router, stages["router"]), "bytes": bytes_router},
         "scan": {"ms": stages["scan"]},
-        "scatter": {"ms": stages["scatter"], "GB/s": gbs(bytes_scatter, stages["scatter"]), "bytes": bytes_scatter},
+        ("select" if ec else "scatter"): {"ms": stages["scatter"], "GB/s": gbs(bytes_scatter, stages["scatter"]),
+                                          "bytes": bytes_scatter},
         "expert_phase1": {"ms": stages["expert_phase1"], "TFLOP/s": tfs(gemm_flops, stages["expert_phase1"]),
                           "GB/s": gbs(bytes_gemm1, stages["expert_phase1"]), "flops": gemm_flops},
         "expert_phase2": {"ms": stages["expert_phase2"], "TFLOP/s": tfs(gemm_flops, stages["expert_phase2"]),
@@ -245,10 +272,10 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device copies done")
 
-    variant = ""
+    variant = f", expert-choice routing C={C} tokens per expert" if ec else ""
     if c.activation != "gelu" or not c.expert_bias or c.min_capacity:
-        variant = (f", {c.activation} experts" + ("" if c.expert_bias else " without bias") +
-                   (f", min_capacity={c.min_capacity}" if c.min_capacity else ""))
+        variant += (f", {c.activation} experts" + ("" if c.expert_bias else " without bias") +
+                    (f", min_capacity={c.min_capacity}" if c.min_capacity else ""))
     result = {
         "metric": METRIC,
         "value": T * args.steps / wall,
@@ -266,7 +293,10 @@ def main():
                                f"capacity_factor={c.cf} {c.dtype}" + variant,
                    "T": T, "d": d, "h": h, "E": E, "k": k, "n_shared": S, "capacity_factor": c.cf,
                    "activation": c.activation, "expert_bias": c.expert_bias, "min_capacity": c.min_capacity,
-                   "kept_assignments": a_kept, "dropped_assignments": T * k - a_kept},
+                   "kept_assignments": a_kept, "routing": args.routing,
+                   **({"tokens_per_expert": C,
+                       "untaken_tokens": T - int(torch.unique(ec_token).numel())} if ec else
+                      {"dropped_assignments": T * k - a_kept})},
         "roofline": roof,
         "stages": per_stage,
         "layer_ms_events": float(stage_ms.sum()),
@@ -274,7 +304,7 @@ def main():
     if not args.no_cpu_baseline:
         ntok = args.cpu_tokens or CPU_SAMPLE_TOKENS[args.workload]
         log(f"cpu baseline: oracle on {ntok} tokens")
-        result["cpu_baseline"] = cpu_baseline(inp, stacked, ntok)
+        result["cpu_baseline"] = cpu_baseline(inp, stacked, ntok, ec)
     print(json.dumps(result), flush=True)
 
 

@@ -131,6 +131,45 @@ moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const v
                          int32_t* topk_idx, float* topk_w, float* aux_loss,
                          const moe_launch_t* launch);
 
+/* ---- Expert-choice routing ------------------------------------------------
+ * Pages: "AI-Research-SKILLs MoE 训练实战…全指南" §4.2 (the router scores are
+ * transposed to experts x tokens and each expert takes a top-k over tokens
+ * with k = its capacity: perfect balance); "第7章 Mixture of Experts（MoE）架构"
+ * §7.2 (each expert picks its top-C tokens; a token may be picked by several
+ * experts or by none) and §7.1 (the gate weighting an expert's output is the
+ * router's softmax).
+ *
+ *   l, p      as above (b_g included)
+ *   tok[e,:]  the C tokens t with the largest l[t,e], ties to the lower token
+ *             index, listed in ascending token order
+ *   w[e,c]    = p[tok[e,c], e]                                 not renormalised
+ *   out[t]    = sum_{(e,c): tok[e,c] = t} w[e,c] FFN_e(x[t])  + shared experts
+ *   aux       = E * sum_e f_e P_e with f_e = C / (E C): exactly sum_e P_e, i.e. 1
+ *   z         router z-loss as above
+ *
+ * Bytes of device workspace for moe_forward_expert_choice (0 if the shape is
+ * invalid): hidden and expert-output buffers of E*C + S*T rows, plus an
+ * expert-major float64 copy of the logits and an int32 [E, T] rank table. */
+size_t moe_workspace_bytes_expert_choice(int32_t T, int32_t d, int32_t h, int32_t E, int32_t C,
+                                         int32_t n_shared, moe_dtype_t dtype);
+
+/* The layer forward with expert-choice routing.
+ *   x, W_g, W1, b1, W2, b2, n_shared, out   as for moe_forward (b1, b2 may be NULL)
+ *   E        routed experts, 1..MOE_MAX_EXPERTS
+ *   C        tokens per expert, 1..T (e.g. ceil(capacity_factor * T / E), at most T)
+ *   ec_token [E, C] int32 out: expert e's tokens, ascending token order
+ *   ec_w     [E, C] float32 out: their weights p[t, e]
+ *   aux_loss [1] float32 out, or NULL
+ *   launch   as for moe_forward; expert_counts / expert_kept (if given) receive C for
+ *            every expert, z_loss and activation apply, slot_pos and min_capacity are
+ *            ignored
+ * Errors as for moe_forward; C < 1 or C > T is MOE_ERR_ARG, E*C + S*T or E*T
+ * above INT32_MAX is MOE_ERR_UNSUPPORTED (k and its limit do not apply). */
+moe_status_t moe_forward_expert_choice(const void* x, const void* W_g, const void* W1, const void* b1,
+                                       const void* W2, const void* b2, int32_t E, int32_t C,
+                                       int32_t n_shared, void* out, int32_t* ec_token, float* ec_w,
+                                       float* aux_loss, const moe_launch_t* launch);
+
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status_t s);
 

@@ -9,17 +9,20 @@ passes torch's current stream.  Nothing here computes any part of the layer.
 from __future__ import annotations
 
 import ctypes
+import math
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
 from ._lib import (EXPORTS, LIB_PATH, MOE_ACT_GELU, MOE_ACT_SILU, MOE_BF16, MOE_ERR_ARG, MOE_ERR_HIP,
                    MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_F32, MOE_MAX_EXPERTS, MOE_MAX_SHARED,
-                   MOE_MAX_TOPK, MOE_NUM_STAGE_EVENTS, MOE_OK, MoeLaunch, moe_forward, moe_status_string,
-                   moe_workspace_bytes)
+                   MOE_MAX_TOPK, MOE_NUM_STAGE_EVENTS, MOE_OK, MoeLaunch, moe_forward, moe_forward_expert_choice,
+                   moe_status_string, moe_workspace_bytes, moe_workspace_bytes_expert_choice)
 
 ACTIVATIONS = {"gelu": MOE_ACT_GELU, "silu": MOE_ACT_SILU}
 
 STAGES = ("router", "scan", "scatter", "expert_phase1", "expert_phase2", "combine")
+# under expert choice the third stage is the per-expert selection
+STAGES_EXPERT_CHOICE = ("router", "scan", "select", "expert_phase1", "expert_phase2", "combine")
 
 
 @dataclass
@@ -43,6 +46,51 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
 
 
+def _check_tensors(x, W_g, W1, b1, W2, b2, b_g, n_shared: int, activation: str) -> None:
+    """Shapes, dtypes and placement of the layer's inputs (b1, b2, b_g may be None)."""
+    import torch
+    dev = x.device
+    for t in (x, W_g, W1, b1, W2, b2):
+        if t is not None and (not t.is_cuda or t.device != dev or not t.is_contiguous() or t.dtype != x.dtype):
+            raise ValueError("x, W_g, W1, b1, W2, b2 must be contiguous tensors of one dtype on one GPU")
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}")
+    T, d = x.shape
+    E = W_g.shape[0]
+    h = W1.shape[1]
+    S = n_shared
+    if W_g.shape != (E, d) or W1.shape != (E + S, h, d) or W2.shape != (E + S, d, h) or \
+            (b1 is not None and b1.shape != (E + S, h)) or (b2 is not None and b2.shape != (E + S, d)):
+        raise ValueError("inconsistent shapes")
+    if b_g is not None and (b_g.dtype != torch.float32 or b_g.shape != (E,) or b_g.device != dev):
+        raise ValueError("b_g must be float32 [E] on the same GPU")
+
+
+def _launch(x, T, d, h, dt, b_g, workspace, zl, activation, min_capacity, stage_events):
+    """A moe_launch_t on torch's current stream; returns it and the event-handle
+    array that must stay alive until the call returns."""
+    import torch
+    launch = MoeLaunch()
+    launch.T, launch.d, launch.h, launch.dtype = T, d, h, dt
+    launch.b_g = b_g.data_ptr() if b_g is not None else None
+    launch.workspace = workspace.data_ptr()
+    launch.workspace_bytes = workspace.numel()
+    launch.stream = torch.cuda.current_stream(x.device).cuda_stream
+    launch.z_loss = zl.data_ptr()
+    launch.activation = ACTIVATIONS[activation]
+    launch.min_capacity = int(min_capacity)
+    ev_arr = None
+    if stage_events is not None:
+        if len(stage_events) != MOE_NUM_STAGE_EVENTS:
+            raise ValueError(f"stage_events needs {MOE_NUM_STAGE_EVENTS} events")
+        handles = [int(e.cuda_event) for e in stage_events]
+        if not all(handles):
+            raise ValueError("record each stage event once before passing it (creates its handle)")
+        ev_arr = (ctypes.c_void_p * MOE_NUM_STAGE_EVENTS)(*handles)
+        launch.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
+    return launch, ev_arr
+
+
 def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shared: int = 0, b_g=None,
             *, activation: str = "gelu", min_capacity: int = 0, stage_events: Optional[Sequence] = None,
             workspace=None) -> MoEOutput:
@@ -57,22 +105,12 @@ def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shar
     records at its stage boundaries.  Raises RuntimeError on a non-zero status.
     """
     import torch
-    tensors = [t for t in (x, W_g, W1, b1, W2, b2) if t is not None]
-    dev = x.device
-    for t in tensors:
-        if not t.is_cuda or t.device != dev or not t.is_contiguous() or t.dtype != x.dtype:
-            raise ValueError("x, W_g, W1, b1, W2, b2 must be contiguous tensors of one dtype on one GPU")
-    if activation not in ACTIVATIONS:
-        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}")
+    _check_tensors(x, W_g, W1, b1, W2, b2, b_g, n_shared, activation)
     T, d = x.shape
     E = W_g.shape[0]
     h = W1.shape[1]
     S = n_shared
-    if W_g.shape != (E, d) or W1.shape != (E + S, h, d) or W2.shape != (E + S, d, h) or \
-            (b1 is not None and b1.shape != (E + S, h)) or (b2 is not None and b2.shape != (E + S, d)):
-        raise ValueError("inconsistent shapes")
-    if b_g is not None and (b_g.dtype != torch.float32 or b_g.shape != (E,) or b_g.device != dev):
-        raise ValueError("b_g must be float32 [E] on the same GPU")
+    dev = x.device
     dt = _dtype_code(x)
     nbytes = moe_workspace_bytes(T, d, h, E, k, S, dt)
     if nbytes == 0:
@@ -88,37 +126,75 @@ def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shar
     kept = torch.empty((E,), dtype=torch.int32, device=dev)
     slot_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
 
-    launch = MoeLaunch()
-    launch.T, launch.d, launch.h, launch.dtype = T, d, h, dt
-    launch.b_g = b_g.data_ptr() if b_g is not None else None
+    launch, keep = _launch(x, T, d, h, dt, b_g, workspace, zl, activation, min_capacity, stage_events)
     launch.expert_counts = counts.data_ptr()
     launch.expert_kept = kept.data_ptr()
     launch.slot_pos = slot_pos.data_ptr()
-    launch.workspace = workspace.data_ptr()
-    launch.workspace_bytes = workspace.numel()
-    launch.stream = torch.cuda.current_stream(dev).cuda_stream
-    launch.z_loss = zl.data_ptr()
-    launch.activation = ACTIVATIONS[activation]
-    launch.min_capacity = int(min_capacity)
-    ev_arr = None
-    if stage_events is not None:
-        if len(stage_events) != MOE_NUM_STAGE_EVENTS:
-            raise ValueError(f"stage_events needs {MOE_NUM_STAGE_EVENTS} events")
-        handles = [int(e.cuda_event) for e in stage_events]
-        if not all(handles):
-            raise ValueError("record each stage event once before passing it (creates its handle)")
-        ev_arr = (ctypes.c_void_p * MOE_NUM_STAGE_EVENTS)(*handles)
-        launch.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
     ptr = lambda t: t.data_ptr() if t is not None else None
     status = moe_forward(x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), ptr(b1), W2.data_ptr(), ptr(b2), E, k,
                          float(capacity_factor), S, out.data_ptr(), topk_idx.data_ptr(), topk_w.data_ptr(),
                          aux.data_ptr(), launch)
+    del keep
     if status != MOE_OK:
         raise RuntimeError(moe_status_string(status))
     return MoEOutput(out, topk_idx, topk_w, aux, zl, counts, kept, slot_pos)
 
 
+@dataclass
+class ExpertChoiceOutput:
+    out: "object"            # [T, d], dtype of x
+    ec_token: "object"       # [E, C] int32, ascending token order per expert
+    ec_w: "object"           # [E, C] float32
+    aux_loss: "object"       # [1] float32
+    z_loss: "object"         # [1] float32
+
+
+def expert_choice_capacity(capacity_factor: float, T: int, E: int, min_capacity: int = 0) -> int:
+    """Tokens per expert from a capacity factor: min(T, max(ceil(cf T / E), min_capacity)),
+    the ceiling taken in double precision of the float32 factor the layer uses elsewhere."""
+    if not capacity_factor > 0:
+        raise ValueError("expert choice needs a capacity factor > 0")
+    cf = ctypes.c_float(capacity_factor).value
+    return min(T, max(int(math.ceil(cf * T / E)), int(min_capacity)))
+
+
+def forward_expert_choice(x, W_g, W1, b1, W2, b2, C: int, n_shared: int = 0, b_g=None, *,
+                          activation: str = "gelu", stage_events: Optional[Sequence] = None,
+                          workspace=None) -> ExpertChoiceOutput:
+    """Run the layer with expert-choice routing (each expert takes its C
+    best-scoring tokens) on torch tensors that live on one GPU.  Arguments as
+    for ``forward``; C in 1..T."""
+    import torch
+    _check_tensors(x, W_g, W1, b1, W2, b2, b_g, n_shared, activation)
+    T, d = x.shape
+    E = W_g.shape[0]
+    h = W1.shape[1]
+    dt = _dtype_code(x)
+    nbytes = moe_workspace_bytes_expert_choice(T, d, h, E, C, n_shared, dt)
+    if nbytes == 0:
+        raise RuntimeError("invalid problem shape for moe_workspace_bytes_expert_choice")
+    dev = x.device
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((T, d), dtype=x.dtype, device=dev)
+    ec_token = torch.empty((E, C), dtype=torch.int32, device=dev)
+    ec_w = torch.empty((E, C), dtype=torch.float32, device=dev)
+    aux = torch.empty((1,), dtype=torch.float32, device=dev)
+    zl = torch.empty((1,), dtype=torch.float32, device=dev)
+    launch, keep = _launch(x, T, d, h, dt, b_g, workspace, zl, activation, 0, stage_events)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    status = moe_forward_expert_choice(x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), ptr(b1), W2.data_ptr(),
+                                       ptr(b2), E, C, n_shared, out.data_ptr(), ec_token.data_ptr(),
+                                       ec_w.data_ptr(), aux.data_ptr(), launch)
+    del keep
+    if status != MOE_OK:
+        raise RuntimeError(moe_status_string(status))
+    return ExpertChoiceOutput(out, ec_token, ec_w, aux, zl)
+
+
 __all__ = ["forward", "MoEOutput", "moe_forward", "moe_workspace_bytes", "moe_status_string", "MoeLaunch",
+           "forward_expert_choice", "ExpertChoiceOutput", "moe_forward_expert_choice",
+           "moe_workspace_bytes_expert_choice", "expert_choice_capacity", "STAGES_EXPERT_CHOICE",
            "ACTIVATIONS", "MOE_ACT_GELU", "MOE_ACT_SILU", "MOE_F32", "MOE_BF16", "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
            "MOE_ERR_HIP", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SHARED", "MOE_NUM_STAGE_EVENTS",
            "STAGES", "EXPORTS", "LIB_PATH"]

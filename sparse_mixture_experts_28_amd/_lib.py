@@ -30,7 +30,8 @@ MOE_MAX_SHARED = 8
 MOE_NUM_STAGE_EVENTS = 7
 
 # names of the C ABI entry points (include/moe.h)
-EXPORTS = ("moe_forward", "moe_workspace_bytes", "moe_status_string")
+EXPORTS = ("moe_forward", "moe_workspace_bytes", "moe_status_string", "moe_forward_expert_choice",
+           "moe_workspace_bytes_expert_choice")
 
 
 class MoeLaunch(ctypes.Structure):
@@ -67,6 +68,15 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     lib.moe_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_workspace_bytes.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_int]
+    lib.moe_workspace_bytes_expert_choice.restype = ctypes.c_size_t
+    lib.moe_workspace_bytes_expert_choice.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_int]
+    lib.moe_forward_expert_choice.restype = ctypes.c_int
+    lib.moe_forward_expert_choice.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.POINTER(MoeLaunch),
+    ]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_forward.restype = ctypes.c_int
@@ -86,6 +96,10 @@ def moe_workspace_bytes(T: int, d: int, h: int, E: int, k: int, n_shared: int, d
     return int(LIB.moe_workspace_bytes(T, d, h, E, k, n_shared, dtype))
 
 
+def moe_workspace_bytes_expert_choice(T: int, d: int, h: int, E: int, C: int, n_shared: int, dtype: int) -> int:
+    return int(LIB.moe_workspace_bytes_expert_choice(T, d, h, E, C, n_shared, dtype))
+
+
 def moe_status_string(status: int) -> str:
     return LIB.moe_status_string(status).decode()
 
@@ -95,3 +109,10 @@ def moe_forward(x, W_g, W1, b1, W2, b2, E, k, capacity_factor, n_shared, out, to
     """Raw call of the C entry point: every array argument is a device address (int)."""
     return int(LIB.moe_forward(x, W_g, W1, b1, W2, b2, E, k, capacity_factor, n_shared, out, topk_idx, topk_w,
                                aux_loss, ctypes.byref(launch)))
+
+
+def moe_forward_expert_choice(x, W_g, W1, b1, W2, b2, E, C, n_shared, out, ec_token, ec_w, aux_loss,
+                              launch: MoeLaunch) -> int:
+    """Raw call of the expert-choice entry point: every array argument is a device address (int)."""
+    return int(LIB.moe_forward_expert_choice(x, W_g, W1, b1, W2, b2, E, C, n_shared, out, ec_token, ec_w,
+                                             aux_loss, ctypes.byref(launch)))

@@ -10,6 +10,10 @@
 // A gather, not a scatter: one workgroup per token reads its k expert rows and
 // its shared rows, accumulates in float32 in slot order then shared order, and
 // rounds once.  No atomics, so the result is bitwise reproducible.
+//
+// Expert choice ("第7章 Mixture of Experts" §7.2; the guide's §4.2): a token's
+// routed rows are those of the experts that took it, 0 to E of them, added in
+// ascending expert order with the weights the selection recorded.
 #include "moe_internal.h"
 
 namespace moe {
@@ -38,7 +42,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(Problem p, const u32x
     s_w[threadIdx.x] = topk_w[static_cast<size_t>(t) * k + threadIdx.x];
   }
   __syncthreads();
-  const size_t routed_rows = static_cast<size_t>(p.T) * p.k;
+  const size_t routed_rows = static_cast<size_t>(p.A);
   for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
@@ -70,7 +74,7 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(Problem p, const float
     s_w[threadIdx.x] = topk_w[static_cast<size_t>(t) * k + threadIdx.x];
   }
   __syncthreads();
-  const size_t routed_rows = static_cast<size_t>(p.T) * p.k;
+  const size_t routed_rows = static_cast<size_t>(p.A);
   for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
@@ -96,7 +100,118 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(Problem p, const float
   }
 }
 
+// Expert choice: the rows of token t, in ascending expert order.  Wave 0 reads
+// pos[e][t] for every expert (lane l: experts 4l .. 4l+3, E <= 256) and packs
+// the takers with a lane prefix count; returns their number.
+__device__ int ec_token_rows(const Problem& p, const int32_t* __restrict__ pos, const float* __restrict__ ec_w,
+                             int t, int32_t* s_row, float* s_w, int* s_n) {
+  if (threadIdx.x < kWave) {
+    const int l = threadIdx.x;
+    int32_t c4[4];
+    int own = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * l + i;
+      c4[i] = e < p.E ? pos[static_cast<size_t>(e) * p.T + t] : -1;
+      own += c4[i] >= 0;
+    }
+    int incl = own;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(incl, off, kWave);
+      if (l >= off) incl += o;
+    }
+    int at = incl - own;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (c4[i] >= 0) {
+        const int row = (4 * l + i) * p.ec_C + c4[i];
+        s_row[at] = row;
+        s_w[at] = ec_w[row];
+        ++at;
+      }
+    }
+    if (l == kWave - 1) *s_n = incl;
+  }
+  __syncthreads();
+  return *s_n;
+}
+
+__global__ __launch_bounds__(256) void combine_ec_bf16_kernel(Problem p, const u32x4* __restrict__ y,
+                                                              const int32_t* __restrict__ pos,
+                                                              const float* __restrict__ ec_w,
+                                                              u32x4* __restrict__ out, int vec_per_row) {
+  __shared__ int32_t s_row[MOE_MAX_EXPERTS];
+  __shared__ float s_w[MOE_MAX_EXPERTS];
+  __shared__ int s_n;
+  const int t = blockIdx.x;
+  const int n = ec_token_rows(p, pos, ec_w, t, s_row, s_w, &s_n);
+  const size_t routed_rows = static_cast<size_t>(p.A);
+  for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < n; ++j) acc_bf16x8(a, y[static_cast<size_t>(s_row[j]) * vec_per_row + c], s_w[j]);
+    for (int s = 0; s < p.S; ++s) {
+      const size_t row = routed_rows + static_cast<size_t>(s) * p.T + t;
+      acc_bf16x8(a, y[row * vec_per_row + c], 1.0f);
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = static_cast<uint32_t>(f32_to_bf16(a[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(a[2 * i + 1])) << 16);
+    out[static_cast<size_t>(t) * vec_per_row + c] = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_ec_f32_kernel(Problem p, const float4* __restrict__ y,
+                                                             const int32_t* __restrict__ pos,
+                                                             const float* __restrict__ ec_w,
+                                                             float4* __restrict__ out, int vec_per_row) {
+  __shared__ int32_t s_row[MOE_MAX_EXPERTS];
+  __shared__ float s_w[MOE_MAX_EXPERTS];
+  __shared__ int s_n;
+  const int t = blockIdx.x;
+  const int n = ec_token_rows(p, pos, ec_w, t, s_row, s_w, &s_n);
+  const size_t routed_rows = static_cast<size_t>(p.A);
+  for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < n; ++j) {
+      const float4 v = y[static_cast<size_t>(s_row[j]) * vec_per_row + c];
+      const float w = s_w[j];
+      a.x = fmaf(w, v.x, a.x);
+      a.y = fmaf(w, v.y, a.y);
+      a.z = fmaf(w, v.z, a.z);
+      a.w = fmaf(w, v.w, a.w);
+    }
+    for (int s = 0; s < p.S; ++s) {
+      const size_t row = routed_rows + static_cast<size_t>(s) * p.T + t;
+      const float4 v = y[row * vec_per_row + c];
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+    }
+    out[static_cast<size_t>(t) * vec_per_row + c] = a;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_combine_ec(const Problem& p, const float* ec_w, const Workspace& ws, void* out,
+                             hipStream_t st) {
+  const int elem = p.dtype == MOE_BF16 ? 2 : 4;
+  const int vec_per_row = p.d * elem / 16;
+  // at least one wave: wave 0 gathers the token's expert list
+  const int threads = vec_per_row >= 256 ? 256 : (vec_per_row >= 128 ? 128 : 64);
+  if (p.dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_ec_bf16_kernel, dim3(p.T), dim3(threads), 0, st, p,
+                       static_cast<const u32x4*>(ws.ybuf), ws.ec_pos, ec_w, static_cast<u32x4*>(out),
+                       vec_per_row);
+  else
+    hipLaunchKernelGGL(combine_ec_f32_kernel, dim3(p.T), dim3(threads), 0, st, p,
+                       static_cast<const float4*>(ws.ybuf), ws.ec_pos, ec_w, static_cast<float4*>(out),
+                       vec_per_row);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const Problem& p, const float* topk_w, const Workspace& ws, void* out,
                           hipStream_t st) {

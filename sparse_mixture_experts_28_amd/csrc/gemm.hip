@@ -584,7 +584,7 @@ int num_cus() {
 bool gemm_fast_path(const Problem& p) {
   if (p.dtype != MOE_BF16 || p.h % kBN != 0 || p.d % kBN != 0 || p.d % kBK != 0 || p.h % kBK != 0) return false;
   // buffer offsets are 32-bit: every operand region must stay below 2 GiB
-  const long long rows = static_cast<long long>(p.T) * p.k + static_cast<long long>(p.S) * p.T + 256;
+  const long long rows = static_cast<long long>(p.A) + static_cast<long long>(p.S) * p.T + 256;
   const long long widest = p.d > p.h ? p.d : p.h;
   return rows * widest * 2 < (1LL << 31) && static_cast<long long>(p.h) * p.d * 2 < (1LL << 31);
 }
@@ -593,13 +593,14 @@ bool gemm_fast_path(const Problem& p) {
 // compute-bound case).  Otherwise the height in {128, 160, 256} that
 // covers the expected rows of an expert with the fewest padded rows: the
 // capacity when it binds (an expert then holds exactly that many rows when
-// full), else 1.25 x the mean T k / E as headroom for uneven routing; ties
-// go to the taller tile, which streams each weight panel for more rows.
+// full; under expert choice every expert holds exactly C), else 1.25 x the
+// mean rows per expert as headroom for uneven routing; ties go to the taller
+// tile, which streams each weight panel for more rows.
 int gemm_m_tile(const Problem& p) {
   if (!gemm_fast_path(p)) return kSB;
-  const long long mean = (static_cast<long long>(p.T) * p.k + p.E - 1) / p.E;
+  const long long mean = (static_cast<long long>(p.A) + p.E - 1) / p.E;
   if (mean >= 512 && p.cap >= 512) return 256;
-  const long long want = p.cap < mean ? p.cap : (mean * 5 + 3) / 4;
+  const long long want = p.cap <= mean ? p.cap : (mean * 5 + 3) / 4;
   int best = 256;
   long long best_pad = (want + 255) / 256 * 256;
   for (int bm : {160, 128}) {
@@ -630,7 +631,7 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
     g.K = p.d;
   } else {
     g.A = ws.hbuf;
-    g.a_rows = p.T * p.k + p.S * p.T;
+    g.a_rows = p.A + p.S * p.T;
     g.row_token = nullptr;
     g.a_by_o_off = 1;
     g.W = W2;
@@ -669,7 +670,7 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
 #undef MOE_GEMM_LAUNCH
   } else {
     // upper bound of M tiles: sum_e ceil(rows_e / 64) <= ceil(T k / 64) + E + S ceil(T / 64)
-    const long long max_mt = (static_cast<long long>(p.T) * p.k + kSB - 1) / kSB + p.E +
+    const long long max_mt = (static_cast<long long>(p.A) + kSB - 1) / kSB + p.E +
                              static_cast<long long>(p.S) * ((p.T + kSB - 1) / kSB);
     dim3 grid(static_cast<unsigned>(max_mt), (g.N + kSB - 1) / kSB);
 #define MOE_SIMT_LAUNCH(TIN_)                                                                               \

@@ -1,6 +1,7 @@
 // Host side of the C ABI (include/moe.h): validation, workspace carving and the
-// launch sequence router -> scan -> scatter -> expert phase 1 -> phase 2 -> combine,
-// all enqueued on the caller's stream with no host synchronisation.
+// launch sequence router -> scan -> scatter -> expert phase 1 -> phase 2 -> combine
+// (expert choice: router -> scan -> per-expert selection -> phase 1 -> phase 2 ->
+// combine), all enqueued on the caller's stream with no host synchronisation.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -23,30 +24,37 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t elem_bytes(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t row_token, hbuf, ybuf, local_rank, tile_hist, p_part, z_part, counts, kept, slot_pos, seg, logits, part,
-      total;
+  size_t row_token, hbuf, ybuf, local_rank, tile_hist, p_part, z_part, counts, kept, slot_pos, seg, logits, ec_logits,
+      ec_m, ec_z, ec_pos, part, total;
   int part_cap;
 };
 
 Layout layout_of(const Problem& p) {
   const size_t s = elem_bytes(p.dtype);
-  const size_t A = static_cast<size_t>(p.T) * p.k;
+  const size_t A = static_cast<size_t>(p.A);
   const size_t R = A + static_cast<size_t>(p.S) * p.T;
   const size_t te = static_cast<size_t>(p.ntile) * p.E;
+  const size_t tk = static_cast<size_t>(p.T) * p.k;          // token-choice slots (0 under expert choice)
+  const size_t et = p.ec_C > 0 ? static_cast<size_t>(p.E) * p.T : 0;
+  const size_t ect = p.ec_C > 0 ? static_cast<size_t>(p.T) : 0;
   Layout L;
   size_t off = 0;
   L.row_token = off;  off += align_up(A * 4);
   L.hbuf = off;       off += align_up(R * p.h * s);
   L.ybuf = off;       off += align_up(R * p.d * s);
-  L.local_rank = off; off += align_up(A * 4);
+  L.local_rank = off; off += align_up(tk * 4);
   L.tile_hist = off;  off += align_up(te * 4);
   L.p_part = off;     off += align_up(te * 4);
   L.z_part = off;     off += align_up(static_cast<size_t>(p.ntile) * 8);
   L.counts = off;     off += align_up(static_cast<size_t>(p.E) * 4);
   L.kept = off;       off += align_up(static_cast<size_t>(p.E) * 4);
-  L.slot_pos = off;   off += align_up(A * 4);
+  L.slot_pos = off;   off += align_up(tk * 4);
   L.seg = off;        off += align_up(seg_table_ints(p.E + p.S, p.E) * 4);
   L.logits = off;     off += align_up(static_cast<size_t>(logit_splits(p)) * p.T * logit_pad(p.E) * 8);
+  L.ec_logits = off;  off += align_up(et * 8);
+  L.ec_m = off;       off += align_up(ect * 8);
+  L.ec_z = off;       off += align_up(ect * 4);
+  L.ec_pos = off;     off += align_up(et * 4);
   // sized for the tallest tile: moe_workspace_bytes has no capacity factor,
   // and the tile height moe_forward picks can depend on it
   L.part_cap = gemm_fast_path(p) ? kGemmPartCap : 0;
@@ -77,6 +85,10 @@ Workspace carve_workspace(const Problem& p, void* base, size_t bytes_available, 
   w.slot_pos = reinterpret_cast<int32_t*>(b + L.slot_pos);
   w.seg = reinterpret_cast<int32_t*>(b + L.seg);
   w.logits = reinterpret_cast<double*>(b + L.logits);
+  w.ec_logits = reinterpret_cast<double*>(b + L.ec_logits);
+  w.ec_m = reinterpret_cast<double*>(b + L.ec_m);
+  w.ec_z = reinterpret_cast<float*>(b + L.ec_z);
+  w.ec_pos = reinterpret_cast<int32_t*>(b + L.ec_pos);
   w.part = reinterpret_cast<float*>(b + L.part);
   w.part_cap = L.part_cap;
   w.bytes = L.total;
@@ -108,6 +120,8 @@ Problem make_problem(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int3
   p.S = S;
   p.dtype = dt;
   p.act = act;
+  p.ec_C = 0;
+  p.A = T * k;
   p.ntile = (T + kRouterTile - 1) / kRouterTile;
   if (cf > 0.f) {
     double c = std::ceil(static_cast<double>(cf) * static_cast<double>(T) / static_cast<double>(E));
@@ -120,6 +134,52 @@ Problem make_problem(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int3
   return p;
 }
 
+// Expert choice: every expert takes exactly C tokens, so C is also its
+// capacity and the routed rows are E * C.
+moe_status_t check_shape_ec(int32_t T, int32_t d, int32_t h, int32_t E, int32_t C, int32_t S, int dtype) {
+  if (T < 1 || d < 1 || h < 1 || E < 1 || C < 1 || C > T || S < 0) return MOE_ERR_ARG;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (E > MOE_MAX_EXPERTS || S > MOE_MAX_SHARED) return MOE_ERR_UNSUPPORTED;
+  if (d % 8 != 0 || h % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long rows = static_cast<long long>(E) * C + static_cast<long long>(S) * T;
+  if (rows > INT32_MAX || static_cast<long long>(E) * T > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+Problem make_problem_ec(int32_t T, int32_t d, int32_t h, int32_t E, int32_t C, int32_t S, moe_dtype_t dt,
+                        int act = MOE_ACT_GELU) {
+  Problem p;
+  p.T = T;
+  p.d = d;
+  p.h = h;
+  p.E = E;
+  p.k = 0;
+  p.S = S;
+  p.dtype = dt;
+  p.act = act;
+  p.ec_C = C;
+  p.A = E * C;
+  p.ntile = (T + kRouterTile - 1) / kRouterTile;
+  p.cap = C;
+  p.gemm_bm = gemm_m_tile(p);
+  return p;
+}
+
+// Records the optional stage events and reports a failed launch by stage.
+struct StageCheck {
+  hipStream_t st;
+  hipEvent_t* ev;
+  int ei = 0;
+  bool operator()(hipError_t e, const char* stage) {
+    if (e == hipSuccess && ev != nullptr) e = hipEventRecord(ev[ei++], st);
+    if (e != hipSuccess) {
+      std::fprintf(stderr, "libmoe: %s failed: %s (%s)\n", stage, hipGetErrorName(e), hipGetErrorString(e));
+      return false;
+    }
+    return true;
+  }
+};
+
 }  // namespace
 }  // namespace moe
 
@@ -129,6 +189,12 @@ size_t moe_workspace_bytes(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k
                            moe_dtype_t dtype) {
   if (moe::check_shape(T, d, h, E, k, n_shared, static_cast<int>(dtype)) != MOE_OK) return 0;
   return moe::workspace_bytes(moe::make_problem(T, d, h, E, k, n_shared, dtype, 0.f));
+}
+
+size_t moe_workspace_bytes_expert_choice(int32_t T, int32_t d, int32_t h, int32_t E, int32_t C, int32_t n_shared,
+                                         moe_dtype_t dtype) {
+  if (moe::check_shape_ec(T, d, h, E, C, n_shared, static_cast<int>(dtype)) != MOE_OK) return 0;
+  return moe::workspace_bytes(moe::make_problem_ec(T, d, h, E, C, n_shared, dtype));
 }
 
 const char* moe_status_string(moe_status_t s) {
@@ -171,18 +237,9 @@ moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const v
   if (launch->slot_pos) ws.slot_pos = launch->slot_pos;
 
   hipStream_t st = launch->stream;
-  hipEvent_t* ev = launch->stage_events;
-  int ei = 0;
+  StageCheck check{st, launch->stage_events};
   // a stale error from an earlier, unrelated HIP call must not be blamed on a launch here
   (void)hipGetLastError();
-  auto check = [&](hipError_t e, const char* stage) -> bool {
-    if (e == hipSuccess && ev != nullptr) e = hipEventRecord(ev[ei++], st);
-    if (e != hipSuccess) {
-      std::fprintf(stderr, "libmoe: %s failed: %s (%s)\n", stage, hipGetErrorName(e), hipGetErrorString(e));
-      return false;
-    }
-    return true;
-  };
 
   if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
   if (!check(launch_router(p, x, W_g, launch->b_g, topk_idx, topk_w, ws, st), "router launch")) return MOE_ERR_HIP;
@@ -193,6 +250,46 @@ moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const v
   if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 1, st), "expert phase 1 launch")) return MOE_ERR_HIP;
   if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 2, st), "expert phase 2 launch")) return MOE_ERR_HIP;
   if (!check(launch_combine(p, topk_w, ws, out, st), "combine launch")) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status_t moe_forward_expert_choice(const void* x, const void* W_g, const void* W1, const void* b1,
+                                       const void* W2, const void* b2, int32_t E, int32_t C, int32_t n_shared,
+                                       void* out, int32_t* ec_token, float* ec_w, float* aux_loss,
+                                       const moe_launch_t* launch) {
+  using namespace moe;
+  if (launch == nullptr) return MOE_ERR_ARG;
+  if (!x || !W_g || !W1 || !W2 || !out || !ec_token || !ec_w) return MOE_ERR_ARG;
+  if (launch->activation != MOE_ACT_GELU && launch->activation != MOE_ACT_SILU) return MOE_ERR_UNSUPPORTED;
+  const moe_status_t sc = check_shape_ec(launch->T, launch->d, launch->h, E, C, n_shared,
+                                         static_cast<int>(launch->dtype));
+  if (sc != MOE_OK) return sc;
+  const void* a16[] = {x, W_g, W1, b1, W2, b2, out};
+  for (const void* q : a16)
+    if (q && !aligned(q, 16)) return MOE_ERR_UNSUPPORTED;
+  const void* a4[] = {ec_token, ec_w, aux_loss, launch->z_loss, launch->b_g, launch->expert_counts,
+                      launch->expert_kept};
+  for (const void* q : a4)
+    if (q && !aligned(q, 4)) return MOE_ERR_UNSUPPORTED;
+
+  const Problem p = make_problem_ec(launch->T, launch->d, launch->h, E, C, n_shared, launch->dtype,
+                                    launch->activation);
+  bool ok = false;
+  Workspace ws = carve_workspace(p, launch->workspace, launch->workspace_bytes, &ok);
+  if (!ok) return MOE_ERR_WORKSPACE;
+
+  hipStream_t st = launch->stream;
+  StageCheck check{st, launch->stage_events};
+  (void)hipGetLastError();
+  if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
+  if (!check(launch_router(p, x, W_g, launch->b_g, nullptr, nullptr, ws, st), "router launch")) return MOE_ERR_HIP;
+  if (!check(launch_scan(p, ws, aux_loss, launch->z_loss, launch->expert_counts, launch->expert_kept, st),
+             "scan launch"))
+    return MOE_ERR_HIP;
+  if (!check(launch_ec_select(p, ec_token, ec_w, ws, st), "expert-choice selection launch")) return MOE_ERR_HIP;
+  if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 1, st), "expert phase 1 launch")) return MOE_ERR_HIP;
+  if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 2, st), "expert phase 2 launch")) return MOE_ERR_HIP;
+  if (!check(launch_combine_ec(p, ec_w, ws, out, st), "combine launch")) return MOE_ERR_HIP;
   return MOE_OK;
 }
 

@@ -34,9 +34,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // ----------------------------------------------------- workspace layout --
 // All regions are carved from one caller-owned device buffer, each aligned to
-// 256 bytes.  Row counts: A = T*k routed rows (worst case, no drops),
-// R = A + S*T rows of the expert hidden / output buffers (shared experts at
-// the fixed row offset A + s*T).
+// 256 bytes.  Row counts: A = routed rows (T*k, the worst case without drops,
+// or E*C under expert choice), R = A + S*T rows of the expert hidden / output
+// buffers (shared experts at the fixed row offset A + s*T).
 struct Workspace {
   int32_t* row_token;   // [A]        token of each row of the expert-sorted order (kept assignments)
   void* hbuf;           // [R, h]     GELU(x W1^T + b1)
@@ -50,6 +50,10 @@ struct Workspace {
   int32_t* slot_pos;    // [T, k]
   int32_t* seg;         // segment table, see SegTable
   double* logits;       // [KS, T, Epad] float64 partial router logits (bf16 path)
+  double* ec_logits;    // [E, T]     expert choice: float64 logits, expert-major
+  double* ec_m;         // [T]        expert choice: each token's largest logit
+  float* ec_z;          // [T]        expert choice: each token's sum of exp(l - m)
+  int32_t* ec_pos;      // [E, T]     expert choice: rank of t among e's chosen tokens, -1 if not chosen
   float* part;          // [part_cap, BM, 256] float32 partial tiles of the grouped GEMM's split tail
   int part_cap;         // partial tiles the buffer holds (0: no split)
   size_t bytes;
@@ -86,6 +90,8 @@ inline size_t seg_table_ints(int nseg, int E) { return static_cast<size_t>(4 * n
 
 struct Problem {
   int T, d, h, E, k, S;
+  int ec_C;      // expert choice: tokens per expert (0: token choice, top-k per token)
+  int A;         // routed rows: T * k, or E * ec_C under expert choice
   moe_dtype_t dtype;
   int act;       // moe_activation_t of the experts
   int cap;       // capacity per expert (min_capacity applied); INT32_MAX when unlimited
@@ -108,6 +114,13 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
                              hipStream_t st);
 hipError_t launch_combine(const Problem& p, const float* topk_w, const Workspace& ws, void* out,
                           hipStream_t st);
+// expert choice: each expert's top-C tokens (ec_token, ec_w [E, C]; the GEMM's
+// row -> token index; the per-(expert, token) rank table), and the combine
+// over the experts that took each token
+hipError_t launch_ec_select(const Problem& p, int32_t* ec_token, float* ec_w, const Workspace& ws,
+                            hipStream_t st);
+hipError_t launch_combine_ec(const Problem& p, const float* ec_w, const Workspace& ws, void* out,
+                             hipStream_t st);
 
 // Which GEMM kernel serves a problem; the M tile decides the tile prefix.
 bool gemm_fast_path(const Problem& p);

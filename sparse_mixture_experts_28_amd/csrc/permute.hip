@@ -55,10 +55,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
   double psum = 0.0;
   const int32_t* hrow = tile_hist + static_cast<size_t>(e) * p.ntile;
   const float* prow = p_part + static_cast<size_t>(e) * p.ntile;
+  const bool ec = p.ec_C > 0;   // expert choice: every expert takes exactly ec_C tokens
   if (active) {
 #pragma unroll 8
     for (int tile = tb; tile < te; ++tile) {
-      sum += hrow[tile];
+      if (!ec) sum += hrow[tile];
       psum += static_cast<double>(prow[tile]);
     }
     s_sum[c * E + e] = sum;
@@ -75,6 +76,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
       run += v;
       pr += s_psum[q * E + t];
     }
+    if (ec) run = p.ec_C;
     const int kp = min(run, p.cap);
     counts[t] = run;
     kept[t] = kp;
@@ -85,8 +87,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
     s_P[t] = pr / static_cast<double>(p.T);
   }
   __syncthreads();
-  // 3. tile bases within the chunk
-  if (active) {
+  // 3. tile bases within the chunk (token choice only)
+  if (active && !ec) {
     int run = s_sum[c * E + e];
     int32_t* wrow = tile_hist + static_cast<size_t>(e) * p.ntile;
 #pragma unroll 8
@@ -108,7 +110,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
     for (int tile = zb; tile < ze; ++tile) zs += z_part[tile];
     s_z[t] = zs;
   }
-  const double tk = static_cast<double>(p.T) * static_cast<double>(p.k);
+  // f_e = c_e / (all assignments): T k, or E C under expert choice
+  const double tk = static_cast<double>(p.A);
   if (t < MOE_MAX_EXPERTS) s_aux[t] = t < E ? (static_cast<double>(s_cnt[t]) / tk) * s_P[t] : 0.0;
   // 5. segment table: one thread per segment (routed experts, then shared)
   constexpr int kSegSlots = 512;   // >= MOE_MAX_EXPERTS + MOE_MAX_SHARED
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
     if (t < w) s_aux[t] += s_aux[t + w];
     __syncthreads();
   }
-  if (t == 0) *aux_loss = static_cast<float>(static_cast<double>(E) * s_aux[0]);
+  if (t == 0 && aux_loss) *aux_loss = static_cast<float>(static_cast<double>(E) * s_aux[0]);
   for (int w = kScanThreads / 2; w > 0; w >>= 1) {
     if (t < w) s_z[t] += s_z[t + w];
     __syncthreads();
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
     __syncthreads();
   }
   if (t < nseg) {
-    const int routed_rows = p.T * p.k;
+    const int routed_rows = p.A;
     const int excl_rows = s_rows[t] - (t < E ? my_rows : 0);
     st.rows[t] = my_rows;
     st.a_off[t] = t < E ? excl_rows : 0;

@@ -40,6 +40,11 @@ struct RouterArgs {
   int32_t* tile_hist;
   float* p_part;
   double* z_part;
+  // expert-choice mode (ec_logits != nullptr): no top-k; the logits are
+  // written expert-major [E][T] with each token's maximum and exponential sum
+  double* ec_logits;
+  double* ec_m;
+  float* ec_z;
   int T, d, E, k, ntile;
 };
 
@@ -48,6 +53,25 @@ struct RouterArgs {
 __device__ __forceinline__ double lse_sq(double m, float z) {
   const double lse = m + log(static_cast<double>(z));
   return lse * lse;
+}
+
+// Expert-choice mode: token t's logits (lane c of its 16-lane group holds
+// experts nb * 16 + c) go to the expert-major table, its maximum and
+// exponential sum to per-token arrays (the softmax of a chosen pair is
+// rebuilt from them exactly as here).
+template <int NB>
+__device__ __forceinline__ void write_ec(const RouterArgs& a, const double (&val)[NB], double m, float z, int t,
+                                         int c, bool tok_ok) {
+  if (!tok_ok) return;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int e = nb * 16 + c;
+    if (e < a.E) a.ec_logits[static_cast<size_t>(e) * a.T + t] = val[nb];
+  }
+  if (c == 0) {
+    a.ec_m[t] = m;
+    a.ec_z[t] = z;
+  }
 }
 
 // 16-lane argmax: larger value wins, equal values go to the lower index.
@@ -121,6 +145,10 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
       for (int nb = 0; nb < NB; ++nb) pp[nb] += ev[nb] * inv;
     }
     if (c == 0) s_z[r] = tok_ok ? lse_sq(m, z) : 0.0;
+    if (a.ec_logits) {
+      write_ec(a, val, m, z, t, c, tok_ok);
+      continue;
+    }
 
     // k rounds of a 16-lane argmax over the not-yet-chosen experts
     uint32_t taken = 0;
@@ -162,13 +190,14 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
 
   const int ntok = min(kRouterTile, a.T - tile0);
   const int tile = tile0 / kRouterTile;
+  const bool ec = a.ec_logits != nullptr;
   // In-tile ranks in token order.  mask[e] has bit r set iff token r of the
   // tile chose e (a token's k experts are distinct, and OR is order-free, so
   // the masks are deterministic); the rank of (r, j) is the number of earlier
   // tokens in its expert's mask, the tile histogram the mask's population.
   for (int e = threadIdx.x; e < E; e += blockDim.x) s_mask[e] = 0ull;
   __syncthreads();
-  if (threadIdx.x < ntok) {
+  if (threadIdx.x < ntok && !ec) {
     const int r = threadIdx.x;
     for (int j = 0; j < k; ++j) atomicOr(&s_mask[s_idx[r * MOE_MAX_TOPK + j]], 1ull << r);
   }
@@ -176,7 +205,7 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     // per-expert layout [E][ntile]: the scan reads each expert's tiles contiguously
     a.p_part[static_cast<size_t>(e) * a.ntile + tile] = ((s_p[0][e] + s_p[1][e]) + s_p[2][e]) + s_p[3][e];
-    a.tile_hist[static_cast<size_t>(e) * a.ntile + tile] = __popcll(s_mask[e]);
+    if (!ec) a.tile_hist[static_cast<size_t>(e) * a.ntile + tile] = __popcll(s_mask[e]);
   }
   if (threadIdx.x == blockDim.x - 1) {
     // z-loss partial of the tile, tokens in order
@@ -184,7 +213,7 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
     for (int r = 0; r < ntok; ++r) zs += s_z[r];
     a.z_part[tile] = zs;
   }
-  for (int i = threadIdx.x; i < ntok * k; i += blockDim.x) {
+  for (int i = threadIdx.x; i < (ec ? 0 : ntok * k); i += blockDim.x) {
     const int r = i / k, j = i - r * k;
     const unsigned long long below = (1ull << r) - 1ull;
     a.local_rank[static_cast<size_t>(tile0 + r) * k + j] = __popcll(s_mask[s_idx[r * MOE_MAX_TOPK + j]] & below);
@@ -486,13 +515,15 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) s_p[r][nb * 16 + c] = ev[nb] * inv;
   if (c == 0) s_z[r] = tok_ok ? lse_sq(m, z) : 0.0;
+  const bool ec = a.ec_logits != nullptr;
+  if (ec) write_ec(a, val, m, z, t, c, tok_ok);
 
   // k rounds of a 16-lane argmax over the not-yet-chosen experts
   uint32_t taken = 0;
   int my_idx = 0;
   float my_e = 0.f;
   float esum = 0.f;
-  for (int j = 0; j < k; ++j) {
+  for (int j = 0; j < (ec ? 0 : k); ++j) {
     double bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
@@ -506,7 +537,7 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
     esum += ej;
     if (c == j) { my_idx = bi; my_e = ej; }
   }
-  if (c < k) {
+  if (c < k && !ec) {
     s_idx[r * MOE_MAX_TOPK + c] = tok_ok ? my_idx : -1;
     if (tok_ok) {
       a.topk_idx[static_cast<size_t>(t) * k + c] = my_idx;
@@ -520,7 +551,7 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
   const int tile = tile0 / kRouterTile;
   // In-tile ranks in token order, as in route_tile: OR-ed 64-bit token masks
   // per expert (order-free, so deterministic); rank = earlier tokens in the mask.
-  if (threadIdx.x < ntok) {
+  if (threadIdx.x < ntok && !ec) {
     const int rr = threadIdx.x;
     for (int j = 0; j < k; ++j) atomicOr(&s_mask[s_idx[rr * MOE_MAX_TOPK + j]], 1ull << rr);
   }
@@ -530,7 +561,7 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
     float ps = 0.f;
     for (int rr = 0; rr < ntok; ++rr) ps += s_p[rr][e];
     a.p_part[static_cast<size_t>(e) * a.ntile + tile] = ps;
-    a.tile_hist[static_cast<size_t>(e) * a.ntile + tile] = __popcll(s_mask[e]);
+    if (!ec) a.tile_hist[static_cast<size_t>(e) * a.ntile + tile] = __popcll(s_mask[e]);
   }
   if (threadIdx.x == blockDim.x - 1) {
     // z-loss partial of the tile, tokens in order
@@ -538,7 +569,7 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
     for (int rr = 0; rr < ntok; ++rr) zs += s_z[rr];
     a.z_part[tile] = zs;
   }
-  for (int i = threadIdx.x; i < ntok * k; i += blockDim.x) {
+  for (int i = threadIdx.x; i < (ec ? 0 : ntok * k); i += blockDim.x) {
     const int rr = i / k, j = i - rr * k;
     const unsigned long long below = (1ull << rr) - 1ull;
     a.local_rank[static_cast<size_t>(tile0 + rr) * k + j] = __popcll(s_mask[s_idx[rr * MOE_MAX_TOPK + j]] & below);
@@ -588,6 +619,9 @@ hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const
   a.tile_hist = ws.tile_hist;
   a.p_part = ws.p_part;
   a.z_part = ws.z_part;
+  a.ec_logits = p.ec_C > 0 ? ws.ec_logits : nullptr;
+  a.ec_m = ws.ec_m;
+  a.ec_z = ws.ec_z;
   a.T = p.T;
   a.d = p.d;
   a.E = p.E;

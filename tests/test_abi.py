@@ -137,3 +137,67 @@ def test_null_launch():
 ])
 def test_rejected_on_host(kw, code):
     assert call(**kw) == code
+
+
+# ------------------------------------------------------------ expert choice --
+def test_workspace_bytes_expert_choice():
+    f = moe.moe_workspace_bytes_expert_choice
+    T, d, h, E, C = 16384, 2048, 8192, 64, 512
+    n = f(T, d, h, E, C, 0, moe.MOE_BF16)
+    rows = E * C
+    big = rows * h * 2 + rows * d * 2
+    # plus the float64 [E, T] logits and int32 [E, T] ranks (12 bytes per pair)
+    assert big + 12 * E * T <= n <= big + 12 * E * T + 160 * 1024 * 1024
+    assert f(T, d, h, E, C, 1, moe.MOE_BF16) > n
+    for bad in [(T, d, h, E, 0, 0), (T, d, h, E, T + 1, 0), (T, d, h, 257, C, 0), (T, 12, h, E, C, 0),
+                (0, d, h, E, C, 0), (T, d, h, E, C, 9), (T, d, h, E, C, -1)]:
+        assert f(*bad, moe.MOE_BF16) == 0, bad
+    assert f(T, d, h, E, C, 0, 7) == 0
+    assert moe.expert_choice_capacity(2.0, T, E) == C and moe.expert_choice_capacity(100.0, 10, 2) == 10
+
+
+def call_ec(**kw):
+    args = dict(x=FAKE, W_g=FAKE, W1=FAKE, b1=FAKE, W2=FAKE, b2=FAKE, E=8, C=16, S=0, out=FAKE, tok=FAKE,
+                w=FAKE, aux=FAKE)
+    lk = dict(T=64, d=32, h=64, dtype=moe.MOE_BF16, workspace=FAKE, workspace_bytes=0, activation=moe.MOE_ACT_GELU)
+    for key in list(kw):
+        if key in lk:
+            lk[key] = kw.pop(key)
+    args.update(kw)
+    L = moe.MoeLaunch()
+    L.T, L.d, L.h, L.dtype, L.activation = lk["T"], lk["d"], lk["h"], lk["dtype"], lk["activation"]
+    L.workspace = lk["workspace"]
+    need = moe.moe_workspace_bytes_expert_choice(L.T, L.d, L.h, args["E"], args["C"], args["S"], L.dtype)
+    L.workspace_bytes = lk["workspace_bytes"] if lk["workspace_bytes"] else need
+    return moe.moe_forward_expert_choice(args["x"], args["W_g"], args["W1"], args["b1"], args["W2"], args["b2"],
+                                         args["E"], args["C"], args["S"], args["out"], args["tok"], args["w"],
+                                         args["aux"], L)
+
+
+@pytest.mark.parametrize("field", ["x", "W_g", "W1", "W2", "out", "tok", "w"])
+def test_ec_null_required_pointer(field):
+    assert call_ec(**{field: None}) == moe.MOE_ERR_ARG
+
+
+def test_ec_optional_pointers():
+    # NULL biases and aux_loss pass validation; the call then stops at the too-small workspace
+    assert call_ec(b1=None, b2=None, aux=None, workspace_bytes=1024) == moe.MOE_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(C=0), moe.MOE_ERR_ARG), (dict(C=65), moe.MOE_ERR_ARG), (dict(E=0), moe.MOE_ERR_ARG),
+    (dict(E=257), moe.MOE_ERR_UNSUPPORTED), (dict(S=9), moe.MOE_ERR_UNSUPPORTED), (dict(S=-1), moe.MOE_ERR_ARG),
+    (dict(d=36), moe.MOE_ERR_UNSUPPORTED), (dict(dtype=5), moe.MOE_ERR_UNSUPPORTED),
+    (dict(activation=3), moe.MOE_ERR_UNSUPPORTED), (dict(tok=FAKE + 2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(x=FAKE + 8), moe.MOE_ERR_UNSUPPORTED), (dict(workspace=None), moe.MOE_ERR_WORKSPACE),
+    (dict(workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
+    (dict(T=1 << 24, C=1 << 24, E=256, d=8, h=8), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_ec_rejected_on_host(kw, code):
+    assert call_ec(**kw) == code
+
+
+def test_ec_null_launch():
+    st = moe._lib.LIB.moe_forward_expert_choice(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 0, FAKE, FAKE, FAKE,
+                                                FAKE, None)
+    assert st == moe.MOE_ERR_ARG

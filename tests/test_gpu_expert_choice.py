@@ -108,3 +108,29 @@ def test_ec_full_size(name):
     # every expert holds exactly C distinct tokens, on every expert
     assert all(len(set(r.tolist())) == C for r in gpu["tok"])
     _say(f"[ec-full] {name}: {rep}")
+
+
+def test_ec_constant_column_takes_lowest_indices():
+    """Expert 0's router row is zero, so all its logits are equal: its bucket
+    holds every token (more than the directly ranked 1024), the exact radix
+    path runs, and every tie goes to the lower token index: tokens 0..C-1."""
+    inp = make_inputs(CONFIGS["mixtral"].replace(name="ec_const", T=3000, d=256, h=256, E=8), seed=1)
+    W_g = inp.W_g.copy()
+    W_g[0] = 0
+    inp._wg = W_g
+    C = 700
+    _say("[ec] constant column (radix path)")
+    gpu, rep = _run(inp, C)
+    assert gpu["tok"][0].tolist() == list(range(C))
+    _say(f"[ec] constant column: {rep}")
+
+
+def test_ec_long_column_unstaged():
+    """T above the 16384 tokens staged in LDS: the column is read from L2."""
+    inp = make_inputs(CONFIGS["mixtral"].replace(name="ec_long", T=20000, d=256, h=256, E=8), seed=2)
+    C = _C(inp.cfg, 2.0)
+    _say(f"[ec] long column T=20000 C={C}")
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 19999], rng.choice(20000, 200, replace=False)]))
+    gpu, rep = _run(inp, C, rows=rows)
+    _say(f"[ec] long column: {rep}")

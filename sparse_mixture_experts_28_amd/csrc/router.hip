@@ -321,14 +321,15 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(RouterArgs a
 
 // ---- bf16 inputs, d % 256 == 0: logits kernel + selection kernel ----
 //
-// Logits.  A workgroup computes 128 tokens x 64 experts over one of KS
+// Logits.  A workgroup computes 128 tokens x 64 experts (16 when E <= 16) over one of KS
 // contiguous ranges of d (split-K, so that small T or few experts still give
 // ~256 workgroups).  Both operands reach LDS by direct loads (buffer_load ...
 // lds) in 128-deep stages held in a 3-slot ring, so each workgroup reads its
 // x rows and router-weight rows once from L2 (per-wave register loads read
 // the weight once per wave and were bound by L2 requests).  Wave w owns
-// tokens 32 w .. 32 w + 31 x all 64 experts: 2 x 4 blocks of the 16x16x32
-// MFMA, float32 per 256-element chunk of d, chunks added in float64.  Output:
+// tokens 32 w .. 32 w + 31 x all experts of the tile: 2 x (tile / 16) blocks of
+// the 16x16x32 MFMA, float32 per 256-element chunk of d, chunks added in
+// float64.  Output:
 // float64 partial logits [KS][T][Epad]; the selection kernel adds the KS
 // partials in order.
 constexpr uint32_t kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
@@ -345,10 +346,9 @@ struct LogitArgs {
   int T, d, E, Epad, KS;
 };
 
-constexpr int kLgTok = 128, kLgExp = 64, kLgK = 128;   // tile and stage depth
+constexpr int kLgTok = 128, kLgExp = 64, kLgK = 128;   // tile and stage depth (experts: 64, or 16 when E <= 16)
 constexpr int kLgCh = kLgK / 8;                        // 16-byte chunks per stage row
 constexpr int kLgNS = 3;                               // ring slots
-constexpr int kLgLoads = (kLgTok + kLgExp) / 16;       // 1 KB direct loads per wave per stage (12)
 
 // LDS row of 16 chunks (256 bytes): logical chunk c of row r at c ^ (r & 15).
 // Measured with an LDS probe on gfx950, the fragment reads (rows 0..15 of a
@@ -363,19 +363,22 @@ __device__ __forceinline__ void lg_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
+template <int EXP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void router_logits_kernel(LogitArgs a) {
-  constexpr int kStage = (kLgTok + kLgExp) * kLgCh;   // u32x4 per stage (48 KB)
+  constexpr int kStage = (kLgTok + EXP) * kLgCh;     // u32x4 per stage (48 KB at EXP = 64)
+  constexpr int kLgLoads = (kLgTok + EXP) / 16;       // 1 KB direct loads per wave per stage
+  constexpr int kEB = EXP / 16;                       // expert blocks per wave
   __shared__ u32x4 lds[kLgNS * kStage];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int tok0 = blockIdx.x * kLgTok;
-  const int e0 = blockIdx.y * kLgExp;
+  const int e0 = blockIdx.y * EXP;
   const int ks = blockIdx.z;
   const uint32_t rb = static_cast<uint32_t>(a.d) * 2u;   // bytes per row
   const int nrows = min(kLgTok, a.T - tok0);
-  const int nexp = min(kLgExp, a.E - e0);
+  const int nexp = min(EXP, a.E - e0);
   // out-of-range token and expert rows read as zero (buffer range check)
   const __amdgpu_buffer_rsrc_t xs = rsrc(a.x + static_cast<size_t>(tok0) * a.d, static_cast<uint32_t>(nrows) * rb);
   const __amdgpu_buffer_rsrc_t ws = rsrc(a.W + static_cast<size_t>(e0) * a.d, static_cast<uint32_t>(max(nexp, 0)) * rb);
@@ -404,12 +407,12 @@ void router_logits_kernel(LogitArgs a) {
   };
 
   const int rr = lane & 15, cg = lane >> 4;
-  double acc[2][4][4];
-  floatx4 part[2][4];
+  double acc[2][kEB][4];
+  floatx4 part[2][kEB];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int eb = 0; eb < 4; ++eb) {
+    for (int eb = 0; eb < kEB; ++eb) {
       part[tb][eb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[tb][eb][v] = 0.0;
@@ -427,24 +430,24 @@ void router_logits_kernel(LogitArgs a) {
 #pragma unroll
     for (int s = 0; s < kLgK / 32; ++s) {
       const int ch = lgswz(rr, 4 * s + cg);
-      bf16x8 xf[2], wf[4];
+      bf16x8 xf[2], wf[kEB];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
         xf[tb] = __builtin_bit_cast(bf16x8, sa[(32 * wave + 16 * tb + rr) * kLgCh + ch]);
 #pragma unroll
-      for (int eb = 0; eb < 4; ++eb)
+      for (int eb = 0; eb < kEB; ++eb)
         wf[eb] = __builtin_bit_cast(bf16x8, sa[(kLgTok + 16 * eb + rr) * kLgCh + ch]);
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int eb = 0; eb < 4; ++eb)
+        for (int eb = 0; eb < kEB; ++eb)
           part[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[tb], wf[eb], part[tb][eb], 0, 0, 0);
     }
     if (st & 1) {   // a 256-element chunk is complete: add it in float64
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int eb = 0; eb < 4; ++eb) {
+        for (int eb = 0; eb < kEB; ++eb) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[tb][eb][v] += static_cast<double>(part[tb][eb][v]);
           part[tb][eb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -461,7 +464,7 @@ void router_logits_kernel(LogitArgs a) {
       const int t = tok0 + 32 * wave + 16 * tb + 4 * cg + v;
       if (t < a.T) {
 #pragma unroll
-        for (int eb = 0; eb < 4; ++eb) out[static_cast<size_t>(t) * a.Epad + e0 + 16 * eb + rr] = acc[tb][eb][v];
+        for (int eb = 0; eb < kEB; ++eb) out[static_cast<size_t>(t) * a.Epad + e0 + 16 * eb + rr] = acc[tb][eb][v];
       }
     }
 }
@@ -472,9 +475,11 @@ void router_logits_kernel(LogitArgs a) {
 // 4 so that few, wide tiles (small T, many experts) still fill the CUs.
 constexpr int kSelectThreads = kRouterTile * 16;
 
+// The selection of one 64-token tile on 1024 threads (thread = token r =
+// tid / 16, lane c = tid % 16 of its 16-lane group), from the logits lg[nb] of
+// experts nb * 16 + c without the router bias (any value for e >= E).
 template <int NB>
-__global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArgs a, const double* logits, int Epad,
-                                                                       int KS) {
+__device__ __forceinline__ void select_tile(const RouterArgs& a, const double (&lg)[NB], int tile0) {
   __shared__ int32_t s_idx[kRouterTile * MOE_MAX_TOPK];
   __shared__ unsigned long long s_mask[MOE_MAX_EXPERTS];
   __shared__ float s_p[kRouterTile][16 * NB + 1];
@@ -482,7 +487,6 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
 
   const int c = threadIdx.x & 15;
   const int r = threadIdx.x >> 4;          // token within the tile
-  const int tile0 = blockIdx.x * kRouterTile;
   const int t = tile0 + r;
   const bool tok_ok = t < a.T;             // uniform across the 16-lane group
   const int E = a.E, k = a.k;
@@ -493,12 +497,7 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
   for (int nb = 0; nb < NB; ++nb) {
     const int e = nb * 16 + c;
     double l = -INFINITY;
-    if (e < E && tok_ok) {
-      // the split-K partials, added in split order
-      l = logits[static_cast<size_t>(t) * Epad + e];
-      for (int q = 1; q < KS; ++q) l += logits[(static_cast<size_t>(q) * a.T + t) * Epad + e];
-      l += a.b_g ? static_cast<double>(a.b_g[e]) : 0.0;
-    }
+    if (e < E && tok_ok) l = lg[nb] + (a.b_g ? static_cast<double>(a.b_g[e]) : 0.0);
     val[nb] = l;
     m = fmax(m, l);
   }
@@ -577,6 +576,27 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
 }
 
 template <int NB>
+__global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArgs a, const double* logits, int Epad,
+                                                                       int KS) {
+  const int c = threadIdx.x & 15;
+  const int tile0 = blockIdx.x * kRouterTile;
+  const int t = tile0 + (threadIdx.x >> 4);
+  double lg[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int e = nb * 16 + c;
+    double l = 0.0;
+    if (e < a.E && t < a.T) {
+      // the split-K partials, added in split order
+      l = logits[static_cast<size_t>(t) * Epad + e];
+      for (int q = 1; q < KS; ++q) l += logits[(static_cast<size_t>(q) * a.T + t) * Epad + e];
+    }
+    lg[nb] = l;
+  }
+  select_tile<NB>(a, lg, tile0);
+}
+
+template <int NB>
 hipError_t launch_select(const Problem& p, const RouterArgs& a, const double* logits, int Epad, int KS,
                          hipStream_t st) {
   hipLaunchKernelGGL((router_select_kernel<NB>), dim3(p.ntile), dim3(kSelectThreads), 0, st, a, logits, Epad, KS);
@@ -595,12 +615,15 @@ hipError_t launch_nb(const Problem& p, const RouterArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int logit_pad(int E) { return (E + kLgExp - 1) / kLgExp * kLgExp; }
+// expert padding of the logits: one 16-expert tile when E <= 16 (a quarter of
+// the MFMA work and partial-logit traffic of a 64-expert tile), else 64s
+int logit_pad(int E) { return E <= 16 ? 16 : (E + kLgExp - 1) / kLgExp * kLgExp; }
 
 // d is split into KS ranges of whole 256-element chunks so the logits launch
 // has ~256 workgroups (at most 8 splits, at least one chunk each)
 int logit_splits(const Problem& p) {
-  const long long tiles = static_cast<long long>((p.T + kLgTok - 1) / kLgTok) * (logit_pad(p.E) / kLgExp);
+  const int pad = logit_pad(p.E);
+  const long long tiles = static_cast<long long>((p.T + kLgTok - 1) / kLgTok) * (pad / (pad == 16 ? 16 : kLgExp));
   long long ks = (256 + tiles - 1) / tiles;
   if (ks > 8) ks = 8;
   if (ks > p.d / 256) ks = p.d / 256;
@@ -638,8 +661,11 @@ hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const
     la.E = p.E;
     la.Epad = logit_pad(p.E);
     la.KS = logit_splits(p);
-    const dim3 grid((p.T + kLgTok - 1) / kLgTok, la.Epad / kLgExp, la.KS);
-    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, st, la);
+    if (la.Epad == 16)
+      hipLaunchKernelGGL(router_logits_kernel<16>, dim3((p.T + kLgTok - 1) / kLgTok, 1, la.KS), dim3(256), 0, st, la);
+    else
+      hipLaunchKernelGGL(router_logits_kernel<64>, dim3((p.T + kLgTok - 1) / kLgTok, la.Epad / kLgExp, la.KS),
+                         dim3(256), 0, st, la);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (nb <= 1) return launch_select<1>(p, a, la.logits, la.Epad, la.KS, st);

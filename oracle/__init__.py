@@ -2,8 +2,9 @@
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
 leg may import this package.  It shares no code with the HIP library and
-never imports it.  Every function is float64 numpy (``moe_ref``) or pure
-Python (``brute``); see each module's header for the passages it follows.
+never imports it.  Every function is float64 numpy (``moe_ref``, and
+``mxfp8`` for the MXFP8 expert path) or pure Python (``brute``); see each
+module's header for the passages it follows.
 """
 from .moe_ref import (ACTIVATIONS, TIE_EPS, ExpertChoice, ExpertChoiceRef, MoERef, aux_loss, capacity_of,
                       capacity_ranks, expert_choice_capacity, expert_counts, expert_ffn, gelu,

@@ -87,21 +87,35 @@ def block_exponent(amax: float) -> int:
 
 def quantize(a: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """MXFP8 of a [R, K] float64 array (K a multiple of 32) along its rows:
-    codes uint8 [R, K] and E8M0 scale bytes uint8 [R, K/32]."""
+    codes uint8 [R, K] and E8M0 scale bytes uint8 [R, K/32].  The block
+    exponent is floor(log2 amax) - 8 (frexp, exact); each element is
+    v * 2^-s (exact) encoded as e4m3_encode does, elementwise."""
     a = np.asarray(a, dtype=np.float64)
     R, K = a.shape
     if K % BLOCK:
         raise ValueError("K must be a multiple of 32")
-    codes = np.empty((R, K), dtype=np.uint8)
-    scales = np.empty((R, K // BLOCK), dtype=np.uint8)
-    for r in range(R):
-        for b in range(K // BLOCK):
-            blk = a[r, b * BLOCK:(b + 1) * BLOCK]
-            s = block_exponent(float(np.max(np.abs(blk))))
-            scales[r, b] = s + E8M0_BIAS
-            for i, v in enumerate(blk):
-                codes[r, b * BLOCK + i] = e4m3_encode(math.ldexp(float(v), -s))
-    return codes, scales
+    blocks = a.reshape(R, K // BLOCK, BLOCK)
+    amax = np.max(np.abs(blocks), axis=2)
+    _, e = np.frexp(amax)
+    s = np.where(amax > 0, np.clip((e - 1) - E4M3_EMAX, -E8M0_BIAS, E8M0_BIAS), -E8M0_BIAS)
+    y = np.ldexp(blocks, -s[:, :, None]).reshape(R, K)
+    return _encode_array(y), (s + E8M0_BIAS).astype(np.uint8)
+
+
+def _encode_array(y: np.ndarray) -> np.ndarray:
+    """e4m3_encode over an array: the nearest finite value by binary search of
+    the sorted value table, ties to the even code, magnitudes clamped to 448."""
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    hi = np.searchsorted(_POS_VALUES, a)                 # first table value >= a
+    hi_c = np.minimum(hi, len(_POS_VALUES) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _POS_VALUES[lo]
+    dhi = _POS_VALUES[hi_c] - a
+    exact = _POS_VALUES[hi_c] == a
+    pick_lo = (dlo < dhi) | ((dlo == dhi) & (_POS_CODES[lo] % 2 == 0))
+    code = np.where(exact, _POS_CODES[hi_c], np.where(pick_lo, _POS_CODES[lo], _POS_CODES[hi_c]))
+    sign = np.where(np.signbit(y), 0x80, 0).astype(np.uint8)
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:

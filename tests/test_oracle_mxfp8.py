@@ -197,7 +197,16 @@ def check_layer_against_scalar_brute(m=None):
     assert np.allclose(r.out[0], want, rtol=0, atol=1e-12)
 
 
-CHECKS = [check_codec_table, check_encode_against_torch_and_brute, check_block_scale_rule,
+def check_array_encoder_matches_scalar(m=None):
+    m = m or mx
+    pos = sorted(v for v in (m.e4m3_decode(c) for c in range(0x7F)))
+    mids = [(a + b) / 2 for a, b in zip(pos, pos[1:])]
+    rng = np.random.default_rng(25)
+    y = np.concatenate([mids, -np.array(mids), pos, rng.standard_normal(2000) * 100, [500.0, -1e9, 0.0, -0.0]])
+    assert m._encode_array(y).tolist() == [m.e4m3_encode(float(v)) for v in y]
+
+
+CHECKS = [check_array_encoder_matches_scalar, check_codec_table, check_encode_against_torch_and_brute, check_block_scale_rule,
           check_quantize_roundtrip_and_bound, check_quantize_against_brute, check_layer_properties,
           check_layer_against_scalar_brute]
 
@@ -215,8 +224,12 @@ MUTANTS = [
     ("no_clamp", "a = min(abs(v), E4M3_MAX)", "a = abs(v)"),
     ("ties_to_lower", "if dlo < dhi or (dlo == dhi and int(_POS_CODES[lo]) % 2 == 0):", "if dlo <= dhi:"),
     ("ties_to_upper", "if dlo < dhi or (dlo == dhi and int(_POS_CODES[lo]) % 2 == 0):", "if dlo < dhi:"),
-    ("scale_sign", "codes[r, b * BLOCK + i] = e4m3_encode(math.ldexp(float(v), -s))",
-     "codes[r, b * BLOCK + i] = e4m3_encode(math.ldexp(float(v), s))"),
+    ("scale_sign", "y = np.ldexp(blocks, -s[:, :, None]).reshape(R, K)", "y = np.ldexp(blocks, s[:, :, None]).reshape(R, K)"),
+    ("array_ties_to_lower", "pick_lo = (dlo < dhi) | ((dlo == dhi) & (_POS_CODES[lo] % 2 == 0))", "pick_lo = dlo <= dhi"),
+    ("array_sign_dropped", "sign = np.where(np.signbit(y), 0x80, 0).astype(np.uint8)",
+     "sign = np.zeros(y.shape, dtype=np.uint8)"),
+    ("array_ceil_log2", "s = np.where(amax > 0, np.clip((e - 1) - E4M3_EMAX, -E8M0_BIAS, E8M0_BIAS), -E8M0_BIAS)",
+     "s = np.where(amax > 0, np.clip(e - E4M3_EMAX, -E8M0_BIAS, E8M0_BIAS), -E8M0_BIAS)"),
     ("block_16", "BLOCK = 32", "BLOCK = 16"),
     ("bias_126", "E8M0_BIAS = 127", "E8M0_BIAS = 126"),
     ("subnormal_exp", "v = math.ldexp(m / 8.0, -6) if e == 0", "v = math.ldexp(m / 8.0, -7) if e == 0"),

@@ -170,6 +170,41 @@ moe_status_t moe_forward_expert_choice(const void* x, const void* W_g, const voi
                                        int32_t n_shared, void* out, int32_t* ec_token, float* ec_w,
                                        float* aux_loss, const moe_launch_t* launch);
 
+/* ---- MXFP8 expert Linears --------------------------------------------------
+ * Pages: "AI-Research-SKILLs MoE 训练实战…全指南" §9.2 (FP8 quantization for
+ * serving: about 20-30% more throughput than 16-bit, under 1% accuracy loss).
+ * The pages fix no encoding; this library uses the OCP microscaling form MXFP8:
+ *   codes   uint8 [R, K] E4M3 (bias 7, largest finite 448, S.1111.111 NaN)
+ *   scales  uint8 [R, K/32] E8M0: block b of row r is scaled by 2^(byte - 127)
+ * along the contracted dimension K.  Quantizing a block of 32 values v:
+ *   s = floor(log2 max|v|) - 8 (s = -127 for an all-zero block), byte = s + 127,
+ *   code_i = the E4M3 value nearest v_i * 2^-s, ties to even, clamped to +-448.
+ * The layer (W8A8): x is quantized along d, the first Linear's activation
+ * output H along h, the weights are given quantized along their input
+ * dimension; products and sums in float32 on the matrix cores; the router,
+ * biases, combine and outputs are bf16 as in moe_forward.
+ *
+ * bf16 [rows, cols] (cols % 32 == 0, src and codes 16-byte aligned) -> MXFP8,
+ * enqueued on `stream`: for quantizing expert weights. */
+moe_status_t moe_quantize_mxfp8(const void* src, int32_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                                hipStream_t stream);
+
+/* Workspace bytes for moe_forward_mxfp8 (0 if the shape is invalid: bf16 only,
+ * d and h multiples of 256). */
+size_t moe_workspace_bytes_mxfp8(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int32_t n_shared);
+
+/* The layer forward with MXFP8 expert Linears.
+ *   x [T, d], W_g [E, d], b1 [E+S, h] or NULL, b2 [E+S, d] or NULL, out [T, d]: bf16
+ *   W1 [E+S, h, d] codes and W1_scales [E+S, h, d/32]   (quantized along d)
+ *   W2 [E+S, d, h] codes and W2_scales [E+S, d, h/32]   (quantized along h)
+ *   other arguments and launch fields as for moe_forward; launch->dtype must be
+ *   MOE_BF16 (else MOE_ERR_UNSUPPORTED), d and h multiples of 256 (else
+ *   MOE_ERR_UNSUPPORTED); code arrays 16-byte, scale arrays 4-byte aligned. */
+moe_status_t moe_forward_mxfp8(const void* x, const void* W_g, const uint8_t* W1, const uint8_t* W1_scales,
+                               const void* b1, const uint8_t* W2, const uint8_t* W2_scales, const void* b2,
+                               int32_t E, int32_t k, float capacity_factor, int32_t n_shared, void* out,
+                               int32_t* topk_idx, float* topk_w, float* aux_loss, const moe_launch_t* launch);
+
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status_t s);
 

@@ -16,7 +16,8 @@ from typing import Optional, Sequence
 from ._lib import (EXPORTS, LIB_PATH, MOE_ACT_GELU, MOE_ACT_SILU, MOE_BF16, MOE_ERR_ARG, MOE_ERR_HIP,
                    MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_F32, MOE_MAX_EXPERTS, MOE_MAX_SHARED,
                    MOE_MAX_TOPK, MOE_NUM_STAGE_EVENTS, MOE_OK, MoeLaunch, moe_forward, moe_forward_expert_choice,
-                   moe_status_string, moe_workspace_bytes, moe_workspace_bytes_expert_choice)
+                   moe_forward_mxfp8, moe_quantize_mxfp8, moe_status_string, moe_workspace_bytes,
+                   moe_workspace_bytes_expert_choice, moe_workspace_bytes_mxfp8)
 
 ACTIVATIONS = {"gelu": MOE_ACT_GELU, "silu": MOE_ACT_SILU}
 
@@ -192,9 +193,71 @@ def forward_expert_choice(x, W_g, W1, b1, W2, b2, C: int, n_shared: int = 0, b_g
     return ExpertChoiceOutput(out, ec_token, ec_w, aux, zl)
 
 
+def quantize_mxfp8(w):
+    """MXFP8 of a bf16 tensor on the GPU along its last dimension (a multiple of
+    32): returns (codes uint8, same shape; scales uint8, last dimension / 32)."""
+    import torch
+    if w.dtype != torch.bfloat16 or not w.is_cuda or not w.is_contiguous():
+        raise ValueError("quantize_mxfp8 takes a contiguous bf16 tensor on a GPU")
+    cols = w.shape[-1]
+    rows = w.numel() // cols
+    codes = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    scales = torch.empty((*w.shape[:-1], cols // 32), dtype=torch.uint8, device=w.device)
+    st = moe_quantize_mxfp8(w.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(),
+                            torch.cuda.current_stream(w.device).cuda_stream)
+    if st != MOE_OK:
+        raise RuntimeError(moe_status_string(st))
+    return codes, scales
+
+
+def forward_mxfp8(x, W_g, W1, W1s, b1, W2, W2s, b2, k: int, capacity_factor: float = 0.0, n_shared: int = 0,
+                  b_g=None, *, activation: str = "gelu", min_capacity: int = 0,
+                  stage_events: Optional[Sequence] = None, workspace=None) -> MoEOutput:
+    """The layer with MXFP8 expert Linears: x, W_g, biases bf16; W1 / W2 as
+    (codes, scales) from ``quantize_mxfp8`` of [E+S, h, d] / [E+S, d, h]."""
+    import torch
+    if x.dtype != torch.bfloat16:
+        raise ValueError("the MXFP8 layer takes bf16 activations")
+    T, d = x.shape
+    E = W_g.shape[0]
+    h = W1.shape[1]
+    S = n_shared
+    if W1.shape != (E + S, h, d) or W1s.shape != (E + S, h, d // 32) or W2.shape != (E + S, d, h) or \
+            W2s.shape != (E + S, d, h // 32) or W1.dtype != torch.uint8 or W2.dtype != torch.uint8:
+        raise ValueError("inconsistent MXFP8 weight shapes")
+    for t in (x, W_g, W1, W1s, W2, W2s, b1, b2):
+        if t is not None and (not t.is_cuda or t.device != x.device or not t.is_contiguous()):
+            raise ValueError("all tensors must be contiguous on one GPU")
+    dev = x.device
+    nbytes = moe_workspace_bytes_mxfp8(T, d, h, E, k, S)
+    if nbytes == 0:
+        raise RuntimeError("invalid problem shape for moe_workspace_bytes_mxfp8")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((T, d), dtype=x.dtype, device=dev)
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    aux = torch.empty((1,), dtype=torch.float32, device=dev)
+    zl = torch.empty((1,), dtype=torch.float32, device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    kept = torch.empty((E,), dtype=torch.int32, device=dev)
+    slot_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
+    launch, keep = _launch(x, T, d, h, MOE_BF16, b_g, workspace, zl, activation, min_capacity, stage_events)
+    launch.expert_counts, launch.expert_kept, launch.slot_pos = counts.data_ptr(), kept.data_ptr(), slot_pos.data_ptr()
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    status = moe_forward_mxfp8(x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), W1s.data_ptr(), ptr(b1), W2.data_ptr(),
+                               W2s.data_ptr(), ptr(b2), E, k, float(capacity_factor), S, out.data_ptr(),
+                               topk_idx.data_ptr(), topk_w.data_ptr(), aux.data_ptr(), launch)
+    del keep
+    if status != MOE_OK:
+        raise RuntimeError(moe_status_string(status))
+    return MoEOutput(out, topk_idx, topk_w, aux, zl, counts, kept, slot_pos)
+
+
 __all__ = ["forward", "MoEOutput", "moe_forward", "moe_workspace_bytes", "moe_status_string", "MoeLaunch",
            "forward_expert_choice", "ExpertChoiceOutput", "moe_forward_expert_choice",
            "moe_workspace_bytes_expert_choice", "expert_choice_capacity", "STAGES_EXPERT_CHOICE",
+           "quantize_mxfp8", "forward_mxfp8", "moe_quantize_mxfp8", "moe_workspace_bytes_mxfp8", "moe_forward_mxfp8",
            "ACTIVATIONS", "MOE_ACT_GELU", "MOE_ACT_SILU", "MOE_F32", "MOE_BF16", "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
            "MOE_ERR_HIP", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SHARED", "MOE_NUM_STAGE_EVENTS",
            "STAGES", "EXPORTS", "LIB_PATH"]

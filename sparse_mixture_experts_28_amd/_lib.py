@@ -31,7 +31,8 @@ MOE_NUM_STAGE_EVENTS = 7
 
 # names of the C ABI entry points (include/moe.h)
 EXPORTS = ("moe_forward", "moe_workspace_bytes", "moe_status_string", "moe_forward_expert_choice",
-           "moe_workspace_bytes_expert_choice")
+           "moe_workspace_bytes_expert_choice", "moe_quantize_mxfp8", "moe_workspace_bytes_mxfp8",
+           "moe_forward_mxfp8")
 
 
 class MoeLaunch(ctypes.Structure):
@@ -77,6 +78,17 @@ def _load():
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.POINTER(MoeLaunch),
     ]
+    lib.moe_quantize_mxfp8.restype = ctypes.c_int
+    lib.moe_quantize_mxfp8.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_workspace_bytes_mxfp8.restype = ctypes.c_size_t
+    lib.moe_workspace_bytes_mxfp8.argtypes = [ctypes.c_int32] * 6
+    lib.moe_forward_mxfp8.restype = ctypes.c_int
+    lib.moe_forward_mxfp8.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(MoeLaunch),
+    ]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_forward.restype = ctypes.c_int
@@ -116,3 +128,19 @@ def moe_forward_expert_choice(x, W_g, W1, b1, W2, b2, E, C, n_shared, out, ec_to
     """Raw call of the expert-choice entry point: every array argument is a device address (int)."""
     return int(LIB.moe_forward_expert_choice(x, W_g, W1, b1, W2, b2, E, C, n_shared, out, ec_token, ec_w,
                                              aux_loss, ctypes.byref(launch)))
+
+
+def moe_quantize_mxfp8(src, rows: int, cols: int, codes, scales, stream) -> int:
+    """Raw call: bf16 [rows, cols] at device address src -> MXFP8 codes / scales."""
+    return int(LIB.moe_quantize_mxfp8(src, rows, cols, codes, scales, stream))
+
+
+def moe_workspace_bytes_mxfp8(T: int, d: int, h: int, E: int, k: int, n_shared: int) -> int:
+    return int(LIB.moe_workspace_bytes_mxfp8(T, d, h, E, k, n_shared))
+
+
+def moe_forward_mxfp8(x, W_g, W1, W1s, b1, W2, W2s, b2, E, k, capacity_factor, n_shared, out, topk_idx, topk_w,
+                      aux_loss, launch: MoeLaunch) -> int:
+    """Raw call of the MXFP8 entry point: every array argument is a device address (int)."""
+    return int(LIB.moe_forward_mxfp8(x, W_g, W1, W1s, b1, W2, W2s, b2, E, k, capacity_factor, n_shared, out,
+                                     topk_idx, topk_w, aux_loss, ctypes.byref(launch)))

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["router.hip", "permute.hip", "expert_choice.hip", "gemm.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["router.hip", "permute.hip", "expert_choice.hip", "gemm.hip", "mxfp8.hip", "combine.hip", "moe_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [

@@ -25,7 +25,7 @@ size_t elem_bytes(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
 
 struct Layout {
   size_t row_token, hbuf, ybuf, local_rank, tile_hist, p_part, z_part, counts, kept, slot_pos, seg, logits, ec_logits,
-      ec_m, ec_z, ec_pos, part, total;
+      ec_m, ec_z, ec_pos, xq, xq_scales, part, total;
   int part_cap;
 };
 
@@ -55,9 +55,13 @@ Layout layout_of(const Problem& p) {
   L.ec_m = off;       off += align_up(ect * 8);
   L.ec_z = off;       off += align_up(ect * 4);
   L.ec_pos = off;     off += align_up(et * 4);
+  // MXFP8: x's codes and scales (H's go into the hidden buffer, R h + R h / 32 <= R h 2 bytes)
+  const size_t td = p.mx ? static_cast<size_t>(p.T) * p.d : 0;
+  L.xq = off;         off += align_up(td);
+  L.xq_scales = off;  off += align_up(td / 32);
   // sized for the tallest tile: moe_workspace_bytes has no capacity factor,
   // and the tile height moe_forward picks can depend on it
-  L.part_cap = gemm_fast_path(p) ? kGemmPartCap : 0;
+  L.part_cap = gemm_fast_path(p) && !p.mx ? kGemmPartCap : 0;
   L.part = off;       off += align_up(static_cast<size_t>(L.part_cap) * 256 * 256 * 4);
   L.total = off;
   return L;
@@ -89,6 +93,8 @@ Workspace carve_workspace(const Problem& p, void* base, size_t bytes_available, 
   w.ec_m = reinterpret_cast<double*>(b + L.ec_m);
   w.ec_z = reinterpret_cast<float*>(b + L.ec_z);
   w.ec_pos = reinterpret_cast<int32_t*>(b + L.ec_pos);
+  w.xq = reinterpret_cast<uint8_t*>(b + L.xq);
+  w.xq_scales = reinterpret_cast<uint8_t*>(b + L.xq_scales);
   w.part = reinterpret_cast<float*>(b + L.part);
   w.part_cap = L.part_cap;
   w.bytes = L.total;
@@ -120,6 +126,7 @@ Problem make_problem(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int3
   p.S = S;
   p.dtype = dt;
   p.act = act;
+  p.mx = false;
   p.ec_C = 0;
   p.A = T * k;
   p.ntile = (T + kRouterTile - 1) / kRouterTile;
@@ -157,11 +164,32 @@ Problem make_problem_ec(int32_t T, int32_t d, int32_t h, int32_t E, int32_t C, i
   p.S = S;
   p.dtype = dt;
   p.act = act;
+  p.mx = false;
   p.ec_C = C;
   p.A = E * C;
   p.ntile = (T + kRouterTile - 1) / kRouterTile;
   p.cap = C;
   p.gemm_bm = gemm_m_tile(p);
+  return p;
+}
+
+// MXFP8 (bf16 activations, d and h multiples of 256): the MX kernels have
+// 128- and 256-row tiles only and no split tail.
+moe_status_t check_shape_mx(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int32_t S) {
+  const moe_status_t sc = check_shape(T, d, h, E, k, S, MOE_BF16);
+  if (sc != MOE_OK) return sc;
+  if (d % 256 != 0 || h % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long rows = static_cast<long long>(T) * k + static_cast<long long>(S) * T + 256;
+  const long long widest = d > h ? d : h;
+  if (rows * widest >= (1LL << 31) || static_cast<long long>(h) * d >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+Problem make_problem_mx(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int32_t S, float cf, int act,
+                        int32_t min_cap) {
+  Problem p = make_problem(T, d, h, E, k, S, MOE_BF16, cf, act, min_cap);
+  p.mx = true;
+  p.gemm_bm = p.gemm_bm == 256 ? 256 : 128;
   return p;
 }
 
@@ -189,6 +217,76 @@ size_t moe_workspace_bytes(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k
                            moe_dtype_t dtype) {
   if (moe::check_shape(T, d, h, E, k, n_shared, static_cast<int>(dtype)) != MOE_OK) return 0;
   return moe::workspace_bytes(moe::make_problem(T, d, h, E, k, n_shared, dtype, 0.f));
+}
+
+size_t moe_workspace_bytes_mxfp8(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int32_t n_shared) {
+  if (moe::check_shape_mx(T, d, h, E, k, n_shared) != MOE_OK) return 0;
+  return moe::workspace_bytes(moe::make_problem_mx(T, d, h, E, k, n_shared, 0.f, MOE_ACT_GELU, 0));
+}
+
+moe_status_t moe_quantize_mxfp8(const void* src, int32_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                                hipStream_t stream) {
+  using namespace moe;
+  if (!src || !codes || !scales || rows < 1 || cols < 1) return MOE_ERR_ARG;
+  if (cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(src, 16) || !aligned(codes, 16)) return MOE_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  const hipError_t e = launch_mx_quantize(static_cast<const uint16_t*>(src), rows, cols, codes, scales, stream);
+  if (e != hipSuccess) {
+    std::fprintf(stderr, "libmoe: MXFP8 quantize launch failed: %s (%s)\n", hipGetErrorName(e), hipGetErrorString(e));
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status_t moe_forward_mxfp8(const void* x, const void* W_g, const uint8_t* W1, const uint8_t* W1_scales,
+                               const void* b1, const uint8_t* W2, const uint8_t* W2_scales, const void* b2,
+                               int32_t E, int32_t k, float capacity_factor, int32_t n_shared, void* out,
+                               int32_t* topk_idx, float* topk_w, float* aux_loss, const moe_launch_t* launch) {
+  using namespace moe;
+  if (launch == nullptr) return MOE_ERR_ARG;
+  if (!x || !W_g || !W1 || !W1_scales || !W2 || !W2_scales || !out || !topk_idx || !topk_w || !aux_loss)
+    return MOE_ERR_ARG;
+  if (std::isnan(capacity_factor) || launch->min_capacity < 0) return MOE_ERR_ARG;
+  if (launch->activation != MOE_ACT_GELU && launch->activation != MOE_ACT_SILU) return MOE_ERR_UNSUPPORTED;
+  if (launch->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const moe_status_t sc = check_shape_mx(launch->T, launch->d, launch->h, E, k, n_shared);
+  if (sc != MOE_OK) return sc;
+  const void* a16[] = {x, W_g, W1, W2, out, b1, b2};
+  for (const void* q : a16)
+    if (q && !aligned(q, 16)) return MOE_ERR_UNSUPPORTED;
+  const void* a4[] = {W1_scales, W2_scales, topk_idx, topk_w, aux_loss, launch->z_loss, launch->b_g,
+                      launch->expert_counts, launch->expert_kept, launch->slot_pos};
+  for (const void* q : a4)
+    if (q && !aligned(q, 4)) return MOE_ERR_UNSUPPORTED;
+
+  const Problem p = make_problem_mx(launch->T, launch->d, launch->h, E, k, n_shared, capacity_factor,
+                                    launch->activation, launch->min_capacity);
+  bool ok = false;
+  Workspace ws = carve_workspace(p, launch->workspace, launch->workspace_bytes, &ok);
+  if (!ok) return MOE_ERR_WORKSPACE;
+  if (launch->slot_pos) ws.slot_pos = launch->slot_pos;
+  const MxWeights w{W1, W1_scales, b1, W2, W2_scales, b2};
+
+  hipStream_t st = launch->stream;
+  StageCheck check{st, launch->stage_events};
+  (void)hipGetLastError();
+  if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
+  if (!check(launch_router(p, x, W_g, launch->b_g, topk_idx, topk_w, ws, st), "router launch")) return MOE_ERR_HIP;
+  if (!check(launch_scan(p, ws, aux_loss, launch->z_loss, launch->expert_counts, launch->expert_kept, st),
+             "scan launch"))
+    return MOE_ERR_HIP;
+  if (!check(launch_scatter(p, topk_idx, ws, st), "scatter launch")) return MOE_ERR_HIP;
+  // expert phase 1 stage: quantize x, then the first Linear
+  const hipError_t qe = launch_mx_quantize(static_cast<const uint16_t*>(x), p.T, p.d, ws.xq, ws.xq_scales, st);
+  if (qe != hipSuccess) {
+    std::fprintf(stderr, "libmoe: MXFP8 quantize launch failed: %s (%s)\n", hipGetErrorName(qe), hipGetErrorString(qe));
+    return MOE_ERR_HIP;
+  }
+  if (!check(launch_expert_ffn_mx(p, w, ws, 1, st), "expert phase 1 launch")) return MOE_ERR_HIP;
+  if (!check(launch_expert_ffn_mx(p, w, ws, 2, st), "expert phase 2 launch")) return MOE_ERR_HIP;
+  if (!check(launch_combine(p, topk_w, ws, out, st), "combine launch")) return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 size_t moe_workspace_bytes_expert_choice(int32_t T, int32_t d, int32_t h, int32_t E, int32_t C, int32_t n_shared,

@@ -54,6 +54,8 @@ struct Workspace {
   double* ec_m;         // [T]        expert choice: each token's largest logit
   float* ec_z;          // [T]        expert choice: each token's sum of exp(l - m)
   int32_t* ec_pos;      // [E, T]     expert choice: rank of t among e's chosen tokens, -1 if not chosen
+  uint8_t* xq;          // [T, d]     MXFP8: x's E4M3 codes (the hidden buffer then holds H's codes and scales)
+  uint8_t* xq_scales;   // [T, d/32]  MXFP8: x's E8M0 scales
   float* part;          // [part_cap, BM, 256] float32 partial tiles of the grouped GEMM's split tail
   int part_cap;         // partial tiles the buffer holds (0: no split)
   size_t bytes;
@@ -90,6 +92,7 @@ inline size_t seg_table_ints(int nseg, int E) { return static_cast<size_t>(4 * n
 
 struct Problem {
   int T, d, h, E, k, S;
+  bool mx;       // MXFP8 expert Linears
   int ec_C;      // expert choice: tokens per expert (0: token choice, top-k per token)
   int A;         // routed rows: T * k, or E * ec_C under expert choice
   moe_dtype_t dtype;
@@ -121,6 +124,20 @@ hipError_t launch_ec_select(const Problem& p, int32_t* ec_token, float* ec_w, co
                             hipStream_t st);
 hipError_t launch_combine_ec(const Problem& p, const float* ec_w, const Workspace& ws, void* out,
                              hipStream_t st);
+// MXFP8: the caller's pre-quantized expert weights and bf16 biases
+struct MxWeights {
+  const uint8_t* W1;    // [E+S, h, d] E4M3 codes
+  const uint8_t* W1s;   // [E+S, h, d/32] E8M0 scales
+  const void* b1;       // [E+S, h] bf16 or nullptr
+  const uint8_t* W2;    // [E+S, d, h]
+  const uint8_t* W2s;   // [E+S, d, h/32]
+  const void* b2;       // [E+S, d] bf16 or nullptr
+};
+// bf16 [rows, cols] -> MXFP8 codes [rows, cols] and scales [rows, cols/32] (cols % 32 == 0)
+hipError_t launch_mx_quantize(const uint16_t* src, int rows, int cols, uint8_t* codes, uint8_t* scales,
+                              hipStream_t st);
+hipError_t launch_expert_ffn_mx(const Problem& p, const MxWeights& w, const Workspace& ws, int phase,
+                                hipStream_t st);
 
 // Which GEMM kernel serves a problem; the M tile decides the tile prefix.
 bool gemm_fast_path(const Problem& p);

@@ -1,0 +1,453 @@
+// moe_mxfp8: the expert FFNs with MXFP8 operands (OCP microscaling: E4M3
+// elements, one E8M0 power-of-two scale per 32 elements along the
+// contracted dimension) on the gfx950 scaled matrix instruction.
+//
+// Pages: "AI-Research-SKILLs MoE 训练实战…全指南" §9.2 (serving with FP8
+// quantization: vLLM's quantization="fp8", about 20-30% more throughput than
+// 16-bit); the pages fix no encoding, so the OCP MX form is used, which is the
+// FP8 form this part's scaled MFMA consumes directly.
+//
+// Formats.  An MX matrix [R, K] (K a multiple of 128) is uint8 E4M3 codes
+// [R, K] row-major plus uint8 E8M0 scales [R, K / 32] row-major (scale of
+// row r, elements 32 b .. 32 b + 31 is 2^(byte - 127)).  Quantizing a block:
+// s = floor(log2 max|v|) - 8 (-127 for an all-zero block), element =
+// v * 2^-s rounded to the nearest E4M3 value, ties to even, clamped to +-448.
+//
+//   mx_quantize_kernel   bf16 rows -> MX (x at run time; weights through the ABI)
+//   gemm_mx_kernel       phase 1: H = act(xq W1q^T + b1), H written as MX
+//                        phase 2: Y = Hq W2q^T + b2, bf16
+//
+// The scaled 16x16x128 MFMA (measured with probes on gfx950): lane l carries
+// row l % 16 of each operand and, in bytes 0-15, K elements 16 (l / 16) ..
+// +15, in bytes 16-31, K elements 64 + 16 (l / 16) .. +15; the scale of
+// (row r, 32-element block b) comes from lane r + 16 b; the result of
+// mfma(P, Q) puts P's rows at 4 (l / 16) + v and Q's rows at l % 16.  So a
+// lane that reads 16-byte chunks l / 16 and l / 16 + 4 of a 128-byte K stage
+// holds K in memory order, every MX block sits in one hardware block, and the
+// lane's scale is that of its row and block l / 16.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kE4M3Max = 448.f;
+
+// floor(log2 amax) - 8, clamped to [-127, 127]; -127 for amax == 0
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.f)) return -127;
+  const int s = ilogbf(amax) - 8;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// 2^-s as a float for s in [-127, 126] (exact power of two)
+__device__ __forceinline__ float mx_inv_scale(int s) { return __int_as_float((127 - s) << 23); }
+
+// two floats (already scaled) -> two E4M3 codes (round to nearest even) in
+// the low (HI = false) or high half of `old`; the clamp to +-448 first, since
+// the conversion turns magnitudes from 480 up into NaN
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2(float a, float b, uint32_t old) {
+  a = fminf(fmaxf(a, -kE4M3Max), kE4M3Max);
+  b = fminf(fmaxf(b, -kE4M3Max), kE4M3Max);
+  i16x2 o = __builtin_bit_cast(i16x2, old);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, o);
+}
+
+// ------------------------------------------------------------- quantize --
+// One thread per 32-element block of a bf16 row: 64 bytes in, 32 codes and one
+// scale byte out.
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t* __restrict__ src, size_t nblocks,
+                                                          int blocks_per_row, uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  for (size_t b = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; b < nblocks;
+       b += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const u32x4* in = reinterpret_cast<const u32x4*>(src + b * 32);
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = in[i];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        amax = fmaxf(amax, fabsf(__uint_as_float(v[i][j] << 16)));
+        amax = fmaxf(amax, fabsf(__uint_as_float(v[i][j] & 0xffff0000u)));
+      }
+    const int s = mx_exponent(amax);
+    const float inv = mx_inv_scale(s);
+    u32x4 out[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // elements 8 i .. 8 i + 7 -> two code words
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w0 = v[i][2 * h], w1 = v[i][2 * h + 1];
+        uint32_t c = cvt2<false>(__uint_as_float(w0 << 16) * inv, __uint_as_float(w0 & 0xffff0000u) * inv, 0u);
+        c = cvt2<true>(__uint_as_float(w1 << 16) * inv, __uint_as_float(w1 & 0xffff0000u) * inv, c);
+        out[i / 2][(i % 2) * 2 + h] = c;
+      }
+    }
+    u32x4* o = reinterpret_cast<u32x4*>(codes + b * 32);
+    o[0] = out[0];
+    o[1] = out[1];
+    scales[b] = static_cast<uint8_t>(s + 127);
+    (void)blocks_per_row;
+  }
+}
+
+// ---------------------------------------------------------------- GEMM --
+struct MxArgs {
+  const uint8_t* A;        // phase 1: x codes [T, d]; phase 2: H codes [R, h]
+  const uint8_t* As;       // their scales [rows, K / 32]
+  int a_rows;
+  const int32_t* row_token;
+  int a_by_o_off;
+  const uint8_t* W;        // [nseg][N][K] codes
+  const uint8_t* Ws;       // [nseg][N][K / 32] scales
+  const uint16_t* bias;    // [nseg][N] bf16, or nullptr
+  void* C;                 // phase 1: H codes [R, N]; phase 2: Y bf16 [R, N]
+  uint8_t* Cs;             // phase 1: H scales [R, N / 32]
+  const int32_t* seg;
+  int nseg, E, N, K;
+};
+
+constexpr int kMxBN = 256, kMxBK = 128;     // tile columns, K elements (= bytes) per stage
+constexpr int kMxCh = kMxBK / 16;           // 16-byte chunks per stage row
+constexpr int kMxGroupM = 8;
+constexpr int kMxRsrc = 0x00020000;
+
+__device__ __forceinline__ int mx_swz(int row, int c) { return c ^ (row & 7); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           kMxRsrc);
+}
+
+__device__ __forceinline__ void mx_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt 0 only
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int mx_find_segment(const int32_t* tile_start, int nseg, int mt) {
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_start[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int ACT>
+__device__ __forceinline__ float mx_act(float v) {
+  if constexpr (ACT == 1) {   // GELU(erf)
+    return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
+  } else if constexpr (ACT == 2) {   // SiLU
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.44269504088896341f));
+  } else {
+    return v;
+  }
+}
+
+__device__ __forceinline__ uint32_t mx_pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float floatx2 __attribute__((ext_vector_type(2)));
+  const floatx2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// BM x 256 tiles, 128-deep K stages in a 2-slot LDS ring, 4 waves in a 2 x 2
+// grid (wave tile BM/2 x 128 = (BM/32) x 8 blocks of the 16x16x128 MFMA).
+// Codes reach LDS by direct loads (rows of 128 bytes, 16-byte chunks XOR-
+// swizzled by row); the stage's scale dwords (4 blocks of a row) follow them
+// into LDS by 4-byte direct loads, one row per lane.
+template <int ACT, int BM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_mx_kernel(MxArgs g) {
+  constexpr bool kMxOut = ACT != 0;           // phase 1 writes H as MX
+  constexpr int MB = BM / 32;
+  constexpr int NR = MB + 8;                  // code loads per stage per wave (8 rows x 128 B each)
+  constexpr int kStage = (BM + kMxBN) * kMxCh;     // u32x4 of codes per stage
+  constexpr int kScaleStage = BM + kMxBN;          // uint32 of scales per stage
+  __shared__ u32x4 lds[2 * kStage];
+  __shared__ uint32_t lsc[2 * kScaleStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int q = lane >> 4, rr = lane & 15;
+  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
+  const int total_mt = __builtin_amdgcn_readfirstlane(st.tile_start[g.nseg]);
+  const int ntn = g.N / kMxBN;
+  const int total = total_mt * ntn;
+  const int nk = g.K / kMxBK;
+  const uint32_t row_bytes = static_cast<uint32_t>(g.K);
+  const uint32_t srow_bytes = static_cast<uint32_t>(g.K / 32);
+  const int per_xcd = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int dr_row = 8 * wave + (lane >> 3);
+  const int dr_ch = mx_swz(dr_row, lane & 7);
+
+  for (int it = 0;; ++it) {
+    const int L = it * gridDim.x + xcd * per_xcd + slot;
+    if (L >= total) break;
+    int mt, nt;
+    {
+      const int gsz = kMxGroupM * ntn;
+      const int grp = L / gsz;
+      const int first_m = grp * kMxGroupM;
+      const int gm = min(kMxGroupM, total_mt - first_m);
+      const int r = L - grp * gsz;
+      mt = first_m + r % gm;
+      nt = r / gm;
+    }
+    const int s = __builtin_amdgcn_readfirstlane(mx_find_segment(st.tile_start, g.nseg, mt));
+    const int rows = __builtin_amdgcn_readfirstlane(st.rows[s]);
+    const int m0 = (mt - __builtin_amdgcn_readfirstlane(st.tile_start[s])) * BM;
+    const int a_off = __builtin_amdgcn_readfirstlane(g.a_by_o_off ? st.o_off[s] : st.a_off[s]);
+    const int o_off = __builtin_amdgcn_readfirstlane(st.o_off[s]);
+    const bool gather = g.row_token != nullptr && s < g.E;
+    const int n0 = nt * kMxBN;
+    const __amdgpu_buffer_rsrc_t ra = mx_rsrc(g.A, static_cast<uint32_t>(g.a_rows) * row_bytes);
+    const __amdgpu_buffer_rsrc_t ras = mx_rsrc(g.As, static_cast<uint32_t>(g.a_rows) * srow_bytes);
+    const __amdgpu_buffer_rsrc_t rb = mx_rsrc(g.W + static_cast<size_t>(s) * g.N * g.K,
+                                              static_cast<uint32_t>(g.N) * row_bytes);
+    const __amdgpu_buffer_rsrc_t rbs = mx_rsrc(g.Ws + static_cast<size_t>(s) * g.N * (g.K / 32),
+                                               static_cast<uint32_t>(g.N) * srow_bytes);
+    // code loads: load q of wave w fills rows 32 q + 8 w + lane / 8 (A rows, then B rows);
+    // rows past the segment get an offset past the end (the range check reads zero)
+    u32x8 va = {};
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int r = m0 + 32 * i + dr_row;
+      const int arow = r < rows ? (gather ? g.row_token[a_off + r] : a_off + r) : -1;
+      va[i] = arow >= 0 ? static_cast<uint32_t>(arow) * row_bytes + dr_ch * 16 : 0x80000000u;
+    }
+    const uint32_t vb = static_cast<uint32_t>(n0 + dr_row) * row_bytes + dr_ch * 16;
+    // scale loads: 4 bytes (one stage's 4 blocks) per row, one row per lane;
+    // wave w loads the 64-row groups w, w + 4, ... of the BM + 256 stage rows
+    constexpr int kSG = (BM + kMxBN) / 64;            // 64-row groups per stage (6 or 8)
+    constexpr int kSU = (kSG + 3) / 4;                // groups per wave, at most
+    uint32_t vs[kSU];
+#pragma unroll
+    for (int u = 0; u < kSU; ++u) {
+      const int r = 64 * (wave + 4 * u) + lane;       // stage row (>= BM + 256: no load)
+      if (r < BM) {
+        const int rg = m0 + r;
+        const int arow = rg < rows ? (gather ? g.row_token[a_off + rg] : a_off + rg) : -1;
+        vs[u] = arow >= 0 ? static_cast<uint32_t>(arow) * srow_bytes : 0x80000000u;
+      } else {
+        vs[u] = static_cast<uint32_t>(n0 + r - BM) * srow_bytes;
+      }
+    }
+
+    auto issue = [&](int slot_, int t) {
+      u32x4* base = lds + slot_ * kStage + (8 * wave) * kMxCh;
+      const uint32_t kb = static_cast<uint32_t>(t) * kMxBK;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if (i < MB)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(base + 32 * i * kMxCh),
+                                                   16, va[i], kb, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rb, (__attribute__((address_space(3))) void*)(base + (BM + 32 * (i - MB)) * kMxCh), 16, vb,
+              static_cast<uint32_t>(32 * (i - MB)) * row_bytes + kb, 0, 0);
+      }
+      uint32_t* sbase = lsc + slot_ * kScaleStage;
+#pragma unroll
+      for (int u = 0; u < kSU; ++u) {
+        const int r0 = 64 * (wave + 4 * u);
+        if (r0 >= BM + kMxBN) continue;
+        if (r0 < BM)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (__attribute__((address_space(3))) void*)(sbase + r0), 4,
+                                                   vs[u], 4u * t, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (__attribute__((address_space(3))) void*)(sbase + r0), 4,
+                                                   vs[u], 4u * t, 0, 0);
+      }
+    };
+
+    floatx4 acc[MB][8];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    issue(0, 0);
+    for (int t = 0; t < nk; ++t) {
+      const int cur = t & 1;
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0: stage t landed (codes and scales)
+      mx_barrier();                          // ... in every wave; every wave is done with stage t - 1
+      if (t + 1 < nk) issue(cur ^ 1, t + 1);
+      const u32x4* sa = lds + cur * kStage;
+      const uint32_t* ss = lsc + cur * kScaleStage;
+      i32x8 bf[8];
+      int bsc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = BM + wn * 128 + 16 * j + rr;
+        const u32x4 lo = sa[row * kMxCh + mx_swz(row, q)];
+        const u32x4 hi = sa[row * kMxCh + mx_swz(row, q + 4)];
+        bf[j] = __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        bsc[j] = static_cast<int>((ss[row] >> (8 * q)) & 0xffu);
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int row = wm * (BM / 2) + 16 * i + rr;
+        const u32x4 lo = sa[row * kMxCh + mx_swz(row, q)];
+        const u32x4 hi = sa[row * kMxCh + mx_swz(row, q + 4)];
+        const i32x8 af = __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        const int asc = static_cast<int>((ss[row] >> (8 * q)) & 0xffu);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, bsc[j], 0, asc);
+      }
+    }
+    mx_barrier();   // the next tile's loads reuse the ring
+
+    // Epilogue: lane (rr, q) holds, for block (i, j), row 16 i + rr of the wave
+    // tile and columns 16 j + 4 q .. + 3.
+    const int cbase = n0 + wn * 128 + 4 * q;
+    uint2 bq[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      bq[j] = g.bias ? *reinterpret_cast<const uint2*>(g.bias + static_cast<size_t>(s) * g.N + cbase + 16 * j)
+                     : make_uint2(0u, 0u);
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int rl = m0 + wm * (BM / 2) + 16 * i + rr;
+      const bool ok = rl < rows;
+      float v[8][4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[j][0] = mx_act<ACT>(acc[i][j][0] + __uint_as_float(bq[j].x << 16));
+        v[j][1] = mx_act<ACT>(acc[i][j][1] + __uint_as_float(bq[j].x & 0xffff0000u));
+        v[j][2] = mx_act<ACT>(acc[i][j][2] + __uint_as_float(bq[j].y << 16));
+        v[j][3] = mx_act<ACT>(acc[i][j][3] + __uint_as_float(bq[j].y & 0xffff0000u));
+      }
+      if constexpr (kMxOut) {
+        // MX blocks of 32 columns: j pair (2 c, 2 c + 1) x the 4 lanes q of the row
+        uint8_t* crow = static_cast<uint8_t*>(g.C) + static_cast<size_t>(o_off + (ok ? rl : 0)) * g.N;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float am = 0.f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) am = fmaxf(am, fabsf(v[2 * c + h][e]));
+          am = fmaxf(am, __shfl_xor(am, 16));
+          am = fmaxf(am, __shfl_xor(am, 32));
+          const int sx = mx_exponent(am);
+          const float inv = mx_inv_scale(sx);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int j = 2 * c + h;
+            uint32_t w = cvt2<false>(v[j][0] * inv, v[j][1] * inv, 0u);
+            w = cvt2<true>(v[j][2] * inv, v[j][3] * inv, w);
+            if (ok) *reinterpret_cast<uint32_t*>(crow + cbase + 16 * j) = w;
+          }
+          if (ok && q == 0)
+            g.Cs[static_cast<size_t>(o_off + rl) * (g.N / 32) + (n0 + wn * 128) / 32 + c] = static_cast<uint8_t>(sx + 127);
+        }
+      } else {
+        if (ok) {
+          uint16_t* crow = static_cast<uint16_t*>(g.C) + static_cast<size_t>(o_off + rl) * g.N + cbase;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<uint2*>(crow + 16 * j) =
+                make_uint2(mx_pack_bf16x2(v[j][0], v[j][1]), mx_pack_bf16x2(v[j][2], v[j][3]));
+        }
+      }
+    }
+  }
+}
+
+int mx_num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+}  // namespace
+
+hipError_t launch_mx_quantize(const uint16_t* src, int rows, int cols, uint8_t* codes, uint8_t* scales,
+                              hipStream_t st) {
+  const size_t nblocks = static_cast<size_t>(rows) * (cols / 32);
+  if (nblocks == 0) return hipSuccess;
+  size_t grid = (nblocks + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(mx_quantize_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, src, nblocks, cols / 32,
+                     codes, scales);
+  return hipGetLastError();
+}
+
+// Phase 1: A = x as MX (xq codes / scales), output H as MX in the hidden
+// buffer (codes [R, h], then scales [R, h / 32]); phase 2: A = H, output Y bf16.
+hipError_t launch_expert_ffn_mx(const Problem& p, const MxWeights& w, const Workspace& ws, int phase,
+                                hipStream_t st) {
+  MxArgs g;
+  g.seg = ws.seg;
+  g.nseg = p.E + p.S;
+  g.E = p.E;
+  const size_t R = static_cast<size_t>(p.A) + static_cast<size_t>(p.S) * p.T;
+  uint8_t* hcodes = static_cast<uint8_t*>(ws.hbuf);
+  uint8_t* hscales = hcodes + R * p.h;
+  if (phase == 1) {
+    g.A = ws.xq;
+    g.As = ws.xq_scales;
+    g.a_rows = p.T;
+    g.row_token = ws.row_token;
+    g.a_by_o_off = 0;
+    g.W = w.W1;
+    g.Ws = w.W1s;
+    g.bias = static_cast<const uint16_t*>(w.b1);
+    g.C = hcodes;
+    g.Cs = hscales;
+    g.N = p.h;
+    g.K = p.d;
+  } else {
+    g.A = hcodes;
+    g.As = hscales;
+    g.a_rows = static_cast<int>(R);
+    g.row_token = nullptr;
+    g.a_by_o_off = 1;
+    g.W = w.W2;
+    g.Ws = w.W2s;
+    g.bias = static_cast<const uint16_t*>(w.b2);
+    g.C = ws.ybuf;
+    g.Cs = nullptr;
+    g.N = p.d;
+    g.K = p.h;
+  }
+  int grid = mx_num_cus();
+  grid = (grid + 7) / 8 * 8;
+  const int act = phase == 2 ? 0 : (p.act == MOE_ACT_SILU ? 2 : 1);
+#define MOE_MX_LAUNCH(ACT_, BM_) hipLaunchKernelGGL((gemm_mx_kernel<ACT_, BM_>), dim3(grid), dim3(256), 0, st, g)
+  if (p.gemm_bm == 256) {
+    if (act == 1) MOE_MX_LAUNCH(1, 256);
+    else if (act == 2) MOE_MX_LAUNCH(2, 256);
+    else MOE_MX_LAUNCH(0, 256);
+  } else {
+    if (act == 1) MOE_MX_LAUNCH(1, 128);
+    else if (act == 2) MOE_MX_LAUNCH(2, 128);
+    else MOE_MX_LAUNCH(0, 128);
+  }
+#undef MOE_MX_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace moe

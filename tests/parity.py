@@ -188,3 +188,72 @@ def compare_ec(inp, C: int, gpu: dict, stacked=None, rows=None, check_out=True) 
         assert np.all(np.isfinite(go))
         assert rel <= TOL[c.dtype], f"output max-abs error {err} = {rel:.3e} of max|ref| {scale} (tol {TOL[c.dtype]})"
     return report
+
+
+# ------------------------------------------------------------------- MXFP8 --
+def to_bf16_device(a: np.ndarray, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def run_gpu_mx(inp, dev="cuda:0", stacked=None, workspace=None):
+    """bf16 workload -> weights quantized on the GPU by the library -> the MXFP8
+    layer.  Returns the numpy results of compare() plus the weight codes and
+    scales the GPU produced."""
+    import torch
+    import sparse_mixture_experts_28_amd as moe
+    c = inp.cfg
+    assert c.dtype == "bf16"
+    W1, b1, W2, b2 = stacked if stacked is not None else inp.stacked()
+    x, W_g = to_bf16_device(inp.x, dev), to_bf16_device(inp.W_g, dev)
+    W1d, W2d = to_bf16_device(W1, dev), to_bf16_device(W2, dev)
+    b1d = None if b1 is None else to_bf16_device(b1, dev)
+    b2d = None if b2 is None else to_bf16_device(b2, dev)
+    W1c, W1s = moe.quantize_mxfp8(W1d)
+    W2c, W2s = moe.quantize_mxfp8(W2d)
+    b_g = None if inp.b_g is None else torch.from_numpy(inp.b_g).to(dev)
+    r = moe.forward_mxfp8(x, W_g, W1c, W1s, b1d, W2c, W2s, b2d, k=c.k, capacity_factor=c.cf, n_shared=c.S, b_g=b_g,
+                          activation=c.activation, min_capacity=c.min_capacity, workspace=workspace)
+    torch.cuda.synchronize()
+    res = dict(out=r.out.float().cpu().numpy().astype(np.float64), idx=r.topk_idx.cpu().numpy().astype(np.int64),
+               w=r.topk_w.cpu().numpy().astype(np.float64), aux=float(r.aux_loss.cpu().numpy()[0]),
+               z=float(r.z_loss.cpu().numpy()[0]), counts=r.expert_counts.cpu().numpy().astype(np.int64),
+               kept=r.expert_kept.cpu().numpy().astype(np.int64), slot_pos=r.slot_pos.cpu().numpy().astype(np.int64))
+    res["W1q"] = (W1c.cpu().numpy(), W1s.cpu().numpy())
+    res["W2q"] = (W2c.cpu().numpy(), W2s.cpu().numpy())
+    return res
+
+
+def compare_mx(inp, gpu: dict, stacked=None, rows=None) -> dict:
+    """MXFP8 parity: routing, weights, counts, capacity, aux and z-loss by the
+    rules of compare(); the GPU's weight codes and scales bit-exact against the
+    oracle's quantization of the same bf16 weights; outputs against the MXFP8
+    oracle (oracle.mxfp8) within the bf16 tolerance.  The GPU forms H in
+    float32 before quantizing it, so an element near a rounding boundary of
+    E4M3 can take the neighbouring code: one code step is at most 1/8 of that
+    element, and such flips are rare and of random sign, far inside 2e-2."""
+    from oracle import mxfp8
+    c = inp.cfg
+    rep = compare(inp, gpu, stacked=stacked, rows=rows, check_out=False)
+    W1, b1, W2, b2 = stacked if stacked is not None else inp.stacked()
+    n = c.E + c.S
+    W1c, W1s = mxfp8.quantize(ref.widen(W1, "bf16").reshape(n * c.h, c.d))
+    W2c, W2s = mxfp8.quantize(ref.widen(W2, "bf16").reshape(n * c.d, c.h))
+    assert np.array_equal(gpu["W1q"][0].reshape(n * c.h, c.d), W1c), "W1 codes differ"
+    assert np.array_equal(gpu["W1q"][1].reshape(n * c.h, c.d // 32), W1s), "W1 scales differ"
+    assert np.array_equal(gpu["W2q"][0].reshape(n * c.d, c.h), W2c), "W2 codes differ"
+    assert np.array_equal(gpu["W2q"][1].reshape(n * c.d, c.h // 32), W2s), "W2 scales differ"
+    W1c, W1s = W1c.reshape(n, c.h, c.d), W1s.reshape(n, c.h, c.d // 32)
+    W2c, W2s = W2c.reshape(n, c.d, c.h), W2s.reshape(n, c.d, c.h // 32)
+    eq = lambda e: (W1c[e], W1s[e], None if b1 is None else b1[e], W2c[e], W2s[e], None if b2 is None else b2[e])
+    r = mxfp8.moe_forward_mxfp8_ref(inp.x, inp.W_g, eq, c.E, c.k, float(np.float32(c.cf)), c.S, inp.b_g,
+                                    kind="bf16", rows=rows, override_idx=gpu["idx"] if rep["rerun"] else None,
+                                    activation=c.activation, min_capacity=c.min_capacity)
+    go = gpu["out"] if rows is None else gpu["out"][np.asarray(rows)]
+    scale = float(np.max(np.abs(r.out)))
+    err = float(np.max(np.abs(go - r.out)))
+    rel = err / scale if scale > 0 else err
+    rep.update(out_rel=rel, out_scale=scale)
+    assert np.all(np.isfinite(go))
+    assert rel <= TOL["bf16"], f"MXFP8 output max-abs error {err} = {rel:.3e} of max|ref| {scale}"
+    return rep

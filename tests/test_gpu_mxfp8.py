@@ -1,0 +1,82 @@
+"""The MXFP8 expert path on the GPU vs the CPU oracle (oracle/mxfp8.py),
+through the C ABI: the quantizer bit-exact on chosen and random inputs, and
+the layer on reduced shapes (both tile heights, shared experts, capacity
+drops, the Mixtral expert form, one token) and the Mixtral-shaped workload
+at full size with sampled output rows."""
+import sys
+
+import numpy as np
+import pytest
+
+from synthetic import CONFIGS, make_inputs
+from synthetic.gen import f32_to_bf16_bits
+from tests.parity import compare_mx, run_gpu_mx, to_bf16_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_mixture_experts_28_amd  # noqa: F401
+    yield
+
+
+def test_quantizer_bit_exact():
+    import sparse_mixture_experts_28_amd as moe
+    from oracle import mxfp8
+    rng = np.random.default_rng(30)
+    a = (rng.standard_normal((64, 256)) * np.exp(rng.standard_normal((64, 1)) * 3)).astype(np.float32)
+    a[0, :32] = 0.0                                   # an all-zero block
+    a[1, :32] = 448.0                                 # block maximum exactly 448: scale 1
+    a[2, :32] = 2.0 ** -130                           # bf16 subnormals
+    a[3, 5] = 1e30                                    # a huge element
+    pos = sorted(v for v in (mxfp8.e4m3_decode(c) for c in range(0x7F)))
+    mids = np.array([(p + q) / 2 for p, q in zip(pos, pos[1:])][-32:], dtype=np.float32)
+    a[4, :32] = mids                                  # ties between codes (scale 1: max in [256, 448])
+    bits = f32_to_bf16_bits(a)
+    _say("[mx] quantizer")
+    codes, scales = moe.quantize_mxfp8(to_bf16_device(bits, "cuda:0"))
+    wc, ws = mxfp8.quantize(bits.astype(np.uint32).__lshift__(16).view(np.float32).astype(np.float64))
+    assert np.array_equal(scales.cpu().numpy(), ws)
+    assert np.array_equal(codes.cpu().numpy(), wc)
+
+
+REDUCED = {
+    "mx_bm256": ("mixtral", dict(T=2100, d=256, h=512, E=4)),
+    "mx_T600": ("mixtral", dict(T=600, d=512, h=1024)),
+    "mx_shared_fine": ("deepseek", dict(T=512, d=256, h=512, E=32, k=8, S=1)),
+    "mx_capacity": ("glam", dict(T=1000, d=256, h=512, E=16)),
+    "mx_silu_nobias": ("mixtral", dict(T=600, d=512, h=1024, activation="silu", expert_bias=False)),
+    "mx_single_token": ("mixtral", dict(T=1, d=256, h=256, E=8)),
+    "mx_deep_K": ("mixtral", dict(T=512, d=2048, h=512, E=4)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(REDUCED))
+def test_mx_reduced(case):
+    base, kw = REDUCED[case]
+    inp = make_inputs(CONFIGS[base].replace(name=case, **kw), seed=0)
+    c = inp.cfg
+    _say(f"[mx] {case}: T={c.T} d={c.d} h={c.h} E={c.E} k={c.k} S={c.S} cf={c.cf} {c.activation}")
+    stacked = inp.stacked()
+    rep = compare_mx(inp, run_gpu_mx(inp, stacked=stacked), stacked=stacked)
+    _say(f"[mx] {case}: {rep}")
+
+
+def test_mx_full_size_mixtral():
+    inp = make_inputs("mixtral", seed=0)
+    c = inp.cfg
+    _say(f"[mx-full] mixtral T={c.T} d={c.d} h={c.h}")
+    stacked = inp.stacked()
+    rng = np.random.default_rng(99)
+    rows = np.unique(np.concatenate([[0, c.T - 1], rng.choice(c.T, 14, replace=False)]))
+    rep = compare_mx(inp, run_gpu_mx(inp, stacked=stacked), stacked=stacked, rows=rows)
+    _say(f"[mx-full] mixtral: {rep}")

@@ -3,7 +3,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload mixtral] [--no-cpu-baseline]
                     [--activation gelu|silu] [--no-expert-bias] [--min-capacity N]
-                    [--routing top-k|expert-choice]
+                    [--routing top-k|expert-choice] [--mxfp8]
 
 A step is one full layer forward (router, scan, scatter, expert phase 1,
 expert phase 2, combine) over one batch of seeded synthetic tokens already
@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer fwd tokens/s + % bf16 MFMA peak, Mixtral-shape E=8 top-2"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_28_amd", "csrc", "gemm.hip")
@@ -53,6 +54,8 @@ def parse():
                     help="expert activation (silu with --no-expert-bias: the Mixtral expert form)")
     ap.add_argument("--no-expert-bias", action="store_true", help="bias-free expert Linears (NULL b1, b2)")
     ap.add_argument("--min-capacity", type=int, default=0, help="capacity floor (with a capacity factor)")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="MXFP8 expert Linears (weights quantized on the GPU before the timed steps)")
     ap.add_argument("--routing", default="top-k", choices=["top-k", "expert-choice"],
                     help="expert-choice: each expert takes C = ceil(k T / E) tokens (the rows top-k routing makes)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -85,7 +88,7 @@ def measured_traffic(workload: str, phase: str):
     return entry[phase]["fetch_bytes"] + entry[phase]["write_bytes"]
 
 
-def cpu_baseline(inp, stacked, ntok: int, ec: bool = False):
+def cpu_baseline(inp, stacked, ntok: int, ec: bool = False, mx: bool = False):
     from threadpoolctl import threadpool_info
 
     import oracle
@@ -95,7 +98,19 @@ def cpu_baseline(inp, stacked, ntok: int, ec: bool = False):
     x = inp.x[:ntok]
     get = lambda e: (W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e])
     t0 = time.perf_counter()
-    if ec:
+    if mx:
+        from oracle import mxfp8
+        ntok = min(ntok, 1024)
+        x = inp.x[:ntok]
+
+        def eq(e):   # the oracle quantizes each expert's weights itself (timed: it is oracle work)
+            W1q = mxfp8.quantize(oracle.widen(W1[e], "bf16"))
+            W2q = mxfp8.quantize(oracle.widen(W2[e], "bf16"))
+            return (*W1q, None if b1 is None else b1[e], *W2q, None if b2 is None else b2[e])
+        t0 = time.perf_counter()
+        mxfp8.moe_forward_mxfp8_ref(x, inp.W_g, eq, c.E, c.k, float(np.float32(c.cf)), c.S, inp.b_g, kind=c.dtype,
+                                    activation=c.activation, min_capacity=c.min_capacity)
+    elif ec:
         oracle.moe_forward_expert_choice_ref(x, inp.W_g, get, c.E, min(ntok, -(-c.k * ntok // c.E)), c.S, inp.b_g,
                                              kind=c.dtype, activation=c.activation)
     else:
@@ -142,8 +157,17 @@ def main():
     dt_code = moe.MOE_BF16 if c.dtype == "bf16" else moe.MOE_F32
     T, d, h, E, k, S = c.T, c.d, c.h, c.E, c.k, c.S
     ec = args.routing == "expert-choice"
+    mx = args.mxfp8
+    if mx and (ec or c.dtype != "bf16"):
+        raise SystemExit("--mxfp8 runs the bf16 workloads with top-k routing")
     C = min(T, -(-k * T // E))
-    if ec:
+    if mx:
+        nbytes = moe.moe_workspace_bytes_mxfp8(T, d, h, E, k, S)
+        W1c, W1s = moe.quantize_mxfp8(W1)
+        W2c, W2s = moe.quantize_mxfp8(W2)
+        torch.cuda.synchronize()
+        del W1, W2
+    elif ec:
         nbytes = moe.moe_workspace_bytes_expert_choice(T, d, h, E, C, S, dt_code)
         ec_token = torch.empty((E, C), dtype=torch.int32, device=dev)
         ec_w = torch.empty((E, C), dtype=torch.float32, device=dev)
@@ -177,11 +201,18 @@ def main():
             e.record(stream)          # creates the handle
     ev_arrays = [(ctypes.c_void_p * nst)(*[int(e.cuda_event) for e in row]) for row in events]
     ptr = lambda t: None if t is None else t.data_ptr()
-    ptrs = (x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), ptr(b1), W2.data_ptr(), ptr(b2))
+    if mx:
+        ptrs = (x.data_ptr(), W_g.data_ptr(), W1c.data_ptr(), W1s.data_ptr(), ptr(b1), W2c.data_ptr(), W2s.data_ptr(),
+                ptr(b2))
+    else:
+        ptrs = (x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), ptr(b1), W2.data_ptr(), ptr(b2))
 
     def step(ev=None):
         launch.stage_events = None if ev is None else ctypes.cast(ev, ctypes.c_void_p)
-        if ec:
+        if mx:
+            st = moe.moe_forward_mxfp8(*ptrs, E, k, float(c.cf), S, out.data_ptr(), topk_idx.data_ptr(),
+                                       topk_w.data_ptr(), aux.data_ptr(), launch)
+        elif ec:
             st = moe.moe_forward_expert_choice(*ptrs, E, C, S, out.data_ptr(), ec_token.data_ptr(),
                                                ec_w.data_ptr(), aux.data_ptr(), launch)
         else:
@@ -230,6 +261,11 @@ def main():
     # rows), H written once / read once, Y written once
     bytes_gemm1 = active * h * d * s + T * d * s + rows * h * s
     bytes_gemm2 = active * h * d * s + rows * (h + d) * s
+    if mx:
+        # codes 1 byte plus one scale byte per 32 elements for the weights, x and H
+        q = 33.0 / 32.0
+        bytes_gemm1 = active * h * d * q + T * d * q + rows * h * q
+        bytes_gemm2 = active * h * d * q + rows * h * q + rows * d * 2
 
     def gbs(b, ms):
         return b / (ms * 1e-3) / 1e9
@@ -255,7 +291,8 @@ def main():
     if c.dtype == "f32":
         roof = {"bound": "alu", "achieved": tfs(gemm_flops, dom_ms), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
     elif args.workload == "mixtral":
-        roof = {"bound": "mfma", "achieved": tfs(gemm_flops, dom_ms), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        roof = {"bound": "mfma", "achieved": tfs(gemm_flops, dom_ms),
+                "peak": PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     else:   # fine-grained experts stream their weights: HBM-bound
         roof = {"bound": "hbm", "achieved": gbs(dom_bytes, dom_ms), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
@@ -263,6 +300,10 @@ def main():
     roof["kernel"] = f"gemm ({dom})"
     gemm_ms = stages["expert_phase1"] + stages["expert_phase2"]
     roof["gemm_both_phases_frac_of_bf16_peak"] = tfs(2 * gemm_flops, gemm_ms) / PEAK_BF16_TFLOPS
+    if mx:
+        roof["gemm_both_phases_frac_of_fp8_peak"] = tfs(2 * gemm_flops, gemm_ms) / PEAK_FP8_TFLOPS
+        traffic = None   # the committed counter runs cover the bf16 kernels
+        roof["traffic"] = None
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -273,6 +314,8 @@ def main():
         log("copy calibration: 3 x 1 GiB device copies done")
 
     variant = f", expert-choice routing C={C} tokens per expert" if ec else ""
+    if mx:
+        variant += ", MXFP8 expert Linears (E4M3, E8M0 scale per 32)"
     if c.activation != "gelu" or not c.expert_bias or c.min_capacity:
         variant += (f", {c.activation} experts" + ("" if c.expert_bias else " without bias") +
                     (f", min_capacity={c.min_capacity}" if c.min_capacity else ""))
@@ -287,7 +330,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": c.dtype,
+        "dtype": "mxfp8" if mx else c.dtype,
         "data": "synthetic (seeded normal inputs and random-init weights of the named shapes)",
         "config": {"workload": f"{args.workload}-shaped MoE layer: T={T} d={d} h={h} E={E} k={k} shared={S} "
                                f"capacity_factor={c.cf} {c.dtype}" + variant,
@@ -304,7 +347,7 @@ def main():
     if not args.no_cpu_baseline:
         ntok = args.cpu_tokens or CPU_SAMPLE_TOKENS[args.workload]
         log(f"cpu baseline: oracle on {ntok} tokens")
-        result["cpu_baseline"] = cpu_baseline(inp, stacked, ntok, ec)
+        result["cpu_baseline"] = cpu_baseline(inp, stacked, ntok, ec, mx)
     print(json.dumps(result), flush=True)
 
 

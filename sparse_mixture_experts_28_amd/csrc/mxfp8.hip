@@ -167,21 +167,41 @@ __device__ __forceinline__ uint32_t mx_pack_bf16x2(float lo, float hi) {
 // grid (wave tile BM/2 x 128 = (BM/32) x 8 blocks of the 16x16x128 MFMA).
 // Codes reach LDS by direct loads (rows of 128 bytes, 16-byte chunks XOR-
 // swizzled by row); the stage's scale dwords (4 blocks of a row) follow them
-// into LDS by 4-byte direct loads, one row per lane.
+// into LDS by 4-byte direct loads, one row per lane.  A lane's scale operand
+// is read straight from LDS as the byte of its row and block.
+//
+// A fragment is 32 bytes a lane, so one stage's fragments (A and B) fill 128
+// vector registers and cannot be double-buffered whole.  K step t runs its
+// MFMAs in two halves (A rows 0 .. MB/2-1, then the rest), every MFMA followed
+// by at most one fragment read and one direct load, in a fixed order:
+//   half 0: MFMAs; read A rows 2 .. MB-1 of stage t
+//   wait for stage t+1 and the barrier that publishes it; stage t is then in
+//   registers in every wave, so its slot takes stage t+2
+//   half 1: MFMAs, B block outermost; read A rows 0, 1 of stage t+1, and its
+//           B block j as soon as block j of stage t is done; direct loads of
+//           stage t+2
+// so the next stage's B fragments reuse the registers of this stage's, and
+// arrive, with its first two A rows, while this stage's last rows multiply.
 template <int ACT, int BM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_mx_kernel(MxArgs g) {
   constexpr bool kMxOut = ACT != 0;           // phase 1 writes H as MX
-  constexpr int MB = BM / 32;
+  constexpr int MB = BM / 32;                 // 16-row A blocks per wave
+  constexpr int HM = MB / 2 * 8;              // MFMAs per half step
   constexpr int NR = MB + 8;                  // code loads per stage per wave (8 rows x 128 B each)
   constexpr int kStage = (BM + kMxBN) * kMxCh;     // u32x4 of codes per stage
-  constexpr int kScaleStage = BM + kMxBN;          // uint32 of scales per stage
-  __shared__ u32x4 lds[2 * kStage];
-  __shared__ uint32_t lsc[2 * kScaleStage];
+  constexpr int kScaleStage = 2 * kMxBN;           // uint32 of scales per stage: A rows (up to 256), B rows
+  constexpr int ND = NR + 2;                        // direct loads per stage per wave
+  constexpr int NF1 = MB - 2;                       // fragment reads in half 0
+  static_assert(HM >= 2 * NF1 && HM >= ND, "half step too short for its reads and loads");
+  // one LDS object (A code slots, B code slots, then the scale slots), so the
+  // waits the compiler places for direct loads are the ones written below
+  constexpr int kScaleBase = 2 * kStage;                  // u32x4 index of the scale slots
+  __shared__ u32x4 lds[2 * kStage + 2 * kScaleStage / 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: picks descriptors and LDS rows
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 4, rr = lane & 15;
   const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
@@ -195,6 +215,19 @@ void gemm_mx_kernel(MxArgs g) {
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int dr_row = 8 * wave + (lane >> 3);
   const int dr_ch = mx_swz(dr_row, lane & 7);
+  const uint8_t* l8 = reinterpret_cast<const uint8_t*>(lds);
+  // LDS ring: A slots 0, 1 (BM rows each), then B slots 0, 1 (256 rows each),
+  // so every fragment read is one of four lane bases plus an offset under 64 KB
+  // that the read instruction carries.  The bases are hidden from the optimizer
+  // so that it keeps one register each rather than one per offset.
+  constexpr int kASlot = BM * kMxCh, kBSlot = kMxBN * kMxCh;   // u32x4 per slot
+  int a_lo = (wm * (BM / 2) + rr) * kMxCh + mx_swz(rr, q);
+  int a_hi = (wm * (BM / 2) + rr) * kMxCh + mx_swz(rr, q + 4);
+  int b_lo = 2 * kASlot + (wn * 128 + rr) * kMxCh + mx_swz(rr, q);
+  int b_hi = 2 * kASlot + (wn * 128 + rr) * kMxCh + mx_swz(rr, q + 4);
+  int sa_b = kScaleBase * 16 + (wm * (BM / 2) + rr) * 4 + q;
+  int sb_b = kScaleBase * 16 + (kMxBN + wn * 128 + rr) * 4 + q;
+  __asm__ volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi), "+v"(sa_b), "+v"(sb_b));
 
   for (int it = 0;; ++it) {
     const int L = it * gridDim.x + xcd * per_xcd + slot;
@@ -222,7 +255,7 @@ void gemm_mx_kernel(MxArgs g) {
                                               static_cast<uint32_t>(g.N) * row_bytes);
     const __amdgpu_buffer_rsrc_t rbs = mx_rsrc(g.Ws + static_cast<size_t>(s) * g.N * (g.K / 32),
                                                static_cast<uint32_t>(g.N) * srow_bytes);
-    // code loads: load q of wave w fills rows 32 q + 8 w + lane / 8 (A rows, then B rows);
+    // code loads: load n of wave w fills rows 32 n + 8 w + lane / 8 (A rows, then B rows);
     // rows past the segment get an offset past the end (the range check reads zero)
     u32x8 va = {};
 #pragma unroll
@@ -233,47 +266,64 @@ void gemm_mx_kernel(MxArgs g) {
     }
     const uint32_t vb = static_cast<uint32_t>(n0 + dr_row) * row_bytes + dr_ch * 16;
     // scale loads: 4 bytes (one stage's 4 blocks) per row, one row per lane;
-    // wave w loads the 64-row groups w, w + 4, ... of the BM + 256 stage rows
-    constexpr int kSG = (BM + kMxBN) / 64;            // 64-row groups per stage (6 or 8)
-    constexpr int kSU = (kSG + 3) / 4;                // groups per wave, at most
-    uint32_t vs[kSU];
-#pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      const int r = 64 * (wave + 4 * u) + lane;       // stage row (>= BM + 256: no load)
-      if (r < BM) {
-        const int rg = m0 + r;
-        const int arow = rg < rows ? (gather ? g.row_token[a_off + rg] : a_off + rg) : -1;
-        vs[u] = arow >= 0 ? static_cast<uint32_t>(arow) * srow_bytes : 0x80000000u;
-      } else {
-        vs[u] = static_cast<uint32_t>(n0 + r - BM) * srow_bytes;
-      }
+    // wave w loads A rows 64 w .. 64 w + 63 (rows from BM on, and past the
+    // segment, read zero) and B rows 64 w .. 64 w + 63, with no branch
+    uint32_t vs_a, vs_b;
+    {
+      const int r = 64 * wave + lane;
+      const int rg = m0 + r;
+      const int arow = r < BM && rg < rows ? (gather ? g.row_token[a_off + rg] : a_off + rg) : -1;
+      vs_a = arow >= 0 ? static_cast<uint32_t>(arow) * srow_bytes : 0x80000000u;
+      vs_b = static_cast<uint32_t>(n0 + r) * srow_bytes;
     }
 
-    auto issue = [&](int slot_, int t) {
-      u32x4* base = lds + slot_ * kStage + (8 * wave) * kMxCh;
+    // direct load n of stage t into ring slot sl: n < MB -> A rows 32 n + ..,
+    // n < NR -> B rows 32 (n - MB) + .., NR -> A scales, NR + 1 -> B scales
+    auto issue1 = [&](int sl, int t, int n) __attribute__((always_inline)) {
       const uint32_t kb = static_cast<uint32_t>(t) * kMxBK;
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        if (i < MB)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(base + 32 * i * kMxCh),
-                                                   16, va[i], kb, 0, 0);
+      if (n < NR) {
+        if (n < MB)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              ra, (__attribute__((address_space(3))) void*)(lds + sl * kASlot + (32 * n + 8 * wave) * kMxCh), 16,
+              va[n], kb, 0, 0);
         else
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rb, (__attribute__((address_space(3))) void*)(base + (BM + 32 * (i - MB)) * kMxCh), 16, vb,
-              static_cast<uint32_t>(32 * (i - MB)) * row_bytes + kb, 0, 0);
+              rb,
+              (__attribute__((address_space(3))) void*)(lds + 2 * kASlot + sl * kBSlot +
+                                                        (32 * (n - MB) + 8 * wave) * kMxCh),
+              16, vb, static_cast<uint32_t>(32 * (n - MB)) * row_bytes + kb, 0, 0);
+      } else if (n == NR) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ras, (__attribute__((address_space(3))) void*)(lds + kScaleBase + (sl * kScaleStage + 64 * wave) / 4), 4,
+            vs_a, 4u * t, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rbs, (__attribute__((address_space(3))) void*)(lds + kScaleBase + (sl * kScaleStage + kMxBN + 64 * wave) / 4),
+            4, vs_b, 4u * t, 0, 0);
       }
-      uint32_t* sbase = lsc + slot_ * kScaleStage;
-#pragma unroll
-      for (int u = 0; u < kSU; ++u) {
-        const int r0 = 64 * (wave + 4 * u);
-        if (r0 >= BM + kMxBN) continue;
-        if (r0 < BM)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (__attribute__((address_space(3))) void*)(sbase + r0), 4,
-                                                   vs[u], 4u * t, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (__attribute__((address_space(3))) void*)(sbase + r0), 4,
-                                                   vs[u], 4u * t, 0, 0);
-      }
+    };
+
+    // fragments: B blocks 0..7 and A blocks 0..MB-1 with their scale bytes;
+    // a block of the next stage is read into the registers of the same block
+    // of this stage once that block's last MFMA has been issued
+    // (scale bytes stay bytes until the MFMA that takes them, so any widening
+    // is placed there, not at the top of the loop)
+    i32x8 fb[8], fa[MB];
+    uint8_t sb[8], sa[MB];
+    auto frag = [&](int lo_i, int hi_i, int sc_i, i32x8& f, uint8_t& sc) __attribute__((always_inline)) {
+      const u32x4 lo = lds[lo_i];
+      const u32x4 hi = lds[hi_i];
+      f = __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      sc = l8[sc_i];
+    };
+    // slot sl is wave-uniform; its offsets are added to the lane bases once per use site
+    auto readA = [&](int sl, int i) __attribute__((always_inline)) {
+      const int o = sl * kASlot + 16 * i * kMxCh;
+      frag(a_lo + o, a_hi + o, sa_b + sl * kScaleStage * 4 + 64 * i, fa[i], sa[i]);
+    };
+    auto readB = [&](int sl, int j) __attribute__((always_inline)) {
+      const int o = sl * kBSlot + 16 * j * kMxCh;
+      frag(b_lo + o, b_hi + o, sb_b + sl * kScaleStage * 4 + 64 * j, fb[j], sb[j]);
     };
 
     floatx4 acc[MB][8];
@@ -282,35 +332,74 @@ void gemm_mx_kernel(MxArgs g) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    issue(0, 0);
-    for (int t = 0; t < nk; ++t) {
-      const int cur = t & 1;
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0: stage t landed (codes and scales)
-      mx_barrier();                          // ... in every wave; every wave is done with stage t - 1
-      if (t + 1 < nk) issue(cur ^ 1, t + 1);
-      const u32x4* sa = lds + cur * kStage;
-      const uint32_t* ss = lsc + cur * kScaleStage;
-      i32x8 bf[8];
-      int bsc[8];
+    // prologue: stages 0 and 1 in flight, stage 0 published, its B blocks and A rows 0, 1 read
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = BM + wn * 128 + 16 * j + rr;
-        const u32x4 lo = sa[row * kMxCh + mx_swz(row, q)];
-        const u32x4 hi = sa[row * kMxCh + mx_swz(row, q + 4)];
-        bf[j] = __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        bsc[j] = static_cast<int>((ss[row] >> (8 * q)) & 0xffu);
+    for (int n = 0; n < ND; ++n) issue1(0, 0, n);
+    if (nk > 1) {
+#pragma unroll
+      for (int n = 0; n < ND; ++n) issue1(1, 1, n);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0
+    mx_barrier();
+    readA(0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) readB(0, j);
+    readA(0, 1);
+    // Let the prologue's reads land here, once per tile: otherwise the waits
+    // at the top of the loop are sized for them (they land in another order
+    // than the loop's own reads) on every step.
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt 0
+
+    // step t in ring slot cur = t % 2
+    auto kstep = [&](int t) __attribute__((always_inline)) {
+      const int cur = t & 1, nx = cur ^ 1;
+      const int t2 = min(t + 2, nk - 1);   // past the end: the last stage again, into a slot no step reads
+#pragma unroll
+      for (int m = 0; m < HM; ++m) {
+        const int i = m >> 3, j = m & 7;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, sb[j], 0,
+                                                                     sa[i]);
+        if ((m & 1) == 0 && (m >> 1) < NF1) readA(cur, 2 + (m >> 1));
+        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0: stage t+1 landed in this wave
+      mx_barrier();                          // ... in every wave, and every wave has stage t in registers
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int row = wm * (BM / 2) + 16 * i + rr;
-        const u32x4 lo = sa[row * kMxCh + mx_swz(row, q)];
-        const u32x4 hi = sa[row * kMxCh + mx_swz(row, q + 4)];
-        const i32x8 af = __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        const int asc = static_cast<int>((ss[row] >> (8 * q)) & 0xffu);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, bsc[j], 0, asc);
+      for (int m = 0; m < HM; ++m) {
+        // B block outermost: block j of stage t is done after its last row and
+        // block j of stage t+1 takes its registers; A rows 0, 1 are done already
+        const int j = m / (MB / 2), i = MB / 2 + m % (MB / 2);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, sb[j], 0,
+                                                                     sa[i]);
+        if (m < 2) readA(nx, m);
+        if (i == MB - 1) readB(nx, j);
+        if (m < ND) issue1(cur, t2, m);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    // Shorter tiles leave accumulation registers free, and the register
+    // allocator then shuttles accumulators between register files inside the
+    // loop.  Occupying the rest of that file with values pinned there across
+    // the loop keeps the accumulators in place.
+    constexpr int kPad = (256 - MB * 32) / 4;
+    floatx4 pin[kPad > 0 ? kPad : 1];
+    if constexpr (kPad > 0) {
+#pragma unroll
+      for (int k = 0; k < kPad; ++k) {
+        pin[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+        __asm__ volatile("" : "+a"(pin[k]));
+      }
+    }
+    // One branch-free loop body for every step keeps one register assignment
+    // and one basic block, so the interleaving above is what runs.  The last
+    // steps' barrier, next-stage reads and refills are harmless: the reads fill
+    // dead registers and the refills (of the last stage again) land in slots no
+    // later step reads, and are waited for before the tile ends.
+    for (int t = 0; t < nk; ++t) kstep(t);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0
+    if constexpr (kPad > 0) {
+#pragma unroll
+      for (int k = 0; k < kPad; ++k) __asm__ volatile("" ::"a"(pin[k]));
     }
     mx_barrier();   // the next tile's loads reuse the ring
 

@@ -61,7 +61,7 @@ Layout layout_of(const Problem& p) {
   L.xq_scales = off;  off += align_up(td / 32);
   // sized for the tallest tile: moe_workspace_bytes has no capacity factor,
   // and the tile height moe_forward picks can depend on it
-  L.part_cap = gemm_fast_path(p) && !p.mx ? kGemmPartCap : 0;
+  L.part_cap = p.mx || gemm_fast_path(p) ? kGemmPartCap : 0;   // the MXFP8 path always runs its MFMA kernel
   L.part = off;       off += align_up(static_cast<size_t>(L.part_cap) * 256 * 256 * 4);
   L.total = off;
   return L;

@@ -115,6 +115,8 @@ struct MxArgs {
   uint8_t* Cs;             // phase 1: H scales [R, N / 32]
   const int32_t* seg;
   int nseg, E, N, K;
+  float* part;             // [part_cap][BM][256] float32 partial tiles of the split tail
+  int part_cap;            // partial tiles the buffer holds (0: no split)
 };
 
 constexpr int kMxBN = 256, kMxBK = 128;     // tile columns, K elements (= bytes) per stage
@@ -134,6 +136,43 @@ __device__ __forceinline__ void mx_barrier() {
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
+}
+
+// Logical tile L -> (M tile, N tile): groups of kMxGroupM consecutive M tiles
+// sweep all N tiles, M fastest, so tiles that run together share A and B
+// panels in L2.
+__device__ __forceinline__ void mx_tile_of(int L, int total_mt, int ntn, int& mt, int& nt) {
+  const int gsz = kMxGroupM * ntn;
+  const int grp = L / gsz;
+  const int first_m = grp * kMxGroupM;
+  const int gm = min(kMxGroupM, total_mt - first_m);
+  const int r = L - grp * gsz;
+  mt = first_m + r % gm;
+  nt = r / gm;
+}
+
+// Split of the last partial round of a persistent launch of P workgroups
+// over `total` tiles: its tail = total mod P tiles are cut along K into S
+// pieces (S = P / tail, pieces of at least 4 steps, at most part_cap pieces),
+// so that round keeps the whole grid busy.  The pieces leave float32 partial
+// tiles that a fix-up sums in piece order, so results do not depend on timing.
+struct MxTail {
+  int full;   // tiles computed whole
+  int tail;   // tiles computed in pieces (0 if no split)
+  int S;      // pieces per tail tile
+};
+
+__device__ __forceinline__ MxTail mx_tail_plan(int total, int P, int nk, int part_cap) {
+  MxTail tp{total, 0, 1};
+  const int tail = total % P;
+  if (tail == 0) return tp;
+  int S = min(P / tail, nk / 4);
+  S = min(S, part_cap / tail);
+  if (S < 2) return tp;
+  tp.full = total - tail;
+  tp.tail = tail;
+  tp.S = S;
+  return tp;
 }
 
 __device__ __forceinline__ int mx_find_segment(const int32_t* tile_start, int nseg, int mt) {
@@ -229,19 +268,24 @@ void gemm_mx_kernel(MxArgs g) {
   int sb_b = kScaleBase * 16 + (kMxBN + wn * 128 + rr) * 4 + q;
   __asm__ volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi), "+v"(sa_b), "+v"(sb_b));
 
+  const MxTail tp = mx_tail_plan(total, gridDim.x, nk, g.part_cap);
+  const int items = tp.full + tp.tail * tp.S;
+
   for (int it = 0;; ++it) {
-    const int L = it * gridDim.x + xcd * per_xcd + slot;
-    if (L >= total) break;
-    int mt, nt;
-    {
-      const int gsz = kMxGroupM * ntn;
-      const int grp = L / gsz;
-      const int first_m = grp * kMxGroupM;
-      const int gm = min(kMxGroupM, total_mt - first_m);
-      const int r = L - grp * gsz;
-      mt = first_m + r % gm;
-      nt = r / gm;
+    const int w = it * gridDim.x + xcd * per_xcd + slot;
+    if (w >= items) break;
+    // work item w: a whole tile (w < full), or piece p of tail tile full + idx / S,
+    // K steps k0 .. k0 + kn - 1
+    int L = w, k0 = 0, kn = nk, piece = -1;
+    if (w >= tp.full) {
+      piece = w - tp.full;
+      const int pp = piece % tp.S;
+      L = tp.full + piece / tp.S;
+      k0 = pp * nk / tp.S;
+      kn = (pp + 1) * nk / tp.S - k0;        // >= 4
     }
+    int mt, nt;
+    mx_tile_of(L, total_mt, ntn, mt, nt);
     const int s = __builtin_amdgcn_readfirstlane(mx_find_segment(st.tile_start, g.nseg, mt));
     const int rows = __builtin_amdgcn_readfirstlane(st.rows[s]);
     const int m0 = (mt - __builtin_amdgcn_readfirstlane(st.tile_start[s])) * BM;
@@ -277,10 +321,10 @@ void gemm_mx_kernel(MxArgs g) {
       vs_b = static_cast<uint32_t>(n0 + r) * srow_bytes;
     }
 
-    // direct load n of stage t into ring slot sl: n < MB -> A rows 32 n + ..,
+    // direct load n of stage t (K step k0 + t) into ring slot sl: n < MB -> A rows 32 n + ..,
     // n < NR -> B rows 32 (n - MB) + .., NR -> A scales, NR + 1 -> B scales
     auto issue1 = [&](int sl, int t, int n) __attribute__((always_inline)) {
-      const uint32_t kb = static_cast<uint32_t>(t) * kMxBK;
+      const uint32_t kb = static_cast<uint32_t>(k0 + t) * kMxBK;
       if (n < NR) {
         if (n < MB)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -295,11 +339,11 @@ void gemm_mx_kernel(MxArgs g) {
       } else if (n == NR) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ras, (__attribute__((address_space(3))) void*)(lds + kScaleBase + (sl * kScaleStage + 64 * wave) / 4), 4,
-            vs_a, 4u * t, 0, 0);
+            vs_a, 4u * (k0 + t), 0, 0);
       } else {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rbs, (__attribute__((address_space(3))) void*)(lds + kScaleBase + (sl * kScaleStage + kMxBN + 64 * wave) / 4),
-            4, vs_b, 4u * t, 0, 0);
+            4, vs_b, 4u * (k0 + t), 0, 0);
       }
     };
 
@@ -335,7 +379,7 @@ void gemm_mx_kernel(MxArgs g) {
     // prologue: stages 0 and 1 in flight, stage 0 published, its B blocks and A rows 0, 1 read
 #pragma unroll
     for (int n = 0; n < ND; ++n) issue1(0, 0, n);
-    if (nk > 1) {
+    if (kn > 1) {
 #pragma unroll
       for (int n = 0; n < ND; ++n) issue1(1, 1, n);
     }
@@ -353,7 +397,7 @@ void gemm_mx_kernel(MxArgs g) {
     // step t in ring slot cur = t % 2
     auto kstep = [&](int t) __attribute__((always_inline)) {
       const int cur = t & 1, nx = cur ^ 1;
-      const int t2 = min(t + 2, nk - 1);   // past the end: the last stage again, into a slot no step reads
+      const int t2 = min(t + 2, kn - 1);   // past the end: the last stage again, into a slot no step reads
 #pragma unroll
       for (int m = 0; m < HM; ++m) {
         const int i = m >> 3, j = m & 7;
@@ -395,7 +439,7 @@ void gemm_mx_kernel(MxArgs g) {
     // steps' barrier, next-stage reads and refills are harmless: the reads fill
     // dead registers and the refills (of the last stage again) land in slots no
     // later step reads, and are waited for before the tile ends.
-    for (int t = 0; t < nk; ++t) kstep(t);
+    for (int t = 0; t < kn; ++t) kstep(t);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0
     if constexpr (kPad > 0) {
 #pragma unroll
@@ -404,7 +448,11 @@ void gemm_mx_kernel(MxArgs g) {
     mx_barrier();   // the next tile's loads reuse the ring
 
     // Epilogue: lane (rr, q) holds, for block (i, j), row 16 i + rr of the wave
-    // tile and columns 16 j + 4 q .. + 3.
+    // tile and columns 16 j + 4 q .. + 3.  A piece of a tail tile stores its
+    // float32 partial tile (row-major BM x 256); a whole tile adds the bias,
+    // applies the activation (phase 1) and stores MX blocks or bf16.
+    const __amdgpu_buffer_rsrc_t pr = mx_rsrc(g.part, static_cast<uint32_t>(g.part_cap) * BM * kMxBN * 4u);
+    const uint32_t pv = (static_cast<uint32_t>(wm * (BM / 2) + rr) * kMxBN + wn * 128 + 4 * q) * 4u;
     const int cbase = n0 + wn * 128 + 4 * q;
     uint2 bq[8];
 #pragma unroll
@@ -415,34 +463,46 @@ void gemm_mx_kernel(MxArgs g) {
     for (int i = 0; i < MB; ++i) {
       const int rl = m0 + wm * (BM / 2) + 16 * i + rr;
       const bool ok = rl < rows;
-      float v[8][4];
+      if (piece >= 0) {
+        const uint32_t ps = (static_cast<uint32_t>(piece) * BM + 16 * i) * kMxBN * 4u;
+        // (through vector registers: stored from the accumulation registers,
+        // the accumulators of the shorter tiles get shuttled between register
+        // files inside the K loop)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        v[j][0] = mx_act<ACT>(acc[i][j][0] + __uint_as_float(bq[j].x << 16));
-        v[j][1] = mx_act<ACT>(acc[i][j][1] + __uint_as_float(bq[j].x & 0xffff0000u));
-        v[j][2] = mx_act<ACT>(acc[i][j][2] + __uint_as_float(bq[j].y << 16));
-        v[j][3] = mx_act<ACT>(acc[i][j][3] + __uint_as_float(bq[j].y & 0xffff0000u));
-      }
-      if constexpr (kMxOut) {
-        // MX blocks of 32 columns: j pair (2 c, 2 c + 1) x the 4 lanes q of the row
+        for (int j = 0; j < 8; ++j) {
+          floatx4 t = acc[i][j];
+          __asm__ volatile("" : "+v"(t));
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, t), pr, pv + 64 * j, ps, 0);
+        }
+      } else if constexpr (kMxOut) {
+        // MX blocks of 32 columns: j pair (2 c, 2 c + 1) x the 4 lanes q of the
+        // row, computed a block at a time (8 values a lane)
         uint8_t* crow = static_cast<uint8_t*>(g.C) + static_cast<size_t>(o_off + (ok ? rl : 0)) * g.N;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
+          float v[2][4];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int j = 2 * c + h;
+            v[h][0] = mx_act<ACT>(acc[i][j][0] + __uint_as_float(bq[j].x << 16));
+            v[h][1] = mx_act<ACT>(acc[i][j][1] + __uint_as_float(bq[j].x & 0xffff0000u));
+            v[h][2] = mx_act<ACT>(acc[i][j][2] + __uint_as_float(bq[j].y << 16));
+            v[h][3] = mx_act<ACT>(acc[i][j][3] + __uint_as_float(bq[j].y & 0xffff0000u));
+          }
           float am = 0.f;
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) am = fmaxf(am, fabsf(v[2 * c + h][e]));
+            for (int e = 0; e < 4; ++e) am = fmaxf(am, fabsf(v[h][e]));
           am = fmaxf(am, __shfl_xor(am, 16));
           am = fmaxf(am, __shfl_xor(am, 32));
           const int sx = mx_exponent(am);
           const float inv = mx_inv_scale(sx);
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const int j = 2 * c + h;
-            uint32_t w = cvt2<false>(v[j][0] * inv, v[j][1] * inv, 0u);
-            w = cvt2<true>(v[j][2] * inv, v[j][3] * inv, w);
-            if (ok) *reinterpret_cast<uint32_t*>(crow + cbase + 16 * j) = w;
+            uint32_t w = cvt2<false>(v[h][0] * inv, v[h][1] * inv, 0u);
+            w = cvt2<true>(v[h][2] * inv, v[h][3] * inv, w);
+            if (ok) *reinterpret_cast<uint32_t*>(crow + cbase + 16 * (2 * c + h)) = w;
           }
           if (ok && q == 0)
             g.Cs[static_cast<size_t>(o_off + rl) * (g.N / 32) + (n0 + wn * 128) / 32 + c] = static_cast<uint8_t>(sx + 127);
@@ -451,10 +511,73 @@ void gemm_mx_kernel(MxArgs g) {
         if (ok) {
           uint16_t* crow = static_cast<uint16_t*>(g.C) + static_cast<size_t>(o_off + rl) * g.N + cbase;
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
+          for (int j = 0; j < 8; ++j) {
+            const float v0 = acc[i][j][0] + __uint_as_float(bq[j].x << 16);
+            const float v1 = acc[i][j][1] + __uint_as_float(bq[j].x & 0xffff0000u);
+            const float v2 = acc[i][j][2] + __uint_as_float(bq[j].y << 16);
+            const float v3 = acc[i][j][3] + __uint_as_float(bq[j].y & 0xffff0000u);
             *reinterpret_cast<uint2*>(crow + 16 * j) =
-                make_uint2(mx_pack_bf16x2(v[j][0], v[j][1]), mx_pack_bf16x2(v[j][2], v[j][3]));
+                make_uint2(mx_pack_bf16x2(mx_act<ACT>(v0), mx_act<ACT>(v1)), mx_pack_bf16x2(mx_act<ACT>(v2), mx_act<ACT>(v3)));
+          }
         }
+      }
+    }
+  }
+}
+
+// Fix-up of the split tail, in 16-row chunks of the tail tiles strided over
+// the P workgroups.  Each thread owns four consecutive columns of four rows;
+// the S partial tiles are summed in piece order, then the bias, the
+// activation (phase 1) and the store as in the GEMM epilogue: phase 1 MX
+// blocks of 32 columns (8 lanes a block), phase 2 bf16.
+template <int ACT, int BM>
+__global__ __launch_bounds__(256) void mx_tail_fixup_kernel(MxArgs g, int P) {
+  constexpr bool kMxOut = ACT != 0;
+  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
+  const int total_mt = st.tile_start[g.nseg];
+  const int ntn = g.N / kMxBN;
+  const MxTail tp = mx_tail_plan(total_mt * ntn, P, g.K / kMxBK, g.part_cap);
+  if (tp.tail == 0) return;
+  constexpr int kChunks = BM / 16;
+  const int c = 4 * (threadIdx.x & 63);
+  for (int w = blockIdx.x; w < tp.tail * kChunks; w += gridDim.x) {
+    const int tt = w / kChunks, r0 = (w % kChunks) * 16;
+    int mt, nt;
+    mx_tile_of(tp.full + tt, total_mt, ntn, mt, nt);
+    const int s = mx_find_segment(st.tile_start, g.nseg, mt);
+    const int rows = st.rows[s];
+    const int m0 = (mt - st.tile_start[s]) * BM;
+    const int o_off = st.o_off[s];
+    const int n = nt * kMxBN + c;
+    const uint2 b = g.bias ? *reinterpret_cast<const uint2*>(g.bias + static_cast<size_t>(s) * g.N + n)
+                           : make_uint2(0u, 0u);
+    const float b0 = __uint_as_float(b.x << 16), b1 = __uint_as_float(b.x & 0xffff0000u);
+    const float b2 = __uint_as_float(b.y << 16), b3 = __uint_as_float(b.y & 0xffff0000u);
+    const float* part = g.part + static_cast<size_t>(tt) * tp.S * BM * kMxBN;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int rr = r0 + (threadIdx.x >> 6) + 4 * k;   // one row per wave: the lanes of a block agree
+      if (m0 + rr >= rows) break;
+      floatx4 a = *reinterpret_cast<const floatx4*>(part + static_cast<size_t>(rr) * kMxBN + c);
+      for (int p = 1; p < tp.S; ++p)
+        a += *reinterpret_cast<const floatx4*>(part + (static_cast<size_t>(p) * BM + rr) * kMxBN + c);
+      const float v0 = mx_act<ACT>(a[0] + b0), v1 = mx_act<ACT>(a[1] + b1);
+      const float v2 = mx_act<ACT>(a[2] + b2), v3 = mx_act<ACT>(a[3] + b3);
+      const size_t row = static_cast<size_t>(o_off + m0 + rr);
+      if constexpr (kMxOut) {
+        float am = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
+        am = fmaxf(am, __shfl_xor(am, 1));
+        am = fmaxf(am, __shfl_xor(am, 2));
+        am = fmaxf(am, __shfl_xor(am, 4));
+        const int sx = mx_exponent(am);
+        const float inv = mx_inv_scale(sx);
+        uint32_t wq = cvt2<false>(v0 * inv, v1 * inv, 0u);
+        wq = cvt2<true>(v2 * inv, v3 * inv, wq);
+        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(g.C) + row * g.N + n) = wq;
+        if ((threadIdx.x & 7) == 0) g.Cs[row * (g.N / 32) + n / 32] = static_cast<uint8_t>(sx + 127);
+      } else {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.C) + row * g.N + n) =
+            make_uint2(mx_pack_bf16x2(v0, v1), mx_pack_bf16x2(v2, v3));
       }
     }
   }
@@ -522,10 +645,18 @@ hipError_t launch_expert_ffn_mx(const Problem& p, const MxWeights& w, const Work
     g.N = p.d;
     g.K = p.h;
   }
+  g.part = ws.part;
+  g.part_cap = ws.part_cap;
   int grid = mx_num_cus();
   grid = (grid + 7) / 8 * 8;
   const int act = phase == 2 ? 0 : (p.act == MOE_ACT_SILU ? 2 : 1);
-#define MOE_MX_LAUNCH(ACT_, BM_) hipLaunchKernelGGL((gemm_mx_kernel<ACT_, BM_>), dim3(grid), dim3(256), 0, st, g)
+  // the fix-up runs right after the GEMM on the same stream; it returns at
+  // once when the tail was not split
+#define MOE_MX_LAUNCH(ACT_, BM_)                                                              \
+  do {                                                                                        \
+    hipLaunchKernelGGL((gemm_mx_kernel<ACT_, BM_>), dim3(grid), dim3(256), 0, st, g);         \
+    hipLaunchKernelGGL((mx_tail_fixup_kernel<ACT_, BM_>), dim3(grid), dim3(256), 0, st, g, grid); \
+  } while (0)
   if (p.gemm_bm == 256) {
     if (act == 1) MOE_MX_LAUNCH(1, 256);
     else if (act == 2) MOE_MX_LAUNCH(2, 256);

@@ -1,8 +1,9 @@
 """The MXFP8 expert path on the GPU vs the CPU oracle (oracle/mxfp8.py),
 through the C ABI: the quantizer bit-exact on chosen and random inputs, and
 the layer on reduced shapes (both tile heights, shared experts, capacity
-drops, the Mixtral expert form, one token) and the Mixtral-shaped workload
-at full size with sampled output rows."""
+drops, the Mixtral expert form, one token, tiles split along K with their
+fix-up in both phases) and the Mixtral-shaped workload at full size with
+sampled output rows."""
 import sys
 
 import numpy as np
@@ -57,6 +58,9 @@ REDUCED = {
     "mx_silu_nobias": ("mixtral", dict(T=600, d=512, h=1024, activation="silu", expert_bias=False)),
     "mx_single_token": ("mixtral", dict(T=1, d=256, h=256, E=8)),
     "mx_deep_K": ("mixtral", dict(T=512, d=2048, h=512, E=4)),
+    # fewer tiles than workgroups: every tile is cut along K in both phases
+    # (phase 1 pieces end in the MX-quantizing fix-up, phase 2 in the bf16 one)
+    "mx_split_silu": ("mixtral", dict(T=600, d=2048, h=1024, E=8, activation="silu")),
 }
 
 

@@ -83,30 +83,6 @@ __device__ __forceinline__ float gelu_erf(float v) {
 // +inf for v < -88 and the quotient is then -0, the limit.
 __device__ __forceinline__ float silu_exact(float v) { return v / (1.0f + expf(-v)); }
 
-// SiLU with the hardware exp2 and reciprocal (~1 ulp each), for the MFMA
-// epilogue whose results are rounded to bf16; the same limits as above.
-__device__ __forceinline__ float silu_fast(float v) {
-  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.44269504088896341f));
-}
-
-// GELU(v) = v/2 (1 + erf(v / sqrt 2)) with erf from Abramowitz & Stegun 7.1.26
-// (Hastings' rational approximation, |error| <= 1.5e-7 in erf): for z >= 0,
-// erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z);
-// odd in z.  Branch-free: one reciprocal, one exp2 and ~12 VALU operations.
-__device__ __forceinline__ float gelu_as(float v) {
-  const float z = fabsf(v) * 0.70710678118654752440f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  float q = fmaf(t, 1.061405429f, -1.453152027f);
-  q = fmaf(t, q, 1.421413741f);
-  q = fmaf(t, q, -0.284496736f);
-  q = fmaf(t, q, 0.254829592f);
-  q *= t;
-  const float e = __builtin_amdgcn_exp2f((z * -1.44269504088896341f) * z);   // exp(-z^2)
-  const float erf_v = copysignf(fmaf(-q, e, 1.0f), v);
-  const float hv = 0.5f * v;
-  return fmaf(hv, erf_v, hv);
-}
-
 template <int ACT>
 __device__ __forceinline__ float act_fast(float v) {
   if constexpr (ACT == kActGelu) return gelu_as(v);

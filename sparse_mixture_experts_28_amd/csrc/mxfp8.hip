@@ -184,15 +184,12 @@ __device__ __forceinline__ int mx_find_segment(const int32_t* tile_start, int ns
   return lo;
 }
 
+// activation of the first Linear: 1 GELU(erf), 2 SiLU, 0 none (second Linear)
 template <int ACT>
 __device__ __forceinline__ float mx_act(float v) {
-  if constexpr (ACT == 1) {   // GELU(erf)
-    return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
-  } else if constexpr (ACT == 2) {   // SiLU
-    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.44269504088896341f));
-  } else {
-    return v;
-  }
+  if constexpr (ACT == 1) return gelu_as(v);
+  else if constexpr (ACT == 2) return silu_fast(v);
+  else return v;
 }
 
 __device__ __forceinline__ uint32_t mx_pack_bf16x2(float lo, float hi) {

@@ -202,9 +202,11 @@ __device__ __forceinline__ uint32_t mx_pack_bf16x2(float lo, float hi) {
 // BM x 256 tiles, 128-deep K stages in a 2-slot LDS ring, 4 waves in a 2 x 2
 // grid (wave tile BM/2 x 128 = (BM/32) x 8 blocks of the 16x16x128 MFMA).
 // Codes reach LDS by direct loads (rows of 128 bytes, 16-byte chunks XOR-
-// swizzled by row); the stage's scale dwords (4 blocks of a row) follow them
-// into LDS by 4-byte direct loads, one row per lane.  A lane's scale operand
-// is read straight from LDS as the byte of its row and block.
+// swizzled by row).  Scales come SG stages at a time (4 SG bytes of a row,
+// one row per lane; SG = 4, a quarter of the line requests of one load a
+// stage, when rows of scales are a multiple of 16 bytes, else SG = 1) into a
+// 2-group ring of their own; a lane's scale operand is read straight from LDS
+// as the byte of its row, stage and block.
 //
 // A fragment is 32 bytes a lane, so one stage's fragments (A and B) fill 128
 // vector registers and cannot be double-buffered whole.  K step t runs its
@@ -218,7 +220,7 @@ __device__ __forceinline__ uint32_t mx_pack_bf16x2(float lo, float hi) {
 //           stage t+2
 // so the next stage's B fragments reuse the registers of this stage's, and
 // arrive, with its first two A rows, while this stage's last rows multiply.
-template <int ACT, int BM>
+template <int ACT, int BM, int SG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_mx_kernel(MxArgs g) {
   constexpr bool kMxOut = ACT != 0;           // phase 1 writes H as MX
@@ -226,14 +228,20 @@ void gemm_mx_kernel(MxArgs g) {
   constexpr int HM = MB / 2 * 8;              // MFMAs per half step
   constexpr int NR = MB + 8;                  // code loads per stage per wave (8 rows x 128 B each)
   constexpr int kStage = (BM + kMxBN) * kMxCh;     // u32x4 of codes per stage
-  constexpr int kScaleStage = 2 * kMxBN;           // uint32 of scales per stage: A rows (up to 256), B rows
-  constexpr int ND = NR + 2;                        // direct loads per stage per wave
+  constexpr int kSRow = 4 * SG;                     // scale bytes of a row in one group
+  constexpr int kScaleSlot = 2 * kMxBN * kSRow;     // bytes of a scale group: A rows (up to 256), then B rows
   constexpr int NF1 = MB - 2;                       // fragment reads in half 0
-  static_assert(HM >= 2 * NF1 && HM >= ND, "half step too short for its reads and loads");
-  // one LDS object (A code slots, B code slots, then the scale slots), so the
-  // waits the compiler places for direct loads are the ones written below
+  static_assert(SG == 1 || SG == 4, "scale groups of 1 or 4 stages (4- or 16-byte direct loads)");
+  // a step that starts group G loads group G + kLook: the slot of group G - 1
+  // (SG = 4) or of G itself (SG = 1, read up to this step's barrier)
+  constexpr int kLook = SG == 1 ? 2 : 1;
+  static_assert(HM >= 2 * NF1 && HM >= NR + 2, "half step too short for its reads and loads");
+  // one LDS object (A code slots, B code slots, the scale slots, then 64 kSRow
+  // bytes a wave where the skipped scale loads land), so the waits the
+  // compiler places for direct loads are the ones written below
   constexpr int kScaleBase = 2 * kStage;                  // u32x4 index of the scale slots
-  __shared__ u32x4 lds[2 * kStage + 2 * kScaleStage / 4];
+  constexpr int kJunkBase = kScaleBase + 2 * kScaleSlot / 16;
+  __shared__ u32x4 lds[kJunkBase + 4 * 64 * kSRow / 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -261,8 +269,8 @@ void gemm_mx_kernel(MxArgs g) {
   int a_hi = (wm * (BM / 2) + rr) * kMxCh + mx_swz(rr, q + 4);
   int b_lo = 2 * kASlot + (wn * 128 + rr) * kMxCh + mx_swz(rr, q);
   int b_hi = 2 * kASlot + (wn * 128 + rr) * kMxCh + mx_swz(rr, q + 4);
-  int sa_b = kScaleBase * 16 + (wm * (BM / 2) + rr) * 4 + q;
-  int sb_b = kScaleBase * 16 + (kMxBN + wn * 128 + rr) * 4 + q;
+  int sa_b = kScaleBase * 16 + (wm * (BM / 2) + rr) * kSRow + q;
+  int sb_b = kScaleBase * 16 + (kMxBN + wn * 128 + rr) * kSRow + q;
   __asm__ volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi), "+v"(sa_b), "+v"(sb_b));
 
   const MxTail tp = mx_tail_plan(total, gridDim.x, nk, g.part_cap);
@@ -306,7 +314,7 @@ void gemm_mx_kernel(MxArgs g) {
       va[i] = arow >= 0 ? static_cast<uint32_t>(arow) * row_bytes + dr_ch * 16 : 0x80000000u;
     }
     const uint32_t vb = static_cast<uint32_t>(n0 + dr_row) * row_bytes + dr_ch * 16;
-    // scale loads: 4 bytes (one stage's 4 blocks) per row, one row per lane;
+    // scale loads: 4 SG bytes (SG stages of 4 blocks) per row, one row per lane;
     // wave w loads A rows 64 w .. 64 w + 63 (rows from BM on, and past the
     // segment, read zero) and B rows 64 w .. 64 w + 63, with no branch
     uint32_t vs_a, vs_b;
@@ -319,10 +327,10 @@ void gemm_mx_kernel(MxArgs g) {
     }
 
     // direct load n of stage t (K step k0 + t) into ring slot sl: n < MB -> A rows 32 n + ..,
-    // n < NR -> B rows 32 (n - MB) + .., NR -> A scales, NR + 1 -> B scales
+    // else B rows 32 (n - MB) + ..
     auto issue1 = [&](int sl, int t, int n) __attribute__((always_inline)) {
       const uint32_t kb = static_cast<uint32_t>(k0 + t) * kMxBK;
-      if (n < NR) {
+      {
         if (n < MB)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               ra, (__attribute__((address_space(3))) void*)(lds + sl * kASlot + (32 * n + 8 * wave) * kMxCh), 16,
@@ -333,15 +341,26 @@ void gemm_mx_kernel(MxArgs g) {
               (__attribute__((address_space(3))) void*)(lds + 2 * kASlot + sl * kBSlot +
                                                         (32 * (n - MB) + 8 * wave) * kMxCh),
               16, vb, static_cast<uint32_t>(32 * (n - MB)) * row_bytes + kb, 0, 0);
-      } else if (n == NR) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ras, (__attribute__((address_space(3))) void*)(lds + kScaleBase + (sl * kScaleStage + 64 * wave) / 4), 4,
-            vs_a, 4u * (k0 + t), 0, 0);
-      } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rbs, (__attribute__((address_space(3))) void*)(lds + kScaleBase + (sl * kScaleStage + kMxBN + 64 * wave) / 4),
-            4, vs_b, 4u * (k0 + t), 0, 0);
       }
+    };
+    // scale group G (K steps SG G .. SG G + SG - 1) of this wave's A (n = 0) or B
+    // (n = 1) rows into scale slot G % 2; with on false the load reads nothing
+    // (an offset past the end) and lands in this wave's scratch area
+    auto issue_scales = [&](int G, int n, bool on) __attribute__((always_inline)) {
+      const int dst = on ? kScaleBase + ((G & 1) * kScaleSlot + (n * kMxBN + 64 * wave) * kSRow) / 16
+                         : kJunkBase + 64 * wave * kSRow / 16;
+      const uint32_t vo = on ? (n == 0 ? vs_a : vs_b) : 0x80000000u;
+      const uint32_t so = on ? static_cast<uint32_t>(G) * kSRow : 0u;
+      auto* lp = (__attribute__((address_space(3))) void*)(lds + dst);
+      if constexpr (SG == 4)   // (the load width must be a literal)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(n == 0 ? ras : rbs, lp, 16, vo, so, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(n == 0 ? ras : rbs, lp, 4, vo, so, 0, 0);
+    };
+    // byte offset, within the scale slots, of stage t's scales (K step k0 + t)
+    auto sofs = [&](int t) __attribute__((always_inline)) {
+      const int a = k0 + t;
+      return ((a / SG) & 1) * kScaleSlot + (a % SG) * 4;
     };
 
     // fragments: B blocks 0..7 and A blocks 0..MB-1 with their scale bytes;
@@ -357,14 +376,15 @@ void gemm_mx_kernel(MxArgs g) {
       f = __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       sc = l8[sc_i];
     };
-    // slot sl is wave-uniform; its offsets are added to the lane bases once per use site
-    auto readA = [&](int sl, int i) __attribute__((always_inline)) {
-      const int o = sl * kASlot + 16 * i * kMxCh;
-      frag(a_lo + o, a_hi + o, sa_b + sl * kScaleStage * 4 + 64 * i, fa[i], sa[i]);
+    // fragments of stage t (ring slot t % 2); the wave-uniform offsets are added
+    // to the lane bases once per use site
+    auto readA = [&](int t, int i) __attribute__((always_inline)) {
+      const int o = (t & 1) * kASlot + 16 * i * kMxCh;
+      frag(a_lo + o, a_hi + o, sa_b + sofs(t) + 16 * kSRow * i, fa[i], sa[i]);
     };
-    auto readB = [&](int sl, int j) __attribute__((always_inline)) {
-      const int o = sl * kBSlot + 16 * j * kMxCh;
-      frag(b_lo + o, b_hi + o, sb_b + sl * kScaleStage * 4 + 64 * j, fb[j], sb[j]);
+    auto readB = [&](int t, int j) __attribute__((always_inline)) {
+      const int o = (t & 1) * kBSlot + 16 * j * kMxCh;
+      frag(b_lo + o, b_hi + o, sb_b + sofs(t) + 16 * kSRow * j, fb[j], sb[j]);
     };
 
     floatx4 acc[MB][8];
@@ -373,13 +393,16 @@ void gemm_mx_kernel(MxArgs g) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // prologue: stages 0 and 1 in flight, stage 0 published, its B blocks and A rows 0, 1 read
+    // prologue: stages 0 and 1 and the first two scale groups in flight, stage 0
+    // published, its B blocks and A rows 0, 1 read
 #pragma unroll
-    for (int n = 0; n < ND; ++n) issue1(0, 0, n);
+    for (int n = 0; n < NR; ++n) issue1(0, 0, n);
     if (kn > 1) {
 #pragma unroll
-      for (int n = 0; n < ND; ++n) issue1(1, 1, n);
+      for (int n = 0; n < NR; ++n) issue1(1, 1, n);
     }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) issue_scales(k0 / SG + n / 2, n & 1, true);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0
     mx_barrier();
     readA(0, 0);
@@ -391,16 +414,20 @@ void gemm_mx_kernel(MxArgs g) {
     // than the loop's own reads) on every step.
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt 0
 
-    // step t in ring slot cur = t % 2
+    // step t in ring slot cur = t % 2.  A step that starts a scale group G loads
+    // group G + kLook into the slot whose last stage was read before this
+    // step's barrier; the group's first stage is read two steps on or later.
     auto kstep = [&](int t) __attribute__((always_inline)) {
-      const int cur = t & 1, nx = cur ^ 1;
+      const int cur = t & 1;
       const int t2 = min(t + 2, kn - 1);   // past the end: the last stage again, into a slot no step reads
+      const bool group_start = (k0 + t) % SG == 0;
+      const int gnext = (k0 + t) / SG + kLook;
 #pragma unroll
       for (int m = 0; m < HM; ++m) {
         const int i = m >> 3, j = m & 7;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, sb[j], 0,
                                                                      sa[i]);
-        if ((m & 1) == 0 && (m >> 1) < NF1) readA(cur, 2 + (m >> 1));
+        if ((m & 1) == 0 && (m >> 1) < NF1) readA(t, 2 + (m >> 1));
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0: stage t+1 landed in this wave
@@ -412,9 +439,10 @@ void gemm_mx_kernel(MxArgs g) {
         const int j = m / (MB / 2), i = MB / 2 + m % (MB / 2);
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, sb[j], 0,
                                                                      sa[i]);
-        if (m < 2) readA(nx, m);
-        if (i == MB - 1) readB(nx, j);
-        if (m < ND) issue1(cur, t2, m);
+        if (m < 2) readA(t + 1, m);
+        if (i == MB - 1) readB(t + 1, j);
+        if (m < NR) issue1(cur, t2, m);
+        if (m == NR || m == NR + 1) issue_scales(gnext, m - NR, group_start);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -649,9 +677,13 @@ hipError_t launch_expert_ffn_mx(const Problem& p, const MxWeights& w, const Work
   const int act = phase == 2 ? 0 : (p.act == MOE_ACT_SILU ? 2 : 1);
   // the fix-up runs right after the GEMM on the same stream; it returns at
   // once when the tail was not split
+  // scales in groups of 4 stages (16-byte loads) when rows of scales are a
+  // multiple of 16 bytes (K a multiple of 512), else one stage at a time
+  const bool sg4 = g.K % 512 == 0;
 #define MOE_MX_LAUNCH(ACT_, BM_)                                                              \
   do {                                                                                        \
-    hipLaunchKernelGGL((gemm_mx_kernel<ACT_, BM_>), dim3(grid), dim3(256), 0, st, g);         \
+    if (sg4) hipLaunchKernelGGL((gemm_mx_kernel<ACT_, BM_, 4>), dim3(grid), dim3(256), 0, st, g); \
+    else hipLaunchKernelGGL((gemm_mx_kernel<ACT_, BM_, 1>), dim3(grid), dim3(256), 0, st, g);     \
     hipLaunchKernelGGL((mx_tail_fixup_kernel<ACT_, BM_>), dim3(grid), dim3(256), 0, st, g, grid); \
   } while (0)
   if (p.gemm_bm == 256) {

@@ -131,6 +131,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* base, uint
                                            kMxRsrc);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding (n < 64) and does not wait on LDS or export counters
+constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
 __device__ __forceinline__ void mx_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt 0 only
   __asm__ volatile("" ::: "memory");
@@ -199,14 +203,16 @@ __device__ __forceinline__ uint32_t mx_pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// BM x 256 tiles, 128-deep K stages in a 2-slot LDS ring, 4 waves in a 2 x 2
-// grid (wave tile BM/2 x 128 = (BM/32) x 8 blocks of the 16x16x128 MFMA).
+// BM x 256 tiles, 128-deep K stages in an NS-slot LDS ring (NS = 2 at BM =
+// 256; 3 at BM = 128, where the tiles stream weights and more bytes in flight
+// pay), 4 waves in a 2 x 2 grid (wave tile BM/2 x 128 = (BM/32) x 8 blocks of
+// the 16x16x128 MFMA).
 // Codes reach LDS by direct loads (rows of 128 bytes, 16-byte chunks XOR-
 // swizzled by row).  Scales come SG stages at a time (4 SG bytes of a row,
 // one row per lane; SG = 4, a quarter of the line requests of one load a
 // stage, when rows of scales are a multiple of 16 bytes, else SG = 1) into a
-// 2-group ring of their own; a lane's scale operand is read straight from LDS
-// as the byte of its row, stage and block.
+// ring of their own (2 groups, or NS stages at SG = 1); a lane's scale operand
+// is read straight from LDS as the byte of its row, stage and block.
 //
 // A fragment is 32 bytes a lane, so one stage's fragments (A and B) fill 128
 // vector registers and cannot be double-buffered whole.  K step t runs its
@@ -214,10 +220,10 @@ __device__ __forceinline__ uint32_t mx_pack_bf16x2(float lo, float hi) {
 // by at most one fragment read and one direct load, in a fixed order:
 //   half 0: MFMAs; read A rows 2 .. MB-1 of stage t
 //   wait for stage t+1 and the barrier that publishes it; stage t is then in
-//   registers in every wave, so its slot takes stage t+2
+//   registers in every wave, so its slot takes stage t+NS
 //   half 1: MFMAs, B block outermost; read A rows 0, 1 of stage t+1, and its
 //           B block j as soon as block j of stage t is done; direct loads of
-//           stage t+2
+//           stage t+NS, its scale group (if one starts) first
 // so the next stage's B fragments reuse the registers of this stage's, and
 // arrive, with its first two A rows, while this stage's last rows multiply.
 template <int ACT, int BM, int SG>
@@ -228,20 +234,27 @@ void gemm_mx_kernel(MxArgs g) {
   constexpr int HM = MB / 2 * 8;              // MFMAs per half step
   constexpr int NR = MB + 8;                  // code loads per stage per wave (8 rows x 128 B each)
   constexpr int kStage = (BM + kMxBN) * kMxCh;     // u32x4 of codes per stage
+  constexpr int NS = BM == 256 ? 2 : 3;       // LDS ring slots
   constexpr int kSRow = 4 * SG;                     // scale bytes of a row in one group
-  constexpr int kScaleSlot = 2 * kMxBN * kSRow;     // bytes of a scale group: A rows (up to 256), then B rows
+  constexpr int kScaleSlot = (BM + kMxBN) * kSRow;  // bytes of a scale group: A rows, then B rows
+  constexpr int NSS = SG == 1 ? NS : 2;             // scale ring slots
   constexpr int NF1 = MB - 2;                       // fragment reads in half 0
   static_assert(SG == 1 || SG == 4, "scale groups of 1 or 4 stages (4- or 16-byte direct loads)");
-  // a step that starts group G loads group G + kLook: the slot of group G - 1
-  // (SG = 4) or of G itself (SG = 1, read up to this step's barrier)
-  constexpr int kLook = SG == 1 ? 2 : 1;
+  // a step that starts group G loads group G + kLook into the slot whose last
+  // stage was read before the step's barrier: that of group G - 1 (SG = 4) or
+  // of stage G itself (SG = 1: group G + NS goes with the codes of stage G + NS)
+  constexpr int kLook = SG == 1 ? NS : 1;
   static_assert(HM >= 2 * NF1 && HM >= NR + 2, "half step too short for its reads and loads");
+  // the barrier of step t waits for stage t+1: every direct load but those
+  // issued after its codes (the NS - 2 later stages, 2 + NR loads each)
+  constexpr int kVmWait = (NS - 2) * (NR + 2);
   // one LDS object (A code slots, B code slots, the scale slots, then 64 kSRow
-  // bytes a wave where the skipped scale loads land), so the waits the
-  // compiler places for direct loads are the ones written below
-  constexpr int kScaleBase = 2 * kStage;                  // u32x4 index of the scale slots
-  constexpr int kJunkBase = kScaleBase + 2 * kScaleSlot / 16;
-  __shared__ u32x4 lds[kJunkBase + 4 * 64 * kSRow / 16];
+  // bytes where the skipped scale loads land), so the waits the compiler
+  // places for direct loads are the ones written below
+  constexpr int kScaleBase = NS * kStage;                 // u32x4 index of the scale slots
+  constexpr int kJunkBase = kScaleBase + NSS * kScaleSlot / 16;
+  __shared__ u32x4 lds[kJunkBase + 64 * kSRow / 16];
+  static_assert(sizeof(lds) <= 160 * 1024, "LDS");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -267,10 +280,10 @@ void gemm_mx_kernel(MxArgs g) {
   constexpr int kASlot = BM * kMxCh, kBSlot = kMxBN * kMxCh;   // u32x4 per slot
   int a_lo = (wm * (BM / 2) + rr) * kMxCh + mx_swz(rr, q);
   int a_hi = (wm * (BM / 2) + rr) * kMxCh + mx_swz(rr, q + 4);
-  int b_lo = 2 * kASlot + (wn * 128 + rr) * kMxCh + mx_swz(rr, q);
-  int b_hi = 2 * kASlot + (wn * 128 + rr) * kMxCh + mx_swz(rr, q + 4);
+  int b_lo = NS * kASlot + (wn * 128 + rr) * kMxCh + mx_swz(rr, q);
+  int b_hi = NS * kASlot + (wn * 128 + rr) * kMxCh + mx_swz(rr, q + 4);
   int sa_b = kScaleBase * 16 + (wm * (BM / 2) + rr) * kSRow + q;
-  int sb_b = kScaleBase * 16 + (kMxBN + wn * 128 + rr) * kSRow + q;
+  int sb_b = kScaleBase * 16 + (BM + wn * 128 + rr) * kSRow + q;
   __asm__ volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi), "+v"(sa_b), "+v"(sb_b));
 
   const MxTail tp = mx_tail_plan(total, gridDim.x, nk, g.part_cap);
@@ -338,17 +351,18 @@ void gemm_mx_kernel(MxArgs g) {
         else
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               rb,
-              (__attribute__((address_space(3))) void*)(lds + 2 * kASlot + sl * kBSlot +
+              (__attribute__((address_space(3))) void*)(lds + NS * kASlot + sl * kBSlot +
                                                         (32 * (n - MB) + 8 * wave) * kMxCh),
               16, vb, static_cast<uint32_t>(32 * (n - MB)) * row_bytes + kb, 0, 0);
       }
     };
     // scale group G (K steps SG G .. SG G + SG - 1) of this wave's A (n = 0) or B
-    // (n = 1) rows into scale slot G % 2; with on false the load reads nothing
-    // (an offset past the end) and lands in this wave's scratch area
+    // (n = 1) rows 64 w .. 64 w + 63 into scale slot G % NSS; with on false (or
+    // A rows from BM on) the load reads nothing (an offset past the end) and
+    // lands in the scratch area
     auto issue_scales = [&](int G, int n, bool on) __attribute__((always_inline)) {
-      const int dst = on ? kScaleBase + ((G & 1) * kScaleSlot + (n * kMxBN + 64 * wave) * kSRow) / 16
-                         : kJunkBase + 64 * wave * kSRow / 16;
+      on = on && (n == 1 || 64 * wave < BM);
+      const int dst = on ? kScaleBase + ((G % NSS) * kScaleSlot + (n * BM + 64 * wave) * kSRow) / 16 : kJunkBase;
       const uint32_t vo = on ? (n == 0 ? vs_a : vs_b) : 0x80000000u;
       const uint32_t so = on ? static_cast<uint32_t>(G) * kSRow : 0u;
       auto* lp = (__attribute__((address_space(3))) void*)(lds + dst);
@@ -360,7 +374,7 @@ void gemm_mx_kernel(MxArgs g) {
     // byte offset, within the scale slots, of stage t's scales (K step k0 + t)
     auto sofs = [&](int t) __attribute__((always_inline)) {
       const int a = k0 + t;
-      return ((a / SG) & 1) * kScaleSlot + (a % SG) * 4;
+      return ((a / SG) % NSS) * kScaleSlot + (a % SG) * 4;
     };
 
     // fragments: B blocks 0..7 and A blocks 0..MB-1 with their scale bytes;
@@ -376,14 +390,14 @@ void gemm_mx_kernel(MxArgs g) {
       f = __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       sc = l8[sc_i];
     };
-    // fragments of stage t (ring slot t % 2); the wave-uniform offsets are added
-    // to the lane bases once per use site
+    // fragments of stage t (ring slot t % NS); the wave-uniform offsets are
+    // added to the lane bases once per use site
     auto readA = [&](int t, int i) __attribute__((always_inline)) {
-      const int o = (t & 1) * kASlot + 16 * i * kMxCh;
+      const int o = (t % NS) * kASlot + 16 * i * kMxCh;
       frag(a_lo + o, a_hi + o, sa_b + sofs(t) + 16 * kSRow * i, fa[i], sa[i]);
     };
     auto readB = [&](int t, int j) __attribute__((always_inline)) {
-      const int o = (t & 1) * kBSlot + 16 * j * kMxCh;
+      const int o = (t % NS) * kBSlot + 16 * j * kMxCh;
       frag(b_lo + o, b_hi + o, sb_b + sofs(t) + 16 * kSRow * j, fb[j], sb[j]);
     };
 
@@ -393,17 +407,18 @@ void gemm_mx_kernel(MxArgs g) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // prologue: stages 0 and 1 and the first two scale groups in flight, stage 0
-    // published, its B blocks and A rows 0, 1 read
+    // prologue: stages 0 .. NS-1 in flight, each after two scale loads as in the
+    // loop (the first two scale groups, or at SG = 1 the stage's own), stage 0
+    // published, its B blocks and A rows 0, 1 read.  Stages past the end load
+    // the last stage again, into slots no step reads.
 #pragma unroll
-    for (int n = 0; n < NR; ++n) issue1(0, 0, n);
-    if (kn > 1) {
+    for (int sp = 0; sp < NS; ++sp) {
 #pragma unroll
-      for (int n = 0; n < NR; ++n) issue1(1, 1, n);
+      for (int n = 0; n < 2; ++n) issue_scales(SG == 1 ? k0 + sp : k0 / SG + sp, n, SG == 1 || sp < 2);
+#pragma unroll
+      for (int n = 0; n < NR; ++n) issue1(sp, min(sp, kn - 1), n);
     }
-#pragma unroll
-    for (int n = 0; n < 4; ++n) issue_scales(k0 / SG + n / 2, n & 1, true);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm((NS - 1) * (NR + 2)));   // stage 0 (and what came before it)
     mx_barrier();
     readA(0, 0);
 #pragma unroll
@@ -414,12 +429,12 @@ void gemm_mx_kernel(MxArgs g) {
     // than the loop's own reads) on every step.
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt 0
 
-    // step t in ring slot cur = t % 2.  A step that starts a scale group G loads
-    // group G + kLook into the slot whose last stage was read before this
-    // step's barrier; the group's first stage is read two steps on or later.
+    // step t in ring slot cur = t % NS.  A step that starts a scale group G loads
+    // group G + kLook, just before the codes of stage t+NS, so the wait for any
+    // later stage covers it.
     auto kstep = [&](int t) __attribute__((always_inline)) {
-      const int cur = t & 1;
-      const int t2 = min(t + 2, kn - 1);   // past the end: the last stage again, into a slot no step reads
+      const int cur = t % NS;
+      const int t2 = min(t + NS, kn - 1);   // past the end: the last stage again, into a slot no step reads
       const bool group_start = (k0 + t) % SG == 0;
       const int gnext = (k0 + t) / SG + kLook;
 #pragma unroll
@@ -430,7 +445,7 @@ void gemm_mx_kernel(MxArgs g) {
         if ((m & 1) == 0 && (m >> 1) < NF1) readA(t, 2 + (m >> 1));
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0: stage t+1 landed in this wave
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(kVmWait));   // stage t+1 landed in this wave
       mx_barrier();                          // ... in every wave, and every wave has stage t in registers
 #pragma unroll
       for (int m = 0; m < HM; ++m) {
@@ -441,8 +456,8 @@ void gemm_mx_kernel(MxArgs g) {
                                                                      sa[i]);
         if (m < 2) readA(t + 1, m);
         if (i == MB - 1) readB(t + 1, j);
-        if (m < NR) issue1(cur, t2, m);
-        if (m == NR || m == NR + 1) issue_scales(gnext, m - NR, group_start);
+        if (m < 2) issue_scales(gnext, m, group_start);
+        if (m >= 2 && m < NR + 2) issue1(cur, t2, m - 2);
         __builtin_amdgcn_sched_barrier(0);
       }
     };

@@ -10,10 +10,10 @@ from .moe_ref import (ACTIVATIONS, TIE_EPS, ExpertChoice, ExpertChoiceRef, MoERe
                       capacity_ranks, expert_choice_capacity, expert_counts, expert_ffn, gelu,
                       is_valid_expert_choice, is_valid_topk, moe_forward_expert_choice_ref, moe_forward_ref,
                       moe_forward_ref_from_inputs, renormalised_weights, router_logits, router_z_loss,
-                      select_expert_choice, select_topk, silu, softmax, widen)
+                      select_expert_choice, select_topk, selection_keys, silu, softmax, widen)
 
 __all__ = ["ACTIVATIONS", "TIE_EPS", "ExpertChoice", "ExpertChoiceRef", "MoERef", "expert_choice_capacity",
            "is_valid_expert_choice", "moe_forward_expert_choice_ref", "select_expert_choice", "aux_loss", "capacity_of", "capacity_ranks",
            "expert_counts", "expert_ffn", "gelu", "is_valid_topk", "moe_forward_ref",
            "moe_forward_ref_from_inputs", "renormalised_weights", "router_logits", "router_z_loss",
-           "select_topk", "silu", "softmax", "widen"]
+           "select_topk", "selection_keys", "silu", "softmax", "widen"]

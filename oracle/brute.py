@@ -43,11 +43,14 @@ def brute_topk(logits: Sequence[float], k: int):
 
 def brute_layer(x: List[List[float]], W_g: List[List[float]], experts, k: int,
                 cap: Optional[int] = None, n_shared: int = 0,
-                b_g: Optional[Sequence[float]] = None, activation: str = "gelu"):
+                b_g: Optional[Sequence[float]] = None, activation: str = "gelu",
+                b_sel: Optional[Sequence[float]] = None):
     """x: T lists of d floats; W_g: E lists of d floats; experts: list of
     (W1 [h][d], b1 [h] or None, W2 [d][h], b2 [d] or None) for E routed then
     n_shared shared; activation "gelu" (erf form) or "silu" (u / (1 + e^-u),
-    the Mixtral expert of the guide's §6.1).
+    the Mixtral expert of the guide's §6.1); b_sel a per-expert bias that
+    enters the choice of experts only (the subset search ranks l + b_sel; the
+    weights, P and z come from l).
 
     Returns dict(out, idx, w, counts, kept, dropped, slot_kept, aux, z)."""
     T = len(x)
@@ -64,7 +67,10 @@ def brute_layer(x: List[List[float]], W_g: List[List[float]], experts, k: int,
         logits.append(lt)
         probs.append([v / z for v in ex])
 
-    idx = [brute_topk(logits[t], k) for t in range(T)]
+    if b_sel is None:
+        idx = [brute_topk(logits[t], k) for t in range(T)]
+    else:
+        idx = [brute_topk([logits[t][e] + b_sel[e] for e in range(E)], k) for t in range(T)]
     w = []
     for t in range(T):
         sel = [probs[t][e] for e in idx[t]]

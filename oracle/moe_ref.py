@@ -270,20 +270,36 @@ class MoERef:
     P: np.ndarray
     rows: np.ndarray         # token ids whose outputs are in ``out``
     out: np.ndarray          # [len(rows), d] float64
+    keys: Optional[np.ndarray] = None   # [T,E] what the top-k ranks: logits (+ b_sel)
+
+
+def selection_keys(l: np.ndarray, b_sel=None) -> np.ndarray:
+    """What the top-k ranks: the logits, plus an optional float32 per-expert
+    bias b_sel that changes which experts are chosen but not their weights.
+
+    [guide] §4.3 and §7.1 and [bee] (DeepSeek-V3): the balance loss is
+    replaced by a bias on the router logits that is adjusted during training
+    to correct the experts' usage.  The pages write it inside the logits
+    (``b_g`` here); this is the other reading, where only the choice sees it:
+    the softmax weights, the balance loss's P and the z-loss use l."""
+    if b_sel is None:
+        return l
+    return l + np.asarray(b_sel, dtype=np.float32).astype(np.float64)[None, :]
 
 
 def moe_forward_ref(x, W_g, get_expert: Callable[[int], tuple], E: int, k: int,
                     capacity_factor: float = 0.0, n_shared: int = 0, b_g=None,
                     kind: str = "f32", rows: Optional[Sequence[int]] = None,
                     override_idx: Optional[np.ndarray] = None, activation: str = "gelu",
-                    min_capacity: int = 0) -> MoERef:
+                    min_capacity: int = 0, b_sel=None) -> MoERef:
     """The whole layer forward in float64.
 
     x [T,d] and W_g [E,d] are raw inputs of ``kind`` ("f32", "bf16" bit
     patterns, or "f64"); ``get_expert(e)`` returns the raw (W1 [h,d], b1 [h],
     W2 [d,h], b2 [d]) of expert e, routed for e < E and shared for
     E <= e < E + n_shared, either bias possibly None (bias-free Linear);
-    b_g is an optional float32 logit offset [E].  ``activation`` is "gelu"
+    b_g is an optional float32 logit offset [E]; b_sel an optional float32
+    selection-only bias [E] (see selection_keys).  ``activation`` is "gelu"
     or "silu"; ``min_capacity`` floors the capacity (see capacity_of).
 
     ``rows`` restricts the expert computation to those tokens (routing,
@@ -292,14 +308,16 @@ def moe_forward_ref(x, W_g, get_expert: Callable[[int], tuple], E: int, k: int,
     comparison after a near-tie was resolved the other way by rounding).
 
     Steps ([guide] §3.1 and §7.1; [ch7] §7.1 MoE(x) = sum G_i E_i(x)):
-      1 logits  2 softmax  3 top-k  4 renormalise  5 counts, aux and z-loss
-      6 capacity in token order  7 weighted routed experts  8 shared experts.
+      1 logits  2 softmax  3 top-k (of the logits, + b_sel)  4 renormalise
+      5 counts, aux and z-loss  6 capacity in token order  7 weighted routed
+      experts  8 shared experts.
     """
     xf = widen(x, kind)
     T, d = xf.shape
     l = router_logits(xf, widen(W_g, kind), b_g)
     p = softmax(l)
-    sel = select_topk(l, k)
+    keys = selection_keys(l, b_sel)
+    sel = select_topk(keys, k)
     idx = sel.idx if override_idx is None else np.asarray(override_idx, dtype=np.int64).reshape(T, k)
     w = renormalised_weights(p, idx)
     counts = expert_counts(idx, E)
@@ -337,7 +355,7 @@ def moe_forward_ref(x, W_g, get_expert: Callable[[int], tuple], E: int, k: int,
     return MoERef(logits=l, probs=p, idx=idx, w=w, tie_flag=sel.tie_flag,
                   order_flag=sel.order_flag, counts=counts, kept=kept, rank=rank,
                   slot_kept=slot_kept, slot_pos=slot_pos, offsets=offsets, cap=cap,
-                  aux=aux, z=z, f=f, P=P, rows=rows_arr, out=out)
+                  aux=aux, z=z, f=f, P=P, rows=rows_arr, out=out, keys=keys)
 
 
 # --------------------------------------------------------- expert choice --
@@ -456,4 +474,5 @@ def moe_forward_ref_from_inputs(inp, rows=None, override_idx=None) -> MoERef:
     c = inp.cfg
     return moe_forward_ref(inp.x, inp.W_g, inp.expert, c.E, c.k, c.cf, c.S, inp.b_g,
                            kind=c.dtype, rows=rows, override_idx=override_idx,
-                           activation=c.activation, min_capacity=c.min_capacity)
+                           activation=c.activation, min_capacity=c.min_capacity,
+                           b_sel=getattr(inp, "b_sel", None))

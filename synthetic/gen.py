@@ -33,7 +33,7 @@ from typing import Optional
 import numpy as np
 
 # tensor ids of the per-(tensor, expert) random streams
-TID_X, TID_WG, TID_W1, TID_B1, TID_W2, TID_B2, TID_BG = range(7)
+TID_X, TID_WG, TID_W1, TID_B1, TID_W2, TID_B2, TID_BG, TID_BSEL = range(8)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -53,6 +53,7 @@ class MoEConfig:
     activation: str = "gelu"      # expert activation, "gelu" or "silu"
     expert_bias: bool = True      # False: bias-free expert Linears (b1, b2 are None)
     min_capacity: int = 0         # floor under the capacity when cf > 0
+    sel_bias_std: float = 0.0     # std of the fp32 selection-only router bias (0 => none)
 
     def replace(self, **kw) -> "MoEConfig":
         return dataclasses.replace(self, **kw)
@@ -106,6 +107,7 @@ class MoEInputs:
         self._x = None
         self._wg = None
         self._bg = None
+        self._bsel = None
 
     # token activations [T, d]
     @property
@@ -132,6 +134,16 @@ class MoEInputs:
         if self._bg is None:
             self._bg = _normal(self.seed, TID_BG, 0, (c.E,), c.router_bias_std)
         return self._bg
+
+    # optional fp32 selection-only router bias [E]
+    @property
+    def b_sel(self) -> Optional[np.ndarray]:
+        c = self.cfg
+        if c.sel_bias_std <= 0:
+            return None
+        if self._bsel is None:
+            self._bsel = _normal(self.seed, TID_BSEL, 0, (c.E,), c.sel_bias_std)
+        return self._bsel
 
     def expert(self, e: int):
         """(W1 [h,d], b1 [h], W2 [d,h], b2 [d]) of expert e (routed or shared);

@@ -86,6 +86,12 @@ MUTANTS = [
     ("ec_capacity_not_clipped", "    return min(T, cap)", "    return cap"),
     ("ec_shared_weighted_half", "        out = out + expert_ffn(xf[rows_arr], W1, b1, W2, b2, activation)",
      "        out = out + 0.5 * expert_ffn(xf[rows_arr], W1, b1, W2, b2, activation)"),
+    ("sel_bias_ignored", "return l + np.asarray(b_sel, dtype=np.float32).astype(np.float64)[None, :]", "return l"),
+    ("sel_bias_subtracted", "return l + np.asarray(b_sel, dtype=np.float32).astype(np.float64)[None, :]",
+     "return l - np.asarray(b_sel, dtype=np.float32).astype(np.float64)[None, :]"),
+    ("sel_bias_in_weights", "    p = softmax(l)\n    keys = selection_keys(l, b_sel)",
+     "    p = softmax(selection_keys(l, b_sel))\n    keys = selection_keys(l, b_sel)"),
+    ("sel_bias_in_z_loss", "z = router_z_loss(l)", "z = router_z_loss(keys)"),
 ]
 
 

@@ -558,13 +558,76 @@ def check_golden_expert_choice():
     assert np.allclose(r.out[:, 0], want, rtol=0, atol=1e-15)
 
 
+def check_selection_bias_closed_form():
+    """A selection-only router bias ([guide] §4.3 / §7.1 and [bee]: DeepSeek-V3
+    corrects expert usage with a bias on the router logits; this is the reading
+    where only the choice sees it).  One token, logits (2, 1, 0), b_sel =
+    (0, 0, 3), k = 2: the keys (2, 1, 3) choose experts 2 then 0; their weights
+    are the plain softmax probabilities renormalised, 1/(e^2+1) and
+    e^2/(e^2+1); f = (1/2, 0, 1/2) with P the plain softmax, so aux =
+    1.5 (e^2+1)/(e^2+e+1); z = log(e^2+e+1)^2.  Expert e maps x = 1 to
+    GELU(e + 1)."""
+    Phi = lambda u: 0.5 * (1.0 + math.erf(u / math.sqrt(2.0)))
+    gelu = lambda u: u * Phi(u)
+    e2 = math.e ** 2
+    x = np.array([[1.0]])
+    W_g = np.array([[2.0], [1.0], [0.0]])
+    ex = [(np.array([[e + 1.0]]), np.zeros(1), np.array([[1.0]]), np.zeros(1)) for e in range(3)]
+    r = run_ref(x, W_g, ex, 3, 2, b_sel=np.array([0.0, 0.0, 3.0], dtype=np.float32))
+    assert r.idx.tolist() == [[2, 0]]
+    assert np.allclose(r.w[0], [1.0 / (e2 + 1.0), e2 / (e2 + 1.0)], rtol=0, atol=1e-15)
+    assert r.counts.tolist() == [1, 0, 1]
+    assert abs(r.aux - 1.5 * (e2 + 1.0) / (e2 + math.e + 1.0)) < 1e-14
+    assert abs(r.z - math.log(e2 + math.e + 1.0) ** 2) < 1e-14
+    assert np.allclose(r.P, np.array([e2, math.e, 1.0]) / (e2 + math.e + 1.0), rtol=0, atol=1e-15)
+    want = (gelu(3.0) + e2 * gelu(1.0)) / (e2 + 1.0)
+    assert abs(r.out[0, 0] - want) < 1e-14
+    assert np.array_equal(r.keys, np.array([[2.0, 1.0, 3.0]]))
+    # without it the plain top-2 (experts 0, 1)
+    assert run_ref(x, W_g, ex, 3, 2).idx.tolist() == [[0, 1]]
+
+
+def check_selection_bias_invariants_and_brute():
+    """A zero or constant selection bias changes nothing; a random one agrees
+    with brute force (the subset search ranks l + b_sel, weights, P and z from l)
+    with capacity, shared experts and a router offset."""
+    rng = np.random.default_rng(31)
+    x, W_g, ex = rand_case(rng, 30, 5, 3, 6, 2, 1)
+    base = run_ref(x, W_g, ex, 6, 2, 1.25, 1)
+    for b in (np.zeros(6, dtype=np.float32), np.full(6, 5.0, dtype=np.float32)):
+        r = run_ref(x, W_g, ex, 6, 2, 1.25, 1, b_sel=b)
+        assert np.array_equal(r.idx, base.idx) and np.array_equal(r.w, base.w)
+        assert np.array_equal(r.kept, base.kept) and r.aux == base.aux and r.z == base.z
+        assert np.array_equal(r.out, base.out)
+    for (T, d, h, E, k, S, cf) in [(8, 3, 2, 5, 2, 0, None), (7, 2, 3, 4, 3, 1, 0.75), (8, 3, 2, 6, 1, 0, 1.0)]:
+        for trial in range(3):
+            x, W_g, ex = rand_case(rng, T, d, h, E, k, S)
+            b_sel = (rng.standard_normal(E) * 2.0).astype(np.float32)
+            b_g = rng.standard_normal(E) if trial == 1 else None
+            r = run_ref(x, W_g, ex, E, k, cf or 0.0, S, b_g, b_sel=b_sel)
+            assert not r.tie_flag.any()
+            cap = None if not cf else int(math.ceil(cf * T / E))
+            vec = lambda b: None if b is None else list(map(float, b))
+            exl = [(to_lists(W1), vec(b1), to_lists(W2), vec(b2)) for (W1, b1, W2, b2) in ex]
+            b = brute.brute_layer(to_lists(x), to_lists(W_g), exl, k, cap=cap, n_shared=S, b_g=vec(b_g),
+                                  b_sel=vec(b_sel))
+            assert r.idx.tolist() == b["idx"]
+            assert np.allclose(r.w, np.array(b["w"]), rtol=0, atol=1e-13)
+            assert r.kept.tolist() == b["kept"] and r.slot_kept.tolist() == b["slot_kept"]
+            assert abs(r.aux - b["aux"]) < 1e-13 and abs(r.z - b["z"]) < 1e-12
+            assert np.allclose(r.out, np.array(b["out"]), rtol=0, atol=1e-12)
+        # some selections do change
+        assert not np.array_equal(run_ref(x, W_g, ex, E, k, cf or 0.0, S).idx, r.idx) or k == E
+
+
 ALL_CHECKS = [check_weights_sum_to_one, check_against_brute, check_topk_vs_torch, check_tie_rule,
               check_dense_limit, check_aux_closed_forms, check_capacity, check_dropped_contribute_nothing,
               check_ffn_library, check_combine_symmetries, check_shared, check_golden_fixtures,
               check_rows_and_override, check_widen_bf16, check_z_loss_closed_forms,
               check_silu_and_bias_free, check_min_capacity, check_mixtral_expert_against_brute,
               check_golden_silu_min_capacity, check_ec_against_brute, check_ec_dense_limit_and_balance,
-              check_golden_expert_choice]
+              check_golden_expert_choice, check_selection_bias_closed_form,
+              check_selection_bias_invariants_and_brute]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=[c.__name__ for c in ALL_CHECKS])

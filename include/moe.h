@@ -98,6 +98,15 @@ typedef struct {
                              0 = MOE_ACT_GELU (a zero-initialised struct keeps GELU) */
   int32_t min_capacity;   /* >= 0: floor under the capacity when capacity_factor > 0
                              (cap = max(ceil(cf*T/E), min_capacity)); ignored otherwise */
+  const float* b_sel;     /* [E] float32, or NULL: a selection-only router bias.  The top-k
+                             ranks l[t,e] + b_sel[e] (ties to the lower expert index);
+                             the weights, the balance loss's P and the z-loss use l
+                             itself.  The DeepSeek-V3 bias of the MoE training guide
+                             §4.3/§7.1 and the BEE-30064 page (a bias on the router
+                             logits that corrects expert usage), in the reading where
+                             only the choice sees it (b_g is the in-logit reading).
+                             No effect under expert choice: a per-expert constant does
+                             not reorder an expert's tokens. */
 } moe_launch_t;
 
 /* Bytes of device workspace moe_forward needs for this problem shape (0 if
@@ -120,7 +129,8 @@ size_t moe_workspace_bytes(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k
  *            (the ceiling in double precision)
  *   n_shared shared experts S, 0..MOE_MAX_SHARED
  *   out      [T, d]          layer output, dtype (bf16: accumulated in float32, rounded once)
- *   topk_idx [T, k] int32    slot j = the (j+1)-th largest logit (before capacity)
+ *   topk_idx [T, k] int32    slot j = the (j+1)-th largest logit, + launch->b_sel if given
+ *            (before capacity)
  *   topk_w   [T, k] float32  renormalised weights of those slots (before capacity)
  *   aux_loss [1]    float32  E * sum_e f_e P_e
  *   launch   shape, dtype, optional outputs, workspace and stream (required)

@@ -130,7 +130,7 @@ def dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 def moe_forward_mxfp8_ref(x, W_g, experts_q, E: int, k: int, capacity_factor: float = 0.0, n_shared: int = 0,
                           b_g=None, kind: str = "bf16", rows: Optional[Sequence[int]] = None,
                           override_idx: Optional[np.ndarray] = None, activation: str = "gelu",
-                          min_capacity: int = 0):
+                          min_capacity: int = 0, b_sel=None):
     """The layer with MXFP8 expert Linears, in float64.
 
     ``experts_q(e)`` returns (W1 codes [h,d], W1 scales [h,d/32], b1 [h] or
@@ -144,7 +144,7 @@ def moe_forward_mxfp8_ref(x, W_g, experts_q, E: int, k: int, capacity_factor: fl
     and the combine weights y as in the plain layer."""
     base = moe_ref.moe_forward_ref(x, W_g, lambda e: _no_ffn(experts_q, e, kind), E, k, capacity_factor,
                                    n_shared, b_g, kind=kind, rows=rows, override_idx=override_idx,
-                                   activation=activation, min_capacity=min_capacity)
+                                   activation=activation, min_capacity=min_capacity, b_sel=b_sel)
     xf = moe_ref.widen(x, kind)
     T, d = xf.shape
     xq = dequantize(*quantize(xf))

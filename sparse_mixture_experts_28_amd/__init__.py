@@ -67,13 +67,21 @@ def _check_tensors(x, W_g, W1, b1, W2, b2, b_g, n_shared: int, activation: str) 
         raise ValueError("b_g must be float32 [E] on the same GPU")
 
 
-def _launch(x, T, d, h, dt, b_g, workspace, zl, activation, min_capacity, stage_events):
+def _check_b_sel(b_sel, E, dev):
+    import torch
+    if b_sel is not None and (b_sel.dtype != torch.float32 or b_sel.shape != (E,) or b_sel.device != dev
+                              or not b_sel.is_contiguous()):
+        raise ValueError("b_sel must be a contiguous float32 [E] on the same GPU")
+
+
+def _launch(x, T, d, h, dt, b_g, workspace, zl, activation, min_capacity, stage_events, b_sel=None):
     """A moe_launch_t on torch's current stream; returns it and the event-handle
     array that must stay alive until the call returns."""
     import torch
     launch = MoeLaunch()
     launch.T, launch.d, launch.h, launch.dtype = T, d, h, dt
     launch.b_g = b_g.data_ptr() if b_g is not None else None
+    launch.b_sel = b_sel.data_ptr() if b_sel is not None else None
     launch.workspace = workspace.data_ptr()
     launch.workspace_bytes = workspace.numel()
     launch.stream = torch.cuda.current_stream(x.device).cuda_stream
@@ -94,13 +102,15 @@ def _launch(x, T, d, h, dt, b_g, workspace, zl, activation, min_capacity, stage_
 
 def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shared: int = 0, b_g=None,
             *, activation: str = "gelu", min_capacity: int = 0, stage_events: Optional[Sequence] = None,
-            workspace=None) -> MoEOutput:
+            workspace=None, b_sel=None) -> MoEOutput:
     """Run the layer on torch tensors that live on one GPU.
 
     x [T,d]; W_g [E,d]; W1 [E+S,h,d]; b1 [E+S,h] or None; W2 [E+S,d,h];
     b2 [E+S,d] or None (float32 or bfloat16, contiguous; None = bias-free
-    Linear); b_g optional float32 [E].  ``activation`` is "gelu" or "silu";
-    ``min_capacity`` floors the capacity when capacity_factor > 0.
+    Linear); b_g optional float32 [E] added to the logits; b_sel optional
+    float32 [E] seen by the top-k choice only (moe_launch_t.b_sel).
+    ``activation`` is "gelu" or "silu"; ``min_capacity`` floors the capacity
+    when capacity_factor > 0.
     ``stage_events``: optional list of MOE_NUM_STAGE_EVENTS torch.cuda.Event
     objects (already recorded once, so their handles exist) that the library
     records at its stage boundaries.  Raises RuntimeError on a non-zero status.
@@ -112,6 +122,7 @@ def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shar
     h = W1.shape[1]
     S = n_shared
     dev = x.device
+    _check_b_sel(b_sel, E, dev)
     dt = _dtype_code(x)
     nbytes = moe_workspace_bytes(T, d, h, E, k, S, dt)
     if nbytes == 0:
@@ -127,7 +138,7 @@ def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shar
     kept = torch.empty((E,), dtype=torch.int32, device=dev)
     slot_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
 
-    launch, keep = _launch(x, T, d, h, dt, b_g, workspace, zl, activation, min_capacity, stage_events)
+    launch, keep = _launch(x, T, d, h, dt, b_g, workspace, zl, activation, min_capacity, stage_events, b_sel)
     launch.expert_counts = counts.data_ptr()
     launch.expert_kept = kept.data_ptr()
     launch.slot_pos = slot_pos.data_ptr()
@@ -212,9 +223,10 @@ def quantize_mxfp8(w):
 
 def forward_mxfp8(x, W_g, W1, W1s, b1, W2, W2s, b2, k: int, capacity_factor: float = 0.0, n_shared: int = 0,
                   b_g=None, *, activation: str = "gelu", min_capacity: int = 0,
-                  stage_events: Optional[Sequence] = None, workspace=None) -> MoEOutput:
+                  stage_events: Optional[Sequence] = None, workspace=None, b_sel=None) -> MoEOutput:
     """The layer with MXFP8 expert Linears: x, W_g, biases bf16; W1 / W2 as
-    (codes, scales) from ``quantize_mxfp8`` of [E+S, h, d] / [E+S, d, h]."""
+    (codes, scales) from ``quantize_mxfp8`` of [E+S, h, d] / [E+S, d, h];
+    b_g and b_sel as in ``forward``."""
     import torch
     if x.dtype != torch.bfloat16:
         raise ValueError("the MXFP8 layer takes bf16 activations")
@@ -229,6 +241,7 @@ def forward_mxfp8(x, W_g, W1, W1s, b1, W2, W2s, b2, k: int, capacity_factor: flo
         if t is not None and (not t.is_cuda or t.device != x.device or not t.is_contiguous()):
             raise ValueError("all tensors must be contiguous on one GPU")
     dev = x.device
+    _check_b_sel(b_sel, E, dev)
     nbytes = moe_workspace_bytes_mxfp8(T, d, h, E, k, S)
     if nbytes == 0:
         raise RuntimeError("invalid problem shape for moe_workspace_bytes_mxfp8")
@@ -242,7 +255,7 @@ def forward_mxfp8(x, W_g, W1, W1s, b1, W2, W2s, b2, k: int, capacity_factor: flo
     counts = torch.empty((E,), dtype=torch.int32, device=dev)
     kept = torch.empty((E,), dtype=torch.int32, device=dev)
     slot_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
-    launch, keep = _launch(x, T, d, h, MOE_BF16, b_g, workspace, zl, activation, min_capacity, stage_events)
+    launch, keep = _launch(x, T, d, h, MOE_BF16, b_g, workspace, zl, activation, min_capacity, stage_events, b_sel)
     launch.expert_counts, launch.expert_kept, launch.slot_pos = counts.data_ptr(), kept.data_ptr(), slot_pos.data_ptr()
     ptr = lambda t: t.data_ptr() if t is not None else None
     status = moe_forward_mxfp8(x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), W1s.data_ptr(), ptr(b1), W2.data_ptr(),

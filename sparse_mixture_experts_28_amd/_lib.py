@@ -53,6 +53,7 @@ class MoeLaunch(ctypes.Structure):
         ("z_loss", ctypes.c_void_p),
         ("activation", ctypes.c_int32),
         ("min_capacity", ctypes.c_int32),
+        ("b_sel", ctypes.c_void_p),
     ]
 
 

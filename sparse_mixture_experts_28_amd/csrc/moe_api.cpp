@@ -255,7 +255,7 @@ moe_status_t moe_forward_mxfp8(const void* x, const void* W_g, const uint8_t* W1
   const void* a16[] = {x, W_g, W1, W2, out, b1, b2};
   for (const void* q : a16)
     if (q && !aligned(q, 16)) return MOE_ERR_UNSUPPORTED;
-  const void* a4[] = {W1_scales, W2_scales, topk_idx, topk_w, aux_loss, launch->z_loss, launch->b_g,
+  const void* a4[] = {W1_scales, W2_scales, topk_idx, topk_w, aux_loss, launch->z_loss, launch->b_g, launch->b_sel,
                       launch->expert_counts, launch->expert_kept, launch->slot_pos};
   for (const void* q : a4)
     if (q && !aligned(q, 4)) return MOE_ERR_UNSUPPORTED;
@@ -272,7 +272,7 @@ moe_status_t moe_forward_mxfp8(const void* x, const void* W_g, const uint8_t* W1
   StageCheck check{st, launch->stage_events};
   (void)hipGetLastError();
   if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
-  if (!check(launch_router(p, x, W_g, launch->b_g, topk_idx, topk_w, ws, st), "router launch")) return MOE_ERR_HIP;
+  if (!check(launch_router(p, x, W_g, launch->b_g, launch->b_sel, topk_idx, topk_w, ws, st), "router launch")) return MOE_ERR_HIP;
   if (!check(launch_scan(p, ws, aux_loss, launch->z_loss, launch->expert_counts, launch->expert_kept, st),
              "scan launch"))
     return MOE_ERR_HIP;
@@ -322,7 +322,7 @@ moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const v
   const void* a16[] = {x, W_g, W1, b1, W2, b2, out};
   for (const void* q : a16)
     if (q && !aligned(q, 16)) return MOE_ERR_UNSUPPORTED;
-  const void* a4[] = {topk_idx, topk_w, aux_loss, launch->z_loss, launch->b_g, launch->expert_counts,
+  const void* a4[] = {topk_idx, topk_w, aux_loss, launch->z_loss, launch->b_g, launch->b_sel, launch->expert_counts,
                       launch->expert_kept, launch->slot_pos};
   for (const void* q : a4)
     if (q && !aligned(q, 4)) return MOE_ERR_UNSUPPORTED;
@@ -340,7 +340,7 @@ moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const v
   (void)hipGetLastError();
 
   if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
-  if (!check(launch_router(p, x, W_g, launch->b_g, topk_idx, topk_w, ws, st), "router launch")) return MOE_ERR_HIP;
+  if (!check(launch_router(p, x, W_g, launch->b_g, launch->b_sel, topk_idx, topk_w, ws, st), "router launch")) return MOE_ERR_HIP;
   if (!check(launch_scan(p, ws, aux_loss, launch->z_loss, launch->expert_counts, launch->expert_kept, st),
              "scan launch"))
     return MOE_ERR_HIP;
@@ -365,7 +365,7 @@ moe_status_t moe_forward_expert_choice(const void* x, const void* W_g, const voi
   const void* a16[] = {x, W_g, W1, b1, W2, b2, out};
   for (const void* q : a16)
     if (q && !aligned(q, 16)) return MOE_ERR_UNSUPPORTED;
-  const void* a4[] = {ec_token, ec_w, aux_loss, launch->z_loss, launch->b_g, launch->expert_counts,
+  const void* a4[] = {ec_token, ec_w, aux_loss, launch->z_loss, launch->b_g, launch->b_sel, launch->expert_counts,
                       launch->expert_kept};
   for (const void* q : a4)
     if (q && !aligned(q, 4)) return MOE_ERR_UNSUPPORTED;
@@ -380,7 +380,7 @@ moe_status_t moe_forward_expert_choice(const void* x, const void* W_g, const voi
   StageCheck check{st, launch->stage_events};
   (void)hipGetLastError();
   if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
-  if (!check(launch_router(p, x, W_g, launch->b_g, nullptr, nullptr, ws, st), "router launch")) return MOE_ERR_HIP;
+  if (!check(launch_router(p, x, W_g, launch->b_g, nullptr, nullptr, nullptr, ws, st), "router launch")) return MOE_ERR_HIP;
   if (!check(launch_scan(p, ws, aux_loss, launch->z_loss, launch->expert_counts, launch->expert_kept, st),
              "scan launch"))
     return MOE_ERR_HIP;

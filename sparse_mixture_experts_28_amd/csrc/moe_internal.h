@@ -133,7 +133,7 @@ size_t workspace_bytes(const Problem& p);
 
 // ------------------------------------------------------ kernel launchers --
 // Each returns hipGetLastError() after its launch(es).
-hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const float* b_g,
+hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const float* b_g, const float* b_sel,
                          int32_t* topk_idx, float* topk_w, const Workspace& ws, hipStream_t st);
 hipError_t launch_scan(const Problem& p, const Workspace& ws, float* aux_loss, float* z_loss,
                        int32_t* counts_out, int32_t* kept_out, hipStream_t st);

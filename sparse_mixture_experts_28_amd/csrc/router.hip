@@ -34,6 +34,7 @@ struct RouterArgs {
   const void* x;
   const void* W_g;
   const float* b_g;
+  const float* b_sel;   // [E] selection-only bias, or nullptr
   int32_t* topk_idx;
   float* topk_w;
   int32_t* local_rank;
@@ -84,6 +85,18 @@ __device__ __forceinline__ void argmax16(double& v, int& i) {
   }
 }
 
+// argmax16 carrying a payload (the winner's plain logit when the ranking
+// includes the selection-only bias)
+__device__ __forceinline__ void argmax16p(double& v, int& i, double& pl) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    double ov = __shfl_xor(v, m, 16);
+    int oi = __shfl_xor(i, m, 16);
+    double op = __shfl_xor(pl, m, 16);
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; pl = op; }
+  }
+}
+
 __device__ __forceinline__ double max16(double v) {
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) v = fmax(v, __shfl_xor(v, m, 16));
@@ -94,6 +107,41 @@ __device__ __forceinline__ float sum16(float v) {
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m, 16);
   return v;
+}
+
+// k rounds of a 16-lane argmax over the not-yet-chosen experts (ties to the
+// lower index), ranking the logits plus the selection-only bias when there is
+// one; a chosen expert's weight numerator is exp(l - m) of its logit alone.
+// Lane j < k ends with the j-th choice and its numerator; every lane with
+// their sum.
+template <int NB>
+__device__ __forceinline__ void select_k(const RouterArgs& a, const double (&val)[NB], double m, int c, int& my_idx,
+                                         float& my_e, float& esum) {
+  const int E = a.E, k = a.k;
+  double key[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int e = nb * 16 + c;
+    key[nb] = a.b_sel && e < E ? val[nb] + static_cast<double>(a.b_sel[e]) : val[nb];
+  }
+  uint32_t taken = 0;
+  my_idx = 0;
+  my_e = 0.f;
+  esum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    double bv = -INFINITY, bl = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int e = nb * 16 + c;
+      if (e < E && !((taken >> nb) & 1u) && key[nb] > bv) { bv = key[nb]; bi = e; bl = val[nb]; }
+    }
+    argmax16p(bv, bi, bl);
+    if ((bi & 15) == c) taken |= 1u << (bi >> 4);
+    const float ej = __expf(static_cast<float>(bl - m));
+    esum += ej;
+    if (c == j) { my_idx = bi; my_e = ej; }
+  }
 }
 
 // Selection, weights, probability partials and ranks for one 64-token tile,
@@ -150,25 +198,9 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
       continue;
     }
 
-    // k rounds of a 16-lane argmax over the not-yet-chosen experts
-    uint32_t taken = 0;
-    int my_idx = 0;
-    float my_e = 0.f;
-    float esum = 0.f;
-    for (int j = 0; j < k; ++j) {
-      double bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int e = nb * 16 + c;
-        if (e < E && !((taken >> nb) & 1u) && val[nb] > bv) { bv = val[nb]; bi = e; }
-      }
-      argmax16(bv, bi);
-      if ((bi & 15) == c) taken |= 1u << (bi >> 4);
-      const float ej = __expf(static_cast<float>(bv - m));
-      esum += ej;
-      if (c == j) { my_idx = bi; my_e = ej; }
-    }
+    int my_idx;
+    float my_e, esum;
+    select_k<NB>(a, val, m, c, my_idx, my_e, esum);
     if (c < k) {
       s_idx[r * MOE_MAX_TOPK + c] = tok_ok ? my_idx : -1;
       if (tok_ok) {
@@ -517,25 +549,9 @@ __device__ __forceinline__ void select_tile(const RouterArgs& a, const double (&
   const bool ec = a.ec_logits != nullptr;
   if (ec) write_ec(a, val, m, z, t, c, tok_ok);
 
-  // k rounds of a 16-lane argmax over the not-yet-chosen experts
-  uint32_t taken = 0;
   int my_idx = 0;
-  float my_e = 0.f;
-  float esum = 0.f;
-  for (int j = 0; j < (ec ? 0 : k); ++j) {
-    double bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int e = nb * 16 + c;
-      if (e < E && !((taken >> nb) & 1u) && val[nb] > bv) { bv = val[nb]; bi = e; }
-    }
-    argmax16(bv, bi);
-    if ((bi & 15) == c) taken |= 1u << (bi >> 4);
-    const float ej = __expf(static_cast<float>(bv - m));
-    esum += ej;
-    if (c == j) { my_idx = bi; my_e = ej; }
-  }
+  float my_e = 0.f, esum = 0.f;
+  if (!ec) select_k<NB>(a, val, m, c, my_idx, my_e, esum);
   if (c < k && !ec) {
     s_idx[r * MOE_MAX_TOPK + c] = tok_ok ? my_idx : -1;
     if (tok_ok) {
@@ -630,12 +646,13 @@ int logit_splits(const Problem& p) {
   return ks < 1 ? 1 : static_cast<int>(ks);
 }
 
-hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const float* b_g,
+hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const float* b_g, const float* b_sel,
                          int32_t* topk_idx, float* topk_w, const Workspace& ws, hipStream_t st) {
   RouterArgs a;
   a.x = x;
   a.W_g = W_g;
   a.b_g = b_g;
+  a.b_sel = p.ec_C > 0 ? nullptr : b_sel;   // no effect on expert choice
   a.topk_idx = topk_idx;
   a.topk_w = topk_w;
   a.local_rank = ws.local_rank;

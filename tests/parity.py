@@ -33,6 +33,12 @@ def to_device(a: np.ndarray, kind: str, dev):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
 
+def _b_sel_device(inp, dev):
+    import torch
+    b = getattr(inp, "b_sel", None)
+    return None if b is None else torch.from_numpy(np.ascontiguousarray(b, dtype=np.float32)).to(dev)
+
+
 def run_gpu(inp, dev="cuda:0", stacked=None, workspace=None):
     """Upload a workload (synthetic.MoEInputs) and run the layer; returns numpy results."""
     import torch
@@ -41,7 +47,8 @@ def run_gpu(inp, dev="cuda:0", stacked=None, workspace=None):
     W1, b1, W2, b2 = stacked if stacked is not None else inp.stacked()
     args = [None if a is None else to_device(a, c.dtype, dev) for a in (inp.x, inp.W_g, W1, b1, W2, b2)]
     b_g = None if inp.b_g is None else torch.from_numpy(inp.b_g).to(dev)
-    r = moe.forward(*args, k=c.k, capacity_factor=c.cf, n_shared=c.S, b_g=b_g, activation=c.activation,
+    b_sel = _b_sel_device(inp, dev)
+    r = moe.forward(*args, k=c.k, capacity_factor=c.cf, n_shared=c.S, b_g=b_g, b_sel=b_sel, activation=c.activation,
                     min_capacity=c.min_capacity, workspace=workspace)
     torch.cuda.synchronize()
     out = r.out.float().cpu().numpy().astype(np.float64)
@@ -62,7 +69,7 @@ def oracle_for(inp, stacked=None, rows=None, override_idx=None):
     cf = float(np.float32(c.cf))   # the ABI takes the capacity factor as float32
     return ref.moe_forward_ref(inp.x, inp.W_g, get, c.E, c.k, cf, c.S, inp.b_g, kind=c.dtype, rows=rows,
                                override_idx=override_idx, activation=c.activation,
-                               min_capacity=c.min_capacity)
+                               min_capacity=c.min_capacity, b_sel=getattr(inp, "b_sel", None))
 
 
 def compare(inp, gpu: dict, stacked=None, rows=None, check_out=True) -> dict:
@@ -79,7 +86,7 @@ def compare(inp, gpu: dict, stacked=None, rows=None, check_out=True) -> dict:
     same_set = np.all(np.sort(gi, 1) == np.sort(r.idx, 1), axis=1)
     for t in np.nonzero(~same_set)[0]:
         assert r.tie_flag[t], f"token {t}: GPU chose {gi[t]} but the oracle's unflagged top-k is {r.idx[t]}"
-        assert ref.is_valid_topk(r.logits[t], gi[t]), f"token {t}: {gi[t]} is not a top-k set of its logits"
+        assert ref.is_valid_topk(r.keys[t], gi[t]), f"token {t}: {gi[t]} is not a top-k set of its logits (+ b_sel)"
     # slot order: descending logits (exact where unambiguous)
     strict = ~r.order_flag & same_set
     assert np.array_equal(gi[strict], r.idx[strict]), "slot order differs on order-unambiguous tokens"
@@ -213,7 +220,8 @@ def run_gpu_mx(inp, dev="cuda:0", stacked=None, workspace=None):
     W2c, W2s = moe.quantize_mxfp8(W2d)
     b_g = None if inp.b_g is None else torch.from_numpy(inp.b_g).to(dev)
     r = moe.forward_mxfp8(x, W_g, W1c, W1s, b1d, W2c, W2s, b2d, k=c.k, capacity_factor=c.cf, n_shared=c.S, b_g=b_g,
-                          activation=c.activation, min_capacity=c.min_capacity, workspace=workspace)
+                          b_sel=_b_sel_device(inp, dev), activation=c.activation, min_capacity=c.min_capacity,
+                          workspace=workspace)
     torch.cuda.synchronize()
     res = dict(out=r.out.float().cpu().numpy().astype(np.float64), idx=r.topk_idx.cpu().numpy().astype(np.int64),
                w=r.topk_w.cpu().numpy().astype(np.float64), aux=float(r.aux_loss.cpu().numpy()[0]),
@@ -248,7 +256,8 @@ def compare_mx(inp, gpu: dict, stacked=None, rows=None) -> dict:
     eq = lambda e: (W1c[e], W1s[e], None if b1 is None else b1[e], W2c[e], W2s[e], None if b2 is None else b2[e])
     r = mxfp8.moe_forward_mxfp8_ref(inp.x, inp.W_g, eq, c.E, c.k, float(np.float32(c.cf)), c.S, inp.b_g,
                                     kind="bf16", rows=rows, override_idx=gpu["idx"] if rep["rerun"] else None,
-                                    activation=c.activation, min_capacity=c.min_capacity)
+                                    activation=c.activation, min_capacity=c.min_capacity,
+                                    b_sel=getattr(inp, "b_sel", None))
     go = gpu["out"] if rows is None else gpu["out"][np.asarray(rows)]
     scale = float(np.max(np.abs(r.out)))
     err = float(np.max(np.abs(go - r.out)))

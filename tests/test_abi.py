@@ -33,12 +33,13 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_launch_struct_layout():
-    # int32 T, d, h; enum dtype; then 8-byte pointers / size_t; z_loss; int32 activation, min_capacity
+    # int32 T, d, h; enum dtype; then 8-byte pointers / size_t; z_loss; int32 activation, min_capacity; b_sel
     L = moe.MoeLaunch
     assert L.T.offset == 0 and L.d.offset == 4 and L.h.offset == 8 and L.dtype.offset == 12
     assert L.b_g.offset == 16 and L.workspace_bytes.offset == 56 and L.stream.offset == 64
     assert L.stage_events.offset == 72 and L.z_loss.offset == 80
-    assert L.activation.offset == 88 and L.min_capacity.offset == 92 and ctypes.sizeof(L) == 96
+    assert L.activation.offset == 88 and L.min_capacity.offset == 92
+    assert L.b_sel.offset == 96 and ctypes.sizeof(L) == 104
 
 
 def test_launch_struct_matches_header(tmp_path):
@@ -85,7 +86,7 @@ def call(**kw):
     args = dict(x=FAKE, W_g=FAKE, W1=FAKE, b1=FAKE, W2=FAKE, b2=FAKE, E=8, k=2, cf=0.0, S=0, out=FAKE,
                 idx=FAKE, w=FAKE, aux=FAKE)
     lk = dict(T=64, d=32, h=64, dtype=moe.MOE_BF16, workspace=FAKE, workspace_bytes=0, z_loss=None,
-              activation=moe.MOE_ACT_GELU, min_capacity=0)
+              activation=moe.MOE_ACT_GELU, min_capacity=0, b_sel=None)
     for key in list(kw):
         if key in lk:
             lk[key] = kw.pop(key)
@@ -94,6 +95,7 @@ def call(**kw):
     L.T, L.d, L.h, L.dtype = lk["T"], lk["d"], lk["h"], lk["dtype"]
     L.workspace = lk["workspace"]
     L.z_loss, L.activation, L.min_capacity = lk["z_loss"], lk["activation"], lk["min_capacity"]
+    L.b_sel = lk["b_sel"]
     need = moe.moe_workspace_bytes(L.T, L.d, L.h, args["E"], args["k"], args["S"], L.dtype)
     L.workspace_bytes = lk["workspace_bytes"] if lk["workspace_bytes"] else need
     return moe.moe_forward(args["x"], args["W_g"], args["W1"], args["b1"], args["W2"], args["b2"], args["E"],
@@ -134,6 +136,7 @@ def test_null_launch():
     (dict(b1=FAKE + 8), moe.MOE_ERR_UNSUPPORTED),
     (dict(min_capacity=4, cf=1.0, workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
     (dict(activation=moe.MOE_ACT_SILU, workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
+    (dict(b_sel=FAKE + 2), moe.MOE_ERR_UNSUPPORTED), (dict(b_sel=FAKE, workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
 ])
 def test_rejected_on_host(kw, code):
     assert call(**kw) == code

@@ -61,6 +61,8 @@ REDUCED = {
     # fewer tiles than workgroups: every tile is cut along K in both phases
     # (phase 1 pieces end in the MX-quantizing fix-up, phase 2 in the bf16 one)
     "mx_split_silu": ("mixtral", dict(T=600, d=2048, h=1024, E=8, activation="silu")),
+    # the selection-only router bias through the MXFP8 layer's router
+    "mx_sel_bias": ("glam", dict(T=1000, d=512, h=512, E=16, sel_bias_std=1.0)),
 }
 
 

@@ -5,8 +5,10 @@ every kernel and end in ragged tails; the five workloads run at full size
 with the oracle computing a sample of output rows; edge cases cover k = E,
 k = 1, E not a multiple of 16, a single token, empty experts, every token to
 one expert, capacity 1, several shared experts, d = 32, float32 and bf16;
-the Mixtral expert form (SiLU, bias-free) on every GEMM kernel and a capacity
-floor (min_capacity) that binds.  Every case also compares the router z-loss.
+the Mixtral expert form (SiLU, bias-free) on every GEMM kernel, a capacity
+floor (min_capacity) that binds, and a selection-only router bias on both
+router paths (and at full size on the DeepSeek-shaped layer).  Every case
+also compares the router z-loss.
 """
 import sys
 
@@ -84,6 +86,14 @@ REDUCED = {
     "min_capacity_binds_f32": ("switch", dict(T=500, d=64, h=128, E=8, k=1, cf=0.25, min_capacity=30)),
     # a floor above T: nothing is dropped
     "min_capacity_above_T": ("glam", dict(T=300, d=256, h=256, E=8, k=2, cf=0.2, min_capacity=400)),
+    # selection-only router bias: the choice ranks l + b_sel, weights from l;
+    # both router selection paths, with a router offset, capacity, shared
+    # experts, k = 8 over 256 experts and the float32 path
+    "sel_bias_E8": ("mixtral", dict(T=600, d=512, h=1024, sel_bias_std=1.0)),
+    "sel_bias_E64_offset_capacity": ("glam", dict(T=1000, d=256, h=512, E=64, cf=1.5, sel_bias_std=1.0)),
+    "sel_bias_E256_top8_shared": ("deepseek", dict(T=128, d=256, h=256, E=256, k=8, S=1, sel_bias_std=1.0)),
+    "sel_bias_f32": ("switch", dict(T=500, d=64, h=128, E=8, k=2, cf=0.5, sel_bias_std=1.0)),
+    "sel_bias_d32_bf16_simt": ("mixtral", dict(T=100, d=32, h=64, E=6, k=3, sel_bias_std=1.0)),
 }
 
 
@@ -93,7 +103,7 @@ def test_reduced_full_oracle(case):
     inp = _case(base, **kw)
     c = inp.cfg
     _say(f"[parity] {case}: T={c.T} d={c.d} h={c.h} E={c.E} k={c.k} S={c.S} cf={c.cf} "
-         f"min_cap={c.min_capacity} {c.activation} bias={c.expert_bias} {c.dtype}")
+         f"min_cap={c.min_capacity} {c.activation} bias={c.expert_bias} sel_bias={c.sel_bias_std} {c.dtype}")
     stacked = inp.stacked()
     gpu = run_gpu(inp, stacked=stacked)
     rep = compare(inp, gpu, stacked=stacked)
@@ -138,7 +148,8 @@ FULL_ROWS = {"tiny": None, "switch": None, "mixtral": 32, "glam": 32, "deepseek"
 
 # the five workloads, plus the Mixtral-shaped layer with the Mixtral expert form
 FULL = {"tiny": {}, "switch": {}, "mixtral": {}, "glam": {}, "deepseek": {},
-        "mixtral_silu_nobias": dict(activation="silu", expert_bias=False)}
+        "mixtral_silu_nobias": dict(activation="silu", expert_bias=False),
+        "deepseek_sel_bias": dict(sel_bias_std=1.0)}
 
 
 @pytest.mark.parametrize("name", list(FULL))

@@ -58,6 +58,9 @@ def parse():
                     help="MXFP8 expert Linears (weights quantized on the GPU before the timed steps)")
     ap.add_argument("--routing", default="top-k", choices=["top-k", "expert-choice"],
                     help="expert-choice: each expert takes C = ceil(k T / E) tokens (the rows top-k routing makes)")
+    ap.add_argument("--flush-calls", type=int, default=10,
+                    help="after the timed steps, time this many single calls each preceded by a 512 MB write "
+                         "that evicts L2 and the Infinity Cache (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -234,8 +237,31 @@ def main():
     wall = time.perf_counter() - t_start
     log(f"timed {args.steps} steps in {wall * 1e3:.2f} ms")
 
-    stage_ms = np.array([[events[i][s].elapsed_time(events[i][s + 1]) for s in range(nst - 1)]
-                         for i in range(args.steps)]).mean(axis=0)
+    per_step_ms = np.array([[events[i][s].elapsed_time(events[i][s + 1]) for s in range(nst - 1)]
+                            for i in range(args.steps)])
+    stage_ms = per_step_ms.mean(axis=0)
+
+    # Single calls from cold caches: a 512 MB write before each evicts L2 and
+    # the 256 MB Infinity Cache, so weights and activations come from HBM.
+    # Reported beside the back-to-back figure above, which is `value`.
+    flushed = None
+    if args.flush_calls > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.flush_calls)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.flush_calls)]
+        for i in range(args.flush_calls):
+            scratch.fill_(i & 0xff)
+            e0[i].record(stream)
+            step()
+            e1[i].record(stream)
+        torch.cuda.synchronize()
+        fl = np.array([a.elapsed_time(b) for a, b in zip(e0, e1)])
+        unfl = per_step_ms.sum(axis=1)
+        flushed = {"calls": args.flush_calls, "median_ms": float(np.median(fl)), "min_ms": float(fl.min()),
+                   "tokens_per_s_median": T / (float(np.median(fl)) * 1e-3),
+                   "unflushed_median_ms": float(np.median(unfl)), "unflushed_min_ms": float(unfl.min())}
+        del scratch
+        log(f"flushed calls: median {flushed['median_ms']:.3f} ms (unflushed {flushed['unflushed_median_ms']:.3f})")
     stages = dict(zip(moe.STAGES, stage_ms.tolist()))   # under expert choice "scatter" is the selection
 
     kept_np = kept.cpu().numpy().astype(np.int64)
@@ -343,6 +369,7 @@ def main():
         "roofline": roof,
         "stages": per_stage,
         "layer_ms_events": float(stage_ms.sum()),
+        "cold_cache": flushed,
     }
     if not args.no_cpu_baseline:
         ntok = args.cpu_tokens or CPU_SAMPLE_TOKENS[args.workload]

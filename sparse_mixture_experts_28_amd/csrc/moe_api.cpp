@@ -185,11 +185,33 @@ moe_status_t check_shape_mx(int32_t T, int32_t d, int32_t h, int32_t E, int32_t 
   return MOE_OK;
 }
 
+// Tile height of the MXFP8 GEMM, by the rule of the bf16 GEMM's gemm_m_tile
+// over the heights it offers: 256 when experts average >= 512 rows (compute
+// bound), else the height in {128, 192, 256} that pads the expected rows of
+// an expert least (the capacity when it binds, else 1.25 x the mean), ties to
+// the taller tile: every M tile of an expert streams that expert's weights,
+// so fewer, fuller tiles stream fewer bytes.
+int mx_m_tile(const Problem& p) {
+  const long long mean = (static_cast<long long>(p.A) + p.E - 1) / p.E;
+  if (mean >= 512 && p.cap >= 512) return 256;
+  const long long want = p.cap <= mean ? p.cap : (mean * 5 + 3) / 4;
+  int best = 256;
+  long long best_pad = (want + 255) / 256 * 256;
+  for (int bm : {192, 128}) {
+    const long long pad = (want + bm - 1) / bm * bm;
+    if (pad < best_pad) {
+      best = bm;
+      best_pad = pad;
+    }
+  }
+  return best;
+}
+
 Problem make_problem_mx(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int32_t S, float cf, int act,
                         int32_t min_cap) {
   Problem p = make_problem(T, d, h, E, k, S, MOE_BF16, cf, act, min_cap);
   p.mx = true;
-  p.gemm_bm = p.gemm_bm == 256 ? 256 : 128;
+  p.gemm_bm = mx_m_tile(p);
   return p;
 }
 

@@ -203,10 +203,10 @@ __device__ __forceinline__ uint32_t mx_pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// BM x 256 tiles, 128-deep K stages in an NS-slot LDS ring (NS = 2 at BM =
-// 256; 3 at BM = 128, where the tiles stream weights and more bytes in flight
-// pay), 4 waves in a 2 x 2 grid (wave tile BM/2 x 128 = (BM/32) x 8 blocks of
-// the 16x16x128 MFMA).
+// BM x 256 tiles (BM 128, 192 or 256), 128-deep K stages in an NS-slot LDS
+// ring (NS = 3 at BM = 128, where the tiles stream weights and more bytes in
+// flight pay; 2 otherwise, which is all that fits), 4 waves in a 2 x 2 grid
+// (wave tile BM/2 x 128 = (BM/32) x 8 blocks of the 16x16x128 MFMA).
 // Codes reach LDS by direct loads (rows of 128 bytes, 16-byte chunks XOR-
 // swizzled by row).  Scales come SG stages at a time (4 SG bytes of a row,
 // one row per lane; SG = 4, a quarter of the line requests of one load a
@@ -234,12 +234,13 @@ void gemm_mx_kernel(MxArgs g) {
   constexpr int HM = MB / 2 * 8;              // MFMAs per half step
   constexpr int NR = MB + 8;                  // code loads per stage per wave (8 rows x 128 B each)
   constexpr int kStage = (BM + kMxBN) * kMxCh;     // u32x4 of codes per stage
-  constexpr int NS = BM == 256 ? 2 : 3;       // LDS ring slots
+  constexpr int NS = BM == 128 ? 3 : 2;       // LDS ring slots (three only fit at BM = 128)
   constexpr int kSRow = 4 * SG;                     // scale bytes of a row in one group
   constexpr int kScaleSlot = (BM + kMxBN) * kSRow;  // bytes of a scale group: A rows, then B rows
   constexpr int NSS = SG == 1 ? NS : 2;             // scale ring slots
   constexpr int NF1 = MB - 2;                       // fragment reads in half 0
   static_assert(SG == 1 || SG == 4, "scale groups of 1 or 4 stages (4- or 16-byte direct loads)");
+  static_assert(BM == 128 || BM == 192 || BM == 256, "tile heights 128, 192, 256 (an even number of 16-row blocks a wave)");
   // a step that starts group G loads group G + kLook into the slot whose last
   // stage was read before the step's barrier: that of group G - 1 (SG = 4) or
   // of stage G itself (SG = 1: group G + NS goes with the codes of stage G + NS)
@@ -705,6 +706,10 @@ hipError_t launch_expert_ffn_mx(const Problem& p, const MxWeights& w, const Work
     if (act == 1) MOE_MX_LAUNCH(1, 256);
     else if (act == 2) MOE_MX_LAUNCH(2, 256);
     else MOE_MX_LAUNCH(0, 256);
+  } else if (p.gemm_bm == 192) {
+    if (act == 1) MOE_MX_LAUNCH(1, 192);
+    else if (act == 2) MOE_MX_LAUNCH(2, 192);
+    else MOE_MX_LAUNCH(0, 192);
   } else {
     if (act == 1) MOE_MX_LAUNCH(1, 128);
     else if (act == 2) MOE_MX_LAUNCH(2, 128);

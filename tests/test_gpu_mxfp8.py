@@ -1,6 +1,6 @@
 """The MXFP8 expert path on the GPU vs the CPU oracle (oracle/mxfp8.py),
 through the C ABI: the quantizer bit-exact on chosen and random inputs, and
-the layer on reduced shapes (both tile heights, shared experts, capacity
+the layer on reduced shapes (all three tile heights, shared experts, capacity
 drops, the Mixtral expert form, one token, tiles split along K with their
 fix-up in both phases) and the Mixtral-shaped workload at full size with
 sampled output rows."""
@@ -63,6 +63,10 @@ REDUCED = {
     "mx_split_silu": ("mixtral", dict(T=600, d=2048, h=1024, E=8, activation="silu")),
     # the selection-only router bias through the MXFP8 layer's router
     "mx_sel_bias": ("glam", dict(T=1000, d=512, h=512, E=16, sel_bias_std=1.0)),
+    # 128 rows per expert on average: 192-row tiles (two-slot ring), SiLU
+    # through the split tail, and K = 768 (one scale load per stage)
+    "mx_bm192_silu_split": ("deepseek", dict(T=512, d=1024, h=512, E=32, k=8, S=1, activation="silu")),
+    "mx_bm192_scales_per_stage": ("deepseek", dict(T=512, d=768, h=768, E=32, k=8, S=0)),
 }
 
 

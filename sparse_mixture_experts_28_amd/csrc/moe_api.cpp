@@ -138,6 +138,7 @@ Problem make_problem(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int3
     p.cap = INT32_MAX;
   }
   p.gemm_bm = gemm_m_tile(p);
+  p.gemm_mixed = false;
   return p;
 }
 
@@ -170,11 +171,12 @@ Problem make_problem_ec(int32_t T, int32_t d, int32_t h, int32_t E, int32_t C, i
   p.ntile = (T + kRouterTile - 1) / kRouterTile;
   p.cap = C;
   p.gemm_bm = gemm_m_tile(p);
+  p.gemm_mixed = false;
   return p;
 }
 
-// MXFP8 (bf16 activations, d and h multiples of 256): the MX kernels have
-// 128- and 256-row tiles only and no split tail.
+// MXFP8 (bf16 activations, d and h multiples of 256: the MX GEMM's N tiles
+// are 256 columns and its K stages 128 bytes).
 moe_status_t check_shape_mx(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int32_t S) {
   const moe_status_t sc = check_shape(T, d, h, E, k, S, MOE_BF16);
   if (sc != MOE_OK) return sc;
@@ -185,33 +187,19 @@ moe_status_t check_shape_mx(int32_t T, int32_t d, int32_t h, int32_t E, int32_t 
   return MOE_OK;
 }
 
-// Tile height of the MXFP8 GEMM, by the rule of the bf16 GEMM's gemm_m_tile
-// over the heights it offers: 256 when experts average >= 512 rows (compute
-// bound), else the height in {128, 192, 256} that pads the expected rows of
-// an expert least (the capacity when it binds, else 1.25 x the mean), ties to
-// the taller tile: every M tile of an expert streams that expert's weights,
-// so fewer, fuller tiles stream fewer bytes.
-int mx_m_tile(const Problem& p) {
-  const long long mean = (static_cast<long long>(p.A) + p.E - 1) / p.E;
-  if (mean >= 512 && p.cap >= 512) return 256;
-  const long long want = p.cap <= mean ? p.cap : (mean * 5 + 3) / 4;
-  int best = 256;
-  long long best_pad = (want + 255) / 256 * 256;
-  for (int bm : {192, 128}) {
-    const long long pad = (want + bm - 1) / bm * bm;
-    if (pad < best_pad) {
-      best = bm;
-      best_pad = pad;
-    }
-  }
-  return best;
-}
-
+// Tile heights of the MXFP8 GEMM: 256 rows when experts average >= 512 rows
+// and the capacity allows as many (compute bound, as in the bf16 GEMM's
+// gemm_m_tile); else each segment's own, 128 or 192 rows by the rows the scan
+// finds it routed (mx_mixed_tile_height).  Those tiles stream their expert's
+// weights, so an expert's tile count is what a height has to keep low, and
+// only the routed counts show it: loads are often far from even.
 Problem make_problem_mx(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int32_t S, float cf, int act,
                         int32_t min_cap) {
   Problem p = make_problem(T, d, h, E, k, S, MOE_BF16, cf, act, min_cap);
   p.mx = true;
-  p.gemm_bm = mx_m_tile(p);
+  const long long mean = (static_cast<long long>(p.A) + p.E - 1) / p.E;
+  p.gemm_mixed = !(mean >= 512 && p.cap >= 512);
+  p.gemm_bm = p.gemm_mixed ? 128 : 256;
   return p;
 }
 

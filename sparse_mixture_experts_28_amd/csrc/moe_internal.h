@@ -94,14 +94,16 @@ struct Workspace {
 //                     expert-sorted order (row_token) for routed experts, x for
 //                     shared experts
 //   o_off[nseg]       first row of the segment in hbuf / ybuf
-//   tile_start[nseg+1] prefix sum of ceil(rows / BM) (M tiles of the GEMM)
+//   tile_start[nseg+1] prefix sum of ceil(rows / tile_bm) (M tiles of the GEMM)
 //   route_off[E]      exclusive scan of kept (first row of expert e in the expert-sorted order)
+//   tile_bm[nseg]     M tile height of the segment in the grouped GEMM
 struct SegTable {
   int32_t* rows;
   int32_t* a_off;
   int32_t* o_off;
   int32_t* tile_start;
   int32_t* route_off;
+  int32_t* tile_bm;
 };
 
 __host__ __device__ inline SegTable seg_table(int32_t* base, int nseg, int E) {
@@ -111,10 +113,20 @@ __host__ __device__ inline SegTable seg_table(int32_t* base, int nseg, int E) {
   s.o_off = base + 2 * nseg;
   s.tile_start = base + 3 * nseg;
   s.route_off = base + 4 * nseg + 1;
-  (void)E;
+  s.tile_bm = base + 4 * nseg + 1 + E;
   return s;
 }
-inline size_t seg_table_ints(int nseg, int E) { return static_cast<size_t>(4 * nseg + 1 + E); }
+inline size_t seg_table_ints(int nseg, int E) { return static_cast<size_t>(5 * nseg + 1 + E); }
+
+// Per-segment tile heights of the MXFP8 GEMM (Problem::gemm_mixed): a
+// segment of r rows takes 192-row tiles when ceil(r / 192) of them cost less
+// than ceil(r / 128) 128-row tiles, one 192-row tile taking about 1.35 times
+// as long as a 128-row one (measured on the weight-streaming shapes).  Empty
+// and short segments keep 128-row tiles.
+__host__ __device__ inline int mx_mixed_tile_height(int rows) {
+  const int t128 = (rows + 127) / 128, t192 = (rows + 191) / 192;
+  return 27 * t192 < 20 * t128 ? 192 : 128;
+}
 
 struct Problem {
   int T, d, h, E, k, S;
@@ -126,6 +138,7 @@ struct Problem {
   int cap;       // capacity per expert (min_capacity applied); INT32_MAX when unlimited
   int ntile;     // ceil(T / kRouterTile)
   int gemm_bm;   // M tile of the grouped GEMM (for the tile prefix)
+  bool gemm_mixed;   // MXFP8 GEMM: per-segment heights by mx_mixed_tile_height (gemm_bm unused)
 };
 
 Workspace carve_workspace(const Problem& p, void* base, size_t bytes_available, bool* ok);

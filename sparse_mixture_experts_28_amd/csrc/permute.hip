@@ -117,11 +117,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
   constexpr int kSegSlots = 512;   // >= MOE_MAX_EXPERTS + MOE_MAX_SHARED
   __shared__ int32_t s_rows[kSegSlots];
   __shared__ int32_t s_tiles[kSegSlots];
-  const int bm = p.gemm_bm;
-  int my_rows = 0, my_tiles = 0;
+  int my_rows = 0, my_tiles = 0, my_bm = p.gemm_bm;
   if (t < nseg) {
     my_rows = t < E ? s_kept[t] : p.T;
-    my_tiles = (my_rows + bm - 1) / bm;
+    if (p.gemm_mixed) my_bm = mx_mixed_tile_height(my_rows);
+    my_tiles = (my_rows + my_bm - 1) / my_bm;
   }
   if (t < kSegSlots) {
     s_rows[t] = t < E ? my_rows : 0;     // only routed rows are packed in the sorted buffer
@@ -159,6 +159,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
     st.a_off[t] = t < E ? excl_rows : 0;
     st.o_off[t] = t < E ? excl_rows : routed_rows + (t - E) * p.T;
     st.tile_start[t] = s_tiles[t] - my_tiles;
+    st.tile_bm[t] = my_bm;
     if (t < E) st.route_off[t] = excl_rows;
     if (t == nseg - 1) st.tile_start[nseg] = s_tiles[t];
   }

@@ -119,13 +119,15 @@ __host__ __device__ inline SegTable seg_table(int32_t* base, int nseg, int E) {
 inline size_t seg_table_ints(int nseg, int E) { return static_cast<size_t>(5 * nseg + 1 + E); }
 
 // Per-segment tile heights of the MXFP8 GEMM (Problem::gemm_mixed): a
-// segment of r rows takes 192-row tiles when ceil(r / 192) of them cost less
-// than ceil(r / 128) 128-row tiles, one 192-row tile taking about 1.35 times
-// as long as a 128-row one (measured on the weight-streaming shapes).  Empty
-// and short segments keep 128-row tiles.
+// segment of r rows takes 192-row tiles only when they cut its tiles by more
+// than a third, 3 ceil(r / 192) < 2 ceil(r / 128) (r in 129..192, 513..576,
+// 897..960, ...).  A 192-row tile takes 1.3-1.4 times as long as a 128-row
+// one where the weights stream from HBM, and up to 1.6 times in the second
+// Linear of capacity-bound loads (measured), so smaller savings do not pay.
+// Empty and short segments keep 128-row tiles.
 __host__ __device__ inline int mx_mixed_tile_height(int rows) {
   const int t128 = (rows + 127) / 128, t192 = (rows + 191) / 192;
-  return 27 * t192 < 20 * t128 ? 192 : 128;
+  return 3 * t192 < 2 * t128 ? 192 : 128;
 }
 
 struct Problem {

@@ -68,8 +68,8 @@ struct Workspace {
   void* hbuf;           // [R, h]     GELU(x W1^T + b1)
   void* ybuf;           // [R, d]     h W2^T + b2
   int32_t* local_rank;  // [T, k]     rank of (t,j) among earlier tokens of its 64-token tile
-  int32_t* tile_hist;   // [E, ntile] assignments per (expert, tile); becomes the tile base
-  float* p_part;        // [E, ntile] per-tile sums of the softmax probabilities
+  int32_t* tile_hist;   // [ntile, E] assignments per (tile, expert); becomes the tile base
+  float* p_part;        // [ntile, E] per-tile sums of the softmax probabilities
   double* z_part;       // [ntile]    per-tile sums of the squared log-sum-exp of the logits
   int32_t* counts;      // [E]
   int32_t* kept;        // [E]

@@ -31,6 +31,8 @@ constexpr int kScanThreads = 1024;
 // Thread t works on expert e = t % E over the tiles of chunk c = t / E (C
 // chunks of consecutive tiles); per-chunk totals are scanned over c in LDS in
 // fixed order, so bases, counts and the probability sums are deterministic.
+// The per-tile tables are tile-major [ntile][E], so the lanes of a wave
+// (consecutive experts) read and write consecutive words.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* tile_hist, const float* p_part,
                                                             const double* z_part, int32_t* counts, int32_t* kept,
                                                             int32_t* seg_base, float* aux_loss, float* z_loss,
@@ -50,17 +52,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
   const bool active = c < C;
   const int tb = c * tpc, te = min(p.ntile, tb + tpc);
 
-  // 1. chunk totals (per-expert layout [E][ntile]: each thread reads a contiguous run)
+  // 1. chunk totals
   int sum = 0;
   double psum = 0.0;
-  const int32_t* hrow = tile_hist + static_cast<size_t>(e) * p.ntile;
-  const float* prow = p_part + static_cast<size_t>(e) * p.ntile;
+  const int32_t* hcol = tile_hist + e;   // tile i of expert e at i * E
+  const float* pcol = p_part + e;
   const bool ec = p.ec_C > 0;   // expert choice: every expert takes exactly ec_C tokens
   if (active) {
 #pragma unroll 8
     for (int tile = tb; tile < te; ++tile) {
-      if (!ec) sum += hrow[tile];
-      psum += static_cast<double>(prow[tile]);
+      if (!ec) sum += hcol[static_cast<size_t>(tile) * E];
+      psum += static_cast<double>(pcol[static_cast<size_t>(tile) * E]);
     }
     s_sum[c * E + e] = sum;
     s_psum[c * E + e] = psum;
@@ -90,11 +92,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
   // 3. tile bases within the chunk (token choice only)
   if (active && !ec) {
     int run = s_sum[c * E + e];
-    int32_t* wrow = tile_hist + static_cast<size_t>(e) * p.ntile;
+    int32_t* wcol = tile_hist + e;
 #pragma unroll 8
     for (int tile = tb; tile < te; ++tile) {
-      const int h = wrow[tile];
-      wrow[tile] = run;         // becomes the tile's base rank for expert e
+      const int h = wcol[static_cast<size_t>(tile) * E];
+      wcol[static_cast<size_t>(tile) * E] = run;   // becomes the tile's base rank for expert e
       run += h;
     }
   }
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(Problem p, const int32_t* 
   if (i >= p.T * p.k) return;
   const int t = i / p.k;
   const int e = topk_idx[i];
-  const int rank = tile_base[static_cast<size_t>(e) * p.ntile + t / kRouterTile] + local_rank[i];
+  const int rank = tile_base[static_cast<size_t>(t / kRouterTile) * p.E + e] + local_rank[i];
   SegTable st = seg_table(const_cast<int32_t*>(seg_base), p.E + p.S, p.E);
   const int pos = rank < p.cap ? st.route_off[e] + rank : -1;
   slot_pos[i] = pos;

@@ -235,9 +235,9 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    // per-expert layout [E][ntile]: the scan reads each expert's tiles contiguously
-    a.p_part[static_cast<size_t>(e) * a.ntile + tile] = ((s_p[0][e] + s_p[1][e]) + s_p[2][e]) + s_p[3][e];
-    if (!ec) a.tile_hist[static_cast<size_t>(e) * a.ntile + tile] = __popcll(s_mask[e]);
+    // tile-major layout [ntile][E]: the scan's lanes take consecutive experts
+    a.p_part[static_cast<size_t>(tile) * E + e] = ((s_p[0][e] + s_p[1][e]) + s_p[2][e]) + s_p[3][e];
+    if (!ec) a.tile_hist[static_cast<size_t>(tile) * E + e] = __popcll(s_mask[e]);
   }
   if (threadIdx.x == blockDim.x - 1) {
     // z-loss partial of the tile, tokens in order
@@ -575,8 +575,8 @@ __device__ __forceinline__ void select_tile(const RouterArgs& a, const double (&
     // probability sum over the tile's tokens in token order
     float ps = 0.f;
     for (int rr = 0; rr < ntok; ++rr) ps += s_p[rr][e];
-    a.p_part[static_cast<size_t>(e) * a.ntile + tile] = ps;
-    if (!ec) a.tile_hist[static_cast<size_t>(e) * a.ntile + tile] = __popcll(s_mask[e]);
+    a.p_part[static_cast<size_t>(tile) * E + e] = ps;
+    if (!ec) a.tile_hist[static_cast<size_t>(tile) * E + e] = __popcll(s_mask[e]);
   }
   if (threadIdx.x == blockDim.x - 1) {
     // z-loss partial of the tile, tokens in order

@@ -9,7 +9,9 @@
 //
 // A gather, not a scatter: one workgroup per token reads its k expert rows and
 // its shared rows, accumulates in float32 in slot order then shared order, and
-// rounds once.  No atomics, so the result is bitwise reproducible.
+// rounds once.  No atomics, so the result is bitwise reproducible.  The rows
+// of a token are listed in LDS first, and each thread loads up to 8 of them
+// before adding any, so their memory latencies overlap.
 //
 // Expert choice ("第7章 Mixture of Experts" §7.2; the guide's §4.2): a token's
 // routed rows are those of the experts that took it, 0 to E of them, added in
@@ -29,35 +31,94 @@ __device__ __forceinline__ void acc_bf16x8(float (&a)[8], u32x4 v, float w) {
   }
 }
 
+__device__ __forceinline__ void acc_f32x4(float4& a, float4 v, float w) {
+  a.x = fmaf(w, v.x, a.x);
+  a.y = fmaf(w, v.y, a.y);
+  a.z = fmaf(w, v.z, a.z);
+  a.w = fmaf(w, v.w, a.w);
+}
+
+// Accumulates 16-byte column c of rows[0 .. B) times w[0 .. B), in that order:
+// all B loads are issued before the first is used, so a token's rows arrive
+// together rather than one memory latency each.
+template <int B, typename V, typename A>
+__device__ __forceinline__ void gather_batch(A& a, const V* __restrict__ y, const int32_t* rows, const float* w, int c,
+                                             int vec_per_row) {
+  V v[B];
+#pragma unroll
+  for (int j = 0; j < B; ++j) v[j] = y[static_cast<size_t>(rows[j]) * vec_per_row + c];
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    if constexpr (sizeof(V) == 16 && sizeof(A) == 32) acc_bf16x8(a, v[j], w[j]);
+    else acc_f32x4(a, v[j], w[j]);
+  }
+}
+
+// rows[0 .. n) in order, in batches of 8 and one last batch of n mod 8
+template <typename V, typename A>
+__device__ __forceinline__ void gather_rows(A& a, const V* __restrict__ y, const int32_t* rows, const float* w, int n,
+                                            int c, int vec_per_row) {
+  int j = 0;
+  for (; j + 8 <= n; j += 8) gather_batch<8>(a, y, rows + j, w + j, c, vec_per_row);
+  switch (n - j) {
+    case 1: gather_batch<1>(a, y, rows + j, w + j, c, vec_per_row); break;
+    case 2: gather_batch<2>(a, y, rows + j, w + j, c, vec_per_row); break;
+    case 3: gather_batch<3>(a, y, rows + j, w + j, c, vec_per_row); break;
+    case 4: gather_batch<4>(a, y, rows + j, w + j, c, vec_per_row); break;
+    case 5: gather_batch<5>(a, y, rows + j, w + j, c, vec_per_row); break;
+    case 6: gather_batch<6>(a, y, rows + j, w + j, c, vec_per_row); break;
+    case 7: gather_batch<7>(a, y, rows + j, w + j, c, vec_per_row); break;
+    default: break;
+  }
+}
+
+__device__ __forceinline__ u32x4 pack_bf16x8(const float (&a)[8]) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = static_cast<uint32_t>(f32_to_bf16(a[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(a[2 * i + 1])) << 16);
+  return o;
+}
+
+// Top-k: token t's kept slots in slot order, then its shared-expert rows with
+// weight 1 (a fused multiply-add by 1 rounds exactly as the plain sum).
+__device__ __forceinline__ int topk_token_rows(const Problem& p, const int32_t* __restrict__ slot_pos,
+                                               const float* __restrict__ topk_w, int t, int32_t* s_row, float* s_w,
+                                               int* s_n) {
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int j = 0; j < p.k; ++j) {
+      const int pos = slot_pos[static_cast<size_t>(t) * p.k + j];
+      if (pos >= 0) {
+        s_row[n] = pos;
+        s_w[n] = topk_w[static_cast<size_t>(t) * p.k + j];
+        ++n;
+      }
+    }
+    for (int s = 0; s < p.S; ++s) {
+      s_row[n] = p.A + s * p.T + t;
+      s_w[n] = 1.0f;
+      ++n;
+    }
+    *s_n = n;
+  }
+  __syncthreads();
+  return *s_n;
+}
+
 __global__ __launch_bounds__(256) void combine_bf16_kernel(Problem p, const u32x4* __restrict__ y,
                                                            const int32_t* __restrict__ slot_pos,
                                                            const float* __restrict__ topk_w,
                                                            u32x4* __restrict__ out, int vec_per_row) {
-  __shared__ int32_t s_pos[MOE_MAX_TOPK];
-  __shared__ float s_w[MOE_MAX_TOPK];
+  __shared__ int32_t s_row[MOE_MAX_TOPK + MOE_MAX_SHARED];
+  __shared__ float s_w[MOE_MAX_TOPK + MOE_MAX_SHARED];
+  __shared__ int s_n;
   const int t = blockIdx.x;
-  const int k = p.k;
-  if (threadIdx.x < k) {
-    s_pos[threadIdx.x] = slot_pos[static_cast<size_t>(t) * k + threadIdx.x];
-    s_w[threadIdx.x] = topk_w[static_cast<size_t>(t) * k + threadIdx.x];
-  }
-  __syncthreads();
-  const size_t routed_rows = static_cast<size_t>(p.A);
+  const int n = topk_token_rows(p, slot_pos, topk_w, t, s_row, s_w, &s_n);
   for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int pos = s_pos[j];
-      if (pos >= 0) acc_bf16x8(a, y[static_cast<size_t>(pos) * vec_per_row + c], s_w[j]);
-    }
-    for (int s = 0; s < p.S; ++s) {
-      const size_t row = routed_rows + static_cast<size_t>(s) * p.T + t;
-      acc_bf16x8(a, y[row * vec_per_row + c], 1.0f);
-    }
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = static_cast<uint32_t>(f32_to_bf16(a[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(a[2 * i + 1])) << 16);
-    out[static_cast<size_t>(t) * vec_per_row + c] = o;
+    gather_rows(a, y, s_row, s_w, n, c, vec_per_row);
+    out[static_cast<size_t>(t) * vec_per_row + c] = pack_bf16x8(a);
   }
 }
 
@@ -65,44 +126,22 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(Problem p, const float
                                                           const int32_t* __restrict__ slot_pos,
                                                           const float* __restrict__ topk_w,
                                                           float4* __restrict__ out, int vec_per_row) {
-  __shared__ int32_t s_pos[MOE_MAX_TOPK];
-  __shared__ float s_w[MOE_MAX_TOPK];
+  __shared__ int32_t s_row[MOE_MAX_TOPK + MOE_MAX_SHARED];
+  __shared__ float s_w[MOE_MAX_TOPK + MOE_MAX_SHARED];
+  __shared__ int s_n;
   const int t = blockIdx.x;
-  const int k = p.k;
-  if (threadIdx.x < k) {
-    s_pos[threadIdx.x] = slot_pos[static_cast<size_t>(t) * k + threadIdx.x];
-    s_w[threadIdx.x] = topk_w[static_cast<size_t>(t) * k + threadIdx.x];
-  }
-  __syncthreads();
-  const size_t routed_rows = static_cast<size_t>(p.A);
+  const int n = topk_token_rows(p, slot_pos, topk_w, t, s_row, s_w, &s_n);
   for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const int pos = s_pos[j];
-      if (pos >= 0) {
-        const float4 v = y[static_cast<size_t>(pos) * vec_per_row + c];
-        const float w = s_w[j];
-        a.x = fmaf(w, v.x, a.x);
-        a.y = fmaf(w, v.y, a.y);
-        a.z = fmaf(w, v.z, a.z);
-        a.w = fmaf(w, v.w, a.w);
-      }
-    }
-    for (int s = 0; s < p.S; ++s) {
-      const size_t row = routed_rows + static_cast<size_t>(s) * p.T + t;
-      const float4 v = y[row * vec_per_row + c];
-      a.x += v.x;
-      a.y += v.y;
-      a.z += v.z;
-      a.w += v.w;
-    }
+    gather_rows(a, y, s_row, s_w, n, c, vec_per_row);
     out[static_cast<size_t>(t) * vec_per_row + c] = a;
   }
 }
 
 // Expert choice: the rows of token t, in ascending expert order.  Wave 0 reads
 // pos[e][t] for every expert (lane l: experts 4l .. 4l+3, E <= 256) and packs
-// the takers with a lane prefix count; returns their number.
+// the takers with a lane prefix count; the shared-expert rows follow with
+// weight 1.  Returns the number of rows.
 __device__ int ec_token_rows(const Problem& p, const int32_t* __restrict__ pos, const float* __restrict__ ec_w,
                              int t, int32_t* s_row, float* s_w, int* s_n) {
   if (threadIdx.x < kWave) {
@@ -131,7 +170,13 @@ __device__ int ec_token_rows(const Problem& p, const int32_t* __restrict__ pos, 
         ++at;
       }
     }
-    if (l == kWave - 1) *s_n = incl;
+    // the last lane's count is the number of takers; the shared rows follow
+    const int taken = __shfl(incl, kWave - 1, kWave);
+    if (l < p.S) {
+      s_row[taken + l] = p.A + l * p.T + t;
+      s_w[taken + l] = 1.0f;
+    }
+    if (l == kWave - 1) *s_n = taken + p.S;
   }
   __syncthreads();
   return *s_n;
@@ -141,24 +186,15 @@ __global__ __launch_bounds__(256) void combine_ec_bf16_kernel(Problem p, const u
                                                               const int32_t* __restrict__ pos,
                                                               const float* __restrict__ ec_w,
                                                               u32x4* __restrict__ out, int vec_per_row) {
-  __shared__ int32_t s_row[MOE_MAX_EXPERTS];
-  __shared__ float s_w[MOE_MAX_EXPERTS];
+  __shared__ int32_t s_row[MOE_MAX_EXPERTS + MOE_MAX_SHARED];
+  __shared__ float s_w[MOE_MAX_EXPERTS + MOE_MAX_SHARED];
   __shared__ int s_n;
   const int t = blockIdx.x;
   const int n = ec_token_rows(p, pos, ec_w, t, s_row, s_w, &s_n);
-  const size_t routed_rows = static_cast<size_t>(p.A);
   for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < n; ++j) acc_bf16x8(a, y[static_cast<size_t>(s_row[j]) * vec_per_row + c], s_w[j]);
-    for (int s = 0; s < p.S; ++s) {
-      const size_t row = routed_rows + static_cast<size_t>(s) * p.T + t;
-      acc_bf16x8(a, y[row * vec_per_row + c], 1.0f);
-    }
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = static_cast<uint32_t>(f32_to_bf16(a[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(a[2 * i + 1])) << 16);
-    out[static_cast<size_t>(t) * vec_per_row + c] = o;
+    gather_rows(a, y, s_row, s_w, n, c, vec_per_row);
+    out[static_cast<size_t>(t) * vec_per_row + c] = pack_bf16x8(a);
   }
 }
 
@@ -166,30 +202,14 @@ __global__ __launch_bounds__(256) void combine_ec_f32_kernel(Problem p, const fl
                                                              const int32_t* __restrict__ pos,
                                                              const float* __restrict__ ec_w,
                                                              float4* __restrict__ out, int vec_per_row) {
-  __shared__ int32_t s_row[MOE_MAX_EXPERTS];
-  __shared__ float s_w[MOE_MAX_EXPERTS];
+  __shared__ int32_t s_row[MOE_MAX_EXPERTS + MOE_MAX_SHARED];
+  __shared__ float s_w[MOE_MAX_EXPERTS + MOE_MAX_SHARED];
   __shared__ int s_n;
   const int t = blockIdx.x;
   const int n = ec_token_rows(p, pos, ec_w, t, s_row, s_w, &s_n);
-  const size_t routed_rows = static_cast<size_t>(p.A);
   for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < n; ++j) {
-      const float4 v = y[static_cast<size_t>(s_row[j]) * vec_per_row + c];
-      const float w = s_w[j];
-      a.x = fmaf(w, v.x, a.x);
-      a.y = fmaf(w, v.y, a.y);
-      a.z = fmaf(w, v.z, a.z);
-      a.w = fmaf(w, v.w, a.w);
-    }
-    for (int s = 0; s < p.S; ++s) {
-      const size_t row = routed_rows + static_cast<size_t>(s) * p.T + t;
-      const float4 v = y[row * vec_per_row + c];
-      a.x += v.x;
-      a.y += v.y;
-      a.z += v.z;
-      a.w += v.w;
-    }
+    gather_rows(a, y, s_row, s_w, n, c, vec_per_row);
     out[static_cast<size_t>(t) * vec_per_row + c] = a;
   }
 }

@@ -232,37 +232,55 @@ def run_gpu_mx(inp, dev="cuda:0", stacked=None, workspace=None):
     return res
 
 
-def compare_mx(inp, gpu: dict, stacked=None, rows=None) -> dict:
+def compare_mx(inp, gpu: dict, stacked=None, rows=None, extra_experts=4) -> dict:
     """MXFP8 parity: routing, weights, counts, capacity, aux and z-loss by the
     rules of compare(); the GPU's weight codes and scales bit-exact against the
     oracle's quantization of the same bf16 weights; outputs against the MXFP8
     oracle (oracle.mxfp8) within the bf16 tolerance.  The GPU forms H in
     float32 before quantizing it, so an element near a rounding boundary of
     E4M3 can take the neighbouring code: one code step is at most 1/8 of that
-    element, and such flips are rare and of random sign, far inside 2e-2."""
+    element, and such flips are rare and of random sign, far inside 2e-2.
+
+    The weights are quantized by the oracle one expert at a time, when the
+    oracle first uses that expert, and compared there: every expert when all
+    rows are compared; with sampled rows, the experts those rows use, the
+    shared ones, and extra_experts more drawn at random (full-size weights
+    would take tens of GB in float64)."""
     from oracle import mxfp8
     c = inp.cfg
     rep = compare(inp, gpu, stacked=stacked, rows=rows, check_out=False)
     W1, b1, W2, b2 = stacked if stacked is not None else inp.stacked()
     n = c.E + c.S
-    W1c, W1s = mxfp8.quantize(ref.widen(W1, "bf16").reshape(n * c.h, c.d))
-    W2c, W2s = mxfp8.quantize(ref.widen(W2, "bf16").reshape(n * c.d, c.h))
-    assert np.array_equal(gpu["W1q"][0].reshape(n * c.h, c.d), W1c), "W1 codes differ"
-    assert np.array_equal(gpu["W1q"][1].reshape(n * c.h, c.d // 32), W1s), "W1 scales differ"
-    assert np.array_equal(gpu["W2q"][0].reshape(n * c.d, c.h), W2c), "W2 codes differ"
-    assert np.array_equal(gpu["W2q"][1].reshape(n * c.d, c.h // 32), W2s), "W2 scales differ"
-    W1c, W1s = W1c.reshape(n, c.h, c.d), W1s.reshape(n, c.h, c.d // 32)
-    W2c, W2s = W2c.reshape(n, c.d, c.h), W2s.reshape(n, c.d, c.h // 32)
-    eq = lambda e: (W1c[e], W1s[e], None if b1 is None else b1[e], W2c[e], W2s[e], None if b2 is None else b2[e])
+    g1c, g1s = gpu["W1q"][0].reshape(n, c.h, c.d), gpu["W1q"][1].reshape(n, c.h, c.d // 32)
+    g2c, g2s = gpu["W2q"][0].reshape(n, c.d, c.h), gpu["W2q"][1].reshape(n, c.d, c.h // 32)
+    quantized = {}
+
+    def eq(e):
+        if e not in quantized:
+            q1c, q1s = mxfp8.quantize(ref.widen(W1[e], "bf16"))
+            q2c, q2s = mxfp8.quantize(ref.widen(W2[e], "bf16"))
+            assert np.array_equal(g1c[e], q1c), f"W1 codes differ (expert {e})"
+            assert np.array_equal(g1s[e], q1s), f"W1 scales differ (expert {e})"
+            assert np.array_equal(g2c[e], q2c), f"W2 codes differ (expert {e})"
+            assert np.array_equal(g2s[e], q2s), f"W2 scales differ (expert {e})"
+            quantized[e] = (q1c, q1s, None if b1 is None else b1[e], q2c, q2s, None if b2 is None else b2[e])
+        return quantized[e]
+
     r = mxfp8.moe_forward_mxfp8_ref(inp.x, inp.W_g, eq, c.E, c.k, float(np.float32(c.cf)), c.S, inp.b_g,
                                     kind="bf16", rows=rows, override_idx=gpu["idx"] if rep["rerun"] else None,
                                     activation=c.activation, min_capacity=c.min_capacity,
                                     b_sel=getattr(inp, "b_sel", None))
+    if rows is None:
+        for e in range(n):
+            eq(e)
+    else:
+        for e in np.random.default_rng(7).choice(n, min(n, extra_experts), replace=False):
+            eq(int(e))
     go = gpu["out"] if rows is None else gpu["out"][np.asarray(rows)]
     scale = float(np.max(np.abs(r.out)))
     err = float(np.max(np.abs(go - r.out)))
     rel = err / scale if scale > 0 else err
-    rep.update(out_rel=rel, out_scale=scale)
+    rep.update(out_rel=rel, out_scale=scale, experts_checked=len(quantized))
     assert np.all(np.isfinite(go))
     assert rel <= TOL["bf16"], f"MXFP8 output max-abs error {err} = {rel:.3e} of max|ref| {scale}"
     return rep

@@ -2,8 +2,8 @@
 through the C ABI: the quantizer bit-exact on chosen and random inputs, and
 the layer on reduced shapes (all three tile heights, shared experts, capacity
 drops, the Mixtral expert form, one token, tiles split along K with their
-fix-up in both phases) and the Mixtral-shaped workload at full size with
-sampled output rows."""
+fix-up in both phases) and the Mixtral-, GLaM- and DeepSeek-shaped
+workloads at full size with sampled output rows."""
 import sys
 
 import numpy as np
@@ -79,6 +79,23 @@ def test_mx_reduced(case):
     stacked = inp.stacked()
     rep = compare_mx(inp, run_gpu_mx(inp, stacked=stacked), stacked=stacked)
     _say(f"[mx] {case}: {rep}")
+
+
+@pytest.mark.parametrize("workload,nrows", [("glam", 6), ("deepseek", 3)])
+def test_mx_full_size_mixed_heights(workload, nrows):
+    """The GLaM-shaped (skewed, capacity-bound) and DeepSeek-shaped loads at
+    full size, where experts average fewer than 512 rows and the GEMM runs
+    128- and 192-row tiles side by side, each expert's height set by its
+    routed rows.  Sampled output rows; the weight codes of the experts they
+    use (and a few more) bit-exact."""
+    inp = make_inputs(workload, seed=0)
+    c = inp.cfg
+    _say(f"[mx-full] {workload} T={c.T} d={c.d} h={c.h} E={c.E} k={c.k} S={c.S}")
+    stacked = inp.stacked()
+    rng = np.random.default_rng(98)
+    rows = np.unique(np.concatenate([[0, c.T - 1], rng.choice(c.T, nrows - 2, replace=False)]))
+    rep = compare_mx(inp, run_gpu_mx(inp, stacked=stacked), stacked=stacked, rows=rows, extra_experts=2)
+    _say(f"[mx-full] {workload}: {rep}")
 
 
 def test_mx_full_size_mixtral():

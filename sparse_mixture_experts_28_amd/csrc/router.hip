@@ -380,7 +380,14 @@ struct LogitArgs {
 
 constexpr int kLgTok = 128, kLgExp = 64, kLgK = 128;   // tile and stage depth (experts: 64, or 16 when E <= 16)
 constexpr int kLgCh = kLgK / 8;                        // 16-byte chunks per stage row
-constexpr int kLgNS = 3;                               // ring slots
+// ring slots: as many stages as fit in 144 KB of LDS (3 of 48 KB at 64
+// experts, 4 of 36 KB at 16), all but one in flight
+template <int EXP>
+constexpr int lg_slots() { return EXP == 16 ? 4 : 3; }
+
+// s_waitcnt immediate: at most n (< 64) vector-memory operations outstanding,
+// no wait on LDS or export counters
+constexpr int lg_vm_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // LDS row of 16 chunks (256 bytes): logical chunk c of row r at c ^ (r & 15).
 // Measured with an LDS probe on gfx950, the fragment reads (rows 0..15 of a
@@ -401,7 +408,8 @@ void router_logits_kernel(LogitArgs a) {
   constexpr int kStage = (kLgTok + EXP) * kLgCh;     // u32x4 per stage (48 KB at EXP = 64)
   constexpr int kLgLoads = (kLgTok + EXP) / 16;       // 1 KB direct loads per wave per stage
   constexpr int kEB = EXP / 16;                       // expert blocks per wave
-  __shared__ u32x4 lds[kLgNS * kStage];
+  constexpr int NS = lg_slots<EXP>();
+  __shared__ u32x4 lds[NS * kStage];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -424,7 +432,7 @@ void router_logits_kernel(LogitArgs a) {
   const int dr = 4 * wave + (lane >> 4);
   const uint32_t vo = static_cast<uint32_t>(dr) * rb + lgswz(dr, lane & 15) * 16;
   auto issue = [&](int st) {
-    u32x4* base = lds + (st % kLgNS) * kStage + (4 * wave) * kLgCh;
+    u32x4* base = lds + (st % NS) * kStage + (4 * wave) * kLgCh;
     const uint32_t kb = kbase + static_cast<uint32_t>(st) * (kLgK * 2);
 #pragma unroll
     for (int i = 0; i < kLgLoads; ++i) {
@@ -450,15 +458,23 @@ void router_logits_kernel(LogitArgs a) {
       for (int v = 0; v < 4; ++v) acc[tb][eb][v] = 0.0;
     }
 
-  issue(0);
-  issue(1);
+#pragma unroll
+  for (int sp = 0; sp < NS - 1; ++sp)
+    if (sp < nst) issue(sp);
   for (int st = 0; st < nst; ++st) {
-    // stage st landed (stage st+1 may be in flight); every wave is past stage st-1
-    if (st + 1 < nst) __builtin_amdgcn_s_waitcnt(0x0F70 | kLgLoads);
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    // stage st landed (the up to NS - 2 stages after it may be in flight);
+    // every wave is past stage st-1, whose slot then takes stage st + NS - 1
+    if constexpr (NS == 4) {
+      if (st + 2 < nst) __builtin_amdgcn_s_waitcnt(lg_vm_wait(2 * kLgLoads));
+      else if (st + 1 < nst) __builtin_amdgcn_s_waitcnt(lg_vm_wait(kLgLoads));
+      else __builtin_amdgcn_s_waitcnt(lg_vm_wait(0));
+    } else {
+      if (st + 1 < nst) __builtin_amdgcn_s_waitcnt(lg_vm_wait(kLgLoads));
+      else __builtin_amdgcn_s_waitcnt(lg_vm_wait(0));
+    }
     lg_barrier();
-    if (st + 2 < nst) issue(st + 2);
-    const u32x4* sa = lds + (st % kLgNS) * kStage;
+    if (st + NS - 1 < nst) issue(st + NS - 1);
+    const u32x4* sa = lds + (st % NS) * kStage;
 #pragma unroll
     for (int s = 0; s < kLgK / 32; ++s) {
       const int ch = lgswz(rr, 4 * s + cg);

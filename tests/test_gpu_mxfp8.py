@@ -63,10 +63,12 @@ REDUCED = {
     "mx_split_silu": ("mixtral", dict(T=600, d=2048, h=1024, E=8, activation="silu")),
     # the selection-only router bias through the MXFP8 layer's router
     "mx_sel_bias": ("glam", dict(T=1000, d=512, h=512, E=16, sel_bias_std=1.0)),
-    # 128 rows per expert on average: 192-row tiles (two-slot ring), SiLU
-    # through the split tail, and K = 768 (one scale load per stage)
+    # 128 rows per expert on average: per-expert 128- and 192-row tiles in one
+    # launch, SiLU through the split tail, and K = 768 (one scale load per stage)
     "mx_bm192_silu_split": ("deepseek", dict(T=512, d=1024, h=512, E=32, k=8, S=1, activation="silu")),
     "mx_bm192_scales_per_stage": ("deepseek", dict(T=512, d=768, h=768, E=32, k=8, S=0)),
+    # ceil(0.1 * 1000 / 16) = 7 raised to the floor of 40
+    "mx_min_capacity": ("glam", dict(T=1000, d=256, h=512, E=16, cf=0.1, min_capacity=40)),
 }
 
 
@@ -96,6 +98,38 @@ def test_mx_full_size_mixed_heights(workload, nrows):
     rows = np.unique(np.concatenate([[0, c.T - 1], rng.choice(c.T, nrows - 2, replace=False)]))
     rep = compare_mx(inp, run_gpu_mx(inp, stacked=stacked), stacked=stacked, rows=rows, extra_experts=2)
     _say(f"[mx-full] {workload}: {rep}")
+
+
+def _skewed(base, b_g, **kw):
+    inp = make_inputs(CONFIGS[base].replace(name=f"{base}-skewed", **kw), seed=0)
+    inp._bg = np.asarray(b_g, dtype=np.float32)
+    inp.cfg = inp.cfg.replace(router_bias_std=1.0)
+    return inp
+
+
+def test_mx_every_token_to_one_expert():
+    """One segment of 600 rows (128-row tiles: ceil(600 / 192) = 4 does not
+    cut ceil(600 / 128) = 5 by a third) beside seven empty ones."""
+    E = 8
+    inp = _skewed("mixtral", [60.0] + [0.0] * (E - 1), T=600, d=512, h=512, E=E, k=1)
+    _say("[mx] every token to expert 0 (k=1)")
+    stacked = inp.stacked()
+    gpu = run_gpu_mx(inp, stacked=stacked)
+    assert gpu["counts"].tolist() == [600] + [0] * (E - 1)
+    rep = compare_mx(inp, gpu, stacked=stacked)
+    _say(f"[mx] one expert: {rep}")
+
+
+def test_mx_deterministic_bitwise():
+    """Two calls on mixed tile heights with a split tail give the same bits."""
+    inp = make_inputs(CONFIGS["deepseek"].replace(name="mx-det", T=512, d=1024, h=512, E=32, k=8, S=1), seed=1)
+    _say("[mx] determinism: two calls")
+    stacked = inp.stacked()
+    a = run_gpu_mx(inp, stacked=stacked)
+    b = run_gpu_mx(inp, stacked=stacked)
+    for key in ("out", "idx", "w", "counts", "kept", "slot_pos"):
+        assert np.array_equal(a[key], b[key]), key
+    assert a["aux"] == b["aux"] and a["z"] == b["z"]
 
 
 def test_mx_full_size_mixtral():

@@ -138,10 +138,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            static_cast<int>(bytes), kRsrcWord3);
 }
 
-// s_waitcnt immediate that waits until at most n vector-memory operations
-// are outstanding (n < 64) and does not wait on LDS or export counters
-constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
 // Logical tile L -> (M tile, N tile): groups of kGroupM consecutive M tiles
 // (adjacent rows of the same or neighbouring experts) sweep all N tiles,
 // M fastest, so tiles that run together share A and B panels in L2.

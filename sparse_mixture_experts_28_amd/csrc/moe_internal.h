@@ -15,6 +15,10 @@ constexpr int kRouterTile = 64;     // tokens per router workgroup (= permute ra
 constexpr int kRouterThreads = 256; // 4 waves x 16 tokens
 constexpr int kWave = 64;
 
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding (n < 64) and does not wait on LDS or export counters
+constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
 // ---------------------------------------------------------- bf16 helpers --
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));

@@ -131,10 +131,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* base, uint
                                            kMxRsrc);
 }
 
-// s_waitcnt immediate that waits until at most n vector-memory operations
-// are outstanding (n < 64) and does not wait on LDS or export counters
-constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
 __device__ __forceinline__ void mx_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt 0 only
   __asm__ volatile("" ::: "memory");

@@ -385,10 +385,6 @@ constexpr int kLgCh = kLgK / 8;                        // 16-byte chunks per sta
 template <int EXP>
 constexpr int lg_slots() { return EXP == 16 ? 4 : 3; }
 
-// s_waitcnt immediate: at most n (< 64) vector-memory operations outstanding,
-// no wait on LDS or export counters
-constexpr int lg_vm_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
 // LDS row of 16 chunks (256 bytes): logical chunk c of row r at c ^ (r & 15).
 // Measured with an LDS probe on gfx950, the fragment reads (rows 0..15 of a
 // block at chunks 4 s .. 4 s + 3 in the four 16-lane quarters) then have no
@@ -465,12 +461,12 @@ void router_logits_kernel(LogitArgs a) {
     // stage st landed (the up to NS - 2 stages after it may be in flight);
     // every wave is past stage st-1, whose slot then takes stage st + NS - 1
     if constexpr (NS == 4) {
-      if (st + 2 < nst) __builtin_amdgcn_s_waitcnt(lg_vm_wait(2 * kLgLoads));
-      else if (st + 1 < nst) __builtin_amdgcn_s_waitcnt(lg_vm_wait(kLgLoads));
-      else __builtin_amdgcn_s_waitcnt(lg_vm_wait(0));
+      if (st + 2 < nst) __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * kLgLoads));
+      else if (st + 1 < nst) __builtin_amdgcn_s_waitcnt(vm_wait_imm(kLgLoads));
+      else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     } else {
-      if (st + 1 < nst) __builtin_amdgcn_s_waitcnt(lg_vm_wait(kLgLoads));
-      else __builtin_amdgcn_s_waitcnt(lg_vm_wait(0));
+      if (st + 1 < nst) __builtin_amdgcn_s_waitcnt(vm_wait_imm(kLgLoads));
+      else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     }
     lg_barrier();
     if (st + NS - 1 < nst) issue(st + NS - 1);

@@ -106,20 +106,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // segment s containing global M-tile mt: tile_start[s] <= mt < tile_start[s+1]
-__device__ __forceinline__ int find_segment(const int32_t* tile_start, int nseg, int mt) {
-  int lo = 0, hi = nseg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_start[mid] <= mt) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // -------------------------------------------------------------- MFMA path --
 constexpr int kBN = 256, kBK = 64;
-constexpr int kGroupM = 8;
 constexpr int kCh = kBK / 8;                   // 16-byte chunks per tile row
-constexpr int kRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data format (gfx9 family)
 
 // LDS layout of a tile row of 64 bf16 (8 chunks of 16 bytes): logical chunk c
 // of row r is stored at chunk c ^ (r & 7) ^ ((r >> 3) & 1).  Fragment reads
@@ -132,49 +121,6 @@ constexpr int kRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data format
 // use the same assignment, so each MFMA still contracts matching k of A and
 // B; only which 32 k share an MFMA changes.
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7) ^ ((row >> 3) & 1); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), kRsrcWord3);
-}
-
-// Logical tile L -> (M tile, N tile): groups of kGroupM consecutive M tiles
-// (adjacent rows of the same or neighbouring experts) sweep all N tiles,
-// M fastest, so tiles that run together share A and B panels in L2.
-__device__ __forceinline__ void tile_of(int L, int total_mt, int ntn, int& mt, int& nt) {
-  const int gsz = kGroupM * ntn;
-  const int grp = L / gsz;
-  const int first_m = grp * kGroupM;
-  const int gm = min(kGroupM, total_mt - first_m);
-  const int r = L - grp * gsz;
-  mt = first_m + r % gm;
-  nt = r / gm;
-}
-
-// Split of the last partial round of a persistent launch of P workgroups
-// over `total` tiles: the `tail` = total mod P tiles of that round are cut
-// along K into S pieces each (S = P / tail, at most nk / 4 steps per piece
-// and at most part_cap pieces), so the round keeps the whole grid busy.  The
-// pieces leave float32 partial tiles; a fix-up kernel sums each tile's S
-// pieces in order, so results do not depend on timing.
-struct TailPlan {
-  int full;   // tiles computed whole
-  int tail;   // tiles computed in pieces (0 if no split)
-  int S;      // pieces per tail tile
-};
-
-__device__ __forceinline__ TailPlan tail_plan(int total, int P, int nk, int part_cap) {
-  TailPlan tp{total, 0, 1};
-  const int tail = total % P;
-  if (tail == 0) return tp;
-  int S = min(P / tail, nk / 4);
-  S = min(S, part_cap / tail);
-  if (S < 2) return tp;
-  tp.full = total - tail;
-  tp.tail = tail;
-  tp.S = S;
-  return tp;
-}
 
 // ------------------------------------------------------------ MFMA path --
 // BM x 256 x 64 tiles, BM in {128, 160, 256}; 4 waves (one per SIMD) in

@@ -134,6 +134,66 @@ __host__ __device__ inline int mx_mixed_tile_height(int rows) {
   return 3 * t192 < 2 * t128 ? 192 : 128;
 }
 
+// ------------------------------------------------ grouped-GEMM helpers --
+// (shared by the bf16 and MXFP8 grouped GEMMs; the descriptor also by the router)
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kGroupM = 8;
+
+// Buffer descriptor over [base, base + bytes): a load past the end reads zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kRsrcWord3);
+}
+
+// Logical tile L -> (M tile, N tile): groups of kGroupM consecutive M tiles
+// (adjacent rows of the same or neighbouring experts) sweep all N tiles,
+// M fastest, so tiles that run together share A and B panels in L2.
+__device__ __forceinline__ void tile_of(int L, int total_mt, int ntn, int& mt, int& nt) {
+  const int gsz = kGroupM * ntn;
+  const int grp = L / gsz;
+  const int first_m = grp * kGroupM;
+  const int gm = min(kGroupM, total_mt - first_m);
+  const int r = L - grp * gsz;
+  mt = first_m + r % gm;
+  nt = r / gm;
+}
+
+// Split of the last partial round of a persistent launch of P workgroups
+// over `total` tiles: the `tail` = total mod P tiles of that round are cut
+// along K into S pieces each (S = P / tail, at most nk / 4 steps per piece
+// and at most part_cap pieces), so the round keeps the whole grid busy.  The
+// pieces leave float32 partial tiles; a fix-up kernel sums each tile's S
+// pieces in order, so results do not depend on timing.
+struct TailPlan {
+  int full;   // tiles computed whole
+  int tail;   // tiles computed in pieces (0 if no split)
+  int S;      // pieces per tail tile
+};
+
+__device__ __forceinline__ TailPlan tail_plan(int total, int P, int nk, int part_cap) {
+  TailPlan tp{total, 0, 1};
+  const int tail = total % P;
+  if (tail == 0) return tp;
+  int S = min(P / tail, nk / 4);
+  S = min(S, part_cap / tail);
+  if (S < 2) return tp;
+  tp.full = total - tail;
+  tp.tail = tail;
+  tp.S = S;
+  return tp;
+}
+
+// Segment of M tile mt: the last segment whose first tile is <= mt (empty
+// segments share their successor's first tile and are passed over).
+__device__ __forceinline__ int find_segment(const int32_t* tile_start, int nseg, int mt) {
+  int lo = 0, hi = nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_start[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 struct Problem {
   int T, d, h, E, k, S;
   bool mx;       // MXFP8 expert Linears

@@ -121,67 +121,14 @@ struct MxArgs {
 
 constexpr int kMxBN = 256, kMxBK = 128;     // tile columns, K elements (= bytes) per stage
 constexpr int kMxCh = kMxBK / 16;           // 16-byte chunks per stage row
-constexpr int kMxGroupM = 8;
-constexpr int kMxRsrc = 0x00020000;
 
 __device__ __forceinline__ int mx_swz(int row, int c) { return c ^ (row & 7); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
-                                           kMxRsrc);
-}
 
 __device__ __forceinline__ void mx_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt 0 only
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
-}
-
-// Logical tile L -> (M tile, N tile): groups of kMxGroupM consecutive M tiles
-// sweep all N tiles, M fastest, so tiles that run together share A and B
-// panels in L2.
-__device__ __forceinline__ void mx_tile_of(int L, int total_mt, int ntn, int& mt, int& nt) {
-  const int gsz = kMxGroupM * ntn;
-  const int grp = L / gsz;
-  const int first_m = grp * kMxGroupM;
-  const int gm = min(kMxGroupM, total_mt - first_m);
-  const int r = L - grp * gsz;
-  mt = first_m + r % gm;
-  nt = r / gm;
-}
-
-// Split of the last partial round of a persistent launch of P workgroups
-// over `total` tiles: its tail = total mod P tiles are cut along K into S
-// pieces (S = P / tail, pieces of at least 4 steps, at most part_cap pieces),
-// so that round keeps the whole grid busy.  The pieces leave float32 partial
-// tiles that a fix-up sums in piece order, so results do not depend on timing.
-struct MxTail {
-  int full;   // tiles computed whole
-  int tail;   // tiles computed in pieces (0 if no split)
-  int S;      // pieces per tail tile
-};
-
-__device__ __forceinline__ MxTail mx_tail_plan(int total, int P, int nk, int part_cap) {
-  MxTail tp{total, 0, 1};
-  const int tail = total % P;
-  if (tail == 0) return tp;
-  int S = min(P / tail, nk / 4);
-  S = min(S, part_cap / tail);
-  if (S < 2) return tp;
-  tp.full = total - tail;
-  tp.tail = tail;
-  tp.S = S;
-  return tp;
-}
-
-__device__ __forceinline__ int mx_find_segment(const int32_t* tile_start, int nseg, int mt) {
-  int lo = 0, hi = nseg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_start[mid] <= mt) lo = mid; else hi = mid - 1;
-  }
-  return lo;
 }
 
 // activation of the first Linear: 1 GELU(erf), 2 SiLU, 0 none (second Linear)
@@ -299,11 +246,11 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, u32x4* lds, const SegTa
   const int o_off = __builtin_amdgcn_readfirstlane(st.o_off[s]);
   const bool gather = g.row_token != nullptr && s < g.E;
   const int n0 = nt * kMxBN;
-  const __amdgpu_buffer_rsrc_t ra = mx_rsrc(g.A, static_cast<uint32_t>(g.a_rows) * row_bytes);
-  const __amdgpu_buffer_rsrc_t ras = mx_rsrc(g.As, static_cast<uint32_t>(g.a_rows) * srow_bytes);
-  const __amdgpu_buffer_rsrc_t rb = mx_rsrc(g.W + static_cast<size_t>(s) * g.N * g.K,
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, static_cast<uint32_t>(g.a_rows) * row_bytes);
+  const __amdgpu_buffer_rsrc_t ras = make_rsrc(g.As, static_cast<uint32_t>(g.a_rows) * srow_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.W + static_cast<size_t>(s) * g.N * g.K,
                                             static_cast<uint32_t>(g.N) * row_bytes);
-  const __amdgpu_buffer_rsrc_t rbs = mx_rsrc(g.Ws + static_cast<size_t>(s) * g.N * (g.K / 32),
+  const __amdgpu_buffer_rsrc_t rbs = make_rsrc(g.Ws + static_cast<size_t>(s) * g.N * (g.K / 32),
                                              static_cast<uint32_t>(g.N) * srow_bytes);
   // code loads: load n of wave w fills rows 32 n + 8 w + lane / 8 (A rows, then B rows);
   // rows past the segment get an offset past the end (the range check reads zero)
@@ -502,7 +449,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, u32x4* lds, const SegTa
   // tile and columns 16 j + 4 q .. + 3.  A piece of a tail tile stores its
   // float32 partial tile (row-major, rows PBM piece ..); a whole tile adds the bias,
   // applies the activation (phase 1) and stores MX blocks or bf16.
-  const __amdgpu_buffer_rsrc_t pr = mx_rsrc(g.part, static_cast<uint32_t>(g.part_cap) * PBM * kMxBN * 4u);
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(g.part, static_cast<uint32_t>(g.part_cap) * PBM * kMxBN * 4u);
   const uint32_t pv = (static_cast<uint32_t>(wm * (BM / 2) + rr) * kMxBN + wn * 128 + 4 * q) * 4u;
   const int cbase = n0 + wn * 128 + 4 * q;
   uint2 bq[8];
@@ -597,7 +544,7 @@ void gemm_mx_kernel(MxArgs g) {
   const int nk = g.K / kMxBK;
   const int per_xcd = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const MxTail tp = mx_tail_plan(total, gridDim.x, nk, g.part_cap);
+  const TailPlan tp = tail_plan(total, gridDim.x, nk, g.part_cap);
   const int items = tp.full + tp.tail * tp.S;
 
   for (int it = 0;; ++it) {
@@ -614,8 +561,8 @@ void gemm_mx_kernel(MxArgs g) {
       kn = (pp + 1) * nk / tp.S - k0;        // >= 4
     }
     int mt, nt;
-    mx_tile_of(L, total_mt, ntn, mt, nt);
-    const int s = __builtin_amdgcn_readfirstlane(mx_find_segment(st.tile_start, g.nseg, mt));
+    tile_of(L, total_mt, ntn, mt, nt);
+    const int s = __builtin_amdgcn_readfirstlane(find_segment(st.tile_start, g.nseg, mt));
     if constexpr (BM1 == 0) {
       mx_tile<ACT, BM0, SG, PBM>(g, lds, st, s, mt, nt, k0, kn, piece);
     } else {
@@ -640,15 +587,15 @@ __global__ __launch_bounds__(256) void mx_tail_fixup_kernel(MxArgs g, int P) {
   const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
   const int total_mt = st.tile_start[g.nseg];
   const int ntn = g.N / kMxBN;
-  const MxTail tp = mx_tail_plan(total_mt * ntn, P, g.K / kMxBK, g.part_cap);
+  const TailPlan tp = tail_plan(total_mt * ntn, P, g.K / kMxBK, g.part_cap);
   if (tp.tail == 0) return;
   constexpr int kChunks = PBM / 16;
   const int c = 4 * (threadIdx.x & 63);
   for (int w = blockIdx.x; w < tp.tail * kChunks; w += gridDim.x) {
     const int tt = w / kChunks, r0 = (w % kChunks) * 16;
     int mt, nt;
-    mx_tile_of(tp.full + tt, total_mt, ntn, mt, nt);
-    const int s = mx_find_segment(st.tile_start, g.nseg, mt);
+    tile_of(tp.full + tt, total_mt, ntn, mt, nt);
+    const int s = find_segment(st.tile_start, g.nseg, mt);
     const int bm = BM1 == 0 ? BM0 : st.tile_bm[s];
     if (r0 >= bm) continue;   // rows of the next tile
     const int rows = st.rows[s];

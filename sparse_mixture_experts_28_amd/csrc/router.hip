@@ -364,12 +364,6 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(RouterArgs a
 // float64.  Output:
 // float64 partial logits [KS][T][Epad]; the selection kernel adds the KS
 // partials in order.
-constexpr uint32_t kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), kRsrcWord3);
-}
 
 struct LogitArgs {
   const uint16_t* x;
@@ -416,8 +410,8 @@ void router_logits_kernel(LogitArgs a) {
   const int nrows = min(kLgTok, a.T - tok0);
   const int nexp = min(EXP, a.E - e0);
   // out-of-range token and expert rows read as zero (buffer range check)
-  const __amdgpu_buffer_rsrc_t xs = rsrc(a.x + static_cast<size_t>(tok0) * a.d, static_cast<uint32_t>(nrows) * rb);
-  const __amdgpu_buffer_rsrc_t ws = rsrc(a.W + static_cast<size_t>(e0) * a.d, static_cast<uint32_t>(max(nexp, 0)) * rb);
+  const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x + static_cast<size_t>(tok0) * a.d, static_cast<uint32_t>(nrows) * rb);
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.W + static_cast<size_t>(e0) * a.d, static_cast<uint32_t>(max(nexp, 0)) * rb);
   const int nchunk = a.d / 256;                      // 256-element chunks of d
   const int c0 = ks * nchunk / a.KS, c1 = (ks + 1) * nchunk / a.KS;
   const int nst = (c1 - c0) * (256 / kLgK);          // stages of this split (>= 2)

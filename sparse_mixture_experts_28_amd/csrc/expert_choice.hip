@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(EcArgs a) {
   // equal logits everywhere, or a range that does not scale: one bucket
   const bool bucketed = range > 0.0 && isfinite(range) && isfinite(scale);
   auto bucket = [&](double v) -> int {
-    if (!bucketed) return 0;
+    if (!bucketed || !(v >= vmin)) return 0;   // a NaN logit goes to the lowest bucket
     const int b = static_cast<int>((v - vmin) * scale);
     return b < kBins - 1 ? b : kBins - 1;
   };

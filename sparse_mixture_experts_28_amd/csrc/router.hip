@@ -114,6 +114,12 @@ __device__ __forceinline__ float sum16(float v) {
 // one; a chosen expert's weight numerator is exp(l - m) of its logit alone.
 // Lane j < k ends with the j-th choice and its numerator; every lane with
 // their sum.
+//
+// The choice is total: a NaN key ranks as -inf, and every not-yet-chosen
+// expert is a candidate even when its key is -inf, so each round returns an
+// expert in [0, E) (k <= E leaves one untaken).  A token whose logits are NaN
+// (a NaN in its row of x, in W_g or in a bias) then gets valid indices and
+// NaN weights, and the other tokens are unaffected.
 template <int NB>
 __device__ __forceinline__ void select_k(const RouterArgs& a, const double (&val)[NB], double m, int c, int& my_idx,
                                          float& my_e, float& esum) {
@@ -122,19 +128,23 @@ __device__ __forceinline__ void select_k(const RouterArgs& a, const double (&val
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int e = nb * 16 + c;
-    key[nb] = a.b_sel && e < E ? val[nb] + static_cast<double>(a.b_sel[e]) : val[nb];
+    const double kv = a.b_sel && e < E ? val[nb] + static_cast<double>(a.b_sel[e]) : val[nb];
+    key[nb] = kv == kv ? kv : -INFINITY;
   }
+  constexpr int kNone = 0x7fffffff;
   uint32_t taken = 0;
   my_idx = 0;
   my_e = 0.f;
   esum = 0.f;
   for (int j = 0; j < k; ++j) {
     double bv = -INFINITY, bl = -INFINITY;
-    int bi = 0x7fffffff;
+    int bi = kNone;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int e = nb * 16 + c;
-      if (e < E && !((taken >> nb) & 1u) && key[nb] > bv) { bv = key[nb]; bi = e; bl = val[nb]; }
+      // experts ascend with nb: the first untaken one is this lane's candidate
+      // until a strictly larger key replaces it
+      if (e < E && !((taken >> nb) & 1u) && (bi == kNone || key[nb] > bv)) { bv = key[nb]; bi = e; bl = val[nb]; }
     }
     argmax16p(bv, bi, bl);
     if ((bi & 15) == c) taken |= 1u << (bi >> 4);

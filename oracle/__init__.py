@@ -9,11 +9,11 @@ module's header for the passages it follows.
 from .moe_ref import (ACTIVATIONS, TIE_EPS, ExpertChoice, ExpertChoiceRef, MoERef, aux_loss, capacity_of,
                       capacity_ranks, expert_choice_capacity, expert_counts, expert_ffn, gelu,
                       is_valid_expert_choice, is_valid_topk, moe_forward_expert_choice_ref, moe_forward_ref,
-                      moe_forward_ref_from_inputs, renormalised_weights, router_logits, router_z_loss,
+                      renormalised_weights, router_logits, router_z_loss,
                       select_expert_choice, select_topk, selection_keys, silu, softmax, widen)
 
 __all__ = ["ACTIVATIONS", "TIE_EPS", "ExpertChoice", "ExpertChoiceRef", "MoERef", "expert_choice_capacity",
            "is_valid_expert_choice", "moe_forward_expert_choice_ref", "select_expert_choice", "aux_loss", "capacity_of", "capacity_ranks",
            "expert_counts", "expert_ffn", "gelu", "is_valid_topk", "moe_forward_ref",
-           "moe_forward_ref_from_inputs", "renormalised_weights", "router_logits", "router_z_loss",
+           "renormalised_weights", "router_logits", "router_z_loss",
            "select_topk", "selection_keys", "silu", "softmax", "widen"]

@@ -467,12 +467,3 @@ def moe_forward_expert_choice_ref(x, W_g, get_expert: Callable[[int], tuple], E:
     return ExpertChoiceRef(logits=l, probs=p, tok=tok, w=w, flag=sel.flag, per_token=per_token, aux=aux,
                            z=z_ec, P=P, rows=rows_arr, out=out)
 
-
-def moe_forward_ref_from_inputs(inp, rows=None, override_idx=None) -> MoERef:
-    """Convenience wrapper over an object with ``cfg``, ``x``, ``W_g``, ``b_g``
-    and ``expert(e)`` (the seeded workload generator's interface)."""
-    c = inp.cfg
-    return moe_forward_ref(inp.x, inp.W_g, inp.expert, c.E, c.k, c.cf, c.S, inp.b_g,
-                           kind=c.dtype, rows=rows, override_idx=override_idx,
-                           activation=c.activation, min_capacity=c.min_capacity,
-                           b_sel=getattr(inp, "b_sel", None))

@@ -142,13 +142,17 @@ def moe_forward_mxfp8_ref(x, W_g, experts_q, E: int, k: int, capacity_factor: fl
       H   = act(xq W1q^T + b1);  Hq = dequantize(quantize(H))
       y   = Hq W2q^T + b2
     and the combine weights y as in the plain layer."""
-    base = moe_ref.moe_forward_ref(x, W_g, lambda e: _no_ffn(experts_q, e, kind), E, k, capacity_factor,
-                                   n_shared, b_g, kind=kind, rows=rows, override_idx=override_idx,
-                                   activation=activation, min_capacity=min_capacity, b_sel=b_sel)
     xf = moe_ref.widen(x, kind)
     T, d = xf.shape
+    rows_arr = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    # routing, capacity, aux and z-loss of the plain layer; its expert outputs
+    # are not needed (no rows asked), the MXFP8 experts follow below
+    base = moe_ref.moe_forward_ref(x, W_g, lambda e: _no_ffn(experts_q, e, kind), E, k, capacity_factor,
+                                   n_shared, b_g, kind=kind, rows=np.zeros(0, dtype=np.int64),
+                                   override_idx=override_idx, activation=activation, min_capacity=min_capacity,
+                                   b_sel=b_sel)
+    base.rows = rows_arr
     xq = dequantize(*quantize(xf))
-    rows_arr = base.rows
     want = np.zeros(T, dtype=bool)
     want[rows_arr] = True
     row_of = np.full(T, -1, dtype=np.int64)

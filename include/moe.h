@@ -163,6 +163,17 @@ moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const v
 size_t moe_workspace_bytes_expert_choice(int32_t T, int32_t d, int32_t h, int32_t E, int32_t C,
                                          int32_t n_shared, moe_dtype_t dtype);
 
+/* Tokens per expert for expert-choice routing from a capacity factor: the
+ * capacity of "AI-Research-SKILLs MoE 训练实战…全指南" §8.2 (factor x tokens /
+ * experts), floored by min_capacity as in its §5.1 DeepSpeed settings, and at
+ * most T (an expert cannot take more tokens than there are):
+ *   C = min(T, max(ceil(cf * T / E), min_capacity)),
+ * the ceiling taken in double precision of the float32 cf (as moe_forward
+ * computes its capacity).  Host-only arithmetic, no GPU call.  Returns C
+ * (1..T), or -1 when cf is not > 0 (NaN included), T < 1, E < 1 or
+ * min_capacity < 0. */
+int32_t moe_expert_choice_capacity(float capacity_factor, int32_t T, int32_t E, int32_t min_capacity);
+
 /* The layer forward with expert-choice routing.
  *   x, W_g, W1, b1, W2, b2, n_shared, out   as for moe_forward (b1, b2 may be NULL)
  *   E        routed experts, 1..MOE_MAX_EXPERTS

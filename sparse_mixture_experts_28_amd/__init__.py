@@ -9,13 +9,13 @@ passes torch's current stream.  Nothing here computes any part of the layer.
 from __future__ import annotations
 
 import ctypes
-import math
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
 from ._lib import (EXPORTS, LIB_PATH, MOE_ACT_GELU, MOE_ACT_SILU, MOE_BF16, MOE_ERR_ARG, MOE_ERR_HIP,
                    MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_F32, MOE_MAX_EXPERTS, MOE_MAX_SHARED,
-                   MOE_MAX_TOPK, MOE_NUM_STAGE_EVENTS, MOE_OK, MoeLaunch, moe_forward, moe_forward_expert_choice,
+                   MOE_MAX_TOPK, MOE_NUM_STAGE_EVENTS, MOE_OK, MoeLaunch,
+                   moe_expert_choice_capacity, moe_forward, moe_forward_expert_choice,
                    moe_forward_mxfp8, moe_quantize_mxfp8, moe_status_string, moe_workspace_bytes,
                    moe_workspace_bytes_expert_choice, moe_workspace_bytes_mxfp8)
 
@@ -63,8 +63,9 @@ def _check_tensors(x, W_g, W1, b1, W2, b2, b_g, n_shared: int, activation: str) 
     if W_g.shape != (E, d) or W1.shape != (E + S, h, d) or W2.shape != (E + S, d, h) or \
             (b1 is not None and b1.shape != (E + S, h)) or (b2 is not None and b2.shape != (E + S, d)):
         raise ValueError("inconsistent shapes")
-    if b_g is not None and (b_g.dtype != torch.float32 or b_g.shape != (E,) or b_g.device != dev):
-        raise ValueError("b_g must be float32 [E] on the same GPU")
+    if b_g is not None and (b_g.dtype != torch.float32 or b_g.shape != (E,) or b_g.device != dev
+                            or not b_g.is_contiguous()):
+        raise ValueError("b_g must be a contiguous float32 [E] on the same GPU")
 
 
 def _check_b_sel(b_sel, E, dev):
@@ -82,8 +83,8 @@ def _launch(x, T, d, h, dt, b_g, workspace, zl, activation, min_capacity, stage_
     launch.T, launch.d, launch.h, launch.dtype = T, d, h, dt
     launch.b_g = b_g.data_ptr() if b_g is not None else None
     launch.b_sel = b_sel.data_ptr() if b_sel is not None else None
-    launch.workspace = workspace.data_ptr()
-    launch.workspace_bytes = workspace.numel()
+    launch.workspace = workspace.data_ptr() if workspace is not None else None
+    launch.workspace_bytes = workspace.numel() if workspace is not None else 0
     launch.stream = torch.cuda.current_stream(x.device).cuda_stream
     launch.z_loss = zl.data_ptr()
     launch.activation = ACTIVATIONS[activation]
@@ -162,12 +163,12 @@ class ExpertChoiceOutput:
 
 
 def expert_choice_capacity(capacity_factor: float, T: int, E: int, min_capacity: int = 0) -> int:
-    """Tokens per expert from a capacity factor: min(T, max(ceil(cf T / E), min_capacity)),
-    the ceiling taken in double precision of the float32 factor the layer uses elsewhere."""
-    if not capacity_factor > 0:
-        raise ValueError("expert choice needs a capacity factor > 0")
-    cf = ctypes.c_float(capacity_factor).value
-    return min(T, max(int(math.ceil(cf * T / E)), int(min_capacity)))
+    """Tokens per expert from a capacity factor, as the library computes it
+    (``moe_expert_choice_capacity``); raises ValueError for invalid arguments."""
+    C = moe_expert_choice_capacity(float(capacity_factor), int(T), int(E), int(min_capacity))
+    if C < 1:
+        raise ValueError("expert choice needs a capacity factor > 0, T >= 1, E >= 1 and min_capacity >= 0")
+    return C
 
 
 def forward_expert_choice(x, W_g, W1, b1, W2, b2, C: int, n_shared: int = 0, b_g=None, *,
@@ -228,19 +229,29 @@ def forward_mxfp8(x, W_g, W1, W1s, b1, W2, W2s, b2, k: int, capacity_factor: flo
     (codes, scales) from ``quantize_mxfp8`` of [E+S, h, d] / [E+S, d, h];
     b_g and b_sel as in ``forward``."""
     import torch
-    if x.dtype != torch.bfloat16:
-        raise ValueError("the MXFP8 layer takes bf16 activations")
+    for t in (x, W_g, b1, b2):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise ValueError("x, W_g, b1 and b2 of the MXFP8 layer must be bf16")
+    for t in (W1, W1s, W2, W2s):
+        if t.dtype != torch.uint8:
+            raise ValueError("MXFP8 weight codes and scales must be uint8 (from quantize_mxfp8)")
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}")
     T, d = x.shape
     E = W_g.shape[0]
     h = W1.shape[1]
     S = n_shared
-    if W1.shape != (E + S, h, d) or W1s.shape != (E + S, h, d // 32) or W2.shape != (E + S, d, h) or \
-            W2s.shape != (E + S, d, h // 32) or W1.dtype != torch.uint8 or W2.dtype != torch.uint8:
-        raise ValueError("inconsistent MXFP8 weight shapes")
+    if W_g.shape != (E, d) or W1.shape != (E + S, h, d) or W1s.shape != (E + S, h, d // 32) or \
+            W2.shape != (E + S, d, h) or W2s.shape != (E + S, d, h // 32) or \
+            (b1 is not None and b1.shape != (E + S, h)) or (b2 is not None and b2.shape != (E + S, d)):
+        raise ValueError("inconsistent MXFP8 layer shapes")
     for t in (x, W_g, W1, W1s, W2, W2s, b1, b2):
         if t is not None and (not t.is_cuda or t.device != x.device or not t.is_contiguous()):
             raise ValueError("all tensors must be contiguous on one GPU")
     dev = x.device
+    if b_g is not None and (b_g.dtype != torch.float32 or b_g.shape != (E,) or b_g.device != dev
+                            or not b_g.is_contiguous()):
+        raise ValueError("b_g must be a contiguous float32 [E] on the same GPU")
     _check_b_sel(b_sel, E, dev)
     nbytes = moe_workspace_bytes_mxfp8(T, d, h, E, k, S)
     if nbytes == 0:
@@ -269,7 +280,7 @@ def forward_mxfp8(x, W_g, W1, W1s, b1, W2, W2s, b2, k: int, capacity_factor: flo
 
 __all__ = ["forward", "MoEOutput", "moe_forward", "moe_workspace_bytes", "moe_status_string", "MoeLaunch",
            "forward_expert_choice", "ExpertChoiceOutput", "moe_forward_expert_choice",
-           "moe_workspace_bytes_expert_choice", "expert_choice_capacity", "STAGES_EXPERT_CHOICE",
+           "moe_workspace_bytes_expert_choice", "expert_choice_capacity", "moe_expert_choice_capacity", "STAGES_EXPERT_CHOICE",
            "quantize_mxfp8", "forward_mxfp8", "moe_quantize_mxfp8", "moe_workspace_bytes_mxfp8", "moe_forward_mxfp8",
            "ACTIVATIONS", "MOE_ACT_GELU", "MOE_ACT_SILU", "MOE_F32", "MOE_BF16", "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
            "MOE_ERR_HIP", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SHARED", "MOE_NUM_STAGE_EVENTS",

@@ -32,7 +32,7 @@ MOE_NUM_STAGE_EVENTS = 7
 # names of the C ABI entry points (include/moe.h)
 EXPORTS = ("moe_forward", "moe_workspace_bytes", "moe_status_string", "moe_forward_expert_choice",
            "moe_workspace_bytes_expert_choice", "moe_quantize_mxfp8", "moe_workspace_bytes_mxfp8",
-           "moe_forward_mxfp8")
+           "moe_forward_mxfp8", "moe_expert_choice_capacity")
 
 
 class MoeLaunch(ctypes.Structure):
@@ -90,6 +90,8 @@ def _load():
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(MoeLaunch),
     ]
+    lib.moe_expert_choice_capacity.restype = ctypes.c_int32
+    lib.moe_expert_choice_capacity.argtypes = [ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_forward.restype = ctypes.c_int
@@ -111,6 +113,11 @@ def moe_workspace_bytes(T: int, d: int, h: int, E: int, k: int, n_shared: int, d
 
 def moe_workspace_bytes_expert_choice(T: int, d: int, h: int, E: int, C: int, n_shared: int, dtype: int) -> int:
     return int(LIB.moe_workspace_bytes_expert_choice(T, d, h, E, C, n_shared, dtype))
+
+
+def moe_expert_choice_capacity(capacity_factor: float, T: int, E: int, min_capacity: int = 0) -> int:
+    """Raw call: tokens per expert under expert choice, or -1 for invalid arguments."""
+    return int(LIB.moe_expert_choice_capacity(capacity_factor, T, E, min_capacity))
 
 
 def moe_status_string(status: int) -> str:

@@ -61,7 +61,7 @@ Layout layout_of(const Problem& p) {
   L.xq_scales = off;  off += align_up(td / 32);
   // sized for the tallest tile: moe_workspace_bytes has no capacity factor,
   // and the tile height moe_forward picks can depend on it
-  L.part_cap = p.mx || gemm_fast_path(p) ? kGemmPartCap : 0;   // the MXFP8 path always runs its MFMA kernel
+  L.part_cap = p.mx || gemm_fast_path(p) ? p.part_limit : 0;   // the MXFP8 path always runs its MFMA kernel
   L.part = off;       off += align_up(static_cast<size_t>(L.part_cap) * 256 * 256 * 4);
   L.total = off;
   return L;
@@ -114,6 +114,13 @@ moe_status_t check_shape(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, 
   return MOE_OK;
 }
 
+// cap = max(ceil(cf T / E), min_cap) in double (cf > 0), saturated at INT32_MAX
+int capacity_of(float cf, int32_t T, int32_t E, int32_t min_cap) {
+  double c = std::ceil(static_cast<double>(cf) * static_cast<double>(T) / static_cast<double>(E));
+  if (c < static_cast<double>(min_cap)) c = static_cast<double>(min_cap);
+  return c >= static_cast<double>(INT32_MAX) ? INT32_MAX : static_cast<int>(c);
+}
+
 // cap = max(ceil(cf T / E), min_cap) in double when cf > 0, else unlimited
 Problem make_problem(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int32_t S, moe_dtype_t dt,
                      float cf, int act = MOE_ACT_GELU, int32_t min_cap = 0) {
@@ -130,15 +137,10 @@ Problem make_problem(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int3
   p.ec_C = 0;
   p.A = T * k;
   p.ntile = (T + kRouterTile - 1) / kRouterTile;
-  if (cf > 0.f) {
-    double c = std::ceil(static_cast<double>(cf) * static_cast<double>(T) / static_cast<double>(E));
-    if (c < static_cast<double>(min_cap)) c = static_cast<double>(min_cap);
-    p.cap = c >= static_cast<double>(INT32_MAX) ? INT32_MAX : static_cast<int>(c);
-  } else {
-    p.cap = INT32_MAX;
-  }
+  p.cap = cf > 0.f ? capacity_of(cf, T, E, min_cap) : INT32_MAX;
   p.gemm_bm = gemm_m_tile(p);
   p.gemm_mixed = false;
+  p.part_limit = kGemmPartCap;
   return p;
 }
 
@@ -172,6 +174,7 @@ Problem make_problem_ec(int32_t T, int32_t d, int32_t h, int32_t E, int32_t C, i
   p.cap = C;
   p.gemm_bm = gemm_m_tile(p);
   p.gemm_mixed = false;
+  p.part_limit = kGemmPartCap;
   return p;
 }
 
@@ -219,6 +222,52 @@ struct StageCheck {
 };
 
 }  // namespace
+
+// The top-k layer on a given workspace (moe_forward: the caller's; moe_forward_noalloc:
+// the library's fixed scratch), with part_limit float32 partial tiles for the GEMM's split tail.
+moe_status_t forward_top_k(const void* x, const void* W_g, const void* W1, const void* b1, const void* W2,
+                           const void* b2, int32_t E, int32_t k, float capacity_factor, int32_t n_shared, void* out,
+                           int32_t* topk_idx, float* topk_w, float* aux_loss, const moe_launch_t* launch,
+                           void* ws_base, size_t ws_bytes, int part_limit) {
+  if (!x || !W_g || !W1 || !W2 || !out || !topk_idx || !topk_w || !aux_loss) return MOE_ERR_ARG;
+  if (std::isnan(capacity_factor) || launch->min_capacity < 0) return MOE_ERR_ARG;
+  if (launch->activation != MOE_ACT_GELU && launch->activation != MOE_ACT_SILU) return MOE_ERR_UNSUPPORTED;
+  const moe_status_t sc = check_shape(launch->T, launch->d, launch->h, E, k, n_shared,
+                                      static_cast<int>(launch->dtype));
+  if (sc != MOE_OK) return sc;
+  const void* a16[] = {x, W_g, W1, b1, W2, b2, out};
+  for (const void* q : a16)
+    if (q && !aligned(q, 16)) return MOE_ERR_UNSUPPORTED;
+  const void* a4[] = {topk_idx, topk_w, aux_loss, launch->z_loss, launch->b_g, launch->b_sel, launch->expert_counts,
+                      launch->expert_kept, launch->slot_pos};
+  for (const void* q : a4)
+    if (q && !aligned(q, 4)) return MOE_ERR_UNSUPPORTED;
+
+  Problem p = make_problem(launch->T, launch->d, launch->h, E, k, n_shared, launch->dtype, capacity_factor,
+                           launch->activation, launch->min_capacity);
+  p.part_limit = part_limit;
+  bool ok = false;
+  Workspace ws = carve_workspace(p, ws_base, ws_bytes, &ok);
+  if (!ok) return MOE_ERR_WORKSPACE;
+  if (launch->slot_pos) ws.slot_pos = launch->slot_pos;
+
+  hipStream_t st = launch->stream;
+  StageCheck check{st, launch->stage_events};
+  // a stale error from an earlier, unrelated HIP call must not be blamed on a launch here
+  (void)hipGetLastError();
+
+  if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
+  if (!check(launch_router(p, x, W_g, launch->b_g, launch->b_sel, topk_idx, topk_w, ws, st), "router launch")) return MOE_ERR_HIP;
+  if (!check(launch_scan(p, ws, aux_loss, launch->z_loss, launch->expert_counts, launch->expert_kept, st),
+             "scan launch"))
+    return MOE_ERR_HIP;
+  if (!check(launch_scatter(p, topk_idx, ws, st), "scatter launch")) return MOE_ERR_HIP;
+  if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 1, st), "expert phase 1 launch")) return MOE_ERR_HIP;
+  if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 2, st), "expert phase 2 launch")) return MOE_ERR_HIP;
+  if (!check(launch_combine(p, topk_w, ws, out, st), "combine launch")) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 extern "C" {
@@ -299,6 +348,12 @@ moe_status_t moe_forward_mxfp8(const void* x, const void* W_g, const uint8_t* W1
   return MOE_OK;
 }
 
+int32_t moe_expert_choice_capacity(float capacity_factor, int32_t T, int32_t E, int32_t min_capacity) {
+  if (!(capacity_factor > 0.f) || T < 1 || E < 1 || min_capacity < 0) return -1;
+  const int c = moe::capacity_of(capacity_factor, T, E, min_capacity);
+  return c < T ? (c < 1 ? 1 : c) : T;
+}
+
 size_t moe_workspace_bytes_expert_choice(int32_t T, int32_t d, int32_t h, int32_t E, int32_t C, int32_t n_shared,
                                          moe_dtype_t dtype) {
   if (moe::check_shape_ec(T, d, h, E, C, n_shared, static_cast<int>(dtype)) != MOE_OK) return 0;
@@ -321,44 +376,9 @@ moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const v
                          const void* b2, int32_t E, int32_t k, float capacity_factor, int32_t n_shared,
                          void* out, int32_t* topk_idx, float* topk_w, float* aux_loss,
                          const moe_launch_t* launch) {
-  using namespace moe;
   if (launch == nullptr) return MOE_ERR_ARG;
-  if (!x || !W_g || !W1 || !W2 || !out || !topk_idx || !topk_w || !aux_loss) return MOE_ERR_ARG;
-  if (std::isnan(capacity_factor) || launch->min_capacity < 0) return MOE_ERR_ARG;
-  if (launch->activation != MOE_ACT_GELU && launch->activation != MOE_ACT_SILU) return MOE_ERR_UNSUPPORTED;
-  const moe_status_t sc = check_shape(launch->T, launch->d, launch->h, E, k, n_shared,
-                                      static_cast<int>(launch->dtype));
-  if (sc != MOE_OK) return sc;
-  const void* a16[] = {x, W_g, W1, b1, W2, b2, out};
-  for (const void* q : a16)
-    if (q && !aligned(q, 16)) return MOE_ERR_UNSUPPORTED;
-  const void* a4[] = {topk_idx, topk_w, aux_loss, launch->z_loss, launch->b_g, launch->b_sel, launch->expert_counts,
-                      launch->expert_kept, launch->slot_pos};
-  for (const void* q : a4)
-    if (q && !aligned(q, 4)) return MOE_ERR_UNSUPPORTED;
-
-  const Problem p = make_problem(launch->T, launch->d, launch->h, E, k, n_shared, launch->dtype, capacity_factor,
-                                 launch->activation, launch->min_capacity);
-  bool ok = false;
-  Workspace ws = carve_workspace(p, launch->workspace, launch->workspace_bytes, &ok);
-  if (!ok) return MOE_ERR_WORKSPACE;
-  if (launch->slot_pos) ws.slot_pos = launch->slot_pos;
-
-  hipStream_t st = launch->stream;
-  StageCheck check{st, launch->stage_events};
-  // a stale error from an earlier, unrelated HIP call must not be blamed on a launch here
-  (void)hipGetLastError();
-
-  if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
-  if (!check(launch_router(p, x, W_g, launch->b_g, launch->b_sel, topk_idx, topk_w, ws, st), "router launch")) return MOE_ERR_HIP;
-  if (!check(launch_scan(p, ws, aux_loss, launch->z_loss, launch->expert_counts, launch->expert_kept, st),
-             "scan launch"))
-    return MOE_ERR_HIP;
-  if (!check(launch_scatter(p, topk_idx, ws, st), "scatter launch")) return MOE_ERR_HIP;
-  if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 1, st), "expert phase 1 launch")) return MOE_ERR_HIP;
-  if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 2, st), "expert phase 2 launch")) return MOE_ERR_HIP;
-  if (!check(launch_combine(p, topk_w, ws, out, st), "combine launch")) return MOE_ERR_HIP;
-  return MOE_OK;
+  return moe::forward_top_k(x, W_g, W1, b1, W2, b2, E, k, capacity_factor, n_shared, out, topk_idx, topk_w,
+                            aux_loss, launch, launch->workspace, launch->workspace_bytes, moe::kGemmPartCap);
 }
 
 moe_status_t moe_forward_expert_choice(const void* x, const void* W_g, const void* W1, const void* b1,

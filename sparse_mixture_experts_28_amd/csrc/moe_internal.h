@@ -205,6 +205,7 @@ struct Problem {
   int ntile;     // ceil(T / kRouterTile)
   int gemm_bm;   // M tile of the grouped GEMM (for the tile prefix)
   bool gemm_mixed;   // MXFP8 GEMM: per-segment heights by mx_mixed_tile_height (gemm_bm unused)
+  int part_limit;    // float32 partial tiles the workspace reserves for the GEMM's split tail
 };
 
 Workspace carve_workspace(const Problem& p, void* base, size_t bytes_available, bool* ok);
@@ -253,5 +254,11 @@ int logit_pad(int E);
 int logit_splits(const Problem& p);
 // partial tiles reserved for the grouped GEMM's split tail (one per workgroup of a 256-CU part)
 constexpr int kGemmPartCap = 256;
+
+// the top-k layer on a given workspace (moe_api.cpp)
+moe_status_t forward_top_k(const void* x, const void* W_g, const void* W1, const void* b1, const void* W2,
+                           const void* b2, int32_t E, int32_t k, float capacity_factor, int32_t n_shared, void* out,
+                           int32_t* topk_idx, float* topk_w, float* aux_loss, const moe_launch_t* launch,
+                           void* ws_base, size_t ws_bytes, int part_limit);
 
 }  // namespace moe

@@ -204,3 +204,73 @@ def test_ec_null_launch():
     st = moe._lib.LIB.moe_forward_expert_choice(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 0, FAKE, FAKE, FAKE,
                                                 FAKE, None)
     assert st == moe.MOE_ERR_ARG
+
+
+# ------------------------------------------- expert-choice capacity (C ABI) --
+def test_expert_choice_capacity_in_the_library():
+    """The library computes C = min(T, max(ceil(cf T / E), min_capacity)) from
+    the float32 factor; the oracle's capacity formula (guide §8.2, floor of §5.1)
+    gives the same on every case, and the binding only forwards the call."""
+    import numpy as np
+
+    import oracle.moe_ref as ref
+    f = moe.moe_expert_choice_capacity
+    cases = [(2.0, 16384, 64, 0), (1.25, 4096, 64, 0), (1.5, 16384, 64, 0), (0.1, 1000, 16, 40), (100.0, 10, 2, 0),
+             (0.3, 7, 3, 0), (1e-9, 5, 4, 0), (0.03, 200, 8, 0), (0.2, 300, 8, 400), (1.1, 1, 1, 0),
+             (0.7, 12345, 256, 3), (3.3, 999, 7, 0)]
+    for cf, T, E, mc in cases:
+        want = ref.expert_choice_capacity(float(np.float32(cf)), T, E, mc)
+        assert f(cf, T, E, mc) == want, (cf, T, E, mc)
+        assert moe.expert_choice_capacity(cf, T, E, mc) == want
+    for bad in [(0.0, 10, 2, 0), (-1.0, 10, 2, 0), (float("nan"), 10, 2, 0), (1.0, 0, 2, 0), (1.0, 10, 0, 0),
+                (1.0, 10, 2, -1)]:
+        assert f(*bad) == -1, bad
+        with pytest.raises(ValueError):
+            moe.expert_choice_capacity(*bad)
+
+
+def test_binding_has_no_capacity_arithmetic():
+    src = open(os.path.join(ROOT, "sparse_mixture_experts_28_amd", "__init__.py")).read()
+    assert "math.ceil" not in src and "import math" not in src
+
+
+# --------------------------------------------- MXFP8 wrapper argument checks --
+def _mx_args(**over):
+    import torch
+    T, d, h, E = 8, 256, 256, 4
+    a = dict(x=torch.zeros(T, d, dtype=torch.bfloat16), W_g=torch.zeros(E, d, dtype=torch.bfloat16),
+             W1=torch.zeros(E, h, d, dtype=torch.uint8), W1s=torch.zeros(E, h, d // 32, dtype=torch.uint8),
+             b1=torch.zeros(E, h, dtype=torch.bfloat16), W2=torch.zeros(E, d, h, dtype=torch.uint8),
+             W2s=torch.zeros(E, d, h // 32, dtype=torch.uint8), b2=torch.zeros(E, d, dtype=torch.bfloat16))
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("field,dtype", [("x", "float32"), ("W_g", "float32"), ("b1", "float32"),
+                                         ("b2", "float16"), ("W1", "int8"), ("W1s", "float32"), ("W2", "bfloat16"),
+                                         ("W2s", "int32")])
+def test_forward_mxfp8_rejects_wrong_dtypes(field, dtype):
+    import torch
+    a = _mx_args()
+    a[field] = a[field].to(getattr(torch, dtype))
+    with pytest.raises(ValueError):
+        moe.forward_mxfp8(a["x"], a["W_g"], a["W1"], a["W1s"], a["b1"], a["W2"], a["W2s"], a["b2"], k=2)
+
+
+@pytest.mark.parametrize("field,shape", [("W_g", (4, 128)), ("b1", (4, 128)), ("b2", (3, 256)), ("W1s", (4, 256, 4))])
+def test_forward_mxfp8_rejects_wrong_shapes(field, shape):
+    import torch
+    a = _mx_args()
+    a[field] = torch.zeros(shape, dtype=a[field].dtype)
+    with pytest.raises(ValueError):
+        moe.forward_mxfp8(a["x"], a["W_g"], a["W1"], a["W1s"], a["b1"], a["W2"], a["W2s"], a["b2"], k=2)
+
+
+def test_forward_mxfp8_rejects_host_tensors_and_bad_activation():
+    import torch
+    a = _mx_args()
+    with pytest.raises(ValueError):   # host tensors: not on a GPU
+        moe.forward_mxfp8(a["x"], a["W_g"], a["W1"], a["W1s"], a["b1"], a["W2"], a["W2s"], a["b2"], k=2)
+    with pytest.raises(ValueError):
+        moe.forward_mxfp8(a["x"], a["W_g"], a["W1"], a["W1s"], a["b1"], a["W2"], a["W2s"], a["b2"], k=2,
+                          activation="relu")

@@ -198,6 +198,13 @@ def compare_ec(inp, C: int, gpu: dict, stacked=None, rows=None, check_out=True) 
 
 
 # ------------------------------------------------------------------- MXFP8 --
+def _host_threads() -> int:
+    """Worker threads for host-side oracle work: the cores this process may
+    use, at most 16 (a one-GPU machine's CPU share)."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def to_bf16_device(a: np.ndarray, dev):
     import torch
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -232,7 +239,42 @@ def run_gpu_mx(inp, dev="cuda:0", stacked=None, workspace=None):
     return res
 
 
-def compare_mx(inp, gpu: dict, stacked=None, rows=None, extra_experts=4) -> dict:
+def quantize_checked(inp, gpu: dict, stacked, experts, quantized: dict, threads: int = 1) -> dict:
+    """The oracle's MXFP8 quantization of the given experts' bf16 weights,
+    each compared bit for bit with the codes and scales the GPU produced, into
+    ``quantized`` (expert -> the tuple moe_forward_mxfp8_ref takes); several
+    experts at once in ``threads`` threads (numpy releases the GIL in its
+    array operations)."""
+    from oracle import mxfp8
+    c = inp.cfg
+    W1, b1, W2, b2 = stacked
+    n = c.E + c.S
+    g1c, g1s = gpu["W1q"][0].reshape(n, c.h, c.d), gpu["W1q"][1].reshape(n, c.h, c.d // 32)
+    g2c, g2s = gpu["W2q"][0].reshape(n, c.d, c.h), gpu["W2q"][1].reshape(n, c.d, c.h // 32)
+
+    def one(e):
+        if e in quantized:
+            return
+        q1c, q1s = mxfp8.quantize(ref.widen(W1[e], "bf16"))
+        q2c, q2s = mxfp8.quantize(ref.widen(W2[e], "bf16"))
+        assert np.array_equal(g1c[e], q1c), f"W1 codes differ (expert {e})"
+        assert np.array_equal(g1s[e], q1s), f"W1 scales differ (expert {e})"
+        assert np.array_equal(g2c[e], q2c), f"W2 codes differ (expert {e})"
+        assert np.array_equal(g2s[e], q2s), f"W2 scales differ (expert {e})"
+        quantized[e] = (q1c, q1s, None if b1 is None else b1[e], q2c, q2s, None if b2 is None else b2[e])
+
+    experts = [int(e) for e in experts]
+    if threads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, experts))
+    else:
+        for e in experts:
+            one(e)
+    return quantized
+
+
+def compare_mx(inp, gpu: dict, stacked=None, rows=None, extra_experts=4, quantized=None) -> dict:
     """MXFP8 parity: routing, weights, counts, capacity, aux and z-loss by the
     rules of compare(); the GPU's weight codes and scales bit-exact against the
     oracle's quantization of the same bf16 weights; outputs against the MXFP8
@@ -245,25 +287,20 @@ def compare_mx(inp, gpu: dict, stacked=None, rows=None, extra_experts=4) -> dict
     oracle first uses that expert, and compared there: every expert when all
     rows are compared; with sampled rows, the experts those rows use, the
     shared ones, and extra_experts more drawn at random (full-size weights
-    would take tens of GB in float64)."""
+    would take tens of GB in float64).  ``quantized``: experts already
+    quantized and checked by quantize_checked (filled in further here)."""
     from oracle import mxfp8
     c = inp.cfg
     rep = compare(inp, gpu, stacked=stacked, rows=rows, check_out=False)
-    W1, b1, W2, b2 = stacked if stacked is not None else inp.stacked()
+    stacked = stacked if stacked is not None else inp.stacked()
     n = c.E + c.S
-    g1c, g1s = gpu["W1q"][0].reshape(n, c.h, c.d), gpu["W1q"][1].reshape(n, c.h, c.d // 32)
-    g2c, g2s = gpu["W2q"][0].reshape(n, c.d, c.h), gpu["W2q"][1].reshape(n, c.d, c.h // 32)
-    quantized = {}
+    quantized = {} if quantized is None else quantized
+    if rows is None:
+        # every expert is needed: quantize them up front on the host's cores
+        quantize_checked(inp, gpu, stacked, range(n), quantized, threads=_host_threads())
 
     def eq(e):
-        if e not in quantized:
-            q1c, q1s = mxfp8.quantize(ref.widen(W1[e], "bf16"))
-            q2c, q2s = mxfp8.quantize(ref.widen(W2[e], "bf16"))
-            assert np.array_equal(g1c[e], q1c), f"W1 codes differ (expert {e})"
-            assert np.array_equal(g1s[e], q1s), f"W1 scales differ (expert {e})"
-            assert np.array_equal(g2c[e], q2c), f"W2 codes differ (expert {e})"
-            assert np.array_equal(g2s[e], q2s), f"W2 scales differ (expert {e})"
-            quantized[e] = (q1c, q1s, None if b1 is None else b1[e], q2c, q2s, None if b2 is None else b2[e])
+        quantize_checked(inp, gpu, stacked, [e], quantized)
         return quantized[e]
 
     r = mxfp8.moe_forward_mxfp8_ref(inp.x, inp.W_g, eq, c.E, c.k, float(np.float32(c.cf)), c.S, inp.b_g,

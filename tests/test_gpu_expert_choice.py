@@ -5,7 +5,7 @@ height, the split tail, the float32 SIMT path, shared experts, C = 1 and
 C = T (the dense limit), E = 256, a skewed router with untaken tokens, the
 Mixtral expert form and exact ties between duplicate tokens; two workloads run
 at full size with C = ceil(k T / E) (the same expert rows as their top-k
-routing) and the oracle computing a sample of output rows.
+routing) and the oracle computing every output row.
 """
 import math
 import sys
@@ -96,15 +96,14 @@ def test_ec_deterministic_bitwise():
     assert a["aux"] == b["aux"] and a["z"] == b["z"]
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["mixtral", "glam"])
 def test_ec_full_size(name):
     inp = make_inputs(name, seed=0)
     c = inp.cfg
     C = _C(c, c.k)
     _say(f"[ec-full] {name}: T={c.T} d={c.d} h={c.h} E={c.E} C={C} {c.dtype}")
-    rng = np.random.default_rng(4321)
-    rows = np.unique(np.concatenate([[0, c.T - 1], rng.choice(c.T, 30, replace=False)]))
-    gpu, rep = _run(inp, C, rows=rows)
+    gpu, rep = _run(inp, C, rows=None)
     # every expert holds exactly C distinct tokens, on every expert
     assert all(len(set(r.tolist())) == C for r in gpu["tok"])
     _say(f"[ec-full] {name}: {rep}")
@@ -130,7 +129,5 @@ def test_ec_long_column_unstaged():
     inp = make_inputs(CONFIGS["mixtral"].replace(name="ec_long", T=20000, d=256, h=256, E=8), seed=2)
     C = _C(inp.cfg, 2.0)
     _say(f"[ec] long column T=20000 C={C}")
-    rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([[0, 19999], rng.choice(20000, 200, replace=False)]))
-    gpu, rep = _run(inp, C, rows=rows)
+    gpu, rep = _run(inp, C, rows=None)
     _say(f"[ec] long column: {rep}")

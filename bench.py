@@ -91,10 +91,38 @@ def measured_traffic(workload: str, phase: str):
     return entry[phase]["fetch_bytes"] + entry[phase]["write_bytes"]
 
 
-def cpu_baseline(inp, stacked, ntok: int, ec: bool = False, mx: bool = False):
+def host_info():
+    """The host the oracle runs on: CPU model, the cores this process may use
+    (its affinity mask) and the BLAS library numpy calls."""
     from threadpoolctl import threadpool_info
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [f"{p.get('internal_api')} {p.get('version')} ({os.path.basename(p.get('filepath', ''))}, "
+            f"{p.get('threading_layer', 'n/a')} threading)"
+            for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)), "logical_cpus": os.cpu_count(),
+            "blas": "; ".join(blas) or "unknown"}
+
+
+def cpu_baseline(inp, stacked, ntok: int, ec: bool = False, mx: bool = False):
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
+    host = host_info()
+    # BLAS threads = the cores this process may use (its affinity mask), capped
+    # by OMP_NUM_THREADS where the host sets one (the process's CPU share), set explicitly
+    nthreads = host["affinity_cores"]
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        nthreads = min(nthreads, int(env))
+    limiter = threadpool_limits(limits=nthreads, user_api="blas")
     c = inp.cfg
     ntok = min(ntok, c.T)
     W1, b1, W2, b2 = stacked
@@ -121,10 +149,13 @@ def cpu_baseline(inp, stacked, ntok: int, ec: bool = False, mx: bool = False):
                                activation=c.activation, min_capacity=c.min_capacity)
     dt = time.perf_counter() - t0
     threads = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    limiter.restore_original_limits()
     cores = max(threads) if threads else 1
     return {"value": ntok / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {ntok} of {c.T} tokens of the same workload (routing and capacity over the sample), "
-                      f"float64 numpy oracle, {dt:.1f} s"}
+                      f"float64 numpy oracle, {dt:.1f} s",
+            "cpu_model": host["cpu_model"], "affinity_cores": host["affinity_cores"],
+            "logical_cpus": host["logical_cpus"], "blas": host["blas"], "blas_threads": int(cores)}
 
 
 def main():

@@ -620,6 +620,57 @@ def check_selection_bias_invariants_and_brute():
         assert not np.array_equal(run_ref(x, W_g, ex, E, k, cf or 0.0, S).idx, r.idx) or k == E
 
 
+# ------------------------------------------------- the pages' own loops --
+def _page_form_cases():
+    """(label, x, W_g, experts, shared, k, activation, kind) on the tiny fp32
+    workload and reduced shapes (float64 arrays; bf16 cases hold bf16-exact values)."""
+    from synthetic import CONFIGS, make_inputs
+    cases = []
+    tiny = make_inputs("tiny", seed=0)
+    c = tiny.cfg
+    ex = [tuple(None if a is None else ref.widen(a, "f32") for a in tiny.expert(e)) for e in range(c.E)]
+    cases.append(("tiny", ref.widen(tiny.x, "f32"), ref.widen(tiny.W_g, "f32"), ex, [], c.k, "gelu"))
+    for label, base, kw in [
+        ("mixtral-reduced-bf16", "mixtral", dict(T=160, d=64, h=256, E=8, k=2, w_std=0.2)),
+        ("switch-top1", "switch", dict(T=120, d=32, h=64, E=16, k=1, cf=0.0, w_std=0.3)),
+        ("deepseek-shared", "deepseek", dict(T=100, d=64, h=128, E=16, k=4, S=2, w_std=0.2)),
+        ("mixtral-expert-form", "mixtral", dict(T=90, d=32, h=96, E=8, k=2, w_std=0.3, activation="silu",
+                                                expert_bias=False)),
+    ]:
+        inp = make_inputs(CONFIGS[base].replace(name=label, **kw), seed=5)
+        c = inp.cfg
+        wide = lambda a: None if a is None else ref.widen(a, c.dtype)
+        ex = [tuple(wide(a) for a in inp.expert(e)) for e in range(c.E + c.S)]
+        cases.append((label, wide(inp.x), wide(inp.W_g), ex[:c.E], ex[c.E:], c.k, c.activation))
+    return cases
+
+
+def check_pages_own_loops():
+    """The layer as the pages' sketches compute it (tests/page_forms.py: torch
+    CPU float64, torch.topk on the softmax, the guide's §3.1 slot-major loop,
+    the tutorial's part-5 expert-major indexed add, the guide's §7.1 shared
+    plus routed sum) equals the oracle on every unflagged token: the chosen
+    set, the renormalised weights, the output; the tutorial's balance loss is
+    k times the oracle's (its fractions count all k choices per token, summing
+    to k); the router z-loss is the guide's §4.3 logsumexp form."""
+    from tests.page_forms import page_form_layer
+    for label, x, W_g, experts, shared, k, act in _page_form_cases():
+        E, S = len(experts), len(shared)
+        allx = experts + shared
+        r = ref.moe_forward_ref(x, W_g, lambda e: allx[e], E, k, 0.0, S, None, kind="f64", activation=act)
+        assert not r.tie_flag.any(), label
+        for order in ("slot", "expert"):
+            pf = page_form_layer(x, W_g, experts, k, order=order, shared=shared, activation=act)
+            assert np.array_equal(np.sort(pf.idx, 1), np.sort(r.idx, 1)), (label, order)
+            wa = np.take_along_axis(pf.w, np.argsort(pf.idx, 1), 1)
+            wb = np.take_along_axis(r.w, np.argsort(r.idx, 1), 1)
+            assert np.max(np.abs(wa - wb)) <= 1e-13, (label, order)
+            scale = float(np.max(np.abs(r.out)))
+            assert np.max(np.abs(pf.out - r.out)) <= 1e-12 * scale, (label, order)
+            assert abs(pf.aux_tutorial - k * r.aux) <= 1e-12 * k * r.aux, (label, order)
+            assert abs(pf.z - r.z) <= 1e-12 * max(1.0, r.z), (label, order)
+
+
 ALL_CHECKS = [check_weights_sum_to_one, check_against_brute, check_topk_vs_torch, check_tie_rule,
               check_dense_limit, check_aux_closed_forms, check_capacity, check_dropped_contribute_nothing,
               check_ffn_library, check_combine_symmetries, check_shared, check_golden_fixtures,
@@ -627,7 +678,7 @@ ALL_CHECKS = [check_weights_sum_to_one, check_against_brute, check_topk_vs_torch
               check_silu_and_bias_free, check_min_capacity, check_mixtral_expert_against_brute,
               check_golden_silu_min_capacity, check_ec_against_brute, check_ec_dense_limit_and_balance,
               check_golden_expert_choice, check_selection_bias_closed_form,
-              check_selection_bias_invariants_and_brute]
+              check_selection_bias_invariants_and_brute, check_pages_own_loops]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=[c.__name__ for c in ALL_CHECKS])

@@ -60,7 +60,9 @@ typedef enum {
                                d or h not a multiple of 8, pointer not 16-byte aligned, unknown
                                dtype or activation, or a row count that overflows int32 */
   MOE_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than moe_workspace_bytes(...) */
-  MOE_ERR_HIP = 4           /* a HIP launch reported an error (hipGetLastError) */
+  MOE_ERR_HIP = 4,          /* a HIP launch reported an error (hipGetLastError) */
+  MOE_ERR_SCRATCH = 5       /* moe_forward_noalloc: the problem needs more than
+                               MOE_NOALLOC_SCRATCH_BYTES of scratch */
 } moe_status_t;
 
 #define MOE_MAX_EXPERTS 256
@@ -225,6 +227,35 @@ moe_status_t moe_forward_mxfp8(const void* x, const void* W_g, const uint8_t* W1
                                const void* b1, const uint8_t* W2, const uint8_t* W2_scales, const void* b2,
                                int32_t E, int32_t k, float capacity_factor, int32_t n_shared, void* out,
                                int32_t* topk_idx, float* topk_w, float* aux_loss, const moe_launch_t* launch);
+
+/* ---- For callers that cannot allocate ----------------------------------------
+ * For code under HIP graph capture, tight serving loops and harnesses that
+ * forbid device allocation: moe_forward with every argument and result as
+ * above, but its scratch (the hidden and expert-output buffers, routing
+ * tables, partial logits and partial GEMM tiles) in a fixed device array of
+ * the library instead of launch->workspace (ignored, with
+ * launch->workspace_bytes).  The array holds MOE_NOALLOC_SCRATCH_BYTES on
+ * every GPU the library runs on, from the code object's load on that GPU
+ * until the process ends.  Nothing is allocated or freed by the call (no
+ * hipMalloc, hipFree or allocating library routine), and nothing in the
+ * array needs to start at zero.
+ *
+ * The call runs on the calling thread's current device; launch->stream must
+ * belong to it.  Every call on one GPU shares that GPU's array, which keeps
+ * the last call's contents: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.
+ *
+ * Returns MOE_ERR_SCRATCH, before any GPU call, when the problem's scratch
+ * (moe_workspace_bytes' layout with 16 partial GEMM tiles instead of 256)
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES: e.g. T = 4096, d = 512, h = 2048,
+ * E = 64, k = 1 in float32 fits; the Mixtral-shaped layer (0.8 GB) does not.
+ * Other errors as for moe_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status_t moe_forward_noalloc(const void* x, const void* W_g, const void* W1, const void* b1,
+                                 const void* W2, const void* b2, int32_t E, int32_t k,
+                                 float capacity_factor, int32_t n_shared, void* out,
+                                 int32_t* topk_idx, float* topk_w, float* aux_loss,
+                                 const moe_launch_t* launch);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status_t s);

@@ -13,9 +13,9 @@ from dataclasses import dataclass
 from typing import Optional, Sequence
 
 from ._lib import (EXPORTS, LIB_PATH, MOE_ACT_GELU, MOE_ACT_SILU, MOE_BF16, MOE_ERR_ARG, MOE_ERR_HIP,
-                   MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_F32, MOE_MAX_EXPERTS, MOE_MAX_SHARED,
-                   MOE_MAX_TOPK, MOE_NUM_STAGE_EVENTS, MOE_OK, MoeLaunch,
-                   moe_expert_choice_capacity, moe_forward, moe_forward_expert_choice,
+                   MOE_ERR_SCRATCH, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_F32, MOE_MAX_EXPERTS, MOE_MAX_SHARED,
+                   MOE_MAX_TOPK, MOE_NOALLOC_SCRATCH_BYTES, MOE_NUM_STAGE_EVENTS, MOE_OK, MoeLaunch,
+                   moe_expert_choice_capacity, moe_forward, moe_forward_expert_choice, moe_forward_noalloc,
                    moe_forward_mxfp8, moe_quantize_mxfp8, moe_status_string, moe_workspace_bytes,
                    moe_workspace_bytes_expert_choice, moe_workspace_bytes_mxfp8)
 
@@ -103,7 +103,7 @@ def _launch(x, T, d, h, dt, b_g, workspace, zl, activation, min_capacity, stage_
 
 def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shared: int = 0, b_g=None,
             *, activation: str = "gelu", min_capacity: int = 0, stage_events: Optional[Sequence] = None,
-            workspace=None, b_sel=None) -> MoEOutput:
+            workspace=None, b_sel=None, noalloc: bool = False) -> MoEOutput:
     """Run the layer on torch tensors that live on one GPU.
 
     x [T,d]; W_g [E,d]; W1 [E+S,h,d]; b1 [E+S,h] or None; W2 [E+S,d,h];
@@ -114,7 +114,10 @@ def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shar
     when capacity_factor > 0.
     ``stage_events``: optional list of MOE_NUM_STAGE_EVENTS torch.cuda.Event
     objects (already recorded once, so their handles exist) that the library
-    records at its stage boundaries.  Raises RuntimeError on a non-zero status.
+    records at its stage boundaries.  ``noalloc``: call moe_forward_noalloc,
+    whose scratch is the library's fixed device array (no workspace is
+    allocated; problems beyond its size raise).  Raises RuntimeError on a
+    non-zero status.
     """
     import torch
     _check_tensors(x, W_g, W1, b1, W2, b2, b_g, n_shared, activation)
@@ -128,7 +131,9 @@ def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shar
     nbytes = moe_workspace_bytes(T, d, h, E, k, S, dt)
     if nbytes == 0:
         raise RuntimeError("invalid problem shape for moe_workspace_bytes")
-    if workspace is None or workspace.numel() < nbytes:
+    if noalloc:
+        workspace = None
+    elif workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     out = torch.empty((T, d), dtype=x.dtype, device=dev)
     topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -144,9 +149,10 @@ def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shar
     launch.expert_kept = kept.data_ptr()
     launch.slot_pos = slot_pos.data_ptr()
     ptr = lambda t: t.data_ptr() if t is not None else None
-    status = moe_forward(x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), ptr(b1), W2.data_ptr(), ptr(b2), E, k,
-                         float(capacity_factor), S, out.data_ptr(), topk_idx.data_ptr(), topk_w.data_ptr(),
-                         aux.data_ptr(), launch)
+    call = moe_forward_noalloc if noalloc else moe_forward
+    status = call(x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), ptr(b1), W2.data_ptr(), ptr(b2), E, k,
+                  float(capacity_factor), S, out.data_ptr(), topk_idx.data_ptr(), topk_w.data_ptr(),
+                  aux.data_ptr(), launch)
     del keep
     if status != MOE_OK:
         raise RuntimeError(moe_status_string(status))
@@ -282,6 +288,6 @@ __all__ = ["forward", "MoEOutput", "moe_forward", "moe_workspace_bytes", "moe_st
            "forward_expert_choice", "ExpertChoiceOutput", "moe_forward_expert_choice",
            "moe_workspace_bytes_expert_choice", "expert_choice_capacity", "moe_expert_choice_capacity", "STAGES_EXPERT_CHOICE",
            "quantize_mxfp8", "forward_mxfp8", "moe_quantize_mxfp8", "moe_workspace_bytes_mxfp8", "moe_forward_mxfp8",
-           "ACTIVATIONS", "MOE_ACT_GELU", "MOE_ACT_SILU", "MOE_F32", "MOE_BF16", "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
+           "moe_forward_noalloc", "MOE_ERR_SCRATCH", "MOE_NOALLOC_SCRATCH_BYTES", "ACTIVATIONS", "MOE_ACT_GELU", "MOE_ACT_SILU", "MOE_F32", "MOE_BF16", "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
            "MOE_ERR_HIP", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SHARED", "MOE_NUM_STAGE_EVENTS",
            "STAGES", "EXPORTS", "LIB_PATH"]

@@ -23,6 +23,10 @@ MOE_ERR_ARG = 1
 MOE_ERR_UNSUPPORTED = 2
 MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
+MOE_ERR_SCRATCH = 5
+
+# bytes of the fixed device scratch of moe_forward_noalloc
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 8
@@ -32,7 +36,7 @@ MOE_NUM_STAGE_EVENTS = 7
 # names of the C ABI entry points (include/moe.h)
 EXPORTS = ("moe_forward", "moe_workspace_bytes", "moe_status_string", "moe_forward_expert_choice",
            "moe_workspace_bytes_expert_choice", "moe_quantize_mxfp8", "moe_workspace_bytes_mxfp8",
-           "moe_forward_mxfp8", "moe_expert_choice_capacity")
+           "moe_forward_mxfp8", "moe_expert_choice_capacity", "moe_forward_noalloc")
 
 
 class MoeLaunch(ctypes.Structure):
@@ -94,6 +98,13 @@ def _load():
     lib.moe_expert_choice_capacity.argtypes = [ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.POINTER(MoeLaunch),
+    ]
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_forward.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -129,6 +140,14 @@ def moe_forward(x, W_g, W1, b1, W2, b2, E, k, capacity_factor, n_shared, out, to
     """Raw call of the C entry point: every array argument is a device address (int)."""
     return int(LIB.moe_forward(x, W_g, W1, b1, W2, b2, E, k, capacity_factor, n_shared, out, topk_idx, topk_w,
                                aux_loss, ctypes.byref(launch)))
+
+
+def moe_forward_noalloc(x, W_g, W1, b1, W2, b2, E, k, capacity_factor, n_shared, out, topk_idx, topk_w, aux_loss,
+                        launch: MoeLaunch) -> int:
+    """Raw call of the entry point that takes no workspace (the library's fixed
+    device scratch; launch.workspace is ignored)."""
+    return int(LIB.moe_forward_noalloc(x, W_g, W1, b1, W2, b2, E, k, capacity_factor, n_shared, out, topk_idx,
+                                       topk_w, aux_loss, ctypes.byref(launch)))
 
 
 def moe_forward_expert_choice(x, W_g, W1, b1, W2, b2, E, C, n_shared, out, ec_token, ec_w, aux_loss,

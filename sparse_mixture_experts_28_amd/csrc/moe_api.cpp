@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "moe.h"
 #include "moe_internal.h"
@@ -268,6 +269,42 @@ moe_status_t forward_top_k(const void* x, const void* W_g, const void* W1, const
   return MOE_OK;
 }
 
+// ---------------------------------------------------- fixed device scratch --
+// The workspace of moe_forward_noalloc: one array per GPU, allocated when the
+// code object is loaded on that GPU and held until the process ends.  Host
+// code never uses the array's name as an address (on the host it is only a
+// stand-in): the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+moe_status_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    std::fprintf(stderr, "libmoe: no usable current device for the fixed scratch (%s)\n", hipGetErrorName(e));
+    return MOE_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      std::fprintf(stderr, "libmoe: hipGetSymbolAddress of the fixed scratch failed on device %d: %s (%s)\n", dev,
+                   hipGetErrorName(e), hipGetErrorString(e));
+      return MOE_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 extern "C" {
@@ -368,6 +405,8 @@ const char* moe_status_string(moe_status_t s) {
       return "MOE_ERR_UNSUPPORTED: unsupported shape, dtype, activation or pointer alignment";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
+    case MOE_ERR_SCRATCH:
+      return "MOE_ERR_SCRATCH: the problem needs more scratch than moe_forward_noalloc's fixed buffer";
   }
   return "unknown moe_status_t";
 }
@@ -379,6 +418,28 @@ moe_status_t moe_forward(const void* x, const void* W_g, const void* W1, const v
   if (launch == nullptr) return MOE_ERR_ARG;
   return moe::forward_top_k(x, W_g, W1, b1, W2, b2, E, k, capacity_factor, n_shared, out, topk_idx, topk_w,
                             aux_loss, launch, launch->workspace, launch->workspace_bytes, moe::kGemmPartCap);
+}
+
+moe_status_t moe_forward_noalloc(const void* x, const void* W_g, const void* W1, const void* b1, const void* W2,
+                                 const void* b2, int32_t E, int32_t k, float capacity_factor, int32_t n_shared,
+                                 void* out, int32_t* topk_idx, float* topk_w, float* aux_loss,
+                                 const moe_launch_t* launch) {
+  using namespace moe;
+  if (launch == nullptr) return MOE_ERR_ARG;
+  // the scratch size is checked before any HIP call (forward_top_k checks the rest)
+  const moe_status_t sc = check_shape(launch->T, launch->d, launch->h, E, k, n_shared,
+                                      static_cast<int>(launch->dtype));
+  if (sc != MOE_OK) return sc;
+  if (std::isnan(capacity_factor) || launch->min_capacity < 0) return MOE_ERR_ARG;
+  Problem p = make_problem(launch->T, launch->d, launch->h, E, k, n_shared, launch->dtype, capacity_factor,
+                           launch->activation, launch->min_capacity);
+  p.part_limit = kNoallocPartTiles;
+  if (workspace_bytes(p) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* base = nullptr;
+  const moe_status_t ss = scratch_of_current_device(&base);
+  if (ss != MOE_OK) return ss;
+  return forward_top_k(x, W_g, W1, b1, W2, b2, E, k, capacity_factor, n_shared, out, topk_idx, topk_w, aux_loss,
+                       launch, base, MOE_NOALLOC_SCRATCH_BYTES, kNoallocPartTiles);
 }
 
 moe_status_t moe_forward_expert_choice(const void* x, const void* W_g, const void* W1, const void* b1,

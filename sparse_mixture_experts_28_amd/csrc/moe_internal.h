@@ -254,11 +254,15 @@ int logit_pad(int E);
 int logit_splits(const Problem& p);
 // partial tiles reserved for the grouped GEMM's split tail (one per workgroup of a 256-CU part)
 constexpr int kGemmPartCap = 256;
+// the same in the fixed scratch of moe_forward_noalloc (16 tiles of 256 x 256 float32: 4 MB)
+constexpr int kNoallocPartTiles = 16;
 
 // the top-k layer on a given workspace (moe_api.cpp)
 moe_status_t forward_top_k(const void* x, const void* W_g, const void* W1, const void* b1, const void* W2,
                            const void* b2, int32_t E, int32_t k, float capacity_factor, int32_t n_shared, void* out,
                            int32_t* topk_idx, float* topk_w, float* aux_loss, const moe_launch_t* launch,
                            void* ws_base, size_t ws_bytes, int part_limit);
+// device address of the current device's copy of the fixed scratch (looked up once per device)
+moe_status_t scratch_of_current_device(void** out);
 
 }  // namespace moe

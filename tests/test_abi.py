@@ -58,9 +58,37 @@ def test_launch_struct_matches_header(tmp_path):
 
 
 def test_status_strings():
-    for code in range(5):
+    for code in range(6):
         assert moe.moe_status_string(code).startswith(["MOE_OK", "MOE_ERR_ARG", "MOE_ERR_UNSUPPORTED",
-                                                       "MOE_ERR_WORKSPACE", "MOE_ERR_HIP"][code])
+                                                       "MOE_ERR_WORKSPACE", "MOE_ERR_HIP", "MOE_ERR_SCRATCH"][code])
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(HEADER).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)" in src and moe.MOE_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def _call_noalloc(T, d, h, E, k, S, dtype, cf=0.0, **launch_fields):
+    L = moe.MoeLaunch()
+    L.T, L.d, L.h, L.dtype = T, d, h, dtype
+    for key, v in launch_fields.items():
+        setattr(L, key, v)
+    return moe.moe_forward_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, E, k, cf, S, FAKE, FAKE, FAKE, FAKE, L)
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """Rejected on the host before any GPU call: the Mixtral-shaped layer needs
+    ~0.8 GB of scratch against the fixed 64 MB."""
+    assert _call_noalloc(8192, 4096, 14336, 8, 2, 0, moe.MOE_BF16) == moe.MOE_ERR_SCRATCH
+    assert _call_noalloc(16384, 2048, 8192, 64, 2, 0, moe.MOE_BF16, cf=1.5) == moe.MOE_ERR_SCRATCH
+    # invalid shapes and arguments still report as moe_forward does
+    assert _call_noalloc(0, 32, 64, 8, 2, 0, moe.MOE_BF16) == moe.MOE_ERR_ARG
+    assert _call_noalloc(64, 36, 64, 8, 2, 0, moe.MOE_BF16) == moe.MOE_ERR_UNSUPPORTED
+    assert _call_noalloc(64, 32, 64, 8, 2, 0, moe.MOE_BF16, cf=float("nan")) == moe.MOE_ERR_ARG
+    assert _call_noalloc(64, 32, 64, 8, 2, 0, moe.MOE_BF16, min_capacity=-1) == moe.MOE_ERR_ARG
+    st = moe._lib.LIB.moe_forward_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 2, ctypes.c_float(0.0), 0, FAKE,
+                                          FAKE, FAKE, FAKE, None)
+    assert st == moe.MOE_ERR_ARG
 
 
 def test_workspace_bytes():

@@ -5,8 +5,8 @@
                     [--activation gelu|silu] [--no-expert-bias] [--min-capacity N]
                     [--routing top-k|expert-choice] [--mxfp8]
 
-A step is one full layer forward (router, scan, scatter, expert phase 1,
-expert phase 2, combine) over one batch of seeded synthetic tokens already
+A step is one full layer forward (router, permute -- or scan and selection
+under expert choice --, expert phase 1, expert phase 2, combine) over one batch of seeded synthetic tokens already
 resident in HBM.  Prints ONE JSON line with tokens/s, the roofline of the
 dominant kernel (live HIP-event timing of every stage) and the CPU oracle
 timed on a bounded sample of the same workload.
@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer fwd tokens/s + % bf16 MFMA peak, Mixtral-shape E=8 top-2"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
-PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_28_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
@@ -302,9 +302,11 @@ def main():
     gemm_flops = 2.0 * d * h * rows                      # per launch (each phase)
     active = int((kept_np > 0).sum()) + S
     bytes_router = T * d * s + E * d * s + 8 * T * k
-    # the scatter reads each assignment's expert and in-tile rank and writes its
-    # slot and, for kept ones, the row's token (no token row is copied)
-    bytes_scatter = 12 * T * k + 4 * a_kept
+    # the permute reads each assignment's expert and in-tile rank and the per-tile
+    # expert counts, and writes its slot and, for kept ones, the row's token (no
+    # token row is copied)
+    ntile = -(-T // (32 if (c.dtype == "bf16" and d % 256 == 0 and E <= 64 and -(-T // 64) < 256) else 64))
+    bytes_scatter = 12 * T * k + 4 * a_kept + 4 * ntile * E
     bytes_combine = rows * d * s + T * d * s + 8 * T * k
     if ec:
         # router also writes the expert-major float64 logits and each token's max and sum;
@@ -332,9 +334,11 @@ def main():
 
     per_stage = {
         "router": {"ms": stages["router"], "GB/s": gbs(bytes_router, stages["router"]), "bytes": bytes_router},
-        "scan": {"ms": stages["scan"]},
-        ("select" if ec else "scatter"): {"ms": stages["scatter"], "GB/s": gbs(bytes_scatter, stages["scatter"]),
-                                          "bytes": bytes_scatter},
+        **({"scan": {"ms": stages["scan"]},
+            "select": {"ms": stages["scatter"], "GB/s": gbs(bytes_scatter, stages["scatter"]),
+                       "bytes": bytes_scatter}} if ec else
+           {"permute": {"ms": stages["scan"] + stages["scatter"],
+                        "GB/s": gbs(bytes_scatter, stages["scan"] + stages["scatter"]), "bytes": bytes_scatter}}),
         "expert_phase1": {"ms": stages["expert_phase1"], "TFLOP/s": tfs(gemm_flops, stages["expert_phase1"]),
                           "GB/s": gbs(bytes_gemm1, stages["expert_phase1"]), "flops": gemm_flops},
         "expert_phase2": {"ms": stages["expert_phase2"], "TFLOP/s": tfs(gemm_flops, stages["expert_phase2"]),
@@ -346,7 +350,8 @@ def main():
     dom_bytes = bytes_gemm1 if dom == "expert_phase1" else bytes_gemm2
     traffic = measured_traffic(args.workload, dom)
     if c.dtype == "f32":
-        roof = {"bound": "alu", "achieved": tfs(gemm_flops, dom_ms), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
+        # float32 layers run the grouped GEMM on the float32 matrix cores
+        roof = {"bound": "mfma", "achieved": tfs(gemm_flops, dom_ms), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
     elif args.workload == "mixtral":
         roof = {"bound": "mfma", "achieved": tfs(gemm_flops, dom_ms),
                 "peak": PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
@@ -356,7 +361,10 @@ def main():
     roof["traffic"] = traffic
     roof["kernel"] = f"gemm ({dom})"
     gemm_ms = stages["expert_phase1"] + stages["expert_phase2"]
-    roof["gemm_both_phases_frac_of_bf16_peak"] = tfs(2 * gemm_flops, gemm_ms) / PEAK_BF16_TFLOPS
+    if c.dtype == "f32":
+        roof["gemm_both_phases_frac_of_f32_peak"] = tfs(2 * gemm_flops, gemm_ms) / PEAK_F32_TFLOPS
+    else:
+        roof["gemm_both_phases_frac_of_bf16_peak"] = tfs(2 * gemm_flops, gemm_ms) / PEAK_BF16_TFLOPS
     if mx:
         roof["gemm_both_phases_frac_of_fp8_peak"] = tfs(2 * gemm_flops, gemm_ms) / PEAK_FP8_TFLOPS
         traffic = None   # the committed counter runs cover the bf16 kernels

@@ -73,7 +73,9 @@ typedef enum {
  * moe_launch_t.stage_events): before the router, then after the router, the
  * scan, the scatter (each kept assignment's row in the expert-sorted order;
  * token rows are not copied), expert phase 1 (x W1^T + b1, activation), expert phase 2
- * (h W2^T + b2) and the combine. */
+ * (h W2^T + b2) and the combine.  With top-k routing the scan and the scatter
+ * are one permute kernel: both boundaries are recorded after it (the scatter
+ * stage is empty).  Under expert choice the scatter stage is the selection. */
 #define MOE_NUM_STAGE_EVENTS 7
 
 typedef struct {

@@ -7,11 +7,9 @@
 // Experts" §7.1 (MoE(x) = sum_i G(x)_i E_i(x)) and §7.4 (an overflowed token's
 // slot contributes nothing; the residual outside the layer carries it).
 //
-// A gather, not a scatter: one workgroup per token reads its k expert rows and
-// its shared rows, accumulates in float32 in slot order then shared order, and
-// rounds once.  No atomics, so the result is bitwise reproducible.  The rows
-// of a token are listed in LDS first, and each thread loads up to 8 of them
-// before adding any, so their memory latencies overlap.
+// A gather, not a scatter: one wave per token reads its k expert rows and its
+// shared rows, accumulates in float32 in slot order then shared order, and
+// rounds once.  No atomics, so the result is bitwise reproducible.
 //
 // Expert choice ("第7章 Mixture of Experts" §7.2; the guide's §4.2): a token's
 // routed rows are those of the experts that took it, 0 to E of them, added in
@@ -80,62 +78,71 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const float (&a)[8]) {
   return o;
 }
 
-// Top-k: token t's kept slots in slot order, then its shared-expert rows with
-// weight 1 (a fused multiply-add by 1 rounds exactly as the plain sum).
-__device__ __forceinline__ int topk_token_rows(const Problem& p, const int32_t* __restrict__ slot_pos,
-                                               const float* __restrict__ topk_w, int t, int32_t* s_row, float* s_w,
-                                               int* s_n) {
-  if (threadIdx.x == 0) {
-    int n = 0;
-    for (int j = 0; j < p.k; ++j) {
-      const int pos = slot_pos[static_cast<size_t>(t) * p.k + j];
-      if (pos >= 0) {
-        s_row[n] = pos;
-        s_w[n] = topk_w[static_cast<size_t>(t) * p.k + j];
-        ++n;
+// Top-k, one wave per token (grid-stride over tokens).  Lane j < k reads
+// slot j's row and weight, and the wave broadcasts them (uniform values);
+// the shared-expert rows follow with weight 1.  Each lane then takes CU
+// 16-byte column chunks at a time and issues the loads of all the token's
+// rows for them before adding any (ROWS x CU loads in flight per lane), in
+// slot order then shared order, a dropped slot (row -1) skipped.  No
+// workgroup barrier and no serial list building: a wave moves on to its next
+// token as soon as its stores are issued.
+template <int ROWS, typename V, typename A>
+__device__ __forceinline__ void combine_token_wave(const Problem& p, const V* __restrict__ y,
+                                                   const int32_t* __restrict__ slot_pos,
+                                                   const float* __restrict__ topk_w, V* __restrict__ out,
+                                                   int vec_per_row, int t, int lane) {
+  constexpr int CU = ROWS >= 8 ? 1 : 8 / ROWS;
+  int my_pos = -1;
+  float my_w = 0.f;
+  if (lane < p.k) {
+    my_pos = slot_pos[static_cast<size_t>(t) * p.k + lane];
+    my_w = topk_w[static_cast<size_t>(t) * p.k + lane];
+  } else if (lane < p.k + p.S) {
+    my_pos = p.A + (lane - p.k) * p.T + t;   // shared expert lane - k, weight 1
+    my_w = 1.0f;
+  }
+  int row[ROWS];
+  float wt[ROWS];
+#pragma unroll
+  for (int j = 0; j < ROWS; ++j) {
+    row[j] = __builtin_amdgcn_readfirstlane(__shfl(my_pos, j, kWave));
+    wt[j] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, __shfl(my_w, j, kWave))));
+  }
+  for (int c0 = lane; c0 < vec_per_row; c0 += kWave * CU) {
+    V v[ROWS][CU];
+#pragma unroll
+    for (int j = 0; j < ROWS; ++j)
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        const int c = c0 + kWave * u;
+        if (row[j] >= 0 && c < vec_per_row) v[j][u] = y[static_cast<size_t>(row[j]) * vec_per_row + c];
       }
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int c = c0 + kWave * u;
+      if (c >= vec_per_row) break;
+      A a{};
+#pragma unroll
+      for (int j = 0; j < ROWS; ++j) {
+        if (row[j] < 0) continue;
+        if constexpr (sizeof(V) == 16 && sizeof(A) == 32) acc_bf16x8(a, v[j][u], wt[j]);
+        else acc_f32x4(a, v[j][u], wt[j]);
+      }
+      if constexpr (sizeof(A) == 32) out[static_cast<size_t>(t) * vec_per_row + c] = pack_bf16x8(a);
+      else out[static_cast<size_t>(t) * vec_per_row + c] = a;
     }
-    for (int s = 0; s < p.S; ++s) {
-      s_row[n] = p.A + s * p.T + t;
-      s_w[n] = 1.0f;
-      ++n;
-    }
-    *s_n = n;
   }
-  __syncthreads();
-  return *s_n;
 }
 
-__global__ __launch_bounds__(256) void combine_bf16_kernel(Problem p, const u32x4* __restrict__ y,
+template <int ROWS, typename V, typename A>
+__global__ __launch_bounds__(256) void combine_wave_kernel(Problem p, const V* __restrict__ y,
                                                            const int32_t* __restrict__ slot_pos,
-                                                           const float* __restrict__ topk_w,
-                                                           u32x4* __restrict__ out, int vec_per_row) {
-  __shared__ int32_t s_row[MOE_MAX_TOPK + MOE_MAX_SHARED];
-  __shared__ float s_w[MOE_MAX_TOPK + MOE_MAX_SHARED];
-  __shared__ int s_n;
-  const int t = blockIdx.x;
-  const int n = topk_token_rows(p, slot_pos, topk_w, t, s_row, s_w, &s_n);
-  for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
-    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    gather_rows(a, y, s_row, s_w, n, c, vec_per_row);
-    out[static_cast<size_t>(t) * vec_per_row + c] = pack_bf16x8(a);
-  }
-}
-
-__global__ __launch_bounds__(256) void combine_f32_kernel(Problem p, const float4* __restrict__ y,
-                                                          const int32_t* __restrict__ slot_pos,
-                                                          const float* __restrict__ topk_w,
-                                                          float4* __restrict__ out, int vec_per_row) {
-  __shared__ int32_t s_row[MOE_MAX_TOPK + MOE_MAX_SHARED];
-  __shared__ float s_w[MOE_MAX_TOPK + MOE_MAX_SHARED];
-  __shared__ int s_n;
-  const int t = blockIdx.x;
-  const int n = topk_token_rows(p, slot_pos, topk_w, t, s_row, s_w, &s_n);
-  for (int c = threadIdx.x; c < vec_per_row; c += blockDim.x) {
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    gather_rows(a, y, s_row, s_w, n, c, vec_per_row);
-    out[static_cast<size_t>(t) * vec_per_row + c] = a;
-  }
+                                                           const float* __restrict__ topk_w, V* __restrict__ out,
+                                                           int vec_per_row) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nw = gridDim.x * (blockDim.x / kWave);
+  for (int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave); t < p.T; t += nw)
+    combine_token_wave<ROWS, V, A>(p, y, slot_pos, topk_w, out, vec_per_row, t, lane);
 }
 
 // Expert choice: the rows of token t, in ascending expert order.  Wave 0 reads
@@ -237,15 +244,26 @@ hipError_t launch_combine(const Problem& p, const float* topk_w, const Workspace
                           hipStream_t st) {
   const int elem = p.dtype == MOE_BF16 ? 2 : 4;
   const int vec_per_row = p.d * elem / 16;
-  const int threads = vec_per_row >= 256 ? 256 : (vec_per_row >= 128 ? 128 : 64);
-  if (p.dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bf16_kernel, dim3(p.T), dim3(threads), 0, st, p,
-                       static_cast<const u32x4*>(ws.ybuf), ws.slot_pos, topk_w, static_cast<u32x4*>(out),
-                       vec_per_row);
-  else
-    hipLaunchKernelGGL(combine_f32_kernel, dim3(p.T), dim3(threads), 0, st, p,
-                       static_cast<const float4*>(ws.ybuf), ws.slot_pos, topk_w, static_cast<float4*>(out),
-                       vec_per_row);
+  // grid-stride waves: about eight per SIMD of a 256-CU part
+  const int waves = p.T < 8192 ? p.T : 8192;
+  const dim3 grid((waves + 3) / 4), block(256);
+  const int rows = p.k + p.S;
+#define MOE_COMBINE(ROWS_)                                                                                      \
+  do {                                                                                                          \
+    if (p.dtype == MOE_BF16)                                                                                    \
+      hipLaunchKernelGGL((combine_wave_kernel<ROWS_, u32x4, float[8]>), grid, block, 0, st, p,                  \
+                         static_cast<const u32x4*>(ws.ybuf), ws.slot_pos, topk_w, static_cast<u32x4*>(out),      \
+                         vec_per_row);                                                                          \
+    else                                                                                                        \
+      hipLaunchKernelGGL((combine_wave_kernel<ROWS_, float4, float4>), grid, block, 0, st, p,                   \
+                         static_cast<const float4*>(ws.ybuf), ws.slot_pos, topk_w, static_cast<float4*>(out),    \
+                         vec_per_row);                                                                          \
+  } while (0)
+  if (rows <= 2) MOE_COMBINE(2);
+  else if (rows <= 4) MOE_COMBINE(4);
+  else if (rows <= 8) MOE_COMBINE(8);
+  else MOE_COMBINE(16);
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

@@ -28,7 +28,9 @@
 // 8 M-tiles x N, so concurrently running tiles share A and B panels in that
 // XCD's L2.
 //
-// Fallback (any shape, float32 or bf16): 64 x 64 SIMT tiles, float32 accumulation.
+// float32 layers run a float32 matrix-core kernel (BM x 128 tiles, K slabs
+// of 32 through LDS).  Fallback (bf16 with d or h not a multiple of 256):
+// 64 x 64 SIMT tiles, float32 accumulation.
 #include "moe_internal.h"
 
 
@@ -156,6 +158,7 @@ template <int ACT, int BM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_mfma_kernel(GemmArgs g) {
   constexpr int NS = BM <= 160 ? 3 : 2;
+  constexpr bool kExpertMajor = BM <= 160;     // weight streaming: expert-major tile order
   constexpr int MB = BM / 32;                  // 16-row blocks per wave
   constexpr int NR = MB + 8;                   // fragment reads per slice = direct loads per stage, per wave
   constexpr int MF = MB * 8;                   // MFMAs per slice
@@ -203,10 +206,13 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
       k0 = p * nk / tp.S;
       kn = (p + 1) * nk / tp.S - k0;           // >= 4
     }
-    int mt, nt;
-    tile_of(L, total_mt, ntn, mt, nt);
-
-    const int s = uniform(find_segment(st.tile_start, g.nseg, mt));
+    int mt, nt, s;
+    if constexpr (kExpertMajor) {
+      s = uniform(tile_of_expert(L, st.tile_start, g.nseg, ntn, mt, nt));
+    } else {
+      tile_of(L, total_mt, ntn, mt, nt);
+      s = uniform(find_segment(st.tile_start, g.nseg, mt));
+    }
     const int rows = uniform(st.rows[s]);
     const int m0 = (mt - uniform(st.tile_start[s])) * BM;
     const int a_off = uniform(g.a_by_o_off ? st.o_off[s] : st.a_off[s]);
@@ -386,9 +392,13 @@ __global__ __launch_bounds__(256) void gemm_tail_fixup_kernel(GemmArgs g, int P)
   uint16_t* C = static_cast<uint16_t*>(g.C);
   for (int w = blockIdx.x; w < tp.tail * kChunks; w += gridDim.x) {
     const int tt = w / kChunks, r0 = (w % kChunks) * 16;
-    int mt, nt;
-    tile_of(tp.full + tt, total_mt, ntn, mt, nt);
-    const int s = find_segment(st.tile_start, g.nseg, mt);
+    int mt, nt, s;
+    if constexpr (BM <= 160) {   // the GEMM kernel's tile order
+      s = tile_of_expert(tp.full + tt, st.tile_start, g.nseg, ntn, mt, nt);
+    } else {
+      tile_of(tp.full + tt, total_mt, ntn, mt, nt);
+      s = find_segment(st.tile_start, g.nseg, mt);
+    }
     const int rows = st.rows[s];
     const int m0 = (mt - st.tile_start[s]) * BM;
     const int o_off = st.o_off[s];
@@ -413,6 +423,149 @@ __global__ __launch_bounds__(256) void gemm_tail_fixup_kernel(GemmArgs g, int P)
       v3 = act_fast<ACT>(v3);
       *reinterpret_cast<uint2*>(C + static_cast<size_t>(o_off + m0 + rr) * g.N + n) =
           make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+    }
+  }
+}
+
+// ------------------------------------------------------ float32 MFMA path --
+// float32 layers (any d, h: multiples of 8) on the float32 matrix cores
+// (v_mfma_f32_16x16x4_f32: 2048 FLOP per instruction, 157.3 TFLOP/s for the
+// part), float32 products and sums: the same arithmetic class as the float32
+// SIMT loop it replaces.  BM x 128 tiles, BM in {32, 64} chosen per problem
+// (the float32 workloads have short experts: ~64 rows at the switch-shaped
+// layer), K slabs of 32 staged through LDS (rows of 32 k padded to 36 floats,
+// 16-byte stores and fragment reads) with the next slab's loads held in
+// registers while the current one is multiplied.  One workgroup per tile
+// (grid = M tiles x N tiles; the M tiles past the segment table's count exit),
+// several resident per CU.  4 waves in a (BM / 32) x (4 / (BM / 32)) grid,
+// each 32 rows x (128 / wave columns) of 16x16 blocks.  The MFMA takes the B
+// fragment first, so a lane ends with one output row and four consecutive
+// columns: bias, activation (library erff / expf, as the SIMT path) and one
+// 16-byte store.  Rows past a segment, columns past N and k past K read zero.
+constexpr int kFBN = 128, kFBK = 32;
+
+template <int ACT, int BM>
+__global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(GemmArgs g) {
+  constexpr int WM = BM / 32, WN = 4 / WM;      // wave grid
+  constexpr int WTN = kFBN / WN;                // wave tile columns
+  constexpr int NBk = WTN / 16;                 // 16-column blocks per wave
+  constexpr int LDP = kFBK + 4;                 // LDS row pitch (floats): rows of 32 k, 16-byte aligned
+  constexpr int AV = BM * kFBK / 4 / 256;       // float4 loads per thread per slab: A
+  constexpr int BV = kFBN * kFBK / 4 / 256;     //                                   B
+  __shared__ float4 sA[2][BM][LDP / 4];
+  __shared__ float4 sB[2][kFBN][LDP / 4];
+
+  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
+  const int total_mt = st.tile_start[g.nseg];
+  const int mt = blockIdx.x;
+  if (mt >= total_mt) return;
+  const int s = find_segment(st.tile_start, g.nseg, mt);
+  const int rows = st.rows[s];
+  const int m0 = (mt - st.tile_start[s]) * BM;
+  const int n0 = blockIdx.y * kFBN;
+  const int a_off = g.a_by_o_off ? st.o_off[s] : st.a_off[s];
+  const bool gather = g.row_token != nullptr && s < g.E;
+  const float* A = static_cast<const float*>(g.A);
+  const float* B = static_cast<const float*>(g.W) + static_cast<size_t>(s) * g.N * g.K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // global -> register loads: thread tid takes float4 (tid + 256 v) of the
+  // slab: row (tid + 256 v) / 8, k quad (tid % 8) (8 float4 per 32-deep row)
+  const float* arow[AV];
+  bool aok[AV];
+#pragma unroll
+  for (int v = 0; v < AV; ++v) {
+    const int r = (tid + 256 * v) >> 3;
+    const int gm = m0 + r;
+    aok[v] = gm < rows;
+    const int ar = aok[v] ? (gather ? g.row_token[a_off + gm] : a_off + gm) : 0;
+    arow[v] = A + static_cast<size_t>(ar) * g.K;
+  }
+  const int kq = tid & 7;
+  float4 ra[AV], rb[BV];
+  auto load = [&](int k0) {
+    const int kk = k0 + 4 * kq;
+    const bool k_ok = kk < g.K;    // K is a multiple of 8, so a quad is whole or absent
+#pragma unroll
+    for (int v = 0; v < AV; ++v)
+      ra[v] = aok[v] && k_ok ? *reinterpret_cast<const float4*>(arow[v] + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int v = 0; v < BV; ++v) {
+      const int n = n0 + ((tid + 256 * v) >> 3);
+      rb[v] = n < g.N && k_ok ? *reinterpret_cast<const float4*>(B + static_cast<size_t>(n) * g.K + kk)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int v = 0; v < AV; ++v) sA[buf][(tid + 256 * v) >> 3][kq] = ra[v];
+#pragma unroll
+    for (int v = 0; v < BV; ++v) sB[buf][(tid + 256 * v) >> 3][kq] = rb[v];
+  };
+
+  floatx4 acc[2][NBk];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NBk; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // Fragments: lane (r = lane % 16, q = lane / 16) reads k 16 h + 4 q .. + 3 of
+  // its row as one float4, and MFMA c of the group contracts component c: the
+  // four MFMAs cover k 16 h + {c, 4 + c, 8 + c, 12 + c}, all 16 k of the group,
+  // with A and B paired on the same k.
+  const int fr = lane & 15, fq = lane >> 4;
+  const int nslab = (g.K + kFBK - 1) / kFBK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int sl = 0; sl < nslab; ++sl) {
+    const int cur = sl & 1;
+    if (sl + 1 < nslab) load((sl + 1) * kFBK);
+#pragma unroll
+    for (int h = 0; h < kFBK / 16; ++h) {
+      float4 af[2], bf[NBk];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = sA[cur][32 * wm + 16 * i + fr][4 * h + fq];
+#pragma unroll
+      for (int j = 0; j < NBk; ++j) bf[j] = sB[cur][WTN * wn + 16 * j + fr][4 * h + fq];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NBk; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[j].x, af[i].x, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[j].y, af[i].y, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[j].z, af[i].z, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[j].w, af[i].w, acc[i][j], 0, 0, 0);
+        }
+    }
+    if (sl + 1 < nslab) {
+      store(cur ^ 1);   // the other buffer: its last readers finished before the previous barrier
+      __syncthreads();
+    }
+  }
+
+  // lane holds row 32 wm + 16 i + lane % 16 of the tile, columns WTN wn + 16 j + 4 (lane / 16) + 0..3
+  const float* Bias = static_cast<const float*>(g.bias);
+  float* C = static_cast<float*>(g.C);
+  const int o_off = st.o_off[s];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rl = m0 + 32 * wm + 16 * i + fr;
+    if (rl >= rows) continue;
+    float* crow = C + static_cast<size_t>(o_off + rl) * g.N;
+#pragma unroll
+    for (int j = 0; j < NBk; ++j) {
+      const int n = n0 + WTN * wn + 16 * j + 4 * fq;
+      if (n >= g.N) continue;   // N is a multiple of 8: a quad is whole or absent
+      float4 b = Bias ? *reinterpret_cast<const float4*>(Bias + static_cast<size_t>(s) * g.N + n)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 o;
+      o.x = act_exact<ACT>(acc[i][j][0] + b.x);
+      o.y = act_exact<ACT>(acc[i][j][1] + b.y);
+      o.z = act_exact<ACT>(acc[i][j][2] + b.z);
+      o.w = act_exact<ACT>(acc[i][j][3] + b.w);
+      *reinterpret_cast<float4*>(crow + n) = o;
     }
   }
 }
@@ -515,6 +668,13 @@ bool gemm_fast_path(const Problem& p) {
 // mean rows per expert as headroom for uneven routing; ties go to the taller
 // tile, which streams each weight panel for more rows.
 int gemm_m_tile(const Problem& p) {
+  if (p.dtype == MOE_F32) {
+    // float32 matrix-core path: 32 or 64 rows, whichever pads the expected
+    // rows of an expert least (ties to 64)
+    const long long mean = (static_cast<long long>(p.A) + p.E - 1) / p.E;
+    const long long want = p.cap <= mean ? p.cap : (mean * 5 + 3) / 4;
+    return (want + 31) / 32 * 32 < (want + 63) / 64 * 64 ? 32 : 64;
+  }
   if (!gemm_fast_path(p)) return kSB;
   const long long mean = (static_cast<long long>(p.A) + p.E - 1) / p.E;
   if (mean >= 512 && p.cap >= 512) return 256;
@@ -586,6 +746,20 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
     }
 #undef MOE_GEMM_LAUNCH_BM
 #undef MOE_GEMM_LAUNCH
+  } else if (p.dtype == MOE_F32) {
+    const int bm = p.gemm_bm;
+    const long long max_mt = (static_cast<long long>(p.A) + bm - 1) / bm + p.E +
+                             static_cast<long long>(p.S) * ((p.T + bm - 1) / bm);
+    const dim3 grid(static_cast<unsigned>(max_mt), (g.N + kFBN - 1) / kFBN), block(256);
+#define MOE_F32_LAUNCH(BM_)                                                                         \
+  do {                                                                                              \
+    if (act == kActGelu) hipLaunchKernelGGL((gemm_f32_mfma_kernel<kActGelu, BM_>), grid, block, 0, st, g); \
+    else if (act == kActSilu) hipLaunchKernelGGL((gemm_f32_mfma_kernel<kActSilu, BM_>), grid, block, 0, st, g); \
+    else hipLaunchKernelGGL((gemm_f32_mfma_kernel<kActNone, BM_>), grid, block, 0, st, g);          \
+  } while (0)
+    if (bm == 32) MOE_F32_LAUNCH(32);
+    else MOE_F32_LAUNCH(64);
+#undef MOE_F32_LAUNCH
   } else {
     // upper bound of M tiles: sum_e ceil(rows_e / 64) <= ceil(T k / 64) + E + S ceil(T / 64)
     const long long max_mt = (static_cast<long long>(p.A) + kSB - 1) / kSB + p.E +

@@ -137,7 +137,8 @@ Problem make_problem(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int3
   p.mx = false;
   p.ec_C = 0;
   p.A = T * k;
-  p.ntile = (T + kRouterTile - 1) / kRouterTile;
+  p.rtile = router_tile(p);
+  p.ntile = (T + p.rtile - 1) / p.rtile;
   p.cap = cf > 0.f ? capacity_of(cf, T, E, min_cap) : INT32_MAX;
   p.gemm_bm = gemm_m_tile(p);
   p.gemm_mixed = false;
@@ -171,7 +172,8 @@ Problem make_problem_ec(int32_t T, int32_t d, int32_t h, int32_t E, int32_t C, i
   p.mx = false;
   p.ec_C = C;
   p.A = E * C;
-  p.ntile = (T + kRouterTile - 1) / kRouterTile;
+  p.rtile = router_tile(p);
+  p.ntile = (T + p.rtile - 1) / p.rtile;
   p.cap = C;
   p.gemm_bm = gemm_m_tile(p);
   p.gemm_mixed = false;
@@ -259,10 +261,11 @@ moe_status_t forward_top_k(const void* x, const void* W_g, const void* W1, const
 
   if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
   if (!check(launch_router(p, x, W_g, launch->b_g, launch->b_sel, topk_idx, topk_w, ws, st), "router launch")) return MOE_ERR_HIP;
-  if (!check(launch_scan(p, ws, aux_loss, launch->z_loss, launch->expert_counts, launch->expert_kept, st),
-             "scan launch"))
+  // one permute kernel: the scan and scatter stage boundaries are both recorded after it
+  if (!check(launch_permute(p, topk_idx, ws, aux_loss, launch->z_loss, launch->expert_counts, launch->expert_kept, st),
+             "permute launch"))
     return MOE_ERR_HIP;
-  if (!check(launch_scatter(p, topk_idx, ws, st), "scatter launch")) return MOE_ERR_HIP;
+  if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
   if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 1, st), "expert phase 1 launch")) return MOE_ERR_HIP;
   if (!check(launch_expert_ffn(p, x, W1, b1, W2, b2, ws, 2, st), "expert phase 2 launch")) return MOE_ERR_HIP;
   if (!check(launch_combine(p, topk_w, ws, out, st), "combine launch")) return MOE_ERR_HIP;
@@ -369,10 +372,11 @@ moe_status_t moe_forward_mxfp8(const void* x, const void* W_g, const uint8_t* W1
   (void)hipGetLastError();
   if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
   if (!check(launch_router(p, x, W_g, launch->b_g, launch->b_sel, topk_idx, topk_w, ws, st), "router launch")) return MOE_ERR_HIP;
-  if (!check(launch_scan(p, ws, aux_loss, launch->z_loss, launch->expert_counts, launch->expert_kept, st),
-             "scan launch"))
+  // one permute kernel: the scan and scatter stage boundaries are both recorded after it
+  if (!check(launch_permute(p, topk_idx, ws, aux_loss, launch->z_loss, launch->expert_counts, launch->expert_kept, st),
+             "permute launch"))
     return MOE_ERR_HIP;
-  if (!check(launch_scatter(p, topk_idx, ws, st), "scatter launch")) return MOE_ERR_HIP;
+  if (!check(hipSuccess, "stage event")) return MOE_ERR_HIP;
   // expert phase 1 stage: quantize x, then the first Linear
   const hipError_t qe = launch_mx_quantize(static_cast<const uint16_t*>(x), p.T, p.d, ws.xq, ws.xq_scales, st);
   if (qe != hipSuccess) {

@@ -71,8 +71,8 @@ struct Workspace {
   int32_t* row_token;   // [A]        token of each row of the expert-sorted order (kept assignments)
   void* hbuf;           // [R, h]     GELU(x W1^T + b1)
   void* ybuf;           // [R, d]     h W2^T + b2
-  int32_t* local_rank;  // [T, k]     rank of (t,j) among earlier tokens of its 64-token tile
-  int32_t* tile_hist;   // [ntile, E] assignments per (tile, expert); becomes the tile base
+  int32_t* local_rank;  // [T, k]     rank of (t,j) among earlier tokens of its router tile
+  int32_t* tile_hist;   // [ntile, E] assignments per (router tile, expert)
   float* p_part;        // [ntile, E] per-tile sums of the softmax probabilities
   double* z_part;       // [ntile]    per-tile sums of the squared log-sum-exp of the logits
   int32_t* counts;      // [E]
@@ -194,6 +194,21 @@ __device__ __forceinline__ int find_segment(const int32_t* tile_start, int nseg,
   return lo;
 }
 
+// Logical tile L -> (M tile, N tile) in expert-major order, returning the
+// segment: a segment's tiles are contiguous and, within it, its M tiles are
+// adjacent for each N tile (M fastest).  Weight-streaming launches (short
+// experts) use it: the contiguous run of tiles an XCD takes per round then
+// covers few experts, whose weight panels (shared by the expert's M tiles)
+// and row panels (shared by its N tiles) stay in that XCD's L2.
+__device__ __forceinline__ int tile_of_expert(int L, const int32_t* tile_start, int nseg, int ntn, int& mt, int& nt) {
+  const int s = find_segment(tile_start, nseg, L / ntn);
+  const int t0 = tile_start[s], mts = tile_start[s + 1] - t0;
+  const int local = L - t0 * ntn;
+  mt = t0 + local % mts;
+  nt = local / mts;
+  return s;
+}
+
 struct Problem {
   int T, d, h, E, k, S;
   bool mx;       // MXFP8 expert Linears
@@ -202,7 +217,8 @@ struct Problem {
   moe_dtype_t dtype;
   int act;       // moe_activation_t of the experts
   int cap;       // capacity per expert (min_capacity applied); INT32_MAX when unlimited
-  int ntile;     // ceil(T / kRouterTile)
+  int rtile;     // tokens per router tile (router_tile)
+  int ntile;     // ceil(T / rtile)
   int gemm_bm;   // M tile of the grouped GEMM (for the tile prefix)
   bool gemm_mixed;   // MXFP8 GEMM: per-segment heights by mx_mixed_tile_height (gemm_bm unused)
   int part_limit;    // float32 partial tiles the workspace reserves for the GEMM's split tail
@@ -217,7 +233,10 @@ hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const
                          int32_t* topk_idx, float* topk_w, const Workspace& ws, hipStream_t st);
 hipError_t launch_scan(const Problem& p, const Workspace& ws, float* aux_loss, float* z_loss,
                        int32_t* counts_out, int32_t* kept_out, hipStream_t st);
-hipError_t launch_scatter(const Problem& p, const int32_t* topk_idx, const Workspace& ws, hipStream_t st);
+// top-k routing: base ranks, capacity, slot positions, row -> token index, and
+// (workgroup 0) counts, aux, z-loss and the segment table, in one launch
+hipError_t launch_permute(const Problem& p, const int32_t* topk_idx, const Workspace& ws, float* aux_loss,
+                          float* z_loss, int32_t* counts_out, int32_t* kept_out, hipStream_t st);
 hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, const void* b1,
                              const void* W2, const void* b2, const Workspace& ws, int phase,
                              hipStream_t st);
@@ -248,10 +267,14 @@ hipError_t launch_expert_ffn_mx(const Problem& p, const MxWeights& w, const Work
 // Which GEMM kernel serves a problem; the M tile decides the tile prefix.
 bool gemm_fast_path(const Problem& p);
 int gemm_m_tile(const Problem& p);
-// router logits (bf16, d % 256 == 0): expert padding and split-K factor, which
-// size the float64 partial-logit workspace [KS][T][Epad]
+// router logits (bf16, d % 256 == 0, more than 64 experts): expert padding
+// and split-K factor, which size the float64 partial-logit workspace
+// [KS][T][Epad] (KS = 0 on the one-launch path)
 int logit_pad(int E);
 int logit_splits(const Problem& p);
+// the one-launch router and its tile (32 or 64 tokens; needs T, d, E, dtype)
+bool router_fused(const Problem& p);
+int router_tile(const Problem& p);
 // partial tiles reserved for the grouped GEMM's split tail (one per workgroup of a 256-CU part)
 constexpr int kGemmPartCap = 256;
 // the same in the fixed scratch of moe_forward_noalloc (16 tiles of 256 x 256 float32: 4 MB)

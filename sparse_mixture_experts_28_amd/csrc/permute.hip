@@ -8,19 +8,24 @@
 // E * sum f_i P_i); "第7章" tensor-shape trace (the token -> expert reordering
 // is the real cost of the layer).
 //
-// scan    (1 workgroup of 1024): for every expert, an exclusive scan of its
-//         per-tile counts over the tiles in token order gives each tile's base rank;
-//         the total is c_e, kept_e = min(c_e, cap); an exclusive scan of kept
-//         over experts gives the segment offsets; the balance loss is
-//         finalised from c and the per-tile probability sums, the router
+// permute (top-k routing; one workgroup per router tile): each workgroup
+//         adds the per-tile expert counts of the tiles before its own (its
+//         tile's base rank per expert) and of all tiles (c_e), so no workgroup
+//         waits for another; kept_e = min(c_e, cap) and an exclusive scan of
+//         kept over experts give the segment offsets; then each assignment of
+//         the tile: rank = tile base + in-tile rank, kept iff rank < cap, its
+//         row in the expert-sorted order and that row's token are recorded.
+//         No token row is copied: the expert GEMM gathers x rows through
+//         row_token.  Workgroup 0 also writes the counts, finalises the
+//         balance loss from c and the per-tile probability sums and the router
 //         z-loss from the per-tile sums of squared log-sum-exp (both float64,
-//         fixed order); the grouped-GEMM segment table is written.
-// scatter (1 thread per assignment): rank = tile base + in-tile rank; the
-//         assignment is kept iff rank < cap; its row in the expert-sorted
-//         order and that row's token are recorded.  No token row is copied:
-//         the expert GEMM gathers x rows through row_token.
+//         fixed order), and writes the grouped-GEMM segment table.
+// scan    (expert choice; 1 workgroup of 1024): the same finalisation with
+//         every expert taking exactly C tokens (the selection kernel then
+//         lists them).
 //
-// No atomics anywhere: every result is a fixed function of the inputs.
+// Every result is a fixed function of the inputs: the only atomics are
+// integer additions into LDS (exact in any order); float sums run in a fixed order.
 #include "moe_internal.h"
 
 namespace moe {
@@ -167,26 +172,196 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
   }
 }
 
-// One thread per assignment (t, j): its rank among expert e's assignments in
-// token order is the tile base plus the in-tile rank; kept iff rank < cap.
-// Writes the assignment's row in the expert-sorted order (slot_pos, -1 if
-// dropped) and that row's token (row_token), which the expert GEMM gathers
-// its phase-1 rows through.  Every kept row gets exactly one writer.
-__global__ __launch_bounds__(256) void scatter_kernel(Problem p, const int32_t* __restrict__ topk_idx,
-                                                      const int32_t* __restrict__ local_rank,
-                                                      const int32_t* __restrict__ tile_base,
-                                                      const int32_t* __restrict__ seg_base,
-                                                      int32_t* __restrict__ slot_pos,
-                                                      int32_t* __restrict__ row_token) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= p.T * p.k) return;
-  const int t = i / p.k;
-  const int e = topk_idx[i];
-  const int rank = tile_base[static_cast<size_t>(t / kRouterTile) * p.E + e] + local_rank[i];
-  SegTable st = seg_table(const_cast<int32_t*>(seg_base), p.E + p.S, p.E);
-  const int pos = rank < p.cap ? st.route_off[e] + rank : -1;
-  slot_pos[i] = pos;
-  if (pos >= 0) row_token[pos] = t;
+constexpr int kPermThreads = 512;
+constexpr int kSegSlots = 512;   // >= MOE_MAX_EXPERTS + MOE_MAX_SHARED
+
+// Fixed butterfly sums over a wave (the same tree on every call: deterministic).
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// In-place inclusive scan of v[0 .. kSegSlots) by kPermThreads threads.
+__device__ __forceinline__ void block_scan_incl(int32_t* v) {
+  for (int off = 1; off < kSegSlots; off <<= 1) {
+    const int t = threadIdx.x;
+    const int add = t >= off ? v[t - off] : 0;
+    __syncthreads();
+    v[t] += add;
+    __syncthreads();
+  }
+}
+
+// Workgroup 0's finalisation: counts, kept, the balance loss, the router
+// z-loss and the grouped-GEMM segment table, from s_cnt (c_e) and s_off
+// (exclusive scan of kept over the experts).  Float64 sums in a fixed order:
+// lane l of a wave takes items l, l + 64, ... in order, then a fixed butterfly.
+__device__ void finalize_tables(const Problem& p, const float* __restrict__ p_part, const double* __restrict__ z_part,
+                                const int32_t* s_cnt, const int32_t* s_off, int32_t* counts, int32_t* kept,
+                                int32_t* seg_base, float* aux_loss, float* z_loss, int32_t* counts_out,
+                                int32_t* kept_out) {
+  __shared__ double s_term[MOE_MAX_EXPERTS];
+  __shared__ int32_t s_tiles[kSegSlots];
+  const int E = p.E, nseg = p.E + p.S;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  // P_e (sum of the tile sums over all tiles) and the aux term f_e P_e:
+  // thread (q, e), q < G = min(8, 512 / E), adds tiles q, q + G, ... in
+  // order (independent loads, all in flight), then thread e adds the G
+  // partials in order
+  __shared__ double s_ppart[kPermThreads];
+  {
+    const int G = min(8, kPermThreads / E), e = t % E, q = t / E;
+    double ps = 0.0;
+    if (q < G) {
+      // eight loads issued together, then added in order
+      int j = q;
+      for (; j + 7 * G < p.ntile; j += 8 * G) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = p_part[static_cast<size_t>(j + u * G) * E + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ps += static_cast<double>(v[u]);
+      }
+      for (; j < p.ntile; j += G) ps += static_cast<double>(p_part[static_cast<size_t>(j) * E + e]);
+    }
+    s_ppart[t] = ps;
+  }
+  __syncthreads();
+  if (t < E) {
+    const int G = min(8, kPermThreads / E);
+    double ps = 0.0;
+    for (int q = 0; q < G; ++q) ps += s_ppart[q * E + t];
+    s_term[t] = (static_cast<double>(s_cnt[t]) / static_cast<double>(p.A)) * (ps / static_cast<double>(p.T));
+  }
+  const int my_kept = t < E ? min(s_cnt[t], p.cap) : 0;
+  if (t < E) {
+    counts[t] = s_cnt[t];
+    kept[t] = my_kept;
+    if (counts_out) counts_out[t] = s_cnt[t];
+    if (kept_out) kept_out[t] = my_kept;
+  }
+  // segment rows and M tiles (routed experts, then shared)
+  int my_rows = 0, my_tiles = 0, my_bm = p.gemm_bm;
+  if (t < nseg) {
+    my_rows = t < E ? my_kept : p.T;
+    if (p.gemm_mixed) my_bm = mx_mixed_tile_height(my_rows);
+    my_tiles = (my_rows + my_bm - 1) / my_bm;
+  }
+  s_tiles[t] = my_tiles;
+  __syncthreads();
+  block_scan_incl(s_tiles);
+  if (wave == 0) {
+    // aux = E sum_e f_e P_e
+    double a = 0.0;
+    for (int e = lane; e < E; e += kWave) a += s_term[e];
+    a = wave_sum(a);
+    if (lane == 0 && aux_loss) *aux_loss = static_cast<float>(static_cast<double>(E) * a);
+  } else if (wave == 1) {
+    // z = (1/T) sum of the tiles' sums of squared log-sum-exp
+    double z = 0.0;
+#pragma unroll 4
+    for (int j = lane; j < p.ntile; j += kWave) z += z_part[j];
+    z = wave_sum(z);
+    if (lane == 0 && z_loss) *z_loss = static_cast<float>(z / static_cast<double>(p.T));
+  }
+  if (t < nseg) {
+    const SegTable st = seg_table(seg_base, nseg, E);
+    const int excl_rows = t < E ? s_off[t] : 0;
+    st.rows[t] = my_rows;
+    st.a_off[t] = excl_rows;
+    st.o_off[t] = t < E ? excl_rows : p.A + (t - E) * p.T;
+    st.tile_start[t] = s_tiles[t] - my_tiles;
+    st.tile_bm[t] = my_bm;
+    if (t < E) st.route_off[t] = excl_rows;
+    if (t == nseg - 1) st.tile_start[nseg] = s_tiles[t];
+  }
+}
+
+// One workgroup per router tile of p.rtile tokens.
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(Problem p, const int32_t* __restrict__ topk_idx,
+                                                               const int32_t* __restrict__ local_rank,
+                                                               const int32_t* __restrict__ tile_hist,
+                                                               const float* __restrict__ p_part,
+                                                               const double* __restrict__ z_part, int32_t* counts,
+                                                               int32_t* kept, int32_t* seg_base, float* aux_loss,
+                                                               float* z_loss, int32_t* counts_out, int32_t* kept_out,
+                                                               int32_t* __restrict__ slot_pos,
+                                                               int32_t* __restrict__ row_token) {
+  __shared__ int32_t s_base[MOE_MAX_EXPERTS];
+  __shared__ int32_t s_cnt[MOE_MAX_EXPERTS];
+  __shared__ int32_t s_off[MOE_MAX_EXPERTS];
+  const int E = p.E, k = p.k;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  const int tile = blockIdx.x;
+  // 1. per expert, the counts of the tiles before this one (its base rank)
+  // and of all tiles (c_e): the [ntile, E] table read in order by all threads
+  // (coalesced, every load independent), added into LDS with integer atomics
+  // (order-free, so the sums are exact and deterministic)
+  if (t < E) {
+    s_base[t] = 0;
+    s_cnt[t] = 0;
+  }
+  __syncthreads();
+  {
+    const int n = p.ntile * E, before_end = tile * E;
+    auto add = [&](int i, int h) {
+      if (h != 0) {
+        const int ex = i % E;
+        atomicAdd(&s_cnt[ex], h);
+        if (i < before_end) atomicAdd(&s_base[ex], h);
+      }
+    };
+    // eight loads issued together, then their atomics
+    int i = t;
+    for (; i + 7 * kPermThreads < n; i += 8 * kPermThreads) {
+      int h[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) h[u] = tile_hist[i + u * kPermThreads];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) add(i + u * kPermThreads, h[u]);
+    }
+    for (; i < n; i += kPermThreads) add(i, tile_hist[i]);
+  }
+  __syncthreads();
+  // 2. segment offsets: exclusive scan of kept over the experts (wave 0,
+  // four experts per lane)
+  if (wave == 0) {
+    int kp[4], own = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ex = 4 * lane + i;
+      kp[i] = ex < E ? min(s_cnt[ex], p.cap) : 0;
+      own += kp[i];
+    }
+    int incl = own;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += o;
+    }
+    int run = incl - own;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ex = 4 * lane + i;
+      if (ex < E) s_off[ex] = run;
+      run += kp[i];
+    }
+  }
+  __syncthreads();
+  // 3. this tile's assignments
+  const int tok0 = tile * p.rtile;
+  const int n = min(p.rtile, p.T - tok0) * k;
+  for (int i = t; i < n; i += kPermThreads) {
+    const size_t a = static_cast<size_t>(tok0) * k + i;
+    const int ex = topk_idx[a];
+    const int rank = s_base[ex] + local_rank[a];
+    const int pos = rank < p.cap ? s_off[ex] + rank : -1;
+    slot_pos[a] = pos;
+    if (pos >= 0) row_token[pos] = tok0 + i / k;
+  }
+  if (tile == 0)
+    finalize_tables(p, p_part, z_part, s_cnt, s_off, counts, kept, seg_base, aux_loss, z_loss, counts_out, kept_out);
 }
 
 }  // namespace
@@ -198,10 +373,11 @@ hipError_t launch_scan(const Problem& p, const Workspace& ws, float* aux_loss, f
   return hipGetLastError();
 }
 
-hipError_t launch_scatter(const Problem& p, const int32_t* topk_idx, const Workspace& ws, hipStream_t st) {
-  const int n = p.T * p.k;
-  hipLaunchKernelGGL(scatter_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, topk_idx, ws.local_rank,
-                     ws.tile_hist, ws.seg, ws.slot_pos, ws.row_token);
+hipError_t launch_permute(const Problem& p, const int32_t* topk_idx, const Workspace& ws, float* aux_loss,
+                          float* z_loss, int32_t* counts_out, int32_t* kept_out, hipStream_t st) {
+  hipLaunchKernelGGL(permute_kernel, dim3(p.ntile), dim3(kPermThreads), 0, st, p, topk_idx, ws.local_rank, ws.tile_hist,
+                     ws.p_part, ws.z_part, ws.counts, ws.kept, ws.seg, aux_loss, z_loss, counts_out, kept_out,
+                     ws.slot_pos, ws.row_token);
   return hipGetLastError();
 }
 

@@ -154,14 +154,25 @@ __device__ __forceinline__ void select_k(const RouterArgs& a, const double (&val
   }
 }
 
-// Selection, weights, probability partials and ranks for one 64-token tile,
-// given the logits acc[nb][v] in the layout described at the top.
-template <int NB>
-__device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0) {
-  __shared__ int32_t s_idx[kRouterTile * MOE_MAX_TOPK];
-  __shared__ unsigned long long s_mask[16 * NB];
-  __shared__ float s_p[4][16 * NB];
-  __shared__ double s_z[kRouterTile];
+// Selection, weights, probability partials and ranks for one tile of RT
+// tokens (RT = 32 or 64; 4 waves, wave w holding tokens 16 w .. 16 w + 15 of
+// the tile, so waves past RT / 16 hold none), given the logits acc[nb][v] in
+// the layout described at the top.
+//
+// Its LDS tables live in `smem` (route_tile_smem<RT, NB>() bytes, 8-byte
+// aligned), so a kernel whose main loop fills one LDS object by direct loads
+// can hand it a part of that object: a second LDS object would make the
+// compiler wait for every direct load in flight before each read of the first.
+template <int RT, int NB>
+constexpr int route_tile_smem() { return RT * 8 + 16 * NB * 8 + 4 * 16 * NB * 4 + RT * MOE_MAX_TOPK * 4; }
+
+template <int RT, int NB>
+__device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0, unsigned char* smem) {
+  static_assert(RT == 16 || RT == 32 || RT == 64, "router tiles are 16, 32 or 64 tokens");
+  double* s_z = reinterpret_cast<double*>(smem);                                        // [RT]
+  unsigned long long* s_mask = reinterpret_cast<unsigned long long*>(smem + RT * 8);      // [16 NB]
+  float (*s_p)[16 * NB] = reinterpret_cast<float (*)[16 * NB]>(smem + RT * 8 + 16 * NB * 8);   // [4][16 NB]
+  int32_t* s_idx = reinterpret_cast<int32_t*>(smem + RT * 8 + 16 * NB * 8 + 4 * 16 * NB * 4);  // [RT * MOE_MAX_TOPK]
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -177,7 +188,8 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
   for (int v = 0; v < 4; ++v) {
     const int r = wave * 16 + g * 4 + v;   // token within the tile
     const int t = tile0 + r;
-    const bool tok_ok = t < a.T;           // uniform across the 16-lane group
+    const bool in_tile = r < RT;           // uniform across the wave
+    const bool tok_ok = in_tile && t < a.T;   // uniform across the 16-lane group
     double val[NB];
     double m = -INFINITY;
 #pragma unroll
@@ -202,7 +214,7 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) pp[nb] += ev[nb] * inv;
     }
-    if (c == 0) s_z[r] = tok_ok ? lse_sq(m, z) : 0.0;
+    if (c == 0 && in_tile) s_z[r] = tok_ok ? lse_sq(m, z) : 0.0;
     if (a.ec_logits) {
       write_ec(a, val, m, z, t, c, tok_ok);
       continue;
@@ -211,7 +223,7 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
     int my_idx;
     float my_e, esum;
     select_k<NB>(a, val, m, c, my_idx, my_e, esum);
-    if (c < k) {
+    if (c < k && in_tile) {
       s_idx[r * MOE_MAX_TOPK + c] = tok_ok ? my_idx : -1;
       if (tok_ok) {
         a.topk_idx[static_cast<size_t>(t) * k + c] = my_idx;
@@ -230,8 +242,8 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
   }
   __syncthreads();
 
-  const int ntok = min(kRouterTile, a.T - tile0);
-  const int tile = tile0 / kRouterTile;
+  const int ntok = min(RT, a.T - tile0);
+  const int tile = tile0 / RT;
   const bool ec = a.ec_logits != nullptr;
   // In-tile ranks in token order.  mask[e] has bit r set iff token r of the
   // tile chose e (a token's k experts are distinct, and OR is order-free, so
@@ -249,11 +261,12 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0)
     a.p_part[static_cast<size_t>(tile) * E + e] = ((s_p[0][e] + s_p[1][e]) + s_p[2][e]) + s_p[3][e];
     if (!ec) a.tile_hist[static_cast<size_t>(tile) * E + e] = __popcll(s_mask[e]);
   }
-  if (threadIdx.x == blockDim.x - 1) {
-    // z-loss partial of the tile, tokens in order
-    double zs = 0.0;
-    for (int r = 0; r < ntok; ++r) zs += s_z[r];
-    a.z_part[tile] = zs;
+  if (threadIdx.x < kWave) {
+    // z-loss partial of the tile: a fixed butterfly over the tile's tokens
+    double zs = threadIdx.x < ntok ? s_z[threadIdx.x] : 0.0;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) zs += __shfl_xor(zs, m, kWave);
+    if (threadIdx.x == 0) a.z_part[tile] = zs;
   }
   for (int i = threadIdx.x; i < (ec ? 0 : ntok * k); i += blockDim.x) {
     const int r = i / k, j = i - r * k;
@@ -312,24 +325,32 @@ __global__ __launch_bounds__(kRouterThreads) void router_bf16_kernel(RouterArgs 
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[nb][v] += static_cast<double>(part[nb][v]);
 
-  route_tile<NB>(a, acc, tile0);
+  __shared__ __align__(8) unsigned char smem[route_tile_smem<kRouterTile, NB>()];
+  route_tile<kRouterTile, NB>(a, acc, tile0, smem);
 }
 
 // ---- float32 inputs: exact float64 products, float64 sums ----
-template <int NB>
+// RT = 64: wave w holds tokens 16 w .. 16 w + 15 over all of d.  RT = 16 (at
+// most 64 experts, few tokens): the four waves share the tile's 16 tokens and
+// take every fourth group of four columns of d; their float64 sums are added
+// in LDS in wave order, so small batches still fill the GPU.
+template <int RT, int NB>
 __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(RouterArgs a) {
+  static_assert(RT == 64 || (RT == 16 && NB <= 4), "float32 router tiles");
+  constexpr int KW = RT == 16 ? 4 : 1;   // waves sharing a token block
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c = lane & 15;
   const int g = lane >> 4;
-  const int tile0 = blockIdx.x * kRouterTile;
+  const int tile0 = blockIdx.x * RT;
+  const int tb = KW == 1 ? wave : 0, kw = KW == 1 ? 0 : wave;
   const float* X = static_cast<const float*>(a.x);
   const float* W = static_cast<const float*>(a.W_g);
 
   const float* xrow[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int t = tile0 + wave * 16 + g * 4 + v;
+    const int t = tile0 + tb * 16 + g * 4 + v;
     xrow[v] = X + static_cast<size_t>(t < a.T ? t : 0) * a.d;
   }
   double acc[NB][4];
@@ -338,27 +359,62 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(RouterArgs a
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[nb][v] = 0.0;
 
-  for (int kk = 0; kk < a.d; kk += 4) {
-    float4 xv[4];
+  // the loads of the next group of four columns are issued before this
+  // group's products, so each wave keeps two groups of loads in flight
+  auto load = [&](int kk, float4 (&xv)[4], float4 (&wv)[NB]) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) xv[v] = *reinterpret_cast<const float4*>(xrow[v] + kk);
+    for (int v = 0; v < 4; ++v)
+      xv[v] = kk < a.d ? *reinterpret_cast<const float4*>(xrow[v] + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int e = nb * 16 + c;
-      float4 wv = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e < a.E) wv = *reinterpret_cast<const float4*>(W + static_cast<size_t>(e) * a.d + kk);
+      wv[nb] = e < a.E && kk < a.d ? *reinterpret_cast<const float4*>(W + static_cast<size_t>(e) * a.d + kk)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto fold = [&](const float4 (&xv)[4], const float4 (&wv)[NB]) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         double s = acc[nb][v];
-        s = fma(static_cast<double>(xv[v].x), static_cast<double>(wv.x), s);
-        s = fma(static_cast<double>(xv[v].y), static_cast<double>(wv.y), s);
-        s = fma(static_cast<double>(xv[v].z), static_cast<double>(wv.z), s);
-        s = fma(static_cast<double>(xv[v].w), static_cast<double>(wv.w), s);
+        s = fma(static_cast<double>(xv[v].x), static_cast<double>(wv[nb].x), s);
+        s = fma(static_cast<double>(xv[v].y), static_cast<double>(wv[nb].y), s);
+        s = fma(static_cast<double>(xv[v].z), static_cast<double>(wv[nb].z), s);
+        s = fma(static_cast<double>(xv[v].w), static_cast<double>(wv[nb].w), s);
         acc[nb][v] = s;
       }
+  };
+  float4 xa[4], wa[NB], xb[4], wb[NB];
+  int kk = 4 * kw;
+  load(kk, xa, wa);
+  for (; kk < a.d; kk += 8 * KW) {
+    load(kk + 4 * KW, xb, wb);
+    fold(xa, wa);
+    if (kk + 4 * KW >= a.d) break;
+    load(kk + 8 * KW, xa, wa);
+    fold(xb, wb);
+  }
+  constexpr int kRed = KW > 1 ? (KW - 1) * NB * 4 * 64 : 1;
+  __shared__ double red[kRed];
+  if constexpr (KW > 1) {
+    if (wave > 0) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[(((wave - 1) * NB + nb) * 4 + v) * 64 + lane] = acc[nb][v];
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int w = 1; w < KW; ++w)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[nb][v] += red[(((w - 1) * NB + nb) * 4 + v) * 64 + lane];
     }
   }
-  route_tile<NB>(a, acc, tile0);
+  __shared__ __align__(8) unsigned char smem[route_tile_smem<RT, NB>()];
+  route_tile<RT, NB>(a, acc, tile0, smem);
 }
 
 // ---- bf16 inputs, d % 256 == 0: logits kernel + selection kernel ----
@@ -426,6 +482,9 @@ void router_logits_kernel(LogitArgs a) {
   const int c0 = ks * nchunk / a.KS, c1 = (ks + 1) * nchunk / a.KS;
   const int nst = (c1 - c0) * (256 / kLgK);          // stages of this split (>= 2)
   const uint32_t kbase = static_cast<uint32_t>(c0) * 512u;
+  // start at different even stages per token tile and wrap, spreading the
+  // concurrent reads over d (the split's chunk order changes, chunks stay whole)
+  const int s0 = (2 * static_cast<int>(blockIdx.x)) % nst;
 
   // direct loads: load i of wave w fills stage rows 16 i + 4 w + lane / 16 at
   // physical chunk lane % 16 (rows 0..127: x, 128..191: router weight)
@@ -433,7 +492,8 @@ void router_logits_kernel(LogitArgs a) {
   const uint32_t vo = static_cast<uint32_t>(dr) * rb + lgswz(dr, lane & 15) * 16;
   auto issue = [&](int st) {
     u32x4* base = lds + (st % NS) * kStage + (4 * wave) * kLgCh;
-    const uint32_t kb = kbase + static_cast<uint32_t>(st) * (kLgK * 2);
+    const int sc = st + s0 < nst ? st + s0 : st + s0 - nst;
+    const uint32_t kb = kbase + static_cast<uint32_t>(sc) * (kLgK * 2);
 #pragma unroll
     for (int i = 0; i < kLgLoads; ++i) {
       if (i < kLgTok / 16)
@@ -517,6 +577,231 @@ void router_logits_kernel(LogitArgs a) {
     }
 }
 
+// ---- bf16 inputs, d % 256 == 0, E <= 64: one fused launch ----
+//
+// A workgroup owns RT tokens (32 or 64, so that a launch has ~256
+// workgroups) and every expert (padded to EXP = 16 or 64), over all of d, so
+// the selection follows in the same workgroup with the logits in registers:
+// no partial logits leave the CU.  x rows and router-weight rows reach LDS
+// by direct loads in 128-deep stages through an NS-slot ring (NS - 1 stages
+// in flight, up to ~100 KB per CU, so the stream of x is not bound by the
+// memory latency); x is read once, the router weight (<= 64 rows) from L2.
+// Wave w takes token block tb = w % TB (TB = RT / 16) and, when RT = 32, half
+// of each stage's four 32-deep k-steps (kq = w / TB); the two halves' float64
+// sums are added in LDS (kq 0 then kq 1) before the selection, which runs on
+// waves 0 .. TB-1 in the layout of route_tile.  float32 MFMA sums over each
+// 256-element chunk of d, chunks added in float64, as in the other paths.
+template <int RT, int EXP>
+constexpr int fused_slots() {
+  return (144 * 1024) / ((RT + EXP) * kLgK * 2) > 12 ? 12 : (144 * 1024) / ((RT + EXP) * kLgK * 2);
+}
+
+// wait until at most s stages of L direct loads each are in flight (s uniform)
+template <int L, int S>
+__device__ __forceinline__ void wait_stages(int s) {
+  if constexpr (S > 0) {
+    if (s >= S) {
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(S * L));
+      return;
+    }
+    wait_stages<L, S - 1>(s);
+  } else {
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+  }
+}
+
+template <int RT, int EXP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void router_fused_kernel(RouterArgs a) {
+  constexpr int TB = RT / 16;                 // token blocks of 16
+  constexpr int KQ = 4 / TB;                  // waves per token block
+  constexpr int NB = EXP / 16;                // expert blocks of 16
+  constexpr int kRows = RT + EXP;             // stage rows: tokens, then router-weight rows
+  constexpr int kStage = kRows * kLgCh;       // u32x4 per stage
+  constexpr int kLoads = kRows / 16;          // 1 KB direct loads per wave per stage
+  constexpr int NS = fused_slots<RT, EXP>();
+  static_assert(NS >= 3 && NS * (kLoads) < 64, "ring");
+  __shared__ u32x4 lds[NS * kStage];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tb = wave % TB, kq = wave / TB;
+  const int tile0 = blockIdx.x * RT;
+  const uint32_t rb = static_cast<uint32_t>(a.d) * 2u;   // bytes per row
+  const int nrows = min(RT, a.T - tile0);
+  const uint16_t* X = static_cast<const uint16_t*>(a.x);
+  // out-of-range token and expert rows read as zero (buffer range check)
+  const __amdgpu_buffer_rsrc_t xs = make_rsrc(X + static_cast<size_t>(tile0) * a.d, static_cast<uint32_t>(nrows) * rb);
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.W_g, static_cast<uint32_t>(a.E) * rb);
+  const int nst = a.d / kLgK;                 // stages (even: d % 256 == 0)
+
+  // direct loads: load i of wave w fills stage rows 16 i + 4 w + lane / 16 at
+  // physical chunk lane % 16 (rows 0..RT-1: x, then the router weight)
+  const int dr = 4 * wave + (lane >> 4);
+  const uint32_t vo = static_cast<uint32_t>(dr) * rb + lgswz(dr, lane & 15) * 16;
+  // Workgroups start at different even stages of d and wrap around, so the
+  // launch's concurrent row segments spread over d (and the memory channels)
+  // instead of all reading the same columns; each 256-element chunk stays
+  // whole, and a token's chunk order is fixed by its tile.
+  const int s0 = (2 * static_cast<int>(blockIdx.x)) % nst;
+  auto issue = [&](int st) {
+    u32x4* base = lds + (st % NS) * kStage + (4 * wave) * kLgCh;
+    const int sc = st + s0 < nst ? st + s0 : st + s0 - nst;
+    const uint32_t kb = static_cast<uint32_t>(sc) * (kLgK * 2);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      if (i < RT / 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (__attribute__((address_space(3))) void*)(base + 16 * i * kLgCh),
+                                                 16, vo, static_cast<uint32_t>(16 * i) * rb + kb, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, (__attribute__((address_space(3))) void*)(base + 16 * i * kLgCh),
+                                                 16, vo, static_cast<uint32_t>(16 * (i - RT / 16)) * rb + kb, 0, 0);
+    }
+  };
+
+  const int rr = lane & 15, cg = lane >> 4;
+  double acc[NB][4];
+  floatx4 part[NB];
+#pragma unroll
+  for (int eb = 0; eb < NB; ++eb) {
+    part[eb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[eb][v] = 0.0;
+  }
+
+#pragma unroll
+  for (int sp = 0; sp < NS - 1; ++sp)
+    if (sp < nst) issue(sp);
+  for (int st = 0; st < nst; ++st) {
+    // stage st landed (up to NS - 2 later stages may be in flight); every
+    // wave is past stage st-1, whose slot then takes stage st + NS - 1
+    wait_stages<kLoads, NS - 2>(min(NS - 2, nst - 1 - st));
+    lg_barrier();
+    if (st + NS - 1 < nst) issue(st + NS - 1);
+    const u32x4* sa = lds + (st % NS) * kStage;
+#pragma unroll
+    for (int q = 0; q < kLgK / 32 / KQ; ++q) {
+      const int s = q * KQ + kq;   // this wave's k-steps of the stage
+      const int ch = lgswz(rr, 4 * s + cg);
+      const bf16x8 xf = __builtin_bit_cast(bf16x8, sa[(16 * tb + rr) * kLgCh + ch]);
+#pragma unroll
+      for (int eb = 0; eb < NB; ++eb) {
+        const bf16x8 wf = __builtin_bit_cast(bf16x8, sa[(RT + 16 * eb + rr) * kLgCh + ch]);
+        part[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, wf, part[eb], 0, 0, 0);
+      }
+    }
+    if (st & 1) {   // a 256-element chunk is complete: add it in float64
+#pragma unroll
+      for (int eb = 0; eb < NB; ++eb) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[eb][v] += static_cast<double>(part[eb][v]);
+        part[eb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+
+  if constexpr (KQ > 1) {
+    // add the second half's sums into the first (the ring is free: every wave
+    // is past its last stage once all have passed this barrier)
+    lg_barrier();
+    double* red = reinterpret_cast<double*>(lds);
+    if (kq == 1) {
+#pragma unroll
+      for (int eb = 0; eb < NB; ++eb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[((tb * NB + eb) * 4 + v) * 64 + lane] = acc[eb][v];
+    }
+    lg_barrier();
+    if (kq == 0) {
+#pragma unroll
+      for (int eb = 0; eb < NB; ++eb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[eb][v] += red[((tb * NB + eb) * 4 + v) * 64 + lane];
+    }
+    __syncthreads();
+  }
+  // lane (rr, cg) holds tokens 16 tb + 4 cg + v of the tile, experts 16 eb + rr:
+  // the layout of route_tile (waves TB .. 3 hold no tokens there); its tables
+  // go to the start of the ring, free once every wave is past the barrier above
+  // (RT = 64) or the reduction's __syncthreads (RT = 32)
+  if constexpr (KQ == 1) lg_barrier();
+  static_assert(route_tile_smem<RT, NB>() <= NS * kStage * 16, "route_tile tables fit in the ring");
+  route_tile<RT, NB>(a, acc, tile0, reinterpret_cast<unsigned char*>(lds));
+}
+
+// ---- bf16 inputs, d % 256 == 0, E <= 16, T <= 16384: 16-token tiles ----
+//
+// One workgroup per 16 tokens (Mixtral shape: 512 workgroups, two per CU),
+// the four waves splitting d into interleaved 256-element chunks.  Each lane
+// loads its MFMA fragments straight into registers: 16 bytes of its token row
+// (the A operand) and of its expert's router row (the B operand; rows past E
+// read zero through the buffer range check, with no memory traffic), a whole
+// chunk (8 k-steps) ahead of the MFMAs, so ~8 KB per wave and ~128 KB per CU
+// are in flight with no barrier in the loop.  float32 sums per chunk, added in
+// float64; the four waves' sums are added in LDS in wave order, then wave 0
+// holds the tile's logits in the layout of route_tile.
+__global__ __launch_bounds__(256) void router_t16_kernel(RouterArgs a) {
+  constexpr int RT = 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rr = lane & 15, cg = lane >> 4;
+  const int tile0 = blockIdx.x * RT;
+  const uint32_t rb = static_cast<uint32_t>(a.d) * 2u;
+  const int nrows = min(RT, a.T - tile0);
+  const uint16_t* X = static_cast<const uint16_t*>(a.x);
+  const __amdgpu_buffer_rsrc_t xs = make_rsrc(X + static_cast<size_t>(tile0) * a.d, static_cast<uint32_t>(nrows) * rb);
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.W_g, static_cast<uint32_t>(a.E) * rb);
+  const uint32_t vo = static_cast<uint32_t>(rr) * rb + static_cast<uint32_t>(cg) * 16u;
+  const int nch = a.d / 256;
+
+  u32x4 xa0[8], wb0[8], xa1[8], wb1[8];
+  auto load = [&](u32x4 (&xa)[8], u32x4 (&wb)[8], int c) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t so = static_cast<uint32_t>(c) * 512u + static_cast<uint32_t>(s) * 64u;
+      xa[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xs, vo, so, 0));
+      wb[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ws, vo, so, 0));
+    }
+  };
+  double acc[1][4] = {{0.0, 0.0, 0.0, 0.0}};
+  auto chunk = [&](const u32x4 (&xa)[8], const u32x4 (&wb)[8]) {
+    floatx4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[s]), __builtin_bit_cast(bf16x8, wb[s]),
+                                                     part, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[0][v] += static_cast<double>(part[v]);
+  };
+  // wave w takes chunks w, w + 4, ...: two at a time, the next pair's loads
+  // issued before the current pair's MFMAs
+  int c = wave;
+  if (c < nch) load(xa0, wb0, c);
+  if (c + 4 < nch) load(xa1, wb1, c + 4);
+  for (; c < nch; c += 8) {
+    chunk(xa0, wb0);
+    if (c + 8 < nch) load(xa0, wb0, c + 8);
+    if (c + 4 < nch) {
+      chunk(xa1, wb1);
+      if (c + 12 < nch) load(xa1, wb1, c + 12);
+    }
+  }
+  __shared__ double red[3][4][64];
+  if (wave > 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave - 1][v][lane] = acc[0][v];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[0][v] += red[w][v][lane];
+  }
+  __shared__ __align__(8) unsigned char smem[route_tile_smem<RT, 1>()];
+  route_tile<RT, 1>(a, acc, tile0, smem);
+}
+
 // Selection from float64 logits [T, Epad] for one 64-token tile, one token
 // per 16-lane group (1024 threads): lane c of token r's group holds experts
 // nb * 16 + c.  Same results as route_tile, with 16 waves per tile instead of
@@ -587,18 +872,29 @@ __device__ __forceinline__ void select_tile(const RouterArgs& a, const double (&
     for (int j = 0; j < k; ++j) atomicOr(&s_mask[s_idx[rr * MOE_MAX_TOPK + j]], 1ull << rr);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    // probability sum over the tile's tokens in token order
+  // probability sums over the tile's tokens: thread (q, e), q < G = 1024 / E,
+  // adds tokens q, q + G, ... in order; then the G partials in order
+  __shared__ float s_ps[kSelectThreads];
+  {
+    const int G = kSelectThreads / E, e = threadIdx.x % E, q = threadIdx.x / E;
     float ps = 0.f;
-    for (int rr = 0; rr < ntok; ++rr) ps += s_p[rr][e];
-    a.p_part[static_cast<size_t>(tile) * E + e] = ps;
-    if (!ec) a.tile_hist[static_cast<size_t>(tile) * E + e] = __popcll(s_mask[e]);
+    if (q < G)
+      for (int rr = q; rr < ntok; rr += G) ps += s_p[rr][e];
+    s_ps[threadIdx.x] = ps;
+    __syncthreads();
+    if (threadIdx.x < E) {
+      float tot = 0.f;
+      for (int qq = 0; qq < G; ++qq) tot += s_ps[qq * E + threadIdx.x];
+      a.p_part[static_cast<size_t>(tile) * E + threadIdx.x] = tot;
+      if (!ec) a.tile_hist[static_cast<size_t>(tile) * E + threadIdx.x] = __popcll(s_mask[threadIdx.x]);
+    }
   }
-  if (threadIdx.x == blockDim.x - 1) {
-    // z-loss partial of the tile, tokens in order
-    double zs = 0.0;
-    for (int rr = 0; rr < ntok; ++rr) zs += s_z[rr];
-    a.z_part[tile] = zs;
+  if (threadIdx.x < kWave) {
+    // z-loss partial of the tile: a fixed butterfly over the tile's tokens
+    double zs = threadIdx.x < ntok ? s_z[threadIdx.x] : 0.0;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) zs += __shfl_xor(zs, m, kWave);
+    if (threadIdx.x == 0) a.z_part[tile] = zs;
   }
   for (int i = threadIdx.x; i < (ec ? 0 : ntok * k); i += blockDim.x) {
     const int rr = i / k, j = i - rr * k;
@@ -638,14 +934,43 @@ hipError_t launch_select(const Problem& p, const RouterArgs& a, const double* lo
 template <int NB>
 hipError_t launch_nb(const Problem& p, const RouterArgs& a, hipStream_t st) {
   dim3 grid(p.ntile), block(kRouterThreads);
-  if (p.dtype == MOE_BF16)
+  if (p.dtype == MOE_BF16) {
     hipLaunchKernelGGL(router_bf16_kernel<NB>, grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL(router_f32_kernel<NB>, grid, block, 0, st, a);
+  } else {
+    if constexpr (NB <= 4) {
+      if (p.rtile == 16) {
+        hipLaunchKernelGGL((router_f32_kernel<16, NB>), grid, block, 0, st, a);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((router_f32_kernel<64, NB>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
+
+// The one-launch router serves bf16 layers with d a multiple of 256 and at
+// most 64 experts (each workgroup holds every expert's logits); more experts
+// take the split logits kernel and the selection kernel.
+bool router_fused(const Problem& p) { return p.dtype == MOE_BF16 && p.d % 256 == 0 && p.E <= kLgExp; }
+
+// Tokens per router tile (and per-tile permute table row): 16 on the bf16
+// path with at most 16 experts (T <= 16384); else, when 64-token tiles would
+// give the launch fewer than 256 workgroups, 32 on the other one-launch bf16
+// path and 16 on the float32 path (at most 64 experts); else 64.
+// The 16-token bf16 kernel (at most 16 experts): its workgroups each read
+// every tile's expert counts in the permute, so it is kept to T <= 16384.
+bool router_t16(const Problem& p) { return router_fused(p) && p.E <= 16 && p.T <= 16384; }
+
+int router_tile(const Problem& p) {
+  const bool few = (p.T + 63) / 64 < 256;
+  if (router_t16(p)) return 16;
+  if (router_fused(p) && few) return 32;
+  // float32 with at most 64 experts: 16-token tiles, the four waves splitting d
+  if (p.dtype == MOE_F32 && p.E <= 64 && few) return 16;
+  return kRouterTile;
+}
 
 // expert padding of the logits: one 16-expert tile when E <= 16 (a quarter of
 // the MFMA work and partial-logit traffic of a 64-expert tile), else 64s
@@ -654,6 +979,7 @@ int logit_pad(int E) { return E <= 16 ? 16 : (E + kLgExp - 1) / kLgExp * kLgExp;
 // d is split into KS ranges of whole 256-element chunks so the logits launch
 // has ~256 workgroups (at most 8 splits, at least one chunk each)
 int logit_splits(const Problem& p) {
+  if (router_fused(p)) return 0;   // no partial logits
   const int pad = logit_pad(p.E);
   const long long tiles = static_cast<long long>((p.T + kLgTok - 1) / kLgTok) * (pad / (pad == 16 ? 16 : kLgExp));
   long long ks = (256 + tiles - 1) / tiles;
@@ -684,6 +1010,19 @@ hipError_t launch_router(const Problem& p, const void* x, const void* W_g, const
   a.k = p.k;
   a.ntile = p.ntile;
   const int nb = (p.E + 15) / 16;
+  if (router_fused(p)) {
+    const dim3 grid(p.ntile), block(256);
+    if (p.rtile == 16) {
+      hipLaunchKernelGGL(router_t16_kernel, grid, block, 0, st, a);
+    } else if (p.rtile == 32) {
+      if (p.E <= 16) hipLaunchKernelGGL((router_fused_kernel<32, 16>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((router_fused_kernel<32, 64>), grid, block, 0, st, a);
+    } else {
+      if (p.E <= 16) hipLaunchKernelGGL((router_fused_kernel<64, 16>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((router_fused_kernel<64, 64>), grid, block, 0, st, a);
+    }
+    return hipGetLastError();
+  }
   if (p.dtype == MOE_BF16 && p.d % 256 == 0 && ws.logits != nullptr) {
     LogitArgs la;
     la.x = static_cast<const uint16_t*>(x);

@@ -94,6 +94,11 @@ REDUCED = {
     "sel_bias_E256_top8_shared": ("deepseek", dict(T=128, d=256, h=256, E=256, k=8, S=1, sel_bias_std=1.0)),
     "sel_bias_f32": ("switch", dict(T=500, d=64, h=128, E=8, k=2, cf=0.5, sel_bias_std=1.0)),
     "sel_bias_d32_bf16_simt": ("mixtral", dict(T=100, d=32, h=64, E=6, k=3, sel_bias_std=1.0)),
+    # one-launch router with 64-token tiles (T >= 16384): 16 and (padded) 64 experts
+    "router_tile64_E16_capacity": ("glam", dict(T=16500, d=256, h=256, E=16, k=2, cf=1.5)),
+    "router_tile64_E40_top3": ("glam", dict(T=16400, d=512, h=256, E=40, k=3, cf=0.0)),
+    # one-launch router with 32-token tiles and 64 padded experts, deep d
+    "router_tile32_E33_deep_d": ("deepseek", dict(T=300, d=2048, h=256, E=33, k=4, S=0)),
 }
 
 

@@ -35,6 +35,7 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_28_amd", "csrc", "gemm.hip")
+MX_GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_28_amd", "csrc", "mxfp8.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
 
 # oracle sample per workload: the first N tokens (about 10-30 s of host work)
@@ -70,23 +71,23 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def gemm_source_sha():
-    with open(GEMM_SRC, "rb") as f:
+def gemm_source_sha(mx: bool = False):
+    with open(MX_GEMM_SRC if mx else GEMM_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str, phase: str):
+def measured_traffic(workload: str, phase: str, mx: bool = False):
     """HBM bytes per launch of a GEMM phase (read + write, from FETCH_SIZE and
     WRITE_SIZE counter runs scaled by a copy-kernel calibration) as committed
     under profiles/, or None when absent or taken on another version of the
-    kernel source."""
+    kernel source (gemm.hip, or mxfp8.hip for the MXFP8 path)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = t.get(workload)
-    if not entry or entry.get("gemm_source_sha") != gemm_source_sha() or phase not in entry:
+    entry = t.get(workload + ("_mxfp8" if mx else ""))
+    if not entry or entry.get("gemm_source_sha") != gemm_source_sha(mx) or phase not in entry:
         return None
     return entry[phase]["fetch_bytes"] + entry[phase]["write_bytes"]
 
@@ -348,7 +349,7 @@ def main():
     dom = "expert_phase1" if stages["expert_phase1"] >= stages["expert_phase2"] else "expert_phase2"
     dom_ms = stages[dom]
     dom_bytes = bytes_gemm1 if dom == "expert_phase1" else bytes_gemm2
-    traffic = measured_traffic(args.workload, dom)
+    traffic = measured_traffic(args.workload, dom, mx)
     if c.dtype == "f32":
         # float32 layers run the grouped GEMM on the float32 matrix cores
         roof = {"bound": "mfma", "achieved": tfs(gemm_flops, dom_ms), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
@@ -367,8 +368,6 @@ def main():
         roof["gemm_both_phases_frac_of_bf16_peak"] = tfs(2 * gemm_flops, gemm_ms) / PEAK_BF16_TFLOPS
     if mx:
         roof["gemm_both_phases_frac_of_fp8_peak"] = tfs(2 * gemm_flops, gemm_ms) / PEAK_FP8_TFLOPS
-        traffic = None   # the committed counter runs cover the bf16 kernels
-        roof["traffic"] = None
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

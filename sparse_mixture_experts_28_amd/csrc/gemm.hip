@@ -434,7 +434,7 @@ __global__ __launch_bounds__(256) void gemm_tail_fixup_kernel(GemmArgs g, int P)
 // SIMT loop it replaces.  BM x 128 tiles, BM in {32, 64} chosen per problem
 // (the float32 workloads have short experts: ~64 rows at the switch-shaped
 // layer), K slabs of 32 staged through LDS (rows of 32 k padded to 36 floats,
-// 16-byte stores and fragment reads) with the next slab's loads held in
+// 16-byte stores and fragment reads) with the next two slabs' loads held in
 // registers while the current one is multiplied.  One workgroup per tile
 // (grid = M tiles x N tiles; the M tiles past the segment table's count exit),
 // several resident per CU.  4 waves in a (BM / 32) x (4 / (BM / 32)) grid,
@@ -483,8 +483,7 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(GemmArgs g) {
     arow[v] = A + static_cast<size_t>(ar) * g.K;
   }
   const int kq = tid & 7;
-  float4 ra[AV], rb[BV];
-  auto load = [&](int k0) {
+  auto load = [&](int k0, float4 (&ra)[AV], float4 (&rb)[BV]) {
     const int kk = k0 + 4 * kq;
     const bool k_ok = kk < g.K;    // K is a multiple of 8, so a quad is whole or absent
 #pragma unroll
@@ -497,7 +496,7 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(GemmArgs g) {
                               : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, const float4 (&ra)[AV], const float4 (&rb)[BV]) {
 #pragma unroll
     for (int v = 0; v < AV; ++v) sA[buf][(tid + 256 * v) >> 3][kq] = ra[v];
 #pragma unroll
@@ -516,12 +515,7 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(GemmArgs g) {
   // with A and B paired on the same k.
   const int fr = lane & 15, fq = lane >> 4;
   const int nslab = (g.K + kFBK - 1) / kFBK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int sl = 0; sl < nslab; ++sl) {
-    const int cur = sl & 1;
-    if (sl + 1 < nslab) load((sl + 1) * kFBK);
+  auto compute = [&](int cur) {
 #pragma unroll
     for (int h = 0; h < kFBK / 16; ++h) {
       float4 af[2], bf[NBk];
@@ -539,10 +533,27 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(GemmArgs g) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[j].w, af[i].w, acc[i][j], 0, 0, 0);
         }
     }
-    if (sl + 1 < nslab) {
-      store(cur ^ 1);   // the other buffer: its last readers finished before the previous barrier
-      __syncthreads();
-    }
+  };
+  // Two slabs of loads ahead: slab s sits in LDS buffer s % 2 when it is
+  // multiplied, slab s + 1 in the register set of its parity, and slab s + 2
+  // is issued into the register set slab s has left.  A buffer is refilled
+  // only after the barrier that follows its last readers.
+  float4 ra0[AV], rb0[BV], ra1[AV], rb1[BV];
+  load(0, ra0, rb0);
+  store(0, ra0, rb0);
+  if (nslab > 1) load(kFBK, ra1, rb1);
+  __syncthreads();
+  for (int sl = 0; sl < nslab; sl += 2) {
+    if (sl + 2 < nslab) load((sl + 2) * kFBK, ra0, rb0);
+    compute(0);
+    if (sl + 1 >= nslab) break;
+    store(1, ra1, rb1);
+    __syncthreads();
+    if (sl + 3 < nslab) load((sl + 3) * kFBK, ra1, rb1);
+    compute(1);
+    if (sl + 2 >= nslab) break;
+    store(0, ra0, rb0);
+    __syncthreads();
   }
 
   // lane holds row 32 wm + 16 i + lane % 16 of the tile, columns WTN wn + 16 j + 4 (lane / 16) + 0..3

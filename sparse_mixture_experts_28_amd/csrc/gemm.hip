@@ -144,7 +144,11 @@ __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7) ^ ((ro
 //            slice); direct loads of stage t+NS (spread over the slice)
 // so fragment reads have a slice of MFMAs to land and (NS - 1) stages of
 // loads stay in flight.  NS = 3 for BM <= 160 (weight streaming: ~100 KB per
-// CU in flight), 2 for BM = 256 (two 64 KB stages).
+// CU in flight).  At BM = 256 two 64 KB stages would leave one in flight;
+// instead LDS holds five 32 KB operand units (A_t, B_t, A_t+1, ...: 160 KB),
+// the barrier of step t frees stage t's two units for B_t+2 and A_t+3, and
+// about one and a half stages stay in flight.  The LDS address of a direct
+// load (M0) is scalar arithmetic on a per-wave offset taken once.
 //
 // The tile height is chosen per problem so that an expert's rows usually
 // fill whole tiles: every M tile of an expert re-streams that expert's
@@ -165,10 +169,14 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
   constexpr int LS = MF / NR;                  // direct loads go one every LS MFMAs
   constexpr int kStage = (BM + kBN) * kCh;     // u32x4 per LDS stage
   static_assert(MF >= 2 * NR, "slice too short for its reads and loads");
-  __shared__ u32x4 lds[NS * kStage];
+  // BM = 256: a ring of five 256-row operand units instead of whole stages
+  constexpr bool kUnits = BM == 256;
+  constexpr int kUnit = 256 * kCh;             // u32x4 per operand unit
+  __shared__ u32x4 lds[kUnits ? 5 * kUnit : NS * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  // wave-uniform, so the LDS addresses of the direct loads (M0) are scalar arithmetic
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
@@ -190,6 +198,7 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
   const int dr_row = 8 * wave + (lane >> 3);
   const int dr_ch = swz(dr_row, lane & 7);
   const int rd_row = lane & 15;
+  const int wofs = uniform(8 * wave * kCh);    // this wave's first LDS row of a direct load
 
   const TailPlan tp = tail_plan(total, gridDim.x, nk, g.part_cap);
   const int items = tp.full + tp.tail * tp.S;
@@ -245,45 +254,37 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
 
-    // fragment q of 32-deep slice sl of the stage in ring slot rs: q < MB -> A block q,
-    // else B block q - MB; slice sl of every stage lives in fragment buffer sl
+    // fragment q of 32-deep slice sl of a stage whose A rows start at LDS
+    // offset ao and B rows at bo: q < MB -> A block q, else B block q - MB;
+    // slice sl of every stage lives in fragment buffer sl
     bf16x8 fa[2][MB], fb[2][8];
-    auto frag1 = [&](int rs, int sl, int q) {
-      const u32x4* sa = lds + rs * kStage;
+    auto frag1 = [&](int ao, int bo, int sl, int q) {
       const int ch = swz(rd_row, 2 * (lane >> 4) + sl);
       if (q < MB)
-        fa[sl][q] = __builtin_bit_cast(bf16x8, sa[(wm * (BM / 2) + q * 16 + rd_row) * kCh + ch]);
+        fa[sl][q] = __builtin_bit_cast(bf16x8, lds[ao + (wm * (BM / 2) + q * 16 + rd_row) * kCh + ch]);
       else
-        fb[sl][q - MB] = __builtin_bit_cast(bf16x8, sa[(BM + wn * 128 + (q - MB) * 16 + rd_row) * kCh + ch]);
+        fb[sl][q - MB] = __builtin_bit_cast(bf16x8, lds[bo + (wn * 128 + (q - MB) * 16 + rd_row) * kCh + ch]);
     };
-    // direct load q of stage k (K step k0 + k) into ring slot rs: q < MB -> A rows
-    // 32 q + .., else B rows 32 (q - MB) + ..
-    auto issue1 = [&](int rs, int k, int q) {
-      u32x4* base = lds + rs * kStage + (8 * wave) * kCh;
-      const int qq = q < MB ? q : q - MB;
+    // direct load q of stage k (K step k0 + k): q < MB -> A rows 32 q + .. at
+    // offset ao, else B rows 32 (q - MB) + .. at offset bo
+    auto issue1 = [&](int ao, int bo, int k, int q) {
       const uint32_t kbytes = static_cast<uint32_t>((k0 + k) * kBK * 2);
       if (q < MB)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra_rsrc, (__attribute__((address_space(3))) void*)(base + 32 * q * kCh), 16, va[q], kbytes, 0, 0);
+            ra_rsrc, (__attribute__((address_space(3))) void*)(lds + ao + wofs + 32 * q * kCh), 16, va[q], kbytes, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rsrc, (__attribute__((address_space(3))) void*)(base + (BM + 32 * (q - MB)) * kCh),
-                                                 16, vb, static_cast<uint32_t>(qq) * step32 + kbytes, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb_rsrc, (__attribute__((address_space(3))) void*)(lds + bo + wofs + 32 * (q - MB) * kCh), 16, vb,
+            static_cast<uint32_t>(q - MB) * step32 + kbytes, 0, 0);
     };
+    auto slot_a = [&](int rs) { return rs * kStage; };
+    auto slot_b = [&](int rs) { return rs * kStage + BM * kCh; };
 
-    // prologue: stages 0 .. NS-1 in flight, stage 0 published, its slice 0 read
-#pragma unroll
-    for (int k = 0; k < NS; ++k)
-#pragma unroll
-      for (int q = 0; q < NR; ++q) issue1(k, k, q);
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm((NS - 1) * NR));
-    lds_barrier();
-#pragma unroll
-    for (int q = 0; q < NR; ++q) frag1(0, 0, q);
-
-    // cur: ring slot of stage t (t % NS); stage t+1 sits in the next slot and
-    // stage t+NS refills slot cur.  The last NS steps are peeled so every
-    // flag is a compile-time constant in the unrolled body.
-    // pend: stage t+2's loads may be in flight at the wait for stage t+1
+    // Stage ring (BM <= 160): cur = ring slot of stage t (t % NS); stage t+1
+    // sits in the next slot and stage t+NS refills slot cur.  The last NS
+    // steps are peeled so every flag is a compile-time constant in the
+    // unrolled body.  pend: stage t+2's loads may be in flight at the wait
+    // for stage t+1.
     auto kstep = [&](int t, int cur, bool refill, bool next, bool pend) {
       const int nxt = cur + 1 == NS ? 0 : cur + 1;
 #pragma unroll
@@ -298,13 +299,74 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
           }
           const int i = q >> 3, j = q & 7;
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[sl][j], fa[sl][i], acc[i][j], 0, 0, 0);
-          if (sl == 0 && (q & 1) == 0 && (q >> 1) < NR) frag1(cur, 1, q >> 1);
-          if (sl == 1 && (q & 1) == 0 && (q >> 1) < NR && next) frag1(nxt, 0, q >> 1);
-          if (sl == 1 && (q % LS) == LS - 1 && (q / LS) < NR && refill) issue1(cur, t + NS, q / LS);
+          if (sl == 0 && (q & 1) == 0 && (q >> 1) < NR) frag1(slot_a(cur), slot_b(cur), 1, q >> 1);
+          if (sl == 1 && (q & 1) == 0 && (q >> 1) < NR && next) frag1(slot_a(nxt), slot_b(nxt), 0, q >> 1);
+          if (sl == 1 && (q % LS) == LS - 1 && (q / LS) < NR && refill)
+            issue1(slot_a(cur), slot_b(cur), t + NS, q / LS);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     };
+    // Unit ring (BM = 256): five 32 KB units hold operand panels in the order
+    // A_0 B_0 A_1 B_1 ...; A_t sits in unit 2t mod 5 (ua) and B_t in unit
+    // 2t+1 mod 5.  During step t, stage t is being read, stage t+1 has landed
+    // or is landing, and the fifth unit (ua + 4: B_{t-1}'s, freed at the
+    // previous barrier) takes A_{t+2} in slice 0; the barrier of step t frees
+    // stage t's units and B_{t+2} goes into unit ua in slice 1.  So about one
+    // and a half stages stay in flight where whole 64 KB stages would leave
+    // one, and the direct loads are spread over both slices (8 a slice at
+    // BM = 256) rather than 16 in one: the address FIFO in front of the
+    // texture unit then rarely fills and holds up the wave's MFMA issue.
+    // Loads are issued in panel order, so the wait for stage t+1 leaves only
+    // A_{t+2}'s MB loads a wave outstanding.
+    constexpr int LSU = 4;                     // MFMAs between direct loads in a slice
+    static_assert(!kUnits || (8 * LSU <= MF && MB * LSU <= MF), "slice too short for its loads");
+    auto kstep_u = [&](int t, int ua, bool refill, bool next) {
+      const int ub = ua == 4 ? 0 : ua + 1;
+      const int na = ua >= 3 ? ua - 3 : ua + 2, nb = ub >= 3 ? ub - 3 : ub + 2;
+      const int uf = ua == 0 ? 4 : ua - 1;     // the free unit
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+#pragma unroll
+        for (int q = 0; q < MF; ++q) {
+          if (sl == 1 && q == 0 && next) {
+            if (refill) __builtin_amdgcn_s_waitcnt(vm_wait_imm(MB));
+            else __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+            lds_barrier();
+          }
+          const int i = q >> 3, j = q & 7;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[sl][j], fa[sl][i], acc[i][j], 0, 0, 0);
+          if (sl == 0 && (q & 1) == 0 && (q >> 1) < NR) frag1(ua * kUnit, ub * kUnit, 1, q >> 1);
+          if (sl == 1 && (q & 1) == 0 && (q >> 1) < NR && next) frag1(na * kUnit, nb * kUnit, 0, q >> 1);
+          if (refill && (q % LSU) == LSU - 1) {
+            if (sl == 0 && q / LSU < MB) issue1(uf * kUnit, 0, t + 2, q / LSU);
+            if (sl == 1 && q / LSU < 8) issue1(0, ua * kUnit, t + 2, MB + q / LSU);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    if constexpr (kUnits) {
+      // prologue: A_0 B_0 A_1 B_1 in units 0..3, stage 0 published, its slice 0 read
+#pragma unroll
+      for (int q = 0; q < NR; ++q) issue1(0, kUnit, 0, q);
+#pragma unroll
+      for (int q = 0; q < NR; ++q) issue1(2 * kUnit, 3 * kUnit, 1, q);
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(NR));
+      lds_barrier();
+#pragma unroll
+      for (int q = 0; q < NR; ++q) frag1(0, kUnit, 0, q);
+    } else {
+      // prologue: stages 0 .. NS-1 in flight, stage 0 published, its slice 0 read
+#pragma unroll
+      for (int k = 0; k < NS; ++k)
+#pragma unroll
+        for (int q = 0; q < NR; ++q) issue1(slot_a(k), slot_b(k), k, q);
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm((NS - 1) * NR));
+      lds_barrier();
+#pragma unroll
+      for (int q = 0; q < NR; ++q) frag1(slot_a(0), slot_b(0), 0, q);
+    }
     // Shorter tiles leave accumulation registers free, and the register
     // allocator then shuttles accumulators between register files inside the
     // loop.  Occupying the rest of that file with values pinned there across
@@ -318,18 +380,28 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
         __asm__ volatile("" : "+a"(pin[k]));
       }
     }
-    int t = 0, cur = 0;
-    for (; t + NS < kn; ++t) {
-      kstep(t, cur, true, true, NS == 3);
-      cur = cur + 1 == NS ? 0 : cur + 1;
+    if constexpr (kUnits) {
+      // (the unit is derived from t in each step: carried through the loop
+      // instead, it led the register allocator to rotate the accumulators
+      // between registers on every step)
+      int t = 0;
+      for (; t + 2 < kn; ++t) kstep_u(t, (2 * t) % 5, true, true);
+      kstep_u(t, (2 * t) % 5, false, true);
+      kstep_u(t + 1, (2 * t + 2) % 5, false, false);
+    } else {
+      int t = 0, cur = 0;
+      for (; t + NS < kn; ++t) {
+        kstep(t, cur, true, true, NS == 3);
+        cur = cur + 1 == NS ? 0 : cur + 1;
+      }
+      if constexpr (NS == 3) {
+        // stage t+2 = kn-1 was issued a step ago and may still be in flight
+        kstep(t++, cur, false, true, true);
+        cur = cur + 1 == NS ? 0 : cur + 1;
+      }
+      kstep(t, cur, false, true, false);
+      kstep(t + 1, cur + 1 == NS ? 0 : cur + 1, false, false, false);
     }
-    if constexpr (NS == 3) {
-      // stage t+2 = kn-1 was issued a step ago and may still be in flight
-      kstep(t++, cur, false, true, true);
-      cur = cur + 1 == NS ? 0 : cur + 1;
-    }
-    kstep(t, cur, false, true, false);
-    kstep(t + 1, cur + 1 == NS ? 0 : cur + 1, false, false, false);
     if constexpr (kPad > 0) {
 #pragma unroll
       for (int k = 0; k < kPad; ++k) __asm__ volatile("" ::"a"(pin[k]));

@@ -413,9 +413,15 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, u32x4* lds, const SegTa
                                                                    sa[i]);
       if (m < 2) readA(o1, m);
       if (i == MB - 1) readB(o1, j);
-      if (m < 2) issue_scales(gnext, m, group_start);
-      if (m >= 2 && m < MB + 2) issue1(ca, ta, m - 2);
-      if (m >= MB + 2 && m < NR + 2) issue1(cb, tb, m - 2);
+      // the step's NR + 2 direct loads, spread evenly over the half step: issued
+      // back to back they overfill the texture unit's address FIFO, and the
+      // wave's next MFMA waits behind the stalled load
+      if ((m * (NR + 2)) % HM < NR + 2) {
+        const int l = m * (NR + 2) / HM;
+        if (l < 2) issue_scales(gnext, l, group_start);
+        else if (l < MB + 2) issue1(ca, ta, l - 2);
+        else issue1(cb, tb, l - 2);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };

@@ -87,7 +87,7 @@ __device__ __forceinline__ float silu_exact(float v) { return v / (1.0f + expf(-
 
 template <int ACT>
 __device__ __forceinline__ float act_fast(float v) {
-  if constexpr (ACT == kActGelu) return gelu_as(v);
+  if constexpr (ACT == kActGelu) return gelu_fast(v);
   else if constexpr (ACT == kActSilu) return silu_fast(v);
   else return v;
 }
@@ -156,8 +156,9 @@ __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7) ^ ((ro
 //
 // Epilogue: the MFMA takes the B fragment first, so each block is
 // accumulated transposed: lane l holds output row 16 i + l % 16 of the wave
-// tile and the four consecutive columns 16 j + 4 (l / 16) + 0..3; bias, then
-// (phase 1) the activation, in float32, rounded once to bf16, one 8-byte store.
+// tile and the four consecutive columns 16 j + 4 (l / 16) + 0..3; the bias is
+// the accumulators' starting value, then (phase 1) the activation in float32,
+// rounded once to bf16, one 8-byte store.
 template <int ACT, int BM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_mfma_kernel(GemmArgs g) {
@@ -246,13 +247,28 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
     }
     const uint32_t vb = static_cast<uint32_t>(n0 + dr_row) * row_bytes + dr_ch * 16;
 
+    // A whole tile's accumulators start at the bias of their column (the
+    // epilogue then has no bias to add); the pieces of a split tile start at
+    // zero and the fix-up adds the bias once.  The MFMA takes the B fragment
+    // first, so lane l's four accumulators of block j hold columns
+    // 16 j + 4 (l / 16) + 0..3 of the wave tile.
+    const int cbase = n0 + wn * 128 + 4 * (lane >> 4);
+    floatx4 bias0[8];
+    {
+      const uint16_t* brow = Bias + static_cast<size_t>(s) * g.N + cbase;
+      const bool with_bias = Bias != nullptr && piece < 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint2 b = with_bias ? *reinterpret_cast<const uint2*>(brow + 16 * j) : make_uint2(0u, 0u);
+        bias0[j] = floatx4{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
+                           __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u)};
+      }
+    }
     floatx4 acc[MB][8];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
+      for (int j = 0; j < 8; ++j) acc[i][j] = bias0[j];
 
     // fragment q of 32-deep slice sl of a stage whose A rows start at LDS
     // offset ao and B rows at bo: q < MB -> A block q, else B block q - MB;
@@ -411,14 +427,10 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
 
     // Epilogue.  A piece of a tail tile stores its float32 partial tile
     // (row-major BM x 256, buffer stores: one lane offset plus scalar and
-    // immediate offsets); a whole tile adds the bias, applies the activation
-    // (phase 1) and stores bf16.  The choice is made per 16-row block so only that
-    // block's accumulators are live in vector registers at a time.
-    const int cbase = n0 + wn * 128 + 4 * (lane >> 4);
-    const uint16_t* brow = Bias + static_cast<size_t>(s) * g.N + cbase;
-    uint2 bq[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) bq[j] = Bias ? *reinterpret_cast<const uint2*>(brow + 16 * j) : make_uint2(0u, 0u);
+    // immediate offsets); a whole tile (its bias already in the accumulators)
+    // applies the activation (phase 1) and stores bf16.  The choice is made per
+    // 16-row block so only that block's accumulators are live in vector
+    // registers at a time.
     const __amdgpu_buffer_rsrc_t pr = make_rsrc(g.part, static_cast<uint32_t>(g.part_cap) * BM * kBN * 4u);
     const uint32_t pv = (static_cast<uint32_t>(wm * (BM / 2) + (lane & 15)) * kBN + wn * 128 + 4 * (lane >> 4)) * 4u;
 #pragma unroll
@@ -433,14 +445,10 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
         uint16_t* crow = C + static_cast<size_t>(o_off + rl) * g.N + cbase;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          float v0 = acc[i][j][0] + __uint_as_float(bq[j].x << 16);
-          float v1 = acc[i][j][1] + __uint_as_float(bq[j].x & 0xffff0000u);
-          float v2 = acc[i][j][2] + __uint_as_float(bq[j].y << 16);
-          float v3 = acc[i][j][3] + __uint_as_float(bq[j].y & 0xffff0000u);
-          v0 = act_fast<ACT>(v0);
-          v1 = act_fast<ACT>(v1);
-          v2 = act_fast<ACT>(v2);
-          v3 = act_fast<ACT>(v3);
+          const float v0 = act_fast<ACT>(acc[i][j][0]);
+          const float v1 = act_fast<ACT>(acc[i][j][1]);
+          const float v2 = act_fast<ACT>(acc[i][j][2]);
+          const float v3 = act_fast<ACT>(acc[i][j][3]);
           *reinterpret_cast<uint2*>(crow + 16 * j) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
         }
       }

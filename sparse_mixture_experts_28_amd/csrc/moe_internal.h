@@ -44,22 +44,25 @@ __device__ __forceinline__ float silu_fast(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.44269504088896341f));
 }
 
-// GELU(v) = v/2 (1 + erf(v / sqrt 2)) with erf from Abramowitz & Stegun 7.1.26
-// (Hastings' rational approximation, |error| <= 1.5e-7 in erf): for z >= 0,
-// erf(z) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 + p z);
-// odd in z.  Branch-free: one reciprocal, one exp2 and ~12 VALU operations.
-__device__ __forceinline__ float gelu_as(float v) {
-  const float z = fabsf(v) * 0.70710678118654752440f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  float q = fmaf(t, 1.061405429f, -1.453152027f);
-  q = fmaf(t, q, 1.421413741f);
-  q = fmaf(t, q, -0.284496736f);
-  q = fmaf(t, q, 0.254829592f);
-  q *= t;
-  const float e = __builtin_amdgcn_exp2f((z * -1.44269504088896341f) * z);   // exp(-z^2)
-  const float erf_v = copysignf(fmaf(-q, e, 1.0f), v);
-  const float hv = 0.5f * v;
-  return fmaf(hv, erf_v, hv);
+// GELU(v) = v/2 (1 + erf(v / sqrt 2)) = (v + |v| erf(|v| / sqrt 2)) / 2, with
+// erf(u / sqrt 2) = 1 - exp2(Q(u)) for u = min(|v|, 6) and Q a degree-9
+// polynomial fit of log2 erfc(u / sqrt 2) without a constant term (the fit is
+// csrc/fit_gelu.py).  Within 4.2e-7 absolute and 1.1e-7 |v| of GELU in float32;
+// one exp2 and 13 VALU operations (the rational erf it replaced needed a
+// reciprocal as well, and the epilogue of the first Linear is VALU-bound).
+// +inf gives +inf, NaN gives NaN, -inf gives NaN as the exact form does.
+__device__ __forceinline__ float gelu_fast(float v) {
+  const float u = __builtin_amdgcn_fmed3f(fabsf(v), 0.0f, 6.0f);   // min(|v|, 6); NaN gives 6
+  float q = fmaf(u, 1.934985789e-07f, -4.592050573e-06f);
+  q = fmaf(u, q, 4.332197204e-05f);
+  q = fmaf(u, q, -1.772511459e-04f);
+  q = fmaf(u, q, -1.936358894e-04f);
+  q = fmaf(u, q, 7.167997304e-03f);
+  q = fmaf(u, q, -5.258556455e-02f);
+  q = fmaf(u, q, -4.591732323e-01f);
+  q = fmaf(u, q, -1.151110053e+00f);
+  const float erf_u = 1.0f - __builtin_amdgcn_exp2f(q * u);
+  return 0.5f * fmaf(fabsf(v), erf_u, v);
 }
 
 // ----------------------------------------------------- workspace layout --

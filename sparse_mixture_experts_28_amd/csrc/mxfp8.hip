@@ -134,7 +134,7 @@ __device__ __forceinline__ void mx_barrier() {
 // activation of the first Linear: 1 GELU(erf), 2 SiLU, 0 none (second Linear)
 template <int ACT>
 __device__ __forceinline__ float mx_act(float v) {
-  if constexpr (ACT == 1) return gelu_as(v);
+  if constexpr (ACT == 1) return gelu_fast(v);
   else if constexpr (ACT == 2) return silu_fast(v);
   else return v;
 }

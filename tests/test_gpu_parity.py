@@ -80,6 +80,11 @@ REDUCED = {
                                             expert_bias=False)),
     "gelu_nobias_bf16": ("glam", dict(T=700, d=256, h=512, E=16, expert_bias=False)),
     "gelu_nobias_f32": ("tiny", dict(T=130, d=32, h=64, E=4, k=2, expert_bias=False)),
+    # float32 matrix-core path: ~81 expected rows an expert (32-row tiles, three a
+    # segment) with a shared expert; ~250 (64-row tiles, several a segment with a
+    # ragged last one); K and N not multiples of the 32-deep slab or the 128-column tile
+    "f32_tiles96_shared": ("switch", dict(T=260, d=72, h=136, E=8, k=2, S=1, cf=0.0)),
+    "f32_tiles128_ragged": ("tiny", dict(T=400, d=64, h=200, E=4, k=2)),
     # capacity floor: ceil(0.1 * 1000 / 16) = 7 is raised to 40, which still drops
     "min_capacity_binds_bf16": ("glam", dict(T=1000, d=256, h=512, E=16, cf=0.1, min_capacity=40)),
     # ceil(0.25 * 500 / 8) = 16 raised to 30; f32 SIMT path, k = 1

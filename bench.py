@@ -3,7 +3,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload mixtral] [--no-cpu-baseline]
                     [--activation gelu|silu] [--no-expert-bias] [--min-capacity N]
-                    [--routing top-k|expert-choice] [--mxfp8]
+                    [--routing top-k|expert-choice] [--mxfp8] [--packed-weights]
 
 A step is one full layer forward (router, permute -- or scan and selection
 under expert choice --, expert phase 1, expert phase 2, combine) over one batch of seeded synthetic tokens already
@@ -55,6 +55,8 @@ def parse():
                     help="expert activation (silu with --no-expert-bias: the Mixtral expert form)")
     ap.add_argument("--no-expert-bias", action="store_true", help="bias-free expert Linears (NULL b1, b2)")
     ap.add_argument("--min-capacity", type=int, default=0, help="capacity floor (with a capacity factor)")
+    ap.add_argument("--packed-weights", action="store_true",
+                    help="bf16 expert weights in the tile-packed layout (moe_pack_weights, packed once before timing)")
     ap.add_argument("--mxfp8", action="store_true",
                     help="MXFP8 expert Linears (weights quantized on the GPU before the timed steps)")
     ap.add_argument("--routing", default="top-k", choices=["top-k", "expert-choice"],
@@ -195,6 +197,12 @@ def main():
     mx = args.mxfp8
     if mx and (ec or c.dtype != "bf16"):
         raise SystemExit("--mxfp8 runs the bf16 workloads with top-k routing")
+    packed = args.packed_weights
+    if packed and (mx or c.dtype != "bf16" or d % 256 or h % 256):
+        raise SystemExit("--packed-weights needs bf16 expert Linears with d and h multiples of 256 (not --mxfp8)")
+    if packed:
+        W1, W2 = moe.pack_weights(W1), moe.pack_weights(W2)
+        torch.cuda.synchronize()
     C = min(T, -(-k * T // E))
     if mx:
         nbytes = moe.moe_workspace_bytes_mxfp8(T, d, h, E, k, S)
@@ -228,6 +236,7 @@ def main():
     launch.z_loss = z_loss.data_ptr()
     launch.activation = moe.ACTIVATIONS[c.activation]
     launch.min_capacity = c.min_capacity
+    launch.weights_packed = 1 if packed else 0
 
     nst = moe.MOE_NUM_STAGE_EVENTS
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nst)] for _ in range(args.steps)]
@@ -349,7 +358,7 @@ def main():
     dom = "expert_phase1" if stages["expert_phase1"] >= stages["expert_phase2"] else "expert_phase2"
     dom_ms = stages[dom]
     dom_bytes = bytes_gemm1 if dom == "expert_phase1" else bytes_gemm2
-    traffic = measured_traffic(args.workload, dom, mx)
+    traffic = measured_traffic(args.workload + ("_packed" if packed else ""), dom, mx)
     if c.dtype == "f32":
         # float32 layers run the grouped GEMM on the float32 matrix cores
         roof = {"bound": "mfma", "achieved": tfs(gemm_flops, dom_ms), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
@@ -378,6 +387,8 @@ def main():
         log("copy calibration: 3 x 1 GiB device copies done")
 
     variant = f", expert-choice routing C={C} tokens per expert" if ec else ""
+    if packed:
+        variant += ", tile-packed expert weights"
     if mx:
         variant += ", MXFP8 expert Linears (E4M3, E8M0 scale per 32)"
     if c.activation != "gelu" or not c.expert_bias or c.min_capacity:
@@ -400,7 +411,7 @@ def main():
                                f"capacity_factor={c.cf} {c.dtype}" + variant,
                    "T": T, "d": d, "h": h, "E": E, "k": k, "n_shared": S, "capacity_factor": c.cf,
                    "activation": c.activation, "expert_bias": c.expert_bias, "min_capacity": c.min_capacity,
-                   "kept_assignments": a_kept, "routing": args.routing,
+                   "kept_assignments": a_kept, "routing": args.routing, "weights_packed": packed,
                    **({"tokens_per_expert": C,
                        "untaken_tokens": T - int(torch.unique(ec_token).numel())} if ec else
                       {"dropped_assignments": T * k - a_kept})},

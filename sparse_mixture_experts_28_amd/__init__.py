@@ -16,7 +16,7 @@ from ._lib import (EXPORTS, LIB_PATH, MOE_ACT_GELU, MOE_ACT_SILU, MOE_BF16, MOE_
                    MOE_ERR_SCRATCH, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_F32, MOE_MAX_EXPERTS, MOE_MAX_SHARED,
                    MOE_MAX_TOPK, MOE_NOALLOC_SCRATCH_BYTES, MOE_NUM_STAGE_EVENTS, MOE_OK, MoeLaunch,
                    moe_expert_choice_capacity, moe_forward, moe_forward_expert_choice, moe_forward_noalloc,
-                   moe_forward_mxfp8, moe_quantize_mxfp8, moe_status_string, moe_workspace_bytes,
+                   moe_forward_mxfp8, moe_pack_weights, moe_quantize_mxfp8, moe_status_string, moe_workspace_bytes,
                    moe_workspace_bytes_expert_choice, moe_workspace_bytes_mxfp8)
 
 ACTIVATIONS = {"gelu": MOE_ACT_GELU, "silu": MOE_ACT_SILU}
@@ -103,7 +103,7 @@ def _launch(x, T, d, h, dt, b_g, workspace, zl, activation, min_capacity, stage_
 
 def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shared: int = 0, b_g=None,
             *, activation: str = "gelu", min_capacity: int = 0, stage_events: Optional[Sequence] = None,
-            workspace=None, b_sel=None, noalloc: bool = False) -> MoEOutput:
+            workspace=None, b_sel=None, noalloc: bool = False, weights_packed: bool = False) -> MoEOutput:
     """Run the layer on torch tensors that live on one GPU.
 
     x [T,d]; W_g [E,d]; W1 [E+S,h,d]; b1 [E+S,h] or None; W2 [E+S,d,h];
@@ -116,8 +116,9 @@ def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shar
     objects (already recorded once, so their handles exist) that the library
     records at its stage boundaries.  ``noalloc``: call moe_forward_noalloc,
     whose scratch is the library's fixed device array (no workspace is
-    allocated; problems beyond its size raise).  Raises RuntimeError on a
-    non-zero status.
+    allocated; problems beyond its size raise).  ``weights_packed``: W1 and
+    W2 are ``pack_weights`` outputs (same shapes and dtype; bf16, d and h
+    multiples of 256).  Raises RuntimeError on a non-zero status.
     """
     import torch
     _check_tensors(x, W_g, W1, b1, W2, b2, b_g, n_shared, activation)
@@ -148,6 +149,7 @@ def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shar
     launch.expert_counts = counts.data_ptr()
     launch.expert_kept = kept.data_ptr()
     launch.slot_pos = slot_pos.data_ptr()
+    launch.weights_packed = 1 if weights_packed else 0
     ptr = lambda t: t.data_ptr() if t is not None else None
     call = moe_forward_noalloc if noalloc else moe_forward
     status = call(x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), ptr(b1), W2.data_ptr(), ptr(b2), E, k,
@@ -179,7 +181,7 @@ def expert_choice_capacity(capacity_factor: float, T: int, E: int, min_capacity:
 
 def forward_expert_choice(x, W_g, W1, b1, W2, b2, C: int, n_shared: int = 0, b_g=None, *,
                           activation: str = "gelu", stage_events: Optional[Sequence] = None,
-                          workspace=None) -> ExpertChoiceOutput:
+                          workspace=None, weights_packed: bool = False) -> ExpertChoiceOutput:
     """Run the layer with expert-choice routing (each expert takes its C
     best-scoring tokens) on torch tensors that live on one GPU.  Arguments as
     for ``forward``; C in 1..T."""
@@ -201,6 +203,7 @@ def forward_expert_choice(x, W_g, W1, b1, W2, b2, C: int, n_shared: int = 0, b_g
     aux = torch.empty((1,), dtype=torch.float32, device=dev)
     zl = torch.empty((1,), dtype=torch.float32, device=dev)
     launch, keep = _launch(x, T, d, h, dt, b_g, workspace, zl, activation, 0, stage_events)
+    launch.weights_packed = 1 if weights_packed else 0
     ptr = lambda t: t.data_ptr() if t is not None else None
     status = moe_forward_expert_choice(x.data_ptr(), W_g.data_ptr(), W1.data_ptr(), ptr(b1), W2.data_ptr(),
                                        ptr(b2), E, C, n_shared, out.data_ptr(), ec_token.data_ptr(),
@@ -209,6 +212,21 @@ def forward_expert_choice(x, W_g, W1, b1, W2, b2, C: int, n_shared: int = 0, b_g
     if status != MOE_OK:
         raise RuntimeError(moe_status_string(status))
     return ExpertChoiceOutput(out, ec_token, ec_w, aux, zl)
+
+
+def pack_weights(w):
+    """The tile-packed layout (moe_pack_weights) of a contiguous bf16 expert
+    weight [E+S, N, K] on a GPU, N and K multiples of 256: a new tensor of the
+    same shape whose memory holds the packed blocks (for ``weights_packed``)."""
+    import torch
+    if w.dtype != torch.bfloat16 or not w.is_cuda or not w.is_contiguous() or w.dim() != 3:
+        raise ValueError("pack_weights takes a contiguous bf16 [E+S, N, K] tensor on a GPU")
+    m, N, K = w.shape
+    wp = torch.empty_like(w)
+    st = moe_pack_weights(w.data_ptr(), m, N, K, MOE_BF16, wp.data_ptr(), torch.cuda.current_stream(w.device).cuda_stream)
+    if st != MOE_OK:
+        raise RuntimeError(moe_status_string(st))
+    return wp
 
 
 def quantize_mxfp8(w):
@@ -287,7 +305,7 @@ def forward_mxfp8(x, W_g, W1, W1s, b1, W2, W2s, b2, k: int, capacity_factor: flo
 __all__ = ["forward", "MoEOutput", "moe_forward", "moe_workspace_bytes", "moe_status_string", "MoeLaunch",
            "forward_expert_choice", "ExpertChoiceOutput", "moe_forward_expert_choice",
            "moe_workspace_bytes_expert_choice", "expert_choice_capacity", "moe_expert_choice_capacity", "STAGES_EXPERT_CHOICE",
-           "quantize_mxfp8", "forward_mxfp8", "moe_quantize_mxfp8", "moe_workspace_bytes_mxfp8", "moe_forward_mxfp8",
+           "pack_weights", "moe_pack_weights", "quantize_mxfp8", "forward_mxfp8", "moe_quantize_mxfp8", "moe_workspace_bytes_mxfp8", "moe_forward_mxfp8",
            "moe_forward_noalloc", "MOE_ERR_SCRATCH", "MOE_NOALLOC_SCRATCH_BYTES", "ACTIVATIONS", "MOE_ACT_GELU", "MOE_ACT_SILU", "MOE_F32", "MOE_BF16", "MOE_OK", "MOE_ERR_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
            "MOE_ERR_HIP", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_SHARED", "MOE_NUM_STAGE_EVENTS",
            "STAGES", "EXPORTS", "LIB_PATH"]

@@ -36,7 +36,7 @@ MOE_NUM_STAGE_EVENTS = 7
 # names of the C ABI entry points (include/moe.h)
 EXPORTS = ("moe_forward", "moe_workspace_bytes", "moe_status_string", "moe_forward_expert_choice",
            "moe_workspace_bytes_expert_choice", "moe_quantize_mxfp8", "moe_workspace_bytes_mxfp8",
-           "moe_forward_mxfp8", "moe_expert_choice_capacity", "moe_forward_noalloc")
+           "moe_forward_mxfp8", "moe_expert_choice_capacity", "moe_forward_noalloc", "moe_pack_weights")
 
 
 class MoeLaunch(ctypes.Structure):
@@ -58,6 +58,7 @@ class MoeLaunch(ctypes.Structure):
         ("activation", ctypes.c_int32),
         ("min_capacity", ctypes.c_int32),
         ("b_sel", ctypes.c_void_p),
+        ("weights_packed", ctypes.c_int32),
     ]
 
 
@@ -94,6 +95,9 @@ def _load():
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(MoeLaunch),
     ]
+    lib.moe_pack_weights.restype = ctypes.c_int
+    lib.moe_pack_weights.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
     lib.moe_expert_choice_capacity.restype = ctypes.c_int32
     lib.moe_expert_choice_capacity.argtypes = [ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -155,6 +159,11 @@ def moe_forward_expert_choice(x, W_g, W1, b1, W2, b2, E, C, n_shared, out, ec_to
     """Raw call of the expert-choice entry point: every array argument is a device address (int)."""
     return int(LIB.moe_forward_expert_choice(x, W_g, W1, b1, W2, b2, E, C, n_shared, out, ec_token, ec_w,
                                              aux_loss, ctypes.byref(launch)))
+
+
+def moe_pack_weights(W, n_mat: int, N: int, K: int, dtype: int, Wp, stream) -> int:
+    """moe_pack_weights: W [n_mat, N, K] bf16 -> the tile-packed layout in Wp."""
+    return int(LIB.moe_pack_weights(W, n_mat, N, K, dtype, Wp, stream))
 
 
 def moe_quantize_mxfp8(src, rows: int, cols: int, codes, scales, stream) -> int:

@@ -56,6 +56,7 @@ struct GemmArgs {
   int nseg, E, N, K;
   float* part;           // fp32 partial tiles of the split tail (part_cap tiles of BM x 256)
   int part_cap;
+  int packed;            // W in the tile-packed layout (bf16 MFMA path only)
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -245,7 +246,13 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
       const int arow = r < rows ? (gather ? g.row_token[a_off + r] : a_off + r) : -1;
       va[q] = arow >= 0 ? static_cast<uint32_t>(arow) * row_bytes + dr_ch * 16 : 0x80000000u;
     }
-    const uint32_t vb = static_cast<uint32_t>(n0 + dr_row) * row_bytes + dr_ch * 16;
+    // B: row-major W, the lane's row and chunk; or, packed, 256-row x 64-column
+    // blocks of 32 KB each in LDS order, so a direct load is one linear 1 KB
+    // (load q of a wave at (4 (q - MB) + wave) KB of its stage's block)
+    const uint32_t vb = g.packed ? static_cast<uint32_t>(n0) * row_bytes + static_cast<uint32_t>(wave * 1024 + lane * 16)
+                                 : static_cast<uint32_t>(n0 + dr_row) * row_bytes + dr_ch * 16;
+    const uint32_t b_qs = g.packed ? 4096u : step32;               // bytes between a wave's B loads of a stage
+    const uint32_t b_ks = g.packed ? 32768u : static_cast<uint32_t>(kBK * 2);   // bytes per K step
 
     // A whole tile's accumulators start at the bias of their column (the
     // epilogue then has no bias to add); the pieces of a split tile start at
@@ -285,13 +292,14 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
     // offset ao, else B rows 32 (q - MB) + .. at offset bo
     auto issue1 = [&](int ao, int bo, int k, int q) {
       const uint32_t kbytes = static_cast<uint32_t>((k0 + k) * kBK * 2);
+      const uint32_t bk = static_cast<uint32_t>(k0 + k) * b_ks;
       if (q < MB)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ra_rsrc, (__attribute__((address_space(3))) void*)(lds + ao + wofs + 32 * q * kCh), 16, va[q], kbytes, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rb_rsrc, (__attribute__((address_space(3))) void*)(lds + bo + wofs + 32 * (q - MB) * kCh), 16, vb,
-            static_cast<uint32_t>(q - MB) * step32 + kbytes, 0, 0);
+            static_cast<uint32_t>(q - MB) * b_qs + bk, 0, 0);
     };
     auto slot_a = [&](int rs) { return rs * kStage; };
     auto slot_b = [&](int rs) { return rs * kStage + BM * kCh; };
@@ -741,7 +749,36 @@ int num_cus() {
   return n;
 }
 
+// Tile-packed weights (layout in include/moe.h): block b = (m, n / 256,
+// kk / 64) is the LDS image of one 256-row x 64-column B stage, so the GEMM's
+// direct loads of a stage read 32 KB of contiguous memory.  One workgroup per
+// block; thread t moves 16-byte chunks t, t + 256, ... (row = chunk / 8,
+// position = chunk % 8), reading the logical chunk that the GEMM's fragment
+// reads expect at that position.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ W, uint16_t* __restrict__ Wp,
+                                                           int N, int K) {
+  const int nkb = K / 64, nnb = N / 256;
+  const int b = blockIdx.x;
+  const int kb = b % nkb, nb = (b / nkb) % nnb, m = b / (nkb * nnb);
+  const uint16_t* src = W + (static_cast<size_t>(m) * N + static_cast<size_t>(nb) * 256) * K + kb * 64;
+  uint16_t* dst = Wp + static_cast<size_t>(b) * 16384;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ch = threadIdx.x + 256 * i;
+    const int r = ch >> 3, pos = ch & 7;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(r) * K + swz(r, pos) * 8);
+    *reinterpret_cast<u32x4*>(dst + r * 64 + pos * 8) = v;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pack_weights(const void* W, int n_mat, int N, int K, void* Wp, hipStream_t st) {
+  const long long blocks = static_cast<long long>(n_mat) * (N / 256) * (K / 64);
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(Wp), N, K);
+  return hipGetLastError();
+}
 
 bool gemm_fast_path(const Problem& p) {
   if (p.dtype != MOE_BF16 || p.h % kBN != 0 || p.d % kBN != 0 || p.d % kBK != 0 || p.h % kBK != 0) return false;
@@ -811,6 +848,7 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
   }
   g.part = ws.part;
   g.part_cap = ws.part_cap;
+  g.packed = p.packed_w ? 1 : 0;
   // the activation follows the first Linear only
   const int act = phase == 2 ? kActNone : (p.act == MOE_ACT_SILU ? kActSilu : kActGelu);
   if (gemm_fast_path(p)) {

@@ -143,6 +143,7 @@ Problem make_problem(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int3
   p.gemm_bm = gemm_m_tile(p);
   p.gemm_mixed = false;
   p.part_limit = kGemmPartCap;
+  p.packed_w = false;
   return p;
 }
 
@@ -178,6 +179,7 @@ Problem make_problem_ec(int32_t T, int32_t d, int32_t h, int32_t E, int32_t C, i
   p.gemm_bm = gemm_m_tile(p);
   p.gemm_mixed = false;
   p.part_limit = kGemmPartCap;
+  p.packed_w = false;
   return p;
 }
 
@@ -249,6 +251,10 @@ moe_status_t forward_top_k(const void* x, const void* W_g, const void* W1, const
   Problem p = make_problem(launch->T, launch->d, launch->h, E, k, n_shared, launch->dtype, capacity_factor,
                            launch->activation, launch->min_capacity);
   p.part_limit = part_limit;
+  if (launch->weights_packed != 0) {
+    if (launch->weights_packed != 1 || !gemm_fast_path(p)) return MOE_ERR_UNSUPPORTED;
+    p.packed_w = true;
+  }
   bool ok = false;
   Workspace ws = carve_workspace(p, ws_base, ws_bytes, &ok);
   if (!ok) return MOE_ERR_WORKSPACE;
@@ -349,6 +355,7 @@ moe_status_t moe_forward_mxfp8(const void* x, const void* W_g, const uint8_t* W1
   if (std::isnan(capacity_factor) || launch->min_capacity < 0) return MOE_ERR_ARG;
   if (launch->activation != MOE_ACT_GELU && launch->activation != MOE_ACT_SILU) return MOE_ERR_UNSUPPORTED;
   if (launch->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (launch->weights_packed != 0) return MOE_ERR_UNSUPPORTED;   // MX codes have their own layout
   const moe_status_t sc = check_shape_mx(launch->T, launch->d, launch->h, E, k, n_shared);
   if (sc != MOE_OK) return sc;
   const void* a16[] = {x, W_g, W1, W2, out, b1, b2};
@@ -399,6 +406,29 @@ size_t moe_workspace_bytes_expert_choice(int32_t T, int32_t d, int32_t h, int32_
                                          moe_dtype_t dtype) {
   if (moe::check_shape_ec(T, d, h, E, C, n_shared, static_cast<int>(dtype)) != MOE_OK) return 0;
   return moe::workspace_bytes(moe::make_problem_ec(T, d, h, E, C, n_shared, dtype));
+}
+
+moe_status_t moe_pack_weights(const void* W, int32_t n_mat, int32_t N, int32_t K, moe_dtype_t dtype, void* Wp,
+                              hipStream_t stream) {
+  using namespace moe;
+  if (W == nullptr || Wp == nullptr || n_mat < 1 || N < 1 || K < 1) return MOE_ERR_ARG;
+  if (dtype != MOE_BF16 || N % 256 != 0 || K % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  // each matrix within one buffer descriptor's 32-bit range (the GEMM's B
+  // operand), and a launchable number of 32 KB blocks
+  if (static_cast<long long>(N) * K * 2 >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
+  const long long elems = static_cast<long long>(n_mat) * N * K;
+  if (elems / 16384 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(W, 16) || !aligned(Wp, 16)) return MOE_ERR_UNSUPPORTED;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(W), b0 = reinterpret_cast<uintptr_t>(Wp);
+  const uintptr_t len = static_cast<uintptr_t>(elems) * 2u;
+  if (a0 < b0 + len && b0 < a0 + len) return MOE_ERR_ARG;   // overlapping buffers
+  (void)hipGetLastError();
+  const hipError_t e = launch_pack_weights(W, n_mat, N, K, Wp, stream);
+  if (e != hipSuccess) {
+    std::fprintf(stderr, "libmoe: weight packing launch failed: %s\n", hipGetErrorName(e));
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
 }
 
 const char* moe_status_string(moe_status_t s) {
@@ -465,8 +495,11 @@ moe_status_t moe_forward_expert_choice(const void* x, const void* W_g, const voi
   for (const void* q : a4)
     if (q && !aligned(q, 4)) return MOE_ERR_UNSUPPORTED;
 
-  const Problem p = make_problem_ec(launch->T, launch->d, launch->h, E, C, n_shared, launch->dtype,
-                                    launch->activation);
+  Problem p = make_problem_ec(launch->T, launch->d, launch->h, E, C, n_shared, launch->dtype, launch->activation);
+  if (launch->weights_packed != 0) {
+    if (launch->weights_packed != 1 || !gemm_fast_path(p)) return MOE_ERR_UNSUPPORTED;
+    p.packed_w = true;
+  }
   bool ok = false;
   Workspace ws = carve_workspace(p, launch->workspace, launch->workspace_bytes, &ok);
   if (!ok) return MOE_ERR_WORKSPACE;

@@ -225,6 +225,7 @@ struct Problem {
   int gemm_bm;   // M tile of the grouped GEMM (for the tile prefix)
   bool gemm_mixed;   // MXFP8 GEMM: per-segment heights by mx_mixed_tile_height (gemm_bm unused)
   int part_limit;    // float32 partial tiles the workspace reserves for the GEMM's split tail
+  bool packed_w;     // W1, W2 in the tile-packed layout (moe_pack_weights)
 };
 
 Workspace carve_workspace(const Problem& p, void* base, size_t bytes_available, bool* ok);
@@ -269,6 +270,8 @@ hipError_t launch_expert_ffn_mx(const Problem& p, const MxWeights& w, const Work
 
 // Which GEMM kernel serves a problem; the M tile decides the tile prefix.
 bool gemm_fast_path(const Problem& p);
+// W [n_mat, N, K] bf16 -> the tile-packed layout of include/moe.h (N, K multiples of 256)
+hipError_t launch_pack_weights(const void* W, int n_mat, int N, int K, void* Wp, hipStream_t st);
 int gemm_m_tile(const Problem& p);
 // router logits (bf16, d % 256 == 0, more than 64 experts): expert padding
 // and split-K factor, which size the float64 partial-logit workspace

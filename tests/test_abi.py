@@ -33,13 +33,14 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_launch_struct_layout():
-    # int32 T, d, h; enum dtype; then 8-byte pointers / size_t; z_loss; int32 activation, min_capacity; b_sel
+    # int32 T, d, h; enum dtype; then 8-byte pointers / size_t; z_loss; int32 activation, min_capacity; b_sel;
+    # int32 weights_packed (padded to 8)
     L = moe.MoeLaunch
     assert L.T.offset == 0 and L.d.offset == 4 and L.h.offset == 8 and L.dtype.offset == 12
     assert L.b_g.offset == 16 and L.workspace_bytes.offset == 56 and L.stream.offset == 64
     assert L.stage_events.offset == 72 and L.z_loss.offset == 80
     assert L.activation.offset == 88 and L.min_capacity.offset == 92
-    assert L.b_sel.offset == 96 and ctypes.sizeof(L) == 104
+    assert L.b_sel.offset == 96 and L.weights_packed.offset == 104 and ctypes.sizeof(L) == 112
 
 
 def test_launch_struct_matches_header(tmp_path):
@@ -114,7 +115,7 @@ def call(**kw):
     args = dict(x=FAKE, W_g=FAKE, W1=FAKE, b1=FAKE, W2=FAKE, b2=FAKE, E=8, k=2, cf=0.0, S=0, out=FAKE,
                 idx=FAKE, w=FAKE, aux=FAKE)
     lk = dict(T=64, d=32, h=64, dtype=moe.MOE_BF16, workspace=FAKE, workspace_bytes=0, z_loss=None,
-              activation=moe.MOE_ACT_GELU, min_capacity=0, b_sel=None)
+              activation=moe.MOE_ACT_GELU, min_capacity=0, b_sel=None, weights_packed=0)
     for key in list(kw):
         if key in lk:
             lk[key] = kw.pop(key)
@@ -124,6 +125,7 @@ def call(**kw):
     L.workspace = lk["workspace"]
     L.z_loss, L.activation, L.min_capacity = lk["z_loss"], lk["activation"], lk["min_capacity"]
     L.b_sel = lk["b_sel"]
+    L.weights_packed = lk["weights_packed"]
     need = moe.moe_workspace_bytes(L.T, L.d, L.h, args["E"], args["k"], args["S"], L.dtype)
     L.workspace_bytes = lk["workspace_bytes"] if lk["workspace_bytes"] else need
     return moe.moe_forward(args["x"], args["W_g"], args["W1"], args["b1"], args["W2"], args["b2"], args["E"],
@@ -165,9 +167,39 @@ def test_null_launch():
     (dict(min_capacity=4, cf=1.0, workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
     (dict(activation=moe.MOE_ACT_SILU, workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
     (dict(b_sel=FAKE + 2), moe.MOE_ERR_UNSUPPORTED), (dict(b_sel=FAKE, workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
+    # tile-packed weights: bf16 with d and h multiples of 256 only
+    (dict(weights_packed=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(weights_packed=1, d=256, h=512, dtype=moe.MOE_F32), moe.MOE_ERR_UNSUPPORTED),
+    (dict(weights_packed=2, d=256, h=512), moe.MOE_ERR_UNSUPPORTED),
+    (dict(weights_packed=1, d=256, h=512, workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
 ])
 def test_rejected_on_host(kw, code):
     assert call(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 2, 256, 256, "bf16", FAKE * 64), moe.MOE_ERR_ARG),
+    ((FAKE, 2, 256, 256, "bf16", None), moe.MOE_ERR_ARG),
+    ((FAKE, 0, 256, 256, "bf16", FAKE * 64), moe.MOE_ERR_ARG),
+    ((FAKE, 2, 256, 256, "f32", FAKE * 64), moe.MOE_ERR_UNSUPPORTED),
+    ((FAKE, 2, 320, 256, "bf16", FAKE * 64), moe.MOE_ERR_UNSUPPORTED),
+    ((FAKE, 2, 256, 192, "bf16", FAKE * 64), moe.MOE_ERR_UNSUPPORTED),
+    ((FAKE + 8, 2, 256, 256, "bf16", FAKE * 64), moe.MOE_ERR_UNSUPPORTED),
+    ((FAKE, 2, 256, 256, "bf16", FAKE + 1024), moe.MOE_ERR_ARG),          # overlapping buffers
+    ((FAKE, 2, 65536, 32768, "bf16", FAKE * 64), moe.MOE_ERR_UNSUPPORTED),  # a 4 GiB matrix
+])
+def test_pack_weights_rejected_on_host(args, code):
+    W, m, N, K, dt, Wp = args
+    dtype = moe.MOE_BF16 if dt == "bf16" else moe.MOE_F32
+    assert moe.moe_pack_weights(W, m, N, K, dtype, Wp, None) == code
+
+
+def test_mxfp8_rejects_packed_flag():
+    L = moe.MoeLaunch()
+    L.T, L.d, L.h, L.dtype = 64, 256, 256, moe.MOE_BF16
+    L.weights_packed = 1
+    st = moe.moe_forward_mxfp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 2, 0.0, 0, FAKE, FAKE, FAKE, FAKE, L)
+    assert st == moe.MOE_ERR_UNSUPPORTED
 
 
 # ------------------------------------------------------------ expert choice --

@@ -3,9 +3,9 @@
 erfc(u / sqrt 2) = exp2(Q(u)) for u = |v| in [0, 6], Q(u) = sum_{k=1..9} c_k u^k
 (no constant term, so erf(0) = 0 exactly).  Fitted by least squares on 8000
 Chebyshev nodes, each residual weighted by u erfc(u / sqrt 2), the size of its
-effect on GELU(v) = (v + |v| erf(|v| / sqrt 2)) / 2.  Evaluated in float32 as
-the kernel does, the result is within 4.2e-7 of GELU in absolute terms and
-1.1e-7 |v| over [-10, 10] (checked by tests/test_gelu_fast.py).
+effect on GELU(v) = max(v, 0) - |v| erfc(|v| / sqrt 2) / 2.  Evaluated in
+float32 as the kernel does, the result is within 2.5e-7 of GELU in absolute
+terms and 1.3e-7 |v| over [-10, 10] (checked by tests/test_gelu_fast.py).
 
     python sparse_mixture_experts_28_amd/csrc/fit_gelu.py   # prints the c_k
 """

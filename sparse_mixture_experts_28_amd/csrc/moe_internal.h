@@ -44,13 +44,14 @@ __device__ __forceinline__ float silu_fast(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.44269504088896341f));
 }
 
-// GELU(v) = v/2 (1 + erf(v / sqrt 2)) = (v + |v| erf(|v| / sqrt 2)) / 2, with
-// erf(u / sqrt 2) = 1 - exp2(Q(u)) for u = min(|v|, 6) and Q a degree-9
+// GELU(v) = v Phi(v) = max(v, 0) - |v| erfc(|v| / sqrt 2) / 2, with
+// erfc(u / sqrt 2) = exp2(u Q(u)) for u = min(|v|, 6) and u Q(u) a degree-9
 // polynomial fit of log2 erfc(u / sqrt 2) without a constant term (the fit is
-// csrc/fit_gelu.py).  Within 4.2e-7 absolute and 1.1e-7 |v| of GELU in float32;
-// one exp2 and 13 VALU operations (the rational erf it replaced needed a
-// reciprocal as well, and the epilogue of the first Linear is VALU-bound).
-// +inf gives +inf, NaN gives NaN, -inf gives NaN as the exact form does.
+// csrc/fit_gelu.py).  Past |v| = 6 the correction term is below 1e-8 and u
+// stands in for |v| in it.  Within 2.5e-7 absolute and 1.3e-7 |v| of GELU in
+// float32; one exp2 and 12 VALU operations (the epilogue of the first Linear
+// is VALU-bound).  The maximum propagates NaN, so NaN gives NaN and +inf
+// gives +inf; -inf gives about -6e-9 (the limit is 0; the erf form gives NaN).
 __device__ __forceinline__ float gelu_fast(float v) {
   const float u = __builtin_amdgcn_fmed3f(fabsf(v), 0.0f, 6.0f);   // min(|v|, 6); NaN gives 6
   float q = fmaf(u, 1.934985789e-07f, -4.592050573e-06f);
@@ -61,8 +62,8 @@ __device__ __forceinline__ float gelu_fast(float v) {
   q = fmaf(u, q, -5.258556455e-02f);
   q = fmaf(u, q, -4.591732323e-01f);
   q = fmaf(u, q, -1.151110053e+00f);
-  const float erf_u = 1.0f - __builtin_amdgcn_exp2f(q * u);
-  return 0.5f * fmaf(fabsf(v), erf_u, v);
+  const float e = __builtin_amdgcn_exp2f(fmaf(q, u, -1.0f));      // erfc(u / sqrt 2) / 2
+  return fmaf(-u, e, __builtin_elementwise_maximum(v, 0.0f));
 }
 
 // ----------------------------------------------------- workspace layout --

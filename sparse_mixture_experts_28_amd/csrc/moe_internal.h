@@ -45,23 +45,20 @@ __device__ __forceinline__ float silu_fast(float v) {
 }
 
 // GELU(v) = v Phi(v) = max(v, 0) - |v| erfc(|v| / sqrt 2) / 2, with
-// erfc(u / sqrt 2) = exp2(u Q(u)) for u = min(|v|, 6) and u Q(u) a degree-9
+// erfc(u / sqrt 2) = exp2(u Q(u)) for u = min(|v|, 6) and u Q(u) a degree-6
 // polynomial fit of log2 erfc(u / sqrt 2) without a constant term (the fit is
 // csrc/fit_gelu.py).  Past |v| = 6 the correction term is below 1e-8 and u
-// stands in for |v| in it.  Within 2.5e-7 absolute and 1.3e-7 |v| of GELU in
-// float32; one exp2 and 12 VALU operations (the epilogue of the first Linear
+// stands in for |v| in it.  Within 2.5e-7 absolute and 4.8e-7 |v| of GELU in
+// float32; one exp2 and 9 VALU operations (the epilogue of the first Linear
 // is VALU-bound).  The maximum propagates NaN, so NaN gives NaN and +inf
 // gives +inf; -inf gives about -6e-9 (the limit is 0; the erf form gives NaN).
 __device__ __forceinline__ float gelu_fast(float v) {
   const float u = __builtin_amdgcn_fmed3f(fabsf(v), 0.0f, 6.0f);   // min(|v|, 6); NaN gives 6
-  float q = fmaf(u, 1.934985789e-07f, -4.592050573e-06f);
-  q = fmaf(u, q, 4.332197204e-05f);
-  q = fmaf(u, q, -1.772511459e-04f);
-  q = fmaf(u, q, -1.936358894e-04f);
-  q = fmaf(u, q, 7.167997304e-03f);
-  q = fmaf(u, q, -5.258556455e-02f);
-  q = fmaf(u, q, -4.591732323e-01f);
-  q = fmaf(u, q, -1.151110053e+00f);
+  float q = fmaf(u, 3.228566493e-05f, -7.544446853e-04f);
+  q = fmaf(u, q, 8.004920557e-03f);
+  q = fmaf(u, q, -5.324933678e-02f);
+  q = fmaf(u, q, -4.589283466e-01f);
+  q = fmaf(u, q, -1.151139259e+00f);
   const float e = __builtin_amdgcn_exp2f(fmaf(q, u, -1.0f));      // erfc(u / sqrt 2) / 2
   return fmaf(-u, e, __builtin_elementwise_maximum(v, 0.0f));
 }

@@ -15,8 +15,8 @@
 // Both operands are K-contiguous (A rows and nn.Linear weight rows), so
 // C = A B^T is the "NT" product that MFMA prefers.  Tiles are BM x 256 with
 // K steps of 64, BM in {128, 160, 256} chosen per problem; accumulation is
-// float32 on the 16x16x32 bf16 MFMA; the epilogue adds the bias and (phase 1)
-// applies the activation in float32 and rounds once to bf16.  The tail of a
+// float32 on the 16x16x32 bf16 MFMA, starting from the bias; the epilogue
+// (phase 1) applies the activation in float32 and rounds once to bf16.  The tail of a
 // persistent launch is split along K (stream-K style) with a deterministic
 // fix-up.
 //
@@ -181,7 +181,7 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
   // wave-uniform, so the LDS addresses of the direct loads (M0) are scalar arithmetic
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
+  const SegTableRO st = seg_table_ro(g.seg, g.nseg, g.E);
   const int total_mt = uniform(st.tile_start[g.nseg]);
   const int ntn = g.N / kBN;
   const int total = total_mt * ntn;
@@ -470,7 +470,7 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
 // (phase 1) and one bf16 rounding, as in the GEMM epilogue.
 template <int ACT, int BM>
 __global__ __launch_bounds__(256) void gemm_tail_fixup_kernel(GemmArgs g, int P) {
-  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
+  const SegTableRO st = seg_table_ro(g.seg, g.nseg, g.E);
   const int total_mt = st.tile_start[g.nseg];
   const int ntn = g.N / kBN;
   const TailPlan tp = tail_plan(total_mt * ntn, P, g.K / kBK, g.part_cap);
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(GemmArgs g) {
   __shared__ float4 sA[2][BM][LDP / 4];
   __shared__ float4 sB[2][kFBN][LDP / 4];
 
-  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
+  const SegTableRO st = seg_table_ro(g.seg, g.nseg, g.E);
   const int total_mt = st.tile_start[g.nseg];
   const int mt = blockIdx.x;
   if (mt >= total_mt) return;
@@ -681,7 +681,7 @@ template <typename TIn, int ACT>
 __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmArgs g, int max_mt) {
   __shared__ float sA[kSK][kSB + 1];
   __shared__ float sB[kSK][kSB + 1];
-  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
+  const SegTableRO st = seg_table_ro(g.seg, g.nseg, g.E);
   const int total_mt = st.tile_start[g.nseg];
   const int mt = blockIdx.x;
   if (mt >= total_mt) return;

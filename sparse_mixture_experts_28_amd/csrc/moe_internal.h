@@ -123,6 +123,22 @@ __host__ __device__ inline SegTable seg_table(int32_t* base, int nseg, int E) {
 }
 inline size_t seg_table_ints(int nseg, int E) { return static_cast<size_t>(5 * nseg + 1 + E); }
 
+// The segment table as a kernel that only reads it sees it: in the constant
+// address space, so lookups at a uniform index are scalar loads (the scalar
+// cache, no vector-memory wait; the table is written by an earlier launch).
+typedef const __attribute__((address_space(4))) int32_t cint32_t;
+struct SegTableRO {
+  cint32_t* rows;
+  cint32_t* a_off;
+  cint32_t* o_off;
+  cint32_t* tile_start;
+  cint32_t* tile_bm;
+};
+__device__ inline SegTableRO seg_table_ro(const int32_t* base, int nseg, int E) {
+  cint32_t* c = (cint32_t*)base;
+  return SegTableRO{c, c + nseg, c + 2 * nseg, c + 3 * nseg, c + 4 * nseg + 1 + E};
+}
+
 // Per-segment tile heights of the MXFP8 GEMM (Problem::gemm_mixed): a
 // segment of r rows takes 192-row tiles only when they cut its tiles by more
 // than a third, 3 ceil(r / 192) < 2 ceil(r / 128) (r in 129..192, 513..576,
@@ -186,7 +202,8 @@ __device__ __forceinline__ TailPlan tail_plan(int total, int P, int nk, int part
 
 // Segment of M tile mt: the last segment whose first tile is <= mt (empty
 // segments share their successor's first tile and are passed over).
-__device__ __forceinline__ int find_segment(const int32_t* tile_start, int nseg, int mt) {
+template <typename Ptr>
+__device__ __forceinline__ int find_segment(Ptr tile_start, int nseg, int mt) {
   int lo = 0, hi = nseg - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -201,7 +218,8 @@ __device__ __forceinline__ int find_segment(const int32_t* tile_start, int nseg,
 // experts) use it: the contiguous run of tiles an XCD takes per round then
 // covers few experts, whose weight panels (shared by the expert's M tiles)
 // and row panels (shared by its N tiles) stay in that XCD's L2.
-__device__ __forceinline__ int tile_of_expert(int L, const int32_t* tile_start, int nseg, int ntn, int& mt, int& nt) {
+template <typename Ptr>
+__device__ __forceinline__ int tile_of_expert(int L, Ptr tile_start, int nseg, int ntn, int& mt, int& nt) {
   const int s = find_segment(tile_start, nseg, L / ntn);
   const int t0 = tile_start[s], mts = tile_start[s + 1] - t0;
   const int local = L - t0 * ntn;

@@ -190,7 +190,7 @@ struct MxGeom {
 // k0 + kn - 1; piece >= 0 marks a piece of a split tail tile, which leaves a
 // float32 partial tile at rows PBM piece .. of the partial buffer.
 template <int ACT, int BM, int SG, int PBM>
-__device__ __forceinline__ void mx_tile(const MxArgs& g, u32x4* lds, const SegTable& st, int s, int mt, int nt,
+__device__ __forceinline__ void mx_tile(const MxArgs& g, u32x4* lds, const SegTableRO& st, int s, int mt, int nt,
                                         int k0, int kn, int piece) {
   using Geo = MxGeom<BM, SG>;
   constexpr bool kMxOut = ACT != 0;           // phase 1 writes H as MX
@@ -543,7 +543,7 @@ void gemm_mx_kernel(MxArgs g) {
   __shared__ u32x4 lds[kW0 > kW1 ? kW0 : kW1];
   static_assert(sizeof(lds) <= 160 * 1024, "LDS");
 
-  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
+  const SegTableRO st = seg_table_ro(g.seg, g.nseg, g.E);
   const int total_mt = __builtin_amdgcn_readfirstlane(st.tile_start[g.nseg]);
   const int ntn = g.N / kMxBN;
   const int total = total_mt * ntn;
@@ -590,7 +590,7 @@ template <int ACT, int BM0, int BM1>
 __global__ __launch_bounds__(256) void mx_tail_fixup_kernel(MxArgs g, int P) {
   constexpr bool kMxOut = ACT != 0;
   constexpr int PBM = BM1 > BM0 ? BM1 : BM0;
-  const SegTable st = seg_table(const_cast<int32_t*>(g.seg), g.nseg, g.E);
+  const SegTableRO st = seg_table_ro(g.seg, g.nseg, g.E);
   const int total_mt = st.tile_start[g.nseg];
   const int ntn = g.N / kMxBN;
   const TailPlan tp = tail_plan(total_mt * ntn, P, g.K / kMxBK, g.part_cap);

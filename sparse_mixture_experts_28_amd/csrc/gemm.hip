@@ -738,17 +738,6 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmArgs g, int max_mt) 
   }
 }
 
-int num_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
-
 // Tile-packed weights (layout in include/moe.h): block b = (m, n / 256,
 // kk / 64) is the LDS image of one 256-row x 64-column B stage, so the GEMM's
 // direct loads of a stage read 32 KB of contiguous memory.  One workgroup per
@@ -852,7 +841,7 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
   // the activation follows the first Linear only
   const int act = phase == 2 ? kActNone : (p.act == MOE_ACT_SILU ? kActSilu : kActGelu);
   if (gemm_fast_path(p)) {
-    int grid = num_cus();
+    int grid = device_cu_count();
     grid = (grid + 7) / 8 * 8;
     const dim3 gd(grid), bd(256);
     // the fix-up runs right after the GEMM on the same stream; it returns at

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "moe.h"
 
 namespace moe {
@@ -226,6 +228,21 @@ __device__ __forceinline__ int tile_of_expert(int L, Ptr tile_start, int nseg, i
   mt = t0 + local % mts;
   nt = local / mts;
   return s;
+}
+
+// Compute units of the calling thread's current device (the persistent GEMM
+// grids run one workgroup per CU), queried once per device and kept for the
+// process; 256 (MI355X) if the query fails.
+inline int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  int n = dev < kMaxDevices ? cached[dev].load(std::memory_order_relaxed) : 0;
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 struct Problem {

@@ -642,17 +642,6 @@ __global__ __launch_bounds__(256) void mx_tail_fixup_kernel(MxArgs g, int P) {
   }
 }
 
-int mx_num_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
-
 }  // namespace
 
 hipError_t launch_mx_quantize(const uint16_t* src, int rows, int cols, uint8_t* codes, uint8_t* scales,
@@ -706,7 +695,7 @@ hipError_t launch_expert_ffn_mx(const Problem& p, const MxWeights& w, const Work
   }
   g.part = ws.part;
   g.part_cap = ws.part_cap;
-  int grid = mx_num_cus();
+  int grid = device_cu_count();
   grid = (grid + 7) / 8 * 8;
   const int act = phase == 2 ? 0 : (p.act == MOE_ACT_SILU ? 2 : 1);
   // the fix-up runs right after the GEMM on the same stream; it returns at

@@ -94,8 +94,9 @@ typedef struct {
                              256-byte aligned; contents need not be initialised */
   size_t workspace_bytes;
   hipStream_t stream;     /* stream all kernels are enqueued on (0 = default stream) */
-  hipEvent_t* stage_events; /* NULL, or MOE_NUM_STAGE_EVENTS created events that are
-                               recorded on `stream` at the stage boundaries */
+  hipEvent_t* stage_events; /* NULL, or an array of MOE_NUM_STAGE_EVENTS events recorded on
+                               `stream` at the stage boundaries; a NULL entry is skipped
+                               (each event recorded costs a few microseconds of the layer) */
   float* z_loss;          /* [1] out, or NULL: router z-loss (1/T) sum_t (log sum_e exp l[t,e])^2,
                              logits including b_g, unscaled (float64 partials, one rounding) */
   int32_t activation;     /* moe_activation_t of every expert, routed and shared;

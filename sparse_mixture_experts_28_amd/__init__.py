@@ -93,8 +93,8 @@ def _launch(x, T, d, h, dt, b_g, workspace, zl, activation, min_capacity, stage_
     if stage_events is not None:
         if len(stage_events) != MOE_NUM_STAGE_EVENTS:
             raise ValueError(f"stage_events needs {MOE_NUM_STAGE_EVENTS} events")
-        handles = [int(e.cuda_event) for e in stage_events]
-        if not all(handles):
+        handles = [0 if e is None else int(e.cuda_event) for e in stage_events]
+        if not all(h for h, e in zip(handles, stage_events) if e is not None):
             raise ValueError("record each stage event once before passing it (creates its handle)")
         ev_arr = (ctypes.c_void_p * MOE_NUM_STAGE_EVENTS)(*handles)
         launch.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
@@ -113,8 +113,8 @@ def forward(x, W_g, W1, b1, W2, b2, k: int, capacity_factor: float = 0.0, n_shar
     ``activation`` is "gelu" or "silu"; ``min_capacity`` floors the capacity
     when capacity_factor > 0.
     ``stage_events``: optional list of MOE_NUM_STAGE_EVENTS torch.cuda.Event
-    objects (already recorded once, so their handles exist) that the library
-    records at its stage boundaries.  ``noalloc``: call moe_forward_noalloc,
+    objects (already recorded once, so their handles exist) or None entries
+    (skipped) that the library records at its stage boundaries.  ``noalloc``: call moe_forward_noalloc,
     whose scratch is the library's fixed device array (no workspace is
     allocated; problems beyond its size raise).  ``weights_packed``: W1 and
     W2 are ``pack_weights`` outputs (same shapes and dtype; bf16, d and h

@@ -211,13 +211,17 @@ Problem make_problem_mx(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, i
   return p;
 }
 
-// Records the optional stage events and reports a failed launch by stage.
+// Records the optional stage events (a NULL entry is skipped) and reports a
+// failed launch by stage.
 struct StageCheck {
   hipStream_t st;
   hipEvent_t* ev;
   int ei = 0;
   bool operator()(hipError_t e, const char* stage) {
-    if (e == hipSuccess && ev != nullptr) e = hipEventRecord(ev[ei++], st);
+    if (e == hipSuccess && ev != nullptr) {
+      if (ev[ei] != nullptr) e = hipEventRecord(ev[ei], st);
+      ++ei;
+    }
     if (e != hipSuccess) {
       std::fprintf(stderr, "libmoe: %s failed: %s (%s)\n", stage, hipGetErrorName(e), hipGetErrorString(e));
       return false;

@@ -497,14 +497,34 @@ __global__ __launch_bounds__(256) void gemm_tail_fixup_kernel(GemmArgs g, int P)
     const float b0 = __uint_as_float(b.x << 16), b1 = __uint_as_float(b.x & 0xffff0000u);
     const float b2 = __uint_as_float(b.y << 16), b3 = __uint_as_float(b.y & 0xffff0000u);
     const float* part = g.part + static_cast<size_t>(tt) * tp.S * BM * kBN;
+    // every partial of the thread's four rows is loaded before any is added
+    // (up to kFixS pieces at a time), then summed in piece order
+    constexpr int kFixS = 8;
+    floatx4 a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < tp.S; p0 += kFixS) {
+      floatx4 v[4][kFixS];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int rr = r0 + (threadIdx.x >> 6) + 4 * k;
+#pragma unroll
+        for (int p = 0; p < kFixS; ++p)
+          v[k][p] = m0 + rr < rows && p0 + p < tp.S
+                        ? *reinterpret_cast<const floatx4*>(part + (static_cast<size_t>(p0 + p) * BM + rr) * kBN + c)
+                        : floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int p = 0; p < kFixS; ++p)
+          if (p0 + p < tp.S) a[k] = p0 + p == 0 ? v[k][p] : a[k] + v[k][p];
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int rr = r0 + (threadIdx.x >> 6) + 4 * k;
       if (m0 + rr >= rows) break;
-      floatx4 a = *reinterpret_cast<const floatx4*>(part + static_cast<size_t>(rr) * kBN + c);
-      for (int p = 1; p < tp.S; ++p)
-        a += *reinterpret_cast<const floatx4*>(part + (static_cast<size_t>(p) * BM + rr) * kBN + c);
-      float v0 = a[0] + b0, v1 = a[1] + b1, v2 = a[2] + b2, v3 = a[3] + b3;
+      float v0 = a[k][0] + b0, v1 = a[k][1] + b1, v2 = a[k][2] + b2, v3 = a[k][3] + b3;
       v0 = act_fast<ACT>(v0);
       v1 = act_fast<ACT>(v1);
       v2 = act_fast<ACT>(v2);

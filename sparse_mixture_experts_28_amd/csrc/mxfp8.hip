@@ -613,15 +613,35 @@ __global__ __launch_bounds__(256) void mx_tail_fixup_kernel(MxArgs g, int P) {
     const float b0 = __uint_as_float(b.x << 16), b1 = __uint_as_float(b.x & 0xffff0000u);
     const float b2 = __uint_as_float(b.y << 16), b3 = __uint_as_float(b.y & 0xffff0000u);
     const float* part = g.part + static_cast<size_t>(tt) * tp.S * PBM * kMxBN;
+    // every partial of the thread's four rows is loaded before any is added
+    // (up to kFixS pieces at a time), then summed in piece order
+    constexpr int kFixS = 8;
+    floatx4 a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < tp.S; p0 += kFixS) {
+      floatx4 v[4][kFixS];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int rr = r0 + (threadIdx.x >> 6) + 4 * k;
+#pragma unroll
+        for (int p = 0; p < kFixS; ++p)
+          v[k][p] = m0 + rr < rows && p0 + p < tp.S
+                        ? *reinterpret_cast<const floatx4*>(part + (static_cast<size_t>(p0 + p) * PBM + rr) * kMxBN + c)
+                        : floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int p = 0; p < kFixS; ++p)
+          if (p0 + p < tp.S) a[k] = p0 + p == 0 ? v[k][p] : a[k] + v[k][p];
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int rr = r0 + (threadIdx.x >> 6) + 4 * k;   // one row per wave: the lanes of a block agree
       if (m0 + rr >= rows) break;
-      floatx4 a = *reinterpret_cast<const floatx4*>(part + static_cast<size_t>(rr) * kMxBN + c);
-      for (int p = 1; p < tp.S; ++p)
-        a += *reinterpret_cast<const floatx4*>(part + (static_cast<size_t>(p) * PBM + rr) * kMxBN + c);
-      const float v0 = mx_act<ACT>(a[0] + b0), v1 = mx_act<ACT>(a[1] + b1);
-      const float v2 = mx_act<ACT>(a[2] + b2), v3 = mx_act<ACT>(a[3] + b3);
+      const float v0 = mx_act<ACT>(a[k][0] + b0), v1 = mx_act<ACT>(a[k][1] + b1);
+      const float v2 = mx_act<ACT>(a[k][2] + b2), v3 = mx_act<ACT>(a[k][3] + b3);
       const size_t row = static_cast<size_t>(o_off + m0 + rr);
       if constexpr (kMxOut) {
         float am = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));

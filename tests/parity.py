@@ -200,7 +200,7 @@ def compare_ec(inp, C: int, gpu: dict, stacked=None, rows=None, check_out=True) 
 # ------------------------------------------------------------------- MXFP8 --
 def _host_threads() -> int:
     """Worker threads for host-side oracle work: the cores this process may
-    use, at most 16 (a one-GPU machine's CPU share)."""
+    use, at most 16 (the CPU share of a one-GPU node)."""
     import os
     return max(1, min(16, len(os.sched_getaffinity(0))))
 

@@ -26,9 +26,11 @@
  *
  * Conventions
  *   - Every pointer argument is a DEVICE pointer owned by the caller.  The
- *     library allocates no device memory, keeps no state between calls and
- *     never synchronises: moe_forward enqueues its kernels on launch->stream
- *     and returns.  Calls on different streams need distinct workspaces.
+ *     library allocates no device memory, keeps no state between calls that
+ *     affects a result (it caches two per-device lookups: the CU count and,
+ *     for moe_forward_noalloc, its fixed scratch array's address) and never
+ *     synchronises: moe_forward enqueues its kernels on launch->stream and
+ *     returns.  Calls on different streams need distinct workspaces.
  *   - Matrices are row-major.  Weight matrices use the nn.Linear (out, in)
  *     layout.  dtype applies to x, W_g, W1, b1, W2, b2 and out: MOE_F32 is
  *     IEEE float32, MOE_BF16 is bfloat16 (uint16 bit patterns).

@@ -75,38 +75,69 @@ __device__ __forceinline__ void write_ec(const RouterArgs& a, const double (&val
   }
 }
 
-// 16-lane argmax: larger value wins, equal values go to the lower index.
-__device__ __forceinline__ void argmax16(double& v, int& i) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    double ov = __shfl_xor(v, m, 16);
-    int oi = __shfl_xor(i, m, 16);
-    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
-  }
+// 16-lane reductions through DPP row moves instead of LDS permutes (a
+// ds_bpermute per value and step costs an LDS round trip on the selection's
+// critical path).  The four steps exchange between lanes i and i ^ 1, i ^ 2
+// (quad_perm), then between the two quads of each half row (row_half_mirror:
+// lane i and 7 - i) and the two halves of the row (row_mirror: lane i and
+// 15 - i).  After the first two steps a quad's lanes hold equal values, so
+// the mirrors pair the same partial results as the exchanges i ^ 4 and i ^ 8,
+// with each lane's own value on the same side of the operation: the results
+// are those of the plain butterfly, bit for bit.  A DPP row is 16 lanes, the
+// token's lane group.
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, v);
+  const unsigned lo = static_cast<unsigned>(dpp_i<CTRL>(static_cast<int>(static_cast<unsigned>(b))));
+  const unsigned hi = static_cast<unsigned>(dpp_i<CTRL>(static_cast<int>(static_cast<unsigned>(b >> 32))));
+  return __builtin_bit_cast(double, (static_cast<unsigned long long>(hi) << 32) | lo);
 }
 
-// argmax16 carrying a payload (the winner's plain logit when the ranking
-// includes the selection-only bias)
+// one argmax step: the other lane's (value, index, payload) wins if its value
+// is larger, or equal with a lower index
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(double& v, int& i, double& pl) {
+  const double ov = dpp_d<CTRL>(v);
+  const int oi = dpp_i<CTRL>(i);
+  const double op = dpp_d<CTRL>(pl);
+  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; pl = op; }
+}
+
+// 16-lane argmax carrying a payload (the winner's plain logit when the
+// ranking includes the selection-only bias): larger value wins, equal values
+// go to the lower index
 __device__ __forceinline__ void argmax16p(double& v, int& i, double& pl) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    double ov = __shfl_xor(v, m, 16);
-    int oi = __shfl_xor(i, m, 16);
-    double op = __shfl_xor(pl, m, 16);
-    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; pl = op; }
-  }
+  argmax_step<kDppXor1>(v, i, pl);
+  argmax_step<kDppXor2>(v, i, pl);
+  argmax_step<kDppHalfMirror>(v, i, pl);
+  argmax_step<kDppMirror>(v, i, pl);
 }
 
 __device__ __forceinline__ double max16(double v) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) v = fmax(v, __shfl_xor(v, m, 16));
-  return v;
+  v = fmax(v, dpp_d<kDppXor1>(v));
+  v = fmax(v, dpp_d<kDppXor2>(v));
+  v = fmax(v, dpp_d<kDppHalfMirror>(v));
+  return fmax(v, dpp_d<kDppMirror>(v));
 }
 
 __device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m, 16);
-  return v;
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppMirror>(v);
 }
 
 // k rounds of a 16-lane argmax over the not-yet-chosen experts (ties to the
@@ -166,9 +197,15 @@ __device__ __forceinline__ void select_k(const RouterArgs& a, const double (&val
 template <int RT, int NB>
 constexpr int route_tile_smem() { return RT * 8 + 16 * NB * 8 + 4 * 16 * NB * 4 + RT * MOE_MAX_TOPK * 4; }
 
-template <int RT, int NB>
+//
+// VW = 1 (16-token tiles only): the tile's selection is spread over the four
+// waves, wave w holding in acc[nb][0] the logits of tokens 4 g + w (its
+// 16-lane group g), so each wave selects four tokens instead of wave 0
+// selecting all sixteen.
+template <int RT, int NB, int VW = 4>
 __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0, unsigned char* smem) {
   static_assert(RT == 16 || RT == 32 || RT == 64, "router tiles are 16, 32 or 64 tokens");
+  static_assert(VW == 4 || (VW == 1 && RT == 16), "spread selection is for 16-token tiles");
   double* s_z = reinterpret_cast<double*>(smem);                                        // [RT]
   unsigned long long* s_mask = reinterpret_cast<unsigned long long*>(smem + RT * 8);      // [16 NB]
   float (*s_p)[16 * NB] = reinterpret_cast<float (*)[16 * NB]>(smem + RT * 8 + 16 * NB * 8);   // [4][16 NB]
@@ -185,8 +222,8 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0,
   for (int nb = 0; nb < NB; ++nb) pp[nb] = 0.f;
 
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int r = wave * 16 + g * 4 + v;   // token within the tile
+  for (int v = 0; v < VW; ++v) {
+    const int r = VW == 1 ? g * 4 + wave : wave * 16 + g * 4 + v;   // token within the tile
     const int t = tile0 + r;
     const bool in_tile = r < RT;           // uniform across the wave
     const bool tok_ok = in_tile && t < a.T;   // uniform across the 16-lane group
@@ -751,8 +788,10 @@ void router_fused_kernel(RouterArgs a) {
 // read zero through the buffer range check, with no memory traffic), a whole
 // chunk (8 k-steps) ahead of the MFMAs, so ~8 KB per wave and ~128 KB per CU
 // are in flight with no barrier in the loop.  float32 sums per chunk, added in
-// float64; the four waves' sums are added in LDS in wave order, then wave 0
-// holds the tile's logits in the layout of route_tile.
+// float64; the four waves' sums are added in LDS in wave order, each wave
+// taking a quarter of the tokens, whose selection it then runs (route_tile's
+// spread layout: the per-token chain of softmax, top-k and log-sum-exp is a
+// quarter as long as on one wave).
 __global__ __launch_bounds__(256) void router_t16_kernel(RouterArgs a) {
   constexpr int RT = 16;
   const int lane = threadIdx.x & 63;
@@ -799,20 +838,16 @@ __global__ __launch_bounds__(256) void router_t16_kernel(RouterArgs a) {
       if (c + 12 < nch) load(xa1, wb1, c + 12);
     }
   }
-  __shared__ double red[3][4][64];
-  if (wave > 0) {
+  // wave w adds the four waves' sums of tokens 4 g + w in wave order and
+  // selects those four tokens (route_tile's spread layout)
+  __shared__ double red[4][4][64];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave - 1][v][lane] = acc[0][v];
-  }
+  for (int v = 0; v < 4; ++v) red[wave][v][lane] = acc[0][v];
   __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int w = 0; w < 3; ++w)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[0][v] += red[w][v][lane];
-  }
+  double sel[1][4];
+  sel[0][0] = ((red[0][wave][lane] + red[1][wave][lane]) + red[2][wave][lane]) + red[3][wave][lane];
   __shared__ __align__(8) unsigned char smem[route_tile_smem<RT, 1>()];
-  route_tile<RT, 1>(a, acc, tile0, smem);
+  route_tile<RT, 1, 1>(a, sel, tile0, smem);
 }
 
 // Selection from float64 logits [T, Epad] for one 64-token tile, one token

@@ -182,15 +182,26 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// In-place inclusive scan of v[0 .. kSegSlots) by kPermThreads threads.
-__device__ __forceinline__ void block_scan_incl(int32_t* v) {
-  for (int off = 1; off < kSegSlots; off <<= 1) {
-    const int t = threadIdx.x;
-    const int add = t >= off ? v[t - off] : 0;
-    __syncthreads();
-    v[t] += add;
-    __syncthreads();
+// In-place inclusive scan of v[0 .. kSegSlots) by one wave (lane l owns
+// entries 8 l .. 8 l + 7: a serial prefix, then a scan of the lane totals);
+// the caller publishes the result with a barrier.
+__device__ __forceinline__ void wave_scan_incl(int32_t* v, int lane) {
+  static_assert(kSegSlots == 8 * kWave, "eight entries a lane");
+  int x[8], run = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    run += v[8 * lane + i];
+    x[i] = run;
   }
+  int incl = run;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  const int base = incl - run;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[8 * lane + i] = base + x[i];
 }
 
 // Workgroup 0's finalisation: counts, kept, the balance loss, the router
@@ -206,16 +217,23 @@ __device__ void finalize_tables(const Problem& p, const float* __restrict__ p_pa
   const int E = p.E, nseg = p.E + p.S;
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   // P_e (sum of the tile sums over all tiles) and the aux term f_e P_e:
-  // thread (q, e), q < G = min(8, 512 / E), adds tiles q, q + G, ... in
-  // order (independent loads, all in flight), then thread e adds the G
-  // partials in order
+  // thread (q, e), q < G = min(64, 512 / E), adds tiles q, q + G, ... in
+  // order (independent loads, all in flight: one batch for up to 16 G
+  // tiles), then thread e adds the G partials in order
   __shared__ double s_ppart[kPermThreads];
   {
-    const int G = min(8, kPermThreads / E), e = t % E, q = t / E;
+    const int G = min(64, kPermThreads / E), e = t % E, q = t / E;
     double ps = 0.0;
     if (q < G) {
-      // eight loads issued together, then added in order
+      // sixteen, then eight loads issued together, then added in order
       int j = q;
+      for (; j + 15 * G < p.ntile; j += 16 * G) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = p_part[static_cast<size_t>(j + u * G) * E + e];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) ps += static_cast<double>(v[u]);
+      }
       for (; j + 7 * G < p.ntile; j += 8 * G) {
         float v[8];
 #pragma unroll
@@ -229,7 +247,7 @@ __device__ void finalize_tables(const Problem& p, const float* __restrict__ p_pa
   }
   __syncthreads();
   if (t < E) {
-    const int G = min(8, kPermThreads / E);
+    const int G = min(64, kPermThreads / E);
     double ps = 0.0;
     for (int q = 0; q < G; ++q) ps += s_ppart[q * E + t];
     s_term[t] = (static_cast<double>(s_cnt[t]) / static_cast<double>(p.A)) * (ps / static_cast<double>(p.T));
@@ -250,7 +268,8 @@ __device__ void finalize_tables(const Problem& p, const float* __restrict__ p_pa
   }
   s_tiles[t] = my_tiles;
   __syncthreads();
-  block_scan_incl(s_tiles);
+  if (wave == 0) wave_scan_incl(s_tiles, lane);
+  __syncthreads();
   if (wave == 0) {
     // aux = E sum_e f_e P_e
     double a = 0.0;

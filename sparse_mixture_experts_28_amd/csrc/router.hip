@@ -133,6 +133,21 @@ __device__ __forceinline__ double max16(double v) {
   return fmax(v, dpp_d<kDppMirror>(v));
 }
 
+__device__ __forceinline__ double sum16d(double v) {
+  v += dpp_d<kDppXor1>(v);
+  v += dpp_d<kDppXor2>(v);
+  v += dpp_d<kDppHalfMirror>(v);
+  return v + dpp_d<kDppMirror>(v);
+}
+
+// sum over a wave: the 16-lane butterfly by DPP, then the exchanges across
+// lane groups (i ^ 16, i ^ 32); every lane ends with the same value
+__device__ __forceinline__ double wave_sum64(double v) {
+  v = sum16d(v);
+  v += __shfl_xor(v, 16, kWave);
+  return v + __shfl_xor(v, 32, kWave);
+}
+
 __device__ __forceinline__ float sum16(float v) {
   v += dpp_f<kDppXor1>(v);
   v += dpp_f<kDppXor2>(v);
@@ -300,9 +315,7 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0,
   }
   if (threadIdx.x < kWave) {
     // z-loss partial of the tile: a fixed butterfly over the tile's tokens
-    double zs = threadIdx.x < ntok ? s_z[threadIdx.x] : 0.0;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) zs += __shfl_xor(zs, m, kWave);
+    const double zs = wave_sum64(threadIdx.x < ntok ? s_z[threadIdx.x] : 0.0);
     if (threadIdx.x == 0) a.z_part[tile] = zs;
   }
   for (int i = threadIdx.x; i < (ec ? 0 : ntok * k); i += blockDim.x) {
@@ -939,9 +952,7 @@ __device__ __forceinline__ void select_tile(const RouterArgs& a, const double (&
   }
   if (threadIdx.x < kWave) {
     // z-loss partial of the tile: a fixed butterfly over the tile's tokens
-    double zs = threadIdx.x < ntok ? s_z[threadIdx.x] : 0.0;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) zs += __shfl_xor(zs, m, kWave);
+    const double zs = wave_sum64(threadIdx.x < ntok ? s_z[threadIdx.x] : 0.0);
     if (threadIdx.x == 0) a.z_part[tile] = zs;
   }
   for (int i = threadIdx.x; i < (ec ? 0 : ntok * k); i += blockDim.x) {
@@ -1006,7 +1017,10 @@ bool router_fused(const Problem& p) { return p.dtype == MOE_BF16 && p.d % 256 ==
 // Tokens per router tile (and per-tile permute table row): 16 on the bf16
 // path with at most 16 experts (T <= 16384); else, when 64-token tiles would
 // give the launch fewer than 256 workgroups, 32 on the other one-launch bf16
-// path and 16 on the float32 path (at most 64 experts); else 64.
+// path and 16 on the float32 path (at most 64 experts); else 64.  (16-token
+// selection tiles for more than 64 experts were measured at the DeepSeek
+// shape: selection 28 -> 21 us, but the permute, whose workgroups each read
+// the whole [tiles, E] count table, 13 -> 27 us.)
 // The 16-token bf16 kernel (at most 16 experts): its workgroups each read
 // every tile's expert counts in the permute, so it is kept to T <= 16384.
 bool router_t16(const Problem& p) { return router_fused(p) && p.E <= 16 && p.T <= 16384; }

@@ -104,6 +104,10 @@ REDUCED = {
     "router_tile64_E40_top3": ("glam", dict(T=16400, d=512, h=256, E=40, k=3, cf=0.0)),
     # one-launch router with 32-token tiles and 64 padded experts, deep d
     "router_tile32_E33_deep_d": ("deepseek", dict(T=300, d=2048, h=256, E=33, k=4, S=0)),
+    # more than 64 experts (split logits, then the selection): a ragged last
+    # tile, expert counts off the 16-lane blocks, capacity, a deep d
+    "router_split_E100_ragged": ("deepseek", dict(T=203, d=512, h=256, E=100, k=6, S=1, cf=1.25)),
+    "router_split_E160_deep_d": ("deepseek", dict(T=77, d=1792, h=256, E=160, k=3, S=0)),
 }
 
 

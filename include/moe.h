@@ -60,7 +60,10 @@ typedef enum {
                                min_capacity < 0, NaN capacity_factor */
   MOE_ERR_UNSUPPORTED = 2,  /* E > MOE_MAX_EXPERTS, k > MOE_MAX_TOPK, n_shared > MOE_MAX_SHARED,
                                d or h not a multiple of 8, pointer not 16-byte aligned, unknown
-                               dtype or activation, or a row count that overflows int32 */
+                               dtype or activation, a row count that overflows int32, or (bf16) x,
+                               the hidden rows R x h, one expert's weight or the router weight
+                               reaching 4 GiB (the kernels address them through 32-bit buffer
+                               ranges); float32: d x 256 bytes or the router weight reaching 4 GiB */
   MOE_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than moe_workspace_bytes(...) */
   MOE_ERR_HIP = 4,          /* a HIP launch reported an error (hipGetLastError) */
   MOE_ERR_SCRATCH = 5       /* moe_forward_noalloc: the problem needs more than

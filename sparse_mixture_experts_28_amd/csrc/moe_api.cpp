@@ -105,6 +105,17 @@ Workspace carve_workspace(const Problem& p, void* base, size_t bytes_available, 
 namespace {
 
 // Shape checks shared by moe_workspace_bytes and moe_forward.
+// The kernels read x, the hidden rows, an expert's weight matrix and the
+// router weight through buffer resources, whose range (and the offsets into
+// it) is 32-bit: each such operand must stay under 4 GiB (bf16; float32 layers
+// read only router tiles and the router weight that way).
+bool fits_buffer_ranges(long long T, long long d, long long h, long long E, long long rows, int dtype) {
+  constexpr long long kRange = 0xffffffffll;
+  if (dtype == MOE_BF16)
+    return T * d * 2 <= kRange && rows * h * 2 <= kRange && h * d * 2 <= kRange && E * d * 2 <= kRange;
+  return 64 * d * 4 <= kRange && E * d * 4 <= kRange;
+}
+
 moe_status_t check_shape(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, int32_t S, int dtype) {
   if (T < 1 || d < 1 || h < 1 || E < 1 || k < 1 || k > E || S < 0) return MOE_ERR_ARG;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
@@ -112,6 +123,7 @@ moe_status_t check_shape(int32_t T, int32_t d, int32_t h, int32_t E, int32_t k, 
   if (d % 8 != 0 || h % 8 != 0) return MOE_ERR_UNSUPPORTED;
   const long long rows = static_cast<long long>(T) * k + static_cast<long long>(S) * T;
   if (rows > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!fits_buffer_ranges(T, d, h, E, rows, dtype)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -156,6 +168,7 @@ moe_status_t check_shape_ec(int32_t T, int32_t d, int32_t h, int32_t E, int32_t 
   if (d % 8 != 0 || h % 8 != 0) return MOE_ERR_UNSUPPORTED;
   const long long rows = static_cast<long long>(E) * C + static_cast<long long>(S) * T;
   if (rows > INT32_MAX || static_cast<long long>(E) * T > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!fits_buffer_ranges(T, d, h, E, rows, dtype)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

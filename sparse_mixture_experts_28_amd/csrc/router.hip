@@ -167,14 +167,14 @@ __device__ __forceinline__ float sum16(float v) {
 // (a NaN in its row of x, in W_g or in a bias) then gets valid indices and
 // NaN weights, and the other tokens are unaffected.
 template <int NB>
-__device__ __forceinline__ void select_k(const RouterArgs& a, const double (&val)[NB], double m, int c, int& my_idx,
-                                         float& my_e, float& esum) {
+__device__ __forceinline__ void select_k(const RouterArgs& a, const double (&val)[NB], const double (&bsel)[NB],
+                                         double m, int c, int& my_idx, float& my_e, float& esum) {
   const int E = a.E, k = a.k;
   double key[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int e = nb * 16 + c;
-    const double kv = a.b_sel && e < E ? val[nb] + static_cast<double>(a.b_sel[e]) : val[nb];
+    const double kv = a.b_sel && e < E ? val[nb] + bsel[nb] : val[nb];
     key[nb] = kv == kv ? kv : -INFINITY;
   }
   constexpr int kNone = 0x7fffffff;
@@ -198,6 +198,32 @@ __device__ __forceinline__ void select_k(const RouterArgs& a, const double (&val
     esum += ej;
     if (c == j) { my_idx = bi; my_e = ej; }
   }
+}
+
+// The lane's router offsets (b_g, 0 without one) and selection-only biases
+// (b_sel) of experts nb * 16 + c, loaded together once per tile rather than
+// one dependent load per expert and token.
+// (The loads are unconditional at a clamped index inside a branch that is
+// uniform across the workgroup, so they are all in flight before the first
+// wait; lanes past E then take 0.)
+template <int NB>
+__device__ __forceinline__ void lane_bias(const float* b, int c, int E, double (&out)[NB]) {
+  float v[NB];
+  if (b != nullptr) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) v[nb] = b[min(nb * 16 + c, E - 1)];
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) v[nb] = 0.f;
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) out[nb] = nb * 16 + c < E ? static_cast<double>(v[nb]) : 0.0;
+}
+
+template <int NB>
+__device__ __forceinline__ void lane_biases(const RouterArgs& a, int c, double (&bg)[NB], double (&bs)[NB]) {
+  lane_bias<NB>(a.b_g, c, a.E, bg);
+  lane_bias<NB>(a.b_sel, c, a.E, bs);
 }
 
 // Selection, weights, probability partials and ranks for one tile of RT
@@ -235,6 +261,8 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0,
   float pp[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) pp[nb] = 0.f;
+  double bg[NB], bs[NB];
+  lane_biases<NB>(a, c, bg, bs);
 
 #pragma unroll
   for (int v = 0; v < VW; ++v) {
@@ -248,7 +276,7 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0,
     for (int nb = 0; nb < NB; ++nb) {
       const int e = nb * 16 + c;
       double l = -INFINITY;
-      if (e < E) l = acc[nb][v] + (a.b_g ? static_cast<double>(a.b_g[e]) : 0.0);
+      if (e < E) l = acc[nb][v] + bg[nb];
       val[nb] = l;
       m = fmax(m, l);
     }
@@ -274,7 +302,7 @@ __device__ void route_tile(const RouterArgs& a, double (&acc)[NB][4], int tile0,
 
     int my_idx;
     float my_e, esum;
-    select_k<NB>(a, val, m, c, my_idx, my_e, esum);
+    select_k<NB>(a, val, bs, m, c, my_idx, my_e, esum);
     if (c < k && in_tile) {
       s_idx[r * MOE_MAX_TOPK + c] = tok_ok ? my_idx : -1;
       if (tok_ok) {
@@ -395,32 +423,33 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(RouterArgs a
   const int tile0 = blockIdx.x * RT;
   const int tb = KW == 1 ? wave : 0, kw = KW == 1 ? 0 : wave;
   const float* X = static_cast<const float*>(a.x);
-  const float* W = static_cast<const float*>(a.W_g);
-
-  const float* xrow[4];
+  const uint32_t rb = static_cast<uint32_t>(a.d) * 4u;   // bytes per row
+  // buffer loads: token rows past T and router rows past E read zero (range
+  // check); the lane offsets stay fixed over the loop and the column offset is
+  // scalar, so no address registers are rewritten while loads are in flight
+  const __amdgpu_buffer_rsrc_t xs =
+      make_rsrc(X + static_cast<size_t>(tile0) * a.d, static_cast<uint32_t>(min(RT, a.T - tile0)) * rb);
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(a.W_g, static_cast<uint32_t>(a.E) * rb);
+  uint32_t xo[4], wo[NB];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int t = tile0 + tb * 16 + g * 4 + v;
-    xrow[v] = X + static_cast<size_t>(t < a.T ? t : 0) * a.d;
-  }
+  for (int v = 0; v < 4; ++v) xo[v] = static_cast<uint32_t>(tb * 16 + g * 4 + v) * rb;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) wo[nb] = static_cast<uint32_t>(nb * 16 + c) * rb;
   double acc[NB][4];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[nb][v] = 0.0;
 
-  // the loads of the next group of four columns are issued before this
-  // group's products, so each wave keeps two groups of loads in flight
+  // The loads of later groups of four columns are issued before this group's
+  // products (a group past d re-reads column 0 and is never folded).
   auto load = [&](int kk, float4 (&xv)[4], float4 (&wv)[NB]) {
+    const uint32_t ko = static_cast<uint32_t>(kk < a.d ? kk : 0) * 4u;
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      xv[v] = kk < a.d ? *reinterpret_cast<const float4*>(xrow[v] + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int v = 0; v < 4; ++v) xv[v] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xs, xo[v], ko, 0));
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int e = nb * 16 + c;
-      wv[nb] = e < a.E && kk < a.d ? *reinterpret_cast<const float4*>(W + static_cast<size_t>(e) * a.d + kk)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int nb = 0; nb < NB; ++nb)
+      wv[nb] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ws, wo[nb], ko, 0));
   };
   auto fold = [&](const float4 (&xv)[4], const float4 (&wv)[NB]) {
 #pragma unroll
@@ -438,46 +467,54 @@ __global__ __launch_bounds__(kRouterThreads) void router_f32_kernel(RouterArgs a
   // four column groups in registers: group i is folded while groups i+1 ..
   // i+3 are in flight (one group ahead left each fold waiting for its loads:
   // at the switch-shaped layer the kernel took 45 us against ~6 us of float64
-  // arithmetic).  Groups past d load zeros and fold nothing in.
+  // arithmetic).  Only groups inside d are folded.
   float4 x0[4], w0[NB], x1[4], w1[NB], x2[4], w2[NB], x3[4], w3[NB];
   constexpr int GS = 4 * KW;                   // columns between a wave's groups
-  int kk = 4 * kw;
+  int kk = __builtin_amdgcn_readfirstlane(4 * kw);   // wave-uniform: the loop exits are scalar branches
   load(kk, x0, w0);
   load(kk + GS, x1, w1);
   load(kk + 2 * GS, x2, w2);
+  // (the scheduling barriers keep each group's loads ahead of the products
+  // that precede them in program order; without them the loads sank below the
+  // products and each fold waited for every load in flight)
   for (; kk < a.d; kk += 4 * GS) {
     load(kk + 3 * GS, x3, w3);
+    __builtin_amdgcn_sched_barrier(0);
     fold(x0, w0);
     if (kk + GS >= a.d) break;
     load(kk + 4 * GS, x0, w0);
+    __builtin_amdgcn_sched_barrier(0);
     fold(x1, w1);
     if (kk + 2 * GS >= a.d) break;
     load(kk + 5 * GS, x1, w1);
+    __builtin_amdgcn_sched_barrier(0);
     fold(x2, w2);
     if (kk + 3 * GS >= a.d) break;
     load(kk + 6 * GS, x2, w2);
+    __builtin_amdgcn_sched_barrier(0);
     fold(x3, w3);
   }
-  constexpr int kRed = KW > 1 ? (KW - 1) * NB * 4 * 64 : 1;
-  __shared__ double red[kRed];
-  if constexpr (KW > 1) {
-    if (wave > 0) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) red[(((wave - 1) * NB + nb) * 4 + v) * 64 + lane] = acc[nb][v];
-    }
-    __syncthreads();
-    if (wave == 0) {
-      for (int w = 1; w < KW; ++w)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[nb][v] += red[(((w - 1) * NB + nb) * 4 + v) * 64 + lane];
-    }
-  }
   __shared__ __align__(8) unsigned char smem[route_tile_smem<RT, NB>()];
-  route_tile<RT, NB>(a, acc, tile0, smem);
+  if constexpr (KW > 1) {
+    // wave w adds the four waves' sums of tokens 4 g + w in wave order and
+    // selects those four tokens (route_tile's spread layout)
+    __shared__ double red[KW * NB * 4 * 64];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[((wave * NB + nb) * 4 + v) * 64 + lane] = acc[nb][v];
+    __syncthreads();
+    double sel[NB][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      double s = red[((0 * NB + nb) * 4 + wave) * 64 + lane];
+      for (int w = 1; w < KW; ++w) s += red[((w * NB + nb) * 4 + wave) * 64 + lane];
+      sel[nb][0] = s;
+    }
+    route_tile<RT, NB, 1>(a, sel, tile0, smem);
+  } else {
+    route_tile<RT, NB>(a, acc, tile0, smem);
+  }
 }
 
 // ---- bf16 inputs, d % 256 == 0: logits kernel + selection kernel ----
@@ -885,13 +922,15 @@ __device__ __forceinline__ void select_tile(const RouterArgs& a, const double (&
   const bool tok_ok = t < a.T;             // uniform across the 16-lane group
   const int E = a.E, k = a.k;
 
+  double bg[NB], bs[NB];
+  lane_biases<NB>(a, c, bg, bs);
   double val[NB];
   double m = -INFINITY;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int e = nb * 16 + c;
     double l = -INFINITY;
-    if (e < E && tok_ok) l = lg[nb] + (a.b_g ? static_cast<double>(a.b_g[e]) : 0.0);
+    if (e < E && tok_ok) l = lg[nb] + bg[nb];
     val[nb] = l;
     m = fmax(m, l);
   }
@@ -913,7 +952,7 @@ __device__ __forceinline__ void select_tile(const RouterArgs& a, const double (&
 
   int my_idx = 0;
   float my_e = 0.f, esum = 0.f;
-  if (!ec) select_k<NB>(a, val, m, c, my_idx, my_e, esum);
+  if (!ec) select_k<NB>(a, val, bs, m, c, my_idx, my_e, esum);
   if (c < k && !ec) {
     s_idx[r * MOE_MAX_TOPK + c] = tok_ok ? my_idx : -1;
     if (tok_ok) {
@@ -968,17 +1007,26 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(RouterArg
   const int c = threadIdx.x & 15;
   const int tile0 = blockIdx.x * kRouterTile;
   const int t = tile0 + (threadIdx.x >> 4);
+  // the split-K partials, added in split order; every expert's load of a
+  // split is issued before any is added (a load-and-add loop per expert waited
+  // for each load in turn: NB memory round trips per split instead of one)
+  const bool tok_ok = t < a.T;
   double lg[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int e = nb * 16 + c;
-    double l = 0.0;
-    if (e < a.E && t < a.T) {
-      // the split-K partials, added in split order
-      l = logits[static_cast<size_t>(t) * Epad + e];
-      for (int q = 1; q < KS; ++q) l += logits[(static_cast<size_t>(q) * a.T + t) * Epad + e];
+    lg[nb] = e < a.E && tok_ok ? logits[static_cast<size_t>(t) * Epad + e] : 0.0;
+  }
+  for (int q = 1; q < KS; ++q) {
+    const double* lq = logits + static_cast<size_t>(q) * a.T * Epad;
+    double v[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int e = nb * 16 + c;
+      v[nb] = e < a.E && tok_ok ? lq[static_cast<size_t>(t) * Epad + e] : 0.0;
     }
-    lg[nb] = l;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) lg[nb] += v[nb];
   }
   select_tile<NB>(a, lg, tile0);
 }

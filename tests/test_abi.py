@@ -161,6 +161,12 @@ def test_null_launch():
     (dict(out=FAKE + 4), moe.MOE_ERR_UNSUPPORTED), (dict(idx=FAKE + 2), moe.MOE_ERR_UNSUPPORTED),
     (dict(workspace=None), moe.MOE_ERR_WORKSPACE), (dict(workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
     (dict(workspace=FAKE + 16), moe.MOE_ERR_WORKSPACE), (dict(T=1 << 30, k=2, d=8, h=8), moe.MOE_ERR_UNSUPPORTED),
+    # 32-bit buffer ranges (bf16): x at 4 GiB; hidden rows R x h at 4 GiB (Mixtral-sized
+    # experts, T = 74899, k = 2); the limits hold just below
+    (dict(T=1 << 19, d=4096, h=8, E=8, k=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=74899, d=4096, h=14336, E=8, k=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=74898, d=4096, h=14336, E=8, k=2, workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
+    (dict(T=8, d=1 << 21, h=1024, E=8, k=2), moe.MOE_ERR_UNSUPPORTED),
     (dict(activation=2), moe.MOE_ERR_UNSUPPORTED), (dict(activation=-1), moe.MOE_ERR_UNSUPPORTED),
     (dict(min_capacity=-1), moe.MOE_ERR_ARG), (dict(z_loss=FAKE + 2), moe.MOE_ERR_UNSUPPORTED),
     (dict(b1=FAKE + 8), moe.MOE_ERR_UNSUPPORTED),

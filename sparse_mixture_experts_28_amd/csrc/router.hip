@@ -113,7 +113,10 @@ __device__ __forceinline__ void argmax_step(double& v, int& i, double& pl) {
   const double ov = dpp_d<CTRL>(v);
   const int oi = dpp_i<CTRL>(i);
   const double op = dpp_d<CTRL>(pl);
-  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; pl = op; }
+  const bool take = (ov > v) | ((ov == v) & (oi < i));   // selects, not an exec-masked branch
+  v = take ? ov : v;
+  i = take ? oi : i;
+  pl = take ? op : pl;
 }
 
 // 16-lane argmax carrying a payload (the winner's plain logit when the
@@ -190,7 +193,12 @@ __device__ __forceinline__ void select_k(const RouterArgs& a, const double (&val
       const int e = nb * 16 + c;
       // experts ascend with nb: the first untaken one is this lane's candidate
       // until a strictly larger key replaces it
-      if (e < E && !((taken >> nb) & 1u) && (bi == kNone || key[nb] > bv)) { bv = key[nb]; bi = e; bl = val[nb]; }
+      // (selects, not a branch: as an if-block the compiler emitted an
+      // exec-masked branch per expert)
+      const bool take = (e < E) & !((taken >> nb) & 1u) & ((bi == kNone) | (key[nb] > bv));
+      bv = take ? key[nb] : bv;
+      bi = take ? e : bi;
+      bl = take ? val[nb] : bl;
     }
     argmax16p(bv, bi, bl);
     if ((bi & 15) == c) taken |= 1u << (bi >> 4);

@@ -173,6 +173,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
 }
 
 constexpr int kPermThreads = 512;
+static_assert(kPermThreads >= kRouterTile * MOE_MAX_TOPK, "one assignment of a router tile a thread");
 constexpr int kSegSlots = 512;   // >= MOE_MAX_EXPERTS + MOE_MAX_SHARED
 
 // Fixed butterfly sums over a wave (the same tree on every call: deterministic).
@@ -204,47 +205,63 @@ __device__ __forceinline__ void wave_scan_incl(int32_t* v, int lane) {
   for (int i = 0; i < 8; ++i) v[8 * lane + i] = base + x[i];
 }
 
+// Workgroup 0's per-thread partial sums for the balance loss and the z-loss,
+// loaded at the start of the kernel so their loads overlap the count
+// table's: thread (q, e), q < G = min(64, 512 / E), adds the probability sums
+// of tiles q, q + G, ... of expert e in order (independent loads, all in
+// flight: one batch for up to 16 G tiles); lane l of wave 1 adds the z-loss
+// sums of tiles l, l + 64, ... in order.
+struct FinalPartials {
+  double ps;   // P_e partial of thread (q, e)
+  double zs;   // z-loss partial of a wave-1 lane
+};
+
+__device__ FinalPartials final_partials(const Problem& p, const float* __restrict__ p_part,
+                                        const double* __restrict__ z_part) {
+  const int E = p.E;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  FinalPartials fp{0.0, 0.0};
+  const int G = min(64, kPermThreads / E), e = t % E, q = t / E;
+  if (q < G) {
+    // sixteen, then eight loads issued together, then added in order
+    int j = q;
+    for (; j + 15 * G < p.ntile; j += 16 * G) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = p_part[static_cast<size_t>(j + u * G) * E + e];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) fp.ps += static_cast<double>(v[u]);
+    }
+    for (; j + 7 * G < p.ntile; j += 8 * G) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = p_part[static_cast<size_t>(j + u * G) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) fp.ps += static_cast<double>(v[u]);
+    }
+    for (; j < p.ntile; j += G) fp.ps += static_cast<double>(p_part[static_cast<size_t>(j) * E + e]);
+  }
+  if (wave == 1) {
+#pragma unroll 4
+    for (int j = lane; j < p.ntile; j += kWave) fp.zs += z_part[j];
+  }
+  return fp;
+}
+
 // Workgroup 0's finalisation: counts, kept, the balance loss, the router
-// z-loss and the grouped-GEMM segment table, from s_cnt (c_e) and s_off
-// (exclusive scan of kept over the experts).  Float64 sums in a fixed order:
-// lane l of a wave takes items l, l + 64, ... in order, then a fixed butterfly.
-__device__ void finalize_tables(const Problem& p, const float* __restrict__ p_part, const double* __restrict__ z_part,
-                                const int32_t* s_cnt, const int32_t* s_off, int32_t* counts, int32_t* kept,
-                                int32_t* seg_base, float* aux_loss, float* z_loss, int32_t* counts_out,
-                                int32_t* kept_out) {
+// z-loss and the grouped-GEMM segment table, from s_cnt (c_e), s_off
+// (exclusive scan of kept over the experts) and the partial sums above.
+// Float64 sums in a fixed order: the G partials of an expert in order, a
+// fixed butterfly over the lanes of a wave.
+__device__ void finalize_tables(const Problem& p, const FinalPartials& fp, const int32_t* s_cnt,
+                                const int32_t* s_off, int32_t* counts, int32_t* kept, int32_t* seg_base,
+                                float* aux_loss, float* z_loss, int32_t* counts_out, int32_t* kept_out) {
   __shared__ double s_term[MOE_MAX_EXPERTS];
   __shared__ int32_t s_tiles[kSegSlots];
   const int E = p.E, nseg = p.E + p.S;
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
-  // P_e (sum of the tile sums over all tiles) and the aux term f_e P_e:
-  // thread (q, e), q < G = min(64, 512 / E), adds tiles q, q + G, ... in
-  // order (independent loads, all in flight: one batch for up to 16 G
-  // tiles), then thread e adds the G partials in order
   __shared__ double s_ppart[kPermThreads];
-  {
-    const int G = min(64, kPermThreads / E), e = t % E, q = t / E;
-    double ps = 0.0;
-    if (q < G) {
-      // sixteen, then eight loads issued together, then added in order
-      int j = q;
-      for (; j + 15 * G < p.ntile; j += 16 * G) {
-        float v[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = p_part[static_cast<size_t>(j + u * G) * E + e];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) ps += static_cast<double>(v[u]);
-      }
-      for (; j + 7 * G < p.ntile; j += 8 * G) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = p_part[static_cast<size_t>(j + u * G) * E + e];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) ps += static_cast<double>(v[u]);
-      }
-      for (; j < p.ntile; j += G) ps += static_cast<double>(p_part[static_cast<size_t>(j) * E + e]);
-    }
-    s_ppart[t] = ps;
-  }
+  s_ppart[t] = fp.ps;
   __syncthreads();
   if (t < E) {
     const int G = min(64, kPermThreads / E);
@@ -278,10 +295,7 @@ __device__ void finalize_tables(const Problem& p, const float* __restrict__ p_pa
     if (lane == 0 && aux_loss) *aux_loss = static_cast<float>(static_cast<double>(E) * a);
   } else if (wave == 1) {
     // z = (1/T) sum of the tiles' sums of squared log-sum-exp
-    double z = 0.0;
-#pragma unroll 4
-    for (int j = lane; j < p.ntile; j += kWave) z += z_part[j];
-    z = wave_sum(z);
+    const double z = wave_sum(fp.zs);
     if (lane == 0 && z_loss) *z_loss = static_cast<float>(z / static_cast<double>(p.T));
   }
   if (t < nseg) {
@@ -313,6 +327,20 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(Problem p, const 
   const int E = p.E, k = p.k;
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int tile = blockIdx.x;
+  // this tile's assignments (at most 64 tokens x 8 = 512, one a thread): their
+  // expert and in-tile rank are loaded first, so the load overlaps the count
+  // table's
+  const int tok0 = tile * p.rtile;
+  const int n_asg = min(p.rtile, p.T - tok0) * k;
+  int my_ex = 0, my_lr = 0;
+  if (t < n_asg) {
+    const size_t a = static_cast<size_t>(tok0) * k + t;
+    my_ex = topk_idx[a];
+    my_lr = local_rank[a];
+  }
+  // workgroup 0 also starts the loads of the loss partials
+  FinalPartials fp{0.0, 0.0};
+  if (tile == 0) fp = final_partials(p, p_part, z_part);
   // 1. per expert, the counts of the tiles before this one (its base rank)
   // and of all tiles (c_e): the [ntile, E] table read in order by all threads
   // (coalesced, every load independent), added into LDS with integer atomics
@@ -368,19 +396,17 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(Problem p, const 
     }
   }
   __syncthreads();
-  // 3. this tile's assignments
-  const int tok0 = tile * p.rtile;
-  const int n = min(p.rtile, p.T - tok0) * k;
-  for (int i = t; i < n; i += kPermThreads) {
-    const size_t a = static_cast<size_t>(tok0) * k + i;
-    const int ex = topk_idx[a];
-    const int rank = s_base[ex] + local_rank[a];
-    const int pos = rank < p.cap ? s_off[ex] + rank : -1;
+  // 3. this tile's assignments (their expert and in-tile rank were loaded at
+  // the start)
+  if (t < n_asg) {
+    const size_t a = static_cast<size_t>(tok0) * k + t;
+    const int rank = s_base[my_ex] + my_lr;
+    const int pos = rank < p.cap ? s_off[my_ex] + rank : -1;
     slot_pos[a] = pos;
-    if (pos >= 0) row_token[pos] = tok0 + i / k;
+    if (pos >= 0) row_token[pos] = tok0 + t / k;
   }
   if (tile == 0)
-    finalize_tables(p, p_part, z_part, s_cnt, s_off, counts, kept, seg_base, aux_loss, z_loss, counts_out, kept_out);
+    finalize_tables(p, fp, s_cnt, s_off, counts, kept, seg_base, aux_loss, z_loss, counts_out, kept_out);
 }
 
 }  // namespace

@@ -209,8 +209,9 @@ def test_full_size_workloads(name):
 
 
 @pytest.mark.parametrize("base,kw", [
-    ("mixtral", dict(T=300, d=256, h=256, E=8, k=2)),               # logits + selection kernels (d % 256 == 0)
+    ("mixtral", dict(T=300, d=256, h=256, E=8, k=2)),               # one-launch bf16 router, 16-token tiles
     ("switch", dict(T=200, d=64, h=128, E=16, k=2, cf=0.0)),         # one-kernel float32 router
+    ("deepseek", dict(T=200, d=256, h=128, E=80, k=4, S=0)),         # split logits + 64-token selection
 ])
 def test_nan_token_row(base, kw):
     """A NaN in one token's row of x: that token's logits are all NaN, which

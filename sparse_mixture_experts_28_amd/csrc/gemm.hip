@@ -465,9 +465,10 @@ void gemm_bf16_mfma_kernel(GemmArgs g) {
 }
 
 // Fix-up of the split tail, in 16-row chunks of the tail tiles strided over
-// the P workgroups.  Each thread owns four consecutive columns of four rows;
-// the S partial tiles are summed in piece order, then bias, the activation
-// (phase 1) and one bf16 rounding, as in the GEMM epilogue.
+// the launch's workgroups (P is the GEMM's grid, which fixed the tail plan).
+// Each thread owns four consecutive columns of four rows; the S partial tiles
+// are summed in piece order, then bias, the activation (phase 1) and one bf16
+// rounding, as in the GEMM epilogue.
 template <int ACT, int BM>
 __global__ __launch_bounds__(256) void gemm_tail_fixup_kernel(GemmArgs g, int P) {
   const SegTableRO st = seg_table_ro(g.seg, g.nseg, g.E);
@@ -507,12 +508,12 @@ __global__ __launch_bounds__(256) void gemm_tail_fixup_kernel(GemmArgs g, int P)
       floatx4 v[4][kFixS];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int rr = r0 + (threadIdx.x >> 6) + 4 * k;
+        // rows past the segment and pieces past S read a row or piece that is
+        // not used: unconditional loads are all in flight together
+        const int rr = min(r0 + (threadIdx.x >> 6) + 4 * k, rows - 1 - m0);
 #pragma unroll
         for (int p = 0; p < kFixS; ++p)
-          v[k][p] = m0 + rr < rows && p0 + p < tp.S
-                        ? *reinterpret_cast<const floatx4*>(part + (static_cast<size_t>(p0 + p) * BM + rr) * kBN + c)
-                        : floatx4{0.f, 0.f, 0.f, 0.f};
+          v[k][p] = *reinterpret_cast<const floatx4*>(part + (static_cast<size_t>(min(p0 + p, tp.S - 1)) * BM + rr) * kBN + c);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k)
@@ -865,11 +866,13 @@ hipError_t launch_expert_ffn(const Problem& p, const void* x, const void* W1, co
     grid = (grid + 7) / 8 * 8;
     const dim3 gd(grid), bd(256);
     // the fix-up runs right after the GEMM on the same stream; it returns at
-    // once when the tail was not split
+    // once when the tail was not split.  Four workgroups a CU, so that a tail
+    // of up to 4 P 16-row chunks is one chunk a workgroup (Mixtral-shaped
+    // phase 2: 768 chunks; 18 -> 15 us against one workgroup a CU).
 #define MOE_GEMM_LAUNCH(ACT_, BM_)                                                          \
   do {                                                                                      \
     hipLaunchKernelGGL((gemm_bf16_mfma_kernel<ACT_, BM_>), gd, bd, 0, st, g);               \
-    hipLaunchKernelGGL((gemm_tail_fixup_kernel<ACT_, BM_>), gd, bd, 0, st, g, grid);        \
+    hipLaunchKernelGGL((gemm_tail_fixup_kernel<ACT_, BM_>), dim3(4 * grid), bd, 0, st, g, grid); \
   } while (0)
 #define MOE_GEMM_LAUNCH_BM(BM_)                                                             \
   do {                                                                                      \

@@ -581,7 +581,8 @@ void gemm_mx_kernel(MxArgs g) {
 }
 
 // Fix-up of the split tail, in 16-row chunks of the tail tiles strided over
-// the P workgroups.  Each thread owns four consecutive columns of four rows;
+// the launch's workgroups (four a CU; P is the GEMM's grid, which fixed the
+// tail plan).  Each thread owns four consecutive columns of four rows;
 // the S partial tiles are summed in piece order, then the bias, the
 // activation (phase 1) and the store as in the GEMM epilogue: phase 1 MX
 // blocks of 32 columns (8 lanes a block), phase 2 bf16.  Tile heights as in
@@ -623,12 +624,13 @@ __global__ __launch_bounds__(256) void mx_tail_fixup_kernel(MxArgs g, int P) {
       floatx4 v[4][kFixS];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int rr = r0 + (threadIdx.x >> 6) + 4 * k;
+        // rows past the segment and pieces past S read a row or piece that is
+        // not used: unconditional loads are all in flight together
+        const int rr = min(r0 + (threadIdx.x >> 6) + 4 * k, rows - 1 - m0);
 #pragma unroll
         for (int p = 0; p < kFixS; ++p)
-          v[k][p] = m0 + rr < rows && p0 + p < tp.S
-                        ? *reinterpret_cast<const floatx4*>(part + (static_cast<size_t>(p0 + p) * PBM + rr) * kMxBN + c)
-                        : floatx4{0.f, 0.f, 0.f, 0.f};
+          v[k][p] = *reinterpret_cast<const floatx4*>(part + (static_cast<size_t>(min(p0 + p, tp.S - 1)) * PBM + rr) *
+                                                                 kMxBN + c);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k)
@@ -727,7 +729,7 @@ hipError_t launch_expert_ffn_mx(const Problem& p, const MxWeights& w, const Work
   do {                                                                                                   \
     if (sg4) hipLaunchKernelGGL((gemm_mx_kernel<ACT_, BM0_, BM1_, 4>), dim3(grid), dim3(256), 0, st, g); \
     else hipLaunchKernelGGL((gemm_mx_kernel<ACT_, BM0_, BM1_, 1>), dim3(grid), dim3(256), 0, st, g);     \
-    hipLaunchKernelGGL((mx_tail_fixup_kernel<ACT_, BM0_, BM1_>), dim3(grid), dim3(256), 0, st, g, grid); \
+    hipLaunchKernelGGL((mx_tail_fixup_kernel<ACT_, BM0_, BM1_>), dim3(4 * grid), dim3(256), 0, st, g, grid); \
   } while (0)
   // 256-row tiles, or per segment 128 or 192 rows (the table says which)
   if (!p.gemm_mixed) {

@@ -142,13 +142,25 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(EcArgs a) {
     else return col[t] + 0.0;
   };
 
-  // 1. stage, min and max
+  // 1. stage, min and max: eight tokens a thread per round, their loads
+  // issued together (at a clamped index: a load under the t < T condition
+  // would be waited for at once)
   double lo = INFINITY, hi = -INFINITY;
-  for (int t = threadIdx.x; t < T; t += kEcThreads) {
-    const double v = col[t] + 0.0;
-    if constexpr (kStaged) s_val[t] = v;
-    lo = fmin(lo, v);
-    hi = fmax(hi, v);
+  constexpr int kStageU = 8;
+  for (int t0 = threadIdx.x; t0 < T; t0 += kStageU * kEcThreads) {
+    double v[kStageU];
+#pragma unroll
+    for (int u = 0; u < kStageU; ++u) v[u] = col[min(t0 + u * kEcThreads, T - 1)];
+#pragma unroll
+    for (int u = 0; u < kStageU; ++u) {
+      const int t = t0 + u * kEcThreads;
+      if (t < T) {
+        const double x = v[u] + 0.0;
+        if constexpr (kStaged) s_val[t] = x;
+        lo = fmin(lo, x);
+        hi = fmax(hi, x);
+      }
+    }
   }
   lo = wave_min(lo);
   hi = wave_max(hi);

@@ -261,6 +261,10 @@ def test_ec_optional_pointers():
     (dict(x=FAKE + 8), moe.MOE_ERR_UNSUPPORTED), (dict(workspace=None), moe.MOE_ERR_WORKSPACE),
     (dict(workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
     (dict(T=1 << 24, C=1 << 24, E=256, d=8, h=8), moe.MOE_ERR_UNSUPPORTED),
+    # 32-bit buffer ranges (bf16): x at 4 GiB; hidden rows E C x h at 4 GiB
+    (dict(T=1 << 19, C=64, E=8, d=4096, h=8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 17, C=1 << 17, E=8, d=8, h=2048), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 17, C=(1 << 17) - 1, E=8, d=8, h=2048, workspace_bytes=1024), moe.MOE_ERR_WORKSPACE),
 ])
 def test_ec_rejected_on_host(kw, code):
     assert call_ec(**kw) == code

@@ -77,7 +77,24 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Problem p, int32_t* 
   if (t < E) {
     int run = 0;
     double pr = 0.0;
-    for (int q = 0; q < C; ++q) {
+    int q = 0;
+    // eight chunks' reads issued together, then used in chunk order
+    for (; q + 8 <= C; q += 8) {
+      int v[8];
+      double w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        v[u] = s_sum[(q + u) * E + t];
+        w[u] = s_psum[(q + u) * E + t];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s_sum[(q + u) * E + t] = run;
+        run += v[u];
+        pr += w[u];
+      }
+    }
+    for (; q < C; ++q) {
       const int v = s_sum[q * E + t];
       s_sum[q * E + t] = run;
       run += v;
